@@ -1,0 +1,392 @@
+// kvq.hip -- the C ABI of libkvq.so: host-side validation, dispatch and
+// launches of the append, split-K decode and combine kernels (gfx950).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/kvq.h"
+#include "kvq_append.hpp"
+#include "kvq_decode.hpp"
+
+using namespace kvq;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok()
+{
+    g_err[0] = 0;
+    return KVQ_OK;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool quantized(int bits) { return bits == 8 || bits == 4; }
+
+bool bits_pair_ok(int kb, int vb)
+{
+    if (kb == 32 || vb == 32) return kb == 32 && vb == 32;
+    if (kb == 16 || vb == 16) return kb == 16 && vb == 16;
+    return quantized(kb) && quantized(vb);
+}
+
+bool per_row(const kvq_cache *c) { return c->group_size == c->n_kv_heads * c->head_dim && c->group_size != c->head_dim; }
+
+constexpr size_t kMaxLds = 64 * 1024;
+
+// Geometry checks shared by every entry point (no pointer is read).
+int check_geometry(const kvq_cache *c)
+{
+    if (!c) return fail(KVQ_ERR_NULL, "cache descriptor is NULL");
+    if (c->batch < 1 || c->n_kv_heads < 1 || c->capacity < 1)
+        return fail(KVQ_ERR_SHAPE, "batch (%d), n_kv_heads (%d) and capacity (%d) must be >= 1", c->batch,
+                    c->n_kv_heads, c->capacity);
+    if (c->head_dim != 64 && c->head_dim != 128)
+        return fail(KVQ_ERR_SHAPE, "head_dim %d unsupported (64 or 128)", c->head_dim);
+    if ((long long)c->batch * c->n_kv_heads > 65535)
+        return fail(KVQ_ERR_SHAPE, "batch * n_kv_heads = %lld exceeds 65535", (long long)c->batch * c->n_kv_heads);
+    if (!bits_pair_ok(c->k_bits, c->v_bits))
+        return fail(KVQ_ERR_BITS, "unsupported widths k_bits=%d v_bits=%d", c->k_bits, c->v_bits);
+    if (quantized(c->k_bits)) {
+        const int g = c->group_size;
+        const bool in_head = g >= 32 && g % 32 == 0 && c->head_dim % g == 0;
+        if (!in_head && !(g == c->n_kv_heads * c->head_dim))
+            return fail(KVQ_ERR_GROUP, "group_size %d must divide head_dim %d (multiple of 32) or equal n_kv_heads*head_dim",
+                        g, c->head_dim);
+    }
+    if (c->n_anchor < 0 || c->window < 0)
+        return fail(KVQ_ERR_WINDOW, "n_anchor (%d) and window (%d) must be >= 0", c->n_anchor, c->window);
+    if (c->window == 0 && c->n_anchor != 0)
+        return fail(KVQ_ERR_WINDOW, "n_anchor %d without a window", c->n_anchor);
+    if (c->window > 0 && (long long)c->n_anchor + c->window != c->capacity)
+        return fail(KVQ_ERR_WINDOW, "capacity %d != n_anchor %d + window %d", c->capacity, c->n_anchor, c->window);
+    return KVQ_OK;
+}
+
+int check_pointers(const kvq_cache *c)
+{
+    if (!c->k_codes || !c->v_codes) return fail(KVQ_ERR_NULL, "k_codes / v_codes is NULL");
+    if (!aligned(c->k_codes, 16) || !aligned(c->v_codes, 16))
+        return fail(KVQ_ERR_ALIGN, "k_codes / v_codes must be 16-byte aligned");
+    if (quantized(c->k_bits) && !c->k_scales) return fail(KVQ_ERR_NULL, "k_scales is NULL for a quantized key side");
+    if (quantized(c->v_bits) && !c->v_scales) return fail(KVQ_ERR_NULL, "v_scales is NULL for a quantized value side");
+    if ((c->k_scales && !aligned(c->k_scales, 2)) || (c->v_scales && !aligned(c->v_scales, 2)))
+        return fail(KVQ_ERR_ALIGN, "scale buffers must be 2-byte aligned");
+    return KVQ_OK;
+}
+
+int groups_per_head(const kvq_cache *c) { return per_row(c) ? 1 : c->head_dim / c->group_size; }
+
+int check_heads(const kvq_cache *c, int n_q_heads)
+{
+    if (n_q_heads < 1 || n_q_heads % c->n_kv_heads != 0)
+        return fail(KVQ_ERR_SHAPE, "n_q_heads %d must be a positive multiple of n_kv_heads %d", n_q_heads, c->n_kv_heads);
+    const int G = n_q_heads / c->n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(KVQ_ERR_SHAPE, "query heads per KV head %d unsupported (1, 2, 4, 8)", G);
+    return KVQ_OK;
+}
+
+size_t lds_bytes(const kvq_cache *c, int G, int chunk)
+{
+    const int kg = quantized(c->k_bits) ? groups_per_head(c) : 1;
+    const int vg = quantized(c->v_bits) ? groups_per_head(c) : 1;
+    return (size_t)decode_smem(G, c->head_dim, c->k_bits, c->v_bits, chunk, kg, vg).total;
+}
+
+int max_len_of(const kvq_cache *c, int max_seq_len) { return max_seq_len < c->capacity ? max_seq_len : c->capacity; }
+
+int auto_chunk(const kvq_cache *c, int n_q_heads, int max_seq_len)
+{
+    const int G = n_q_heads / c->n_kv_heads;
+    const long long units = (long long)c->batch * c->n_kv_heads;
+    const int L = max_len_of(c, max_seq_len);
+    // The largest chunk that fits the LDS budget and still gives >= 8
+    // workgroups per CU over 256 CUs; when even 64-slot chunks cannot, the
+    // smallest chunk (most workgroups).
+    for (int ch = 4096; ch >= 64; ch >>= 1) {
+        if (lds_bytes(c, G, ch) > kMaxLds) continue;
+        if (units * ((L + ch - 1) / ch) >= 2048) return ch;
+    }
+    return 64;
+}
+
+using DecodeFn = void (*)(DecodeParams);
+
+template <int KB, int VB, int HD>
+DecodeFn pick_g(int G)
+{
+    switch (G) {
+    case 1: return decode_split_kernel<KB, VB, HD, 1, 4, 4>;
+    case 2: return decode_split_kernel<KB, VB, HD, 2, 4, 4>;
+    case 4: return decode_split_kernel<KB, VB, HD, 4, 4, 4>;
+    case 8: return decode_split_kernel<KB, VB, HD, 8, 4, 4>;
+    }
+    return nullptr;
+}
+
+template <int KB, int VB>
+DecodeFn pick_hd(int hd, int G)
+{
+    return hd == 64 ? pick_g<KB, VB, 64>(G) : pick_g<KB, VB, 128>(G);
+}
+
+DecodeFn pick_decode(int kb, int vb, int hd, int G)
+{
+    if (kb == 32) return pick_hd<32, 32>(hd, G);
+    if (kb == 16) return pick_hd<16, 16>(hd, G);
+    if (kb == 8 && vb == 8) return pick_hd<8, 8>(hd, G);
+    if (kb == 8 && vb == 4) return pick_hd<8, 4>(hd, G);
+    if (kb == 4 && vb == 4) return pick_hd<4, 4>(hd, G);
+    if (kb == 4 && vb == 8) return pick_hd<4, 8>(hd, G);
+    return nullptr;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t ws_bytes(int batch, int n_q_heads, int head_dim, int n_chunks)
+{
+    const size_t P = (size_t)batch * n_q_heads;
+    return align256(P * n_chunks * 2 * sizeof(float)) + P * n_chunks * head_dim * sizeof(float);
+}
+
+int hip_status(const char *what)
+{
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+} // namespace
+
+extern "C" {
+
+size_t kvq_bytes_per_token(int k_bits, int v_bits, int n_kv_heads, int head_dim, int group_size)
+{
+    if (n_kv_heads <= 0 || head_dim <= 0) return 0;
+    const size_t D = (size_t)n_kv_heads * head_dim;
+    size_t total = 0;
+    const int sides[2] = {k_bits, v_bits};
+    for (int s : sides) {
+        if (s != 32 && s != 16 && s != 8 && s != 4) return 0;
+        if ((D * s) % 8) return 0;
+        total += D * s / 8;
+        if (s < 16) {
+            if (group_size <= 0 || D % (size_t)group_size) return 0;
+            total += 2 * (D / group_size);
+        }
+    }
+    return total;
+}
+
+int kvq_cache_sizes(const kvq_cache *c, size_t *kc, size_t *vc, size_t *ksb, size_t *vsb)
+{
+    int st = check_geometry(c);
+    if (st) return st;
+    const size_t rows = (size_t)c->batch * c->n_kv_heads * c->capacity;
+    const size_t sc = per_row(c) ? (size_t)c->batch * c->capacity : rows * groups_per_head(c);
+    if (kc) *kc = rows * c->head_dim * c->k_bits / 8;
+    if (vc) *vc = rows * c->head_dim * c->v_bits / 8;
+    if (ksb) *ksb = quantized(c->k_bits) ? sc * 2 : 0;
+    if (vsb) *vsb = quantized(c->v_bits) ? sc * 2 : 0;
+    return ok();
+}
+
+int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n_new, const int32_t *start_pos,
+               void *stream)
+{
+    int st = check_geometry(c);
+    if (st) return st;
+    if (n_new < 0) return fail(KVQ_ERR_SHAPE, "n_new %d < 0", n_new);
+    if (n_new == 0) return ok();
+    if ((st = check_pointers(c))) return st;
+    if (!k_new || !v_new || !start_pos) return fail(KVQ_ERR_NULL, "k_new / v_new / start_pos is NULL");
+    if (!aligned(k_new, 16) || !aligned(v_new, 16)) return fail(KVQ_ERR_ALIGN, "k_new / v_new must be 16-byte aligned");
+    if (!aligned(start_pos, 4)) return fail(KVQ_ERR_ALIGN, "start_pos must be 4-byte aligned");
+    const long long rows = (long long)c->batch * n_new;
+    if (rows > 0x7FFFFFFFLL) return fail(KVQ_ERR_SHAPE, "batch * n_new too large");
+
+    AppendParams p;
+    p.src[0] = k_new;
+    p.src[1] = v_new;
+    p.codes[0] = static_cast<uint8_t *>(c->k_codes);
+    p.codes[1] = static_cast<uint8_t *>(c->v_codes);
+    p.scales[0] = static_cast<uint16_t *>(c->k_scales);
+    p.scales[1] = static_cast<uint16_t *>(c->v_scales);
+    p.bits[0] = c->k_bits;
+    p.bits[1] = c->v_bits;
+    p.start_pos = start_pos;
+    p.n_kv_heads = c->n_kv_heads;
+    p.head_dim = c->head_dim;
+    p.capacity = c->capacity;
+    p.n_new = n_new;
+    p.n_anchor = c->n_anchor;
+    p.window = c->window;
+    p.per_row = per_row(c) && quantized(c->k_bits) ? 1 : 0;
+    p.group = p.per_row ? c->n_kv_heads * c->head_dim : (quantized(c->k_bits) ? c->group_size : c->head_dim);
+    const int R = c->n_kv_heads * c->head_dim;
+    const int passes = p.per_row ? 1 : (R + APPEND_SPAN - 1) / APPEND_SPAN;
+    dim3 grid((unsigned)rows, (unsigned)passes, 2);
+    hipLaunchKernelGGL(append_kernel, grid, dim3(APPEND_THREADS), 0, static_cast<hipStream_t>(stream), p);
+    return hip_status("append_kernel launch");
+}
+
+int kvq_chunk_tokens(const kvq_cache *c, int n_q_heads, int max_seq_len)
+{
+    int st = check_geometry(c);
+    if (st) return st;
+    if ((st = check_heads(c, n_q_heads))) return st;
+    if (max_seq_len < 1) return fail(KVQ_ERR_ARG, "max_seq_len %d < 1", max_seq_len);
+    ok();
+    return auto_chunk(c, n_q_heads, max_seq_len);
+}
+
+static int resolve_chunk(const kvq_cache *c, int n_q_heads, int max_seq_len, int chunk_tokens, int *chunk, int *n_chunks)
+{
+    int st = check_geometry(c);
+    if (st) return st;
+    if ((st = check_heads(c, n_q_heads))) return st;
+    if (max_seq_len < 1) return fail(KVQ_ERR_ARG, "max_seq_len %d < 1", max_seq_len);
+    int ch = chunk_tokens;
+    if (ch == 0) ch = auto_chunk(c, n_q_heads, max_seq_len);
+    if (ch < 64 || ch > 8192 || ch % 64 != 0)
+        return fail(KVQ_ERR_ARG, "chunk_tokens %d must be a multiple of 64 in [64, 8192]", ch);
+    const int G = n_q_heads / c->n_kv_heads;
+    if (lds_bytes(c, G, ch) > kMaxLds)
+        return fail(KVQ_ERR_ARG, "chunk_tokens %d needs %zu bytes of LDS (limit %zu)", ch, lds_bytes(c, G, ch), kMaxLds);
+    const int L = max_len_of(c, max_seq_len);
+    *chunk = ch;
+    *n_chunks = (L + ch - 1) / ch;
+    return KVQ_OK;
+}
+
+size_t kvq_workspace_bytes(const kvq_cache *c, int n_q_heads, int max_seq_len, int chunk_tokens)
+{
+    int ch, nc;
+    if (resolve_chunk(c, n_q_heads, max_seq_len, chunk_tokens, &ch, &nc)) return 0;
+    ok();
+    return ws_bytes(c->batch, n_q_heads, c->head_dim, nc);
+}
+
+int kvq_decode_partials(const kvq_cache *c, const float *q, int n_q_heads, const int32_t *seq_len, int max_seq_len,
+                        float softmax_scale, int chunk_tokens, void *workspace, size_t workspace_bytes, void *stream)
+{
+    int ch, nc;
+    int st = resolve_chunk(c, n_q_heads, max_seq_len, chunk_tokens, &ch, &nc);
+    if (st) return st;
+    if ((st = check_pointers(c))) return st;
+    if (!q || !seq_len || !workspace) return fail(KVQ_ERR_NULL, "q / seq_len / workspace is NULL");
+    if (!aligned(q, 16)) return fail(KVQ_ERR_ALIGN, "q must be 16-byte aligned");
+    if (!aligned(seq_len, 4)) return fail(KVQ_ERR_ALIGN, "seq_len must be 4-byte aligned");
+    if (!aligned(workspace, 256)) return fail(KVQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+    const size_t need = ws_bytes(c->batch, n_q_heads, c->head_dim, nc);
+    if (workspace_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    if (!std::isfinite(softmax_scale) || softmax_scale < 0.0f)
+        return fail(KVQ_ERR_ARG, "softmax_scale must be finite and >= 0");
+    const float scale = softmax_scale == 0.0f ? 1.0f / std::sqrt((float)c->head_dim) : softmax_scale;
+    const int G = n_q_heads / c->n_kv_heads;
+    DecodeFn fn = pick_decode(c->k_bits, c->v_bits, c->head_dim, G);
+    if (!fn) return fail(KVQ_ERR_BITS, "no kernel for k_bits=%d v_bits=%d", c->k_bits, c->v_bits);
+
+    const size_t P = (size_t)c->batch * n_q_heads;
+    DecodeParams p;
+    p.k_codes = static_cast<const uint8_t *>(c->k_codes);
+    p.v_codes = static_cast<const uint8_t *>(c->v_codes);
+    p.k_scales = static_cast<const uint16_t *>(c->k_scales);
+    p.v_scales = static_cast<const uint16_t *>(c->v_scales);
+    p.q = q;
+    p.seq_len = seq_len;
+    p.ws_ml = static_cast<float *>(workspace);
+    p.ws_acc = reinterpret_cast<float *>(static_cast<char *>(workspace) + align256(P * nc * 2 * sizeof(float)));
+    p.n_kv_heads = c->n_kv_heads;
+    p.capacity = c->capacity;
+    p.max_len = max_len_of(c, max_seq_len);
+    p.chunk = ch;
+    p.n_chunks = nc;
+    const bool pr = per_row(c);
+    const int gph = groups_per_head(c);
+    p.kg = quantized(c->k_bits) ? gph : 1;
+    p.vg = quantized(c->v_bits) ? gph : 1;
+    p.k_group = p.v_group = pr ? c->n_kv_heads * c->head_dim : (quantized(c->k_bits) ? c->group_size : c->head_dim);
+    if (pr) {
+        p.k_sc_b = p.v_sc_b = c->capacity;
+        p.k_sc_h = p.v_sc_h = 0;
+        p.k_sc_t = p.v_sc_t = 1;
+    } else {
+        p.k_sc_b = p.v_sc_b = (long long)c->n_kv_heads * c->capacity * gph;
+        p.k_sc_h = p.v_sc_h = (long long)c->capacity * gph;
+        p.k_sc_t = p.v_sc_t = gph;
+    }
+    p.qk_scale = scale * 1.4426950408889634f;   // log2(e): scores kept in log2 units
+    const size_t lds = lds_bytes(c, G, ch);
+    dim3 grid((unsigned)nc, (unsigned)(c->batch * c->n_kv_heads));
+    hipLaunchKernelGGL(fn, grid, dim3(DEC_THREADS), lds, static_cast<hipStream_t>(stream), p);
+    return hip_status("decode_split_kernel launch");
+}
+
+int kvq_combine(int batch, int n_q_heads, int head_dim, int n_chunks, const void *workspace, size_t workspace_bytes,
+                float *out, void *stream)
+{
+    if (batch < 1 || n_q_heads < 1 || n_chunks < 1) return fail(KVQ_ERR_SHAPE, "batch, n_q_heads, n_chunks must be >= 1");
+    if (head_dim != 64 && head_dim != 128) return fail(KVQ_ERR_SHAPE, "head_dim %d unsupported", head_dim);
+    if (!workspace || !out) return fail(KVQ_ERR_NULL, "workspace / out is NULL");
+    if (!aligned(workspace, 256)) return fail(KVQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (!aligned(out, 16)) return fail(KVQ_ERR_ALIGN, "out must be 16-byte aligned");
+    const size_t need = ws_bytes(batch, n_q_heads, head_dim, n_chunks);
+    if (workspace_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    const size_t P = (size_t)batch * n_q_heads;
+    if (P > 0x7FFFFFFFull) return fail(KVQ_ERR_SHAPE, "too many rows");
+    const float *ml = static_cast<const float *>(workspace);
+    const float *acc = reinterpret_cast<const float *>(static_cast<const char *>(workspace) + align256(P * n_chunks * 2 * sizeof(float)));
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)P), dim3(head_dim), 0, static_cast<hipStream_t>(stream), ml, acc,
+                       out, n_chunks, head_dim);
+    return hip_status("combine_kernel launch");
+}
+
+int kvq_decode_attn(const kvq_cache *c, const float *q, int n_q_heads, const int32_t *seq_len, int max_seq_len,
+                    float softmax_scale, int chunk_tokens, float *out, void *workspace, size_t workspace_bytes,
+                    void *stream)
+{
+    int ch, nc;
+    int st = resolve_chunk(c, n_q_heads, max_seq_len, chunk_tokens, &ch, &nc);
+    if (st) return st;
+    if (!out) return fail(KVQ_ERR_NULL, "out is NULL");
+    if (!aligned(out, 16)) return fail(KVQ_ERR_ALIGN, "out must be 16-byte aligned");
+    st = kvq_decode_partials(c, q, n_q_heads, seq_len, max_seq_len, softmax_scale, ch, workspace, workspace_bytes, stream);
+    if (st) return st;
+    return kvq_combine(c->batch, n_q_heads, c->head_dim, nc, workspace, workspace_bytes, out, stream);
+}
+
+const char *kvq_status_str(int status)
+{
+    switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_NULL: return "required pointer is NULL";
+    case KVQ_ERR_BITS: return "unsupported k_bits / v_bits";
+    case KVQ_ERR_SHAPE: return "invalid shape";
+    case KVQ_ERR_GROUP: return "invalid group_size";
+    case KVQ_ERR_WINDOW: return "invalid n_anchor / window";
+    case KVQ_ERR_WORKSPACE: return "workspace too small";
+    case KVQ_ERR_ALIGN: return "misaligned pointer";
+    case KVQ_ERR_HIP: return "HIP launch failed";
+    case KVQ_ERR_ARG: return "argument out of range";
+    }
+    return "unknown status";
+}
+
+const char *kvq_last_error(void) { return g_err; }
+
+} // extern "C"

@@ -1,0 +1,224 @@
+/*
+ * kvq.h -- quantized KV cache for single-query decode attention on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The library stores, for every sequence and KV head, the K and V rows of
+ * each position either as float32 / fp16 values or as symmetric integer
+ * codes (8-bit, or 4-bit packed two per byte) with one fp16 scale per group
+ * of values, and runs decode attention over that cache without ever
+ * expanding it in memory.
+ *
+ * Sources for the operations (page, then the part of it):
+ *   - mni-ml page (donniechu.com), "how the KV cache creates speed": each
+ *     decode step computes one new K and one new V row per head and reuses
+ *     the cached rows; "why INT8 loses no speed": 1 byte per element instead
+ *     of 4, symmetric scaling, decode limited by memory bandwidth.
+ *   - TinyLoop "KV Cache 模式": five-modes table (FP16 KV; INT8 KV = int8
+ *     vectors + one FP16 scale per head; INT4 symmetric with 15 levels,
+ *     nibble-packed) and the memory-formula table (bytes per token).
+ *   - KVSplit page (hada.io): key and value bit widths chosen separately
+ *     (K8V8, K8V4, K4V4; K4V8 as a demo).
+ *   - on-device page (gyaansetu.com): sliding-window eviction keeping the
+ *     first 64 tokens as anchors and the 1536 most recent ones.
+ *   - aihot.vn KV Cache page: Q is only used at the current position.
+ *
+ * Conventions for every entry point:
+ *   - All buffer pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or synchronizes; every call only
+ *     enqueues kernels on `stream` (a hipStream_t passed as void*, NULL for
+ *     the default stream) and returns.
+ *   - Return value: KVQ_OK when the work was enqueued; a negative KVQ_ERR_*
+ *     when a host-side check failed (then nothing was launched), or
+ *     KVQ_ERR_HIP when HIP refused the launch.  kvq_last_error() describes
+ *     the most recent failure of the calling thread.
+ *   - Values that live in device memory (start positions, sequence lengths)
+ *     cannot be checked on the host; their preconditions are stated per call
+ *     and out-of-range values are clamped or skipped, never read or written
+ *     outside the buffers.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define KVQ_OK             0
+#define KVQ_ERR_NULL      -1  /* a required pointer is NULL                         */
+#define KVQ_ERR_BITS      -2  /* unsupported k_bits / v_bits combination             */
+#define KVQ_ERR_SHAPE     -3  /* batch, heads, head_dim, capacity or count invalid  */
+#define KVQ_ERR_GROUP     -4  /* group_size invalid for the widths and head_dim      */
+#define KVQ_ERR_WINDOW    -5  /* n_anchor / window inconsistent with capacity        */
+#define KVQ_ERR_WORKSPACE -6  /* workspace smaller than kvq_workspace_bytes()        */
+#define KVQ_ERR_ALIGN     -7  /* a pointer is not aligned as documented              */
+#define KVQ_ERR_HIP       -8  /* the HIP runtime refused the launch                  */
+#define KVQ_ERR_ARG       -9  /* another argument out of range (scale, chunk, ...)   */
+
+/* ---- the cache descriptor -------------------------------------------- */
+/*
+ * Geometry and storage of one layer's cache.  The struct is read during the
+ * call only; the buffers it points to must stay allocated while kernels
+ * enqueued with it may still run.
+ *
+ * Widths (k_bits, v_bits), per side:
+ *   32 = float32 rows, 16 = fp16 rows (round to nearest even),
+ *    8 = int8 codes in [-127, 127], 4 = int4 codes in [-7, 7], two per byte,
+ *        element 2j in the low nibble of byte j, two's complement.
+ *   Supported pairs: (32,32), (16,16) and any pair from {8,4} x {8,4}.
+ *
+ * group_size: values per fp16 scale on the quantized sides.  Either a
+ *   divisor of head_dim that is a multiple of 32 (one scale per group inside
+ *   a head; head_dim itself is one scale per head and position, the TinyLoop
+ *   INT8-KV layout), or n_kv_heads * head_dim (one scale per position over
+ *   all heads).  Ignored when both sides are 16/32-bit.
+ *
+ * Window (on-device page): n_anchor = window = 0 stores position p in slot
+ *   p (capacity = largest position + 1).  Otherwise capacity must equal
+ *   n_anchor + window; position p < n_anchor lives in slot p and later
+ *   positions cycle through slots n_anchor .. capacity-1
+ *   (slot = n_anchor + (p - n_anchor) % window), so the cache always holds
+ *   the anchors and the `window` most recent positions.
+ *
+ * Layouts (row-major, innermost last; R = head_dim * bits / 8 bytes):
+ *   k_codes / v_codes : [batch][n_kv_heads][capacity][R] bytes, 16-byte aligned
+ *   k_scales / v_scales (quantized sides only, NULL otherwise), fp16 bits:
+ *       groups inside a head : [batch][n_kv_heads][capacity][head_dim/group_size]
+ *       one scale per position: [batch][capacity]
+ *     2-byte aligned.
+ * kvq_cache_sizes() returns the byte size of each buffer.
+ */
+typedef struct kvq_cache {
+    int32_t batch;
+    int32_t n_kv_heads;
+    int32_t head_dim;     /* 64 or 128 */
+    int32_t capacity;     /* slots per (sequence, KV head) */
+    int32_t k_bits;
+    int32_t v_bits;
+    int32_t group_size;
+    int32_t n_anchor;
+    int32_t window;
+    void *k_codes;
+    void *v_codes;
+    void *k_scales;
+    void *v_scales;
+} kvq_cache;
+
+/* ---- accounting ------------------------------------------------------ */
+/*
+ * Bytes one position adds to one layer's cache for one sequence: the K and
+ * V payloads of n_kv_heads * head_dim values plus 2 bytes per fp16 scale on
+ * each quantized side (TinyLoop memory-formula table: FP16 KV = 2*D*2,
+ * INT8 KV = 2*D*1 + 2*n_heads*2; with D = 2048 and 16 heads these are 8192
+ * and 4160).  group_size as in kvq_cache.  Host-only, pure arithmetic.
+ * Returns 0 for an invalid combination.
+ */
+size_t kvq_bytes_per_token(int k_bits, int v_bits, int n_kv_heads, int head_dim, int group_size);
+
+/*
+ * Byte sizes of the four buffers of `c` (pointers in `c` are not read).
+ * Any output pointer may be NULL.  Returns KVQ_OK or a KVQ_ERR_* for an
+ * invalid geometry.  Host-only.
+ */
+int kvq_cache_sizes(const kvq_cache *c, size_t *k_codes_bytes, size_t *v_codes_bytes,
+                    size_t *k_scales_bytes, size_t *v_scales_bytes);
+
+/* ---- append (quantize the new rows into the cache) -------------------- */
+/*
+ * Encode n_new new K rows and V rows per sequence and KV head and store
+ * them at their slots (mni-ml page: one new K and V per step; TinyLoop
+ * five-modes table for the encodings).
+ *
+ * Encoding of one group of g values x (quantized sides):
+ *   amax = max |x|;  s32 = amax / qmax in IEEE float32 (qmax 127 or 7);
+ *   stored scale = fp16(s32) rounded to nearest even, 65504 if it would
+ *   overflow;  s = that stored value;  code = clamp(round_half_even(x / s)
+ *   in float32, -qmax, qmax);  an all-zero group stores scale 0, codes 0.
+ * 16-bit sides store fp16(x) (nearest even); 32-bit sides store x.
+ *
+ * k_new, v_new : float32 [batch][n_kv_heads][n_new][head_dim], 16-byte aligned.
+ * start_pos    : int32 [batch] in device memory; row i of sequence b is
+ *                position start_pos[b] + i.
+ * Device-side rules: a row whose position is negative, or >= capacity with
+ * no window, is not stored.  With a window, a row that a later row of the
+ * same call would evict (position >= n_anchor and at least `window`
+ * positions older than the call's last row) is not stored, so one call with
+ * n_new rows leaves the cache exactly as n_new single-row calls would.
+ * n_new == 0 is a no-op.  Rows written by one call must not be read by
+ * kernels running concurrently on another stream.
+ */
+int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n_new,
+               const int32_t *start_pos, void *stream);
+
+/* ---- decode attention --------------------------------------------------- */
+/*
+ * The attention computed (the current query against every cached row,
+ * aihot.vn page: Q only at the current position):
+ *   for each sequence b and query head hq, with KV head kv = hq / (n_q_heads
+ *   / n_kv_heads) and L = min(seq_len[b], capacity, max_seq_len) slots:
+ *     z_t = softmax_scale * sum_c q[b][hq][c] * Khat[t][c]
+ *     out[b][hq][c] = sum_t exp(z_t - max z) * Vhat[t][c] / sum_t exp(z_t - max z)
+ *   over slots t = 0 .. L-1, where Khat/Vhat = code * scale (or the stored
+ *   float value).  With a window the slots hold exactly the anchors and the
+ *   most recent positions, so slot order differs from position order, which
+ *   softmax does not see.  L == 0 gives out = 0.
+ *
+ * The work is split along the context into chunks of `chunk_tokens` slots:
+ * kvq_decode_partials() writes per-chunk partial results (running max m in
+ * log2 units, sum l, and unnormalized accumulator) into the workspace;
+ * kvq_combine() merges them; kvq_decode_attn() does both.  Splitting the two
+ * lets the partials of several devices be merged by one kvq_combine().
+ *
+ * q, out       : float32 [batch][n_q_heads][head_dim], 16-byte aligned.
+ *                n_q_heads must be n_kv_heads * G with G in {1, 2, 4, 8}.
+ * seq_len      : int32 [batch] in device memory, positions written so far
+ *                (the newest included).
+ * max_seq_len  : host upper bound on seq_len[]; sizes the grid.  Slots at or
+ *                beyond it are not attended.
+ * softmax_scale: > 0, or 0 for 1/sqrt(head_dim).
+ * chunk_tokens : 0 for the library's choice (kvq_chunk_tokens()), or a
+ *                multiple of 64 in [64, 8192] whose working set fits the
+ *                device's LDS (else KVQ_ERR_ARG).
+ * workspace    : device memory of at least kvq_workspace_bytes(...) bytes,
+ *                256-byte aligned.  Layout, for P = batch * n_q_heads rows
+ *                and C chunks: float ml[P][C][2] = (m, l) at offset 0, then
+ *                float acc[P][C][head_dim] at offset round_up(8*P*C, 256).
+ *                An empty chunk has m = -inf, l = 0, acc = 0.
+ * Results are deterministic: no atomics, fixed chunk partition and order.
+ */
+int kvq_chunk_tokens(const kvq_cache *c, int n_q_heads, int max_seq_len);
+
+size_t kvq_workspace_bytes(const kvq_cache *c, int n_q_heads, int max_seq_len, int chunk_tokens);
+
+int kvq_decode_partials(const kvq_cache *c, const float *q, int n_q_heads, const int32_t *seq_len,
+                        int max_seq_len, float softmax_scale, int chunk_tokens,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Merge the partials of `n_chunks` chunks for P = batch * n_q_heads rows
+ * (layout as above) into out[P][head_dim]:
+ *   M = max_i m_i,  out = sum_i acc_i * 2^(m_i - M) / sum_i l_i * 2^(m_i - M),
+ * or 0 when every chunk is empty.
+ */
+int kvq_combine(int batch, int n_q_heads, int head_dim, int n_chunks, const void *workspace,
+                size_t workspace_bytes, float *out, void *stream);
+
+int kvq_decode_attn(const kvq_cache *c, const float *q, int n_q_heads, const int32_t *seq_len,
+                    int max_seq_len, float softmax_scale, int chunk_tokens, float *out,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---- diagnostics ------------------------------------------------------- */
+/* Static text for a status code. */
+const char *kvq_status_str(int status);
+
+/* Text describing the calling thread's most recent failure (or ""). */
+const char *kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,101 @@
+"""Shared helpers of the GPU tests: run the HIP path through the C ABI and
+compare it with the CPU oracle."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+ATOL = 2e-3      # max |gpu - oracle| on attention outputs
+RTOL_L2 = 1e-3   # ||gpu - oracle||_2 / ||oracle||_2
+
+
+def need_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_attention_quantized_kvq_amd as kvq
+    kvq.lib()                       # raises if libkvq.so is missing: no fallback
+    return kvq
+
+
+def assert_close(got, want, ctx=""):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, (got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{ctx}: non-finite output"
+    d = np.abs(got - want)
+    nrm = np.linalg.norm(want)
+    rel = np.linalg.norm(got - want) / nrm if nrm > 0 else np.linalg.norm(got - want)
+    assert d.max() <= ATOL and rel <= RTOL_L2, f"{ctx}: max|d|={d.max():.3e} relL2={rel:.3e}"
+    return float(d.max()), float(rel)
+
+
+def group_size_of(kb, vb, group, hkv, hd):
+    if kb >= 16:
+        return hd
+    if group == -1:
+        return hkv * hd
+    return group or hd
+
+
+def cache_arrays(cache):
+    """(k_codes, v_codes, k_scales, v_scales) of a cache as numpy arrays,
+    codes shaped [B][Hkv][cap][row bytes], scales [B][Hkv][cap][groups] or
+    [B][cap] for one scale per position."""
+    d = cache.desc
+    B, H, HD, cap = d.batch, d.n_kv_heads, d.head_dim, d.capacity
+    kc = cache.k_codes.cpu().numpy().reshape(B, H, cap, HD * d.k_bits // 8)
+    vc = cache.v_codes.cpu().numpy().reshape(B, H, cap, HD * d.v_bits // 8)
+    out = [kc, vc]
+    per_row = d.group_size == H * HD and H > 1
+    for t in (cache.k_scales, cache.v_scales):
+        if t is None:
+            out.append(None)
+        else:
+            a = t.cpu().numpy().view(np.uint16)
+            out.append(a.reshape(B, cap) if per_row else a.reshape(B, H, cap, HD // d.group_size))
+    return out
+
+
+def check_codes(oq, cache, K, V, positions_of_slot):
+    """Bit-exact check of every stored row: K, V float32 [B][Hkv][n_pos][HD];
+    positions_of_slot: {slot: position} that the cache must hold."""
+    d = cache.desc
+    B, H, HD = d.batch, d.n_kv_heads, d.head_dim
+    kc, vc, ks, vs = cache_arrays(cache)
+    slots = np.array(sorted(positions_of_slot), dtype=np.int64)
+    pos = np.array([positions_of_slot[s] for s in slots], dtype=np.int64)
+    per_row = d.group_size == H * HD and H > 1
+    for side, (src, codes, scales, bits) in enumerate(((K, kc, ks, d.k_bits), (V, vc, vs, d.v_bits))):
+        name = "K" if side == 0 else "V"
+        if per_row and bits < 16:
+            for b in range(B):
+                rows_ = src[b][:, pos, :].transpose(1, 0, 2).reshape(len(pos), H * HD)
+                p, s = oq.encode_rows(rows_, H * HD, bits)
+                got = codes[b][:, slots, :].transpose(1, 0, 2).reshape(len(pos), -1)
+                assert np.array_equal(got, p), f"{name} codes differ (b={b}, per-row)"
+                assert np.array_equal(scales[b][slots], s[:, 0]), f"{name} scales differ (b={b})"
+        else:
+            g = d.group_size if bits < 16 else HD
+            p, s = oq.encode_rows(src[:, :, pos, :], g, bits)
+            got = codes[:, :, slots, :]
+            if not np.array_equal(got, p):
+                bad = np.argwhere(got != p)[:5]
+                raise AssertionError(f"{name} codes differ at {bad.tolist()} (bits={bits})")
+            if bits < 16:
+                assert np.array_equal(scales[:, :, slots, :], s), f"{name} scales differ"
+
+
+def linear_slots(n_pos, cap):
+    return {p: p for p in range(min(n_pos, cap))}
+
+
+def window_slots(oq, n_pos, A, W):
+    held = oq.attended_positions(n_pos - 1, A, W)
+    return {oq.slot_of(int(p), A, W): int(p) for p in held}
+
+
+def softmax_default(hd):
+    return 1.0 / math.sqrt(hd)

@@ -1,0 +1,199 @@
+"""Host-side checks of libkvq.so that need no GPU: the library loads, exports
+every entry point kvq.h declares, and rejects every invalid argument before
+launching anything.  No compute call is made here."""
+import ctypes
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+
+
+@pytest.fixture(scope="module")
+def kvq():
+    import decode_attention_quantized_kvq_amd as k
+    if not k.LIB_PATH.exists():
+        pytest.fail("libkvq.so is not built (python -m decode_attention_quantized_kvq_amd.build)")
+    k.lib()
+    return k
+
+
+def header_functions():
+    text = (ROOT / "include" / "kvq.h").read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(kvq):
+    names = header_functions()
+    assert len(names) >= 10
+    lib = ctypes.CDLL(str(kvq.LIB_PATH))
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(kvq.EXPORTED) == names
+
+
+def test_status_strings(kvq):
+    for code in range(0, -10, -1):
+        s = kvq.kvq_status_str(code)
+        assert s and s != "unknown status"
+    assert kvq.kvq_status_str(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("args", [
+    (8, 8, 16, 128, 128), (16, 16, 16, 128, 128), (8, 4, 8, 128, 128), (4, 4, 8, 128, 128),
+    (4, 8, 8, 128, 32), (8, 8, 8, 64, 512), (32, 32, 8, 64, 64), (4, 4, 8, 128, 32),
+    (3, 8, 8, 128, 128), (8, 8, 8, 128, 48), (8, 8, 0, 128, 128), (8, 8, 8, 128, 0),
+])
+def test_bytes_per_token_matches_oracle(kvq, oq, args):
+    assert kvq.kvq_bytes_per_token(*args) == oq.bytes_per_token(*args)
+
+
+def test_bytes_per_token_page_values(kvq):
+    # TinyLoop memory-formula table (D = 2048, 16 heads)
+    assert kvq.kvq_bytes_per_token(8, 8, 16, 128, 128) == 4160
+    assert kvq.kvq_bytes_per_token(16, 16, 16, 128, 128) == 8192
+
+
+def _desc(kvq, **kw):
+    base = dict(batch=2, n_kv_heads=2, head_dim=128, capacity=100, k_bits=8, v_bits=8, group_size=128,
+                n_anchor=0, window=0)
+    base.update(kw)
+    d = kvq.kvq_cache(**base)
+    d.k_codes = d.v_codes = 0x10000
+    d.k_scales = d.v_scales = 0x20000
+    return d
+
+
+def test_cache_sizes(kvq):
+    d = _desc(kvq, batch=3, n_kv_heads=8, head_dim=128, capacity=1600, k_bits=4, v_bits=8, group_size=32)
+    kc, vc, ks, vs = kvq.kvq_cache_sizes(d)
+    rows = 3 * 8 * 1600
+    assert (kc, vc, ks, vs) == (rows * 64, rows * 128, rows * 4 * 2, rows * 4 * 2)
+    d = _desc(kvq, n_kv_heads=4, head_dim=64, group_size=256)           # one scale per position
+    assert kvq.kvq_cache_sizes(d)[2] == 2 * 100 * 2
+    d = _desc(kvq, k_bits=16, v_bits=16)
+    assert kvq.kvq_cache_sizes(d)[2:] == (0, 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), -3), (dict(n_kv_heads=0), -3), (dict(capacity=0), -3), (dict(head_dim=96), -3),
+    (dict(k_bits=16, v_bits=8), -2), (dict(k_bits=2), -2), (dict(k_bits=32, v_bits=16), -2),
+    (dict(group_size=48), -4), (dict(group_size=16), -4), (dict(group_size=0), -4),
+    (dict(n_anchor=4), -5), (dict(window=50), -5), (dict(n_anchor=-1, window=101), -5),
+    (dict(batch=40000, n_kv_heads=2), -3),
+])
+def test_geometry_errors(kvq, kw, code):
+    d = _desc(kvq, **kw)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_cache_sizes(d)
+    assert e.value.status == code
+    assert kvq.kvq_last_error()
+
+
+def test_append_argument_errors(kvq):
+    d = _desc(kvq)
+    ok = 0x30000
+    cases = [
+        (dict(n_new=-1), -3),
+        (dict(k_new=None), -1),
+        (dict(start_pos=None), -1),
+        (dict(k_new=ok + 4), -7),
+        (dict(start_pos=ok + 2), -7),
+    ]
+    for over, code in cases:
+        a = dict(k_new=ok, v_new=ok, n_new=3, start_pos=ok)
+        a.update(over)
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.kvq_append(d, a["k_new"], a["v_new"], a["n_new"], a["start_pos"], 0)
+        assert e.value.status == code, over
+    # n_new == 0 is a no-op that launches nothing
+    kvq.kvq_append(d, None, None, 0, None, 0)
+    # misaligned or missing cache buffers
+    d2 = _desc(kvq)
+    d2.k_codes = 0x10008
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_append(d2, ok, ok, 1, ok, 0)
+    assert e.value.status == -7
+    d3 = _desc(kvq)
+    d3.k_scales = None
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_append(d3, ok, ok, 1, ok, 0)
+    assert e.value.status == -1
+
+
+def test_decode_argument_errors(kvq):
+    d = _desc(kvq)
+    ws_need = kvq.kvq_workspace_bytes(d, 8, 100, 0)
+    ok = 0x40000
+    base = dict(q=ok, n_q_heads=8, seq_len=ok, max_seq_len=100, scale=0.0, chunk=0, out=ok, ws=ok, ws_bytes=ws_need)
+    cases = [
+        (dict(n_q_heads=6), -3), (dict(n_q_heads=2 * 3), -3), (dict(n_q_heads=32), -3),
+        (dict(q=None), -1), (dict(seq_len=None), -1), (dict(ws=None), -1), (dict(out=None), -1),
+        (dict(q=ok + 8), -7), (dict(ws=ok + 128), -7), (dict(out=ok + 4), -7), (dict(seq_len=ok + 1), -7),
+        (dict(ws_bytes=ws_need - 1), -6),
+        (dict(max_seq_len=0), -9), (dict(chunk=100), -9), (dict(chunk=32), -9), (dict(chunk=16384), -9),
+        (dict(scale=-1.0), -9), (dict(scale=float("nan")), -9), (dict(scale=float("inf")), -9),
+    ]
+    for over, code in cases:
+        a = dict(base)
+        a.update(over)
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.kvq_decode_attn(d, a["q"], a["n_q_heads"], a["seq_len"], a["max_seq_len"], a["scale"], a["chunk"],
+                                a["out"], a["ws"], a["ws_bytes"], 0)
+        assert e.value.status == code, over
+
+
+def test_combine_argument_errors(kvq):
+    need = 0
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_combine(0, 8, 128, 4, 0x40000, 1 << 20, 0x50000, 0)
+    assert e.value.status == -3
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_combine(1, 8, 96, 4, 0x40000, 1 << 20, 0x50000, 0)
+    assert e.value.status == -3
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_combine(1, 8, 128, 4, 0x40000, 100, 0x50000, 0)
+    assert e.value.status == -6
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_combine(1, 8, 128, 4, 0x40010, 1 << 20, 0x50000, 0)
+    assert e.value.status == -7
+
+
+def test_workspace_and_chunks(kvq):
+    # 32 sequences x 8 KV heads x 32K slots, 4:1 GQA, int4 K and V
+    d = _desc(kvq, batch=32, n_kv_heads=8, capacity=32768, k_bits=4, v_bits=4)
+    ch = kvq.kvq_chunk_tokens(d, 32, 32768)
+    assert ch % 64 == 0 and 64 <= ch <= 4096
+    n_chunks = -(-32768 // ch)
+    assert 32 * 8 * n_chunks >= 2048                     # enough workgroups for 256 CUs
+    P = 32 * 32
+    want = ((P * n_chunks * 8 + 255) // 256) * 256 + P * n_chunks * 128 * 4
+    assert kvq.kvq_workspace_bytes(d, 32, 32768, 0) == want
+    assert kvq.kvq_workspace_bytes(d, 32, 32768, 64) == ((P * 512 * 8 + 255) // 256) * 256 + P * 512 * 512
+    # max_seq_len beyond capacity sizes by capacity
+    assert kvq.kvq_workspace_bytes(d, 32, 10 ** 9, 1024) == kvq.kvq_workspace_bytes(d, 32, 32768, 1024)
+    # short contexts use the smallest chunk
+    small = _desc(kvq, batch=1, n_kv_heads=4, head_dim=64, capacity=257, group_size=64)
+    assert kvq.kvq_chunk_tokens(small, 4, 257) == 64
+
+
+def test_binding_has_no_fallback(kvq, monkeypatch, tmp_path):
+    """With the library missing, the binding raises instead of computing."""
+    import importlib
+    mod = importlib.import_module("decode_attention_quantized_kvq_amd")
+    monkeypatch.setattr(mod, "_lib", None)
+    monkeypatch.setattr(mod, "LIB_PATH", tmp_path / "missing.so")
+    with pytest.raises(RuntimeError):
+        mod.kvq_bytes_per_token(8, 8, 16, 128, 128)
+
+
+def test_product_does_not_touch_oracle():
+    """The package and its sources never import or link the oracle."""
+    pkg = ROOT / "decode_attention_quantized_kvq_amd"
+    for f in list(pkg.rglob("*.py")) + list(pkg.rglob("*.hip")) + list(pkg.rglob("*.hpp")):
+        text = f.read_text()
+        assert "oracle" not in text.lower() or f.name == "__init__.py" and "import oracle" not in text, f
+        assert "kvq_oracle" not in text and "import oracle" not in text and "from oracle" not in text, f

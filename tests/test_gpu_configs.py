@@ -1,0 +1,111 @@
+"""GPU parity on the five workloads at their full shapes, in the launch
+configuration the bench times (library-chosen chunks): codes and scales
+bit-exact and attention outputs within tolerance, on every sequence for the
+small workloads and on sampled sequences (recomputed by the oracle one by
+one) for the large ones."""
+import numpy as np
+import pytest
+
+import workloads as wl
+from gpu_util import assert_close, cache_arrays, check_codes, group_size_of, linear_slots, need_gpu, window_slots
+
+pytestmark = pytest.mark.gpu
+
+
+def _alloc(kvq, w, mode):
+    gs = group_size_of(mode.k_bits, mode.v_bits, mode.group, w.n_kv_heads, w.head_dim)
+    return kvq.alloc_cache(w.batch, w.n_kv_heads, w.head_dim, w.capacity, mode.k_bits, mode.v_bits, gs,
+                           w.n_anchor, w.window), gs
+
+
+def _check_sequence(oq, w, cache, gs, mode, layer, b, out_b, n_pos, q_b):
+    K = wl.rows(w, wl.K_STREAM, layer, b, n_pos)
+    V = wl.rows(w, wl.V_STREAM, layer, b, n_pos)
+    # codes and scales of this sequence, bit-exact
+    seq = cache.sequence(b)
+    slots = window_slots(oq, n_pos, w.n_anchor, w.window) if w.window else linear_slots(n_pos, w.capacity)
+    check_codes(oq, seq, K[None], V[None], slots)
+    want = oq.decode_step(mode.k_bits, mode.v_bits, gs, w.n_anchor, w.window, K, V, q_b,
+                          1.0 / np.sqrt(w.head_dim))
+    return assert_close(out_b, want, f"{w.name} {mode.name} layer={layer} b={b}")
+
+
+def _run(oq, w, modes, sample_b, layers=(0,)):
+    kvq = need_gpu()
+    import torch
+    from workloads.device import decode, fill, positions, queries
+    for layer in layers:
+        made = [(_alloc(kvq, w, m), m) for m in modes]
+        caches = [c for (c, _), _ in made]
+        # positions 0 .. n_pos-2 as the cached context, then the step's row
+        fill(caches, w, layer, w.n_pos)
+        q = queries(w, layer)
+        qn = q.cpu().numpy()
+        lens = positions([w.n_pos] * w.batch)
+        for (cache, gs), m in made:
+            out = decode(cache, q, w.n_q_heads, lens, w.n_pos).cpu().numpy()
+            for b in sample_b:
+                _check_sequence(oq, w, cache, gs, m, layer, b, out[b], w.n_pos, qn[b])
+        del made, caches
+        torch.cuda.empty_cache()
+
+
+def test_tiny(oq):
+    w = wl.TINY
+    _run(oq, w, w.modes, sample_b=range(w.batch))
+
+
+def test_tinyloop(oq):
+    w = wl.TINYLOOP
+    _run(oq, w, w.modes, sample_b=(0, 5, 7), layers=(0, 33))
+
+
+def test_k8v4_8k(oq):
+    w = wl.K8V4_8K
+    _run(oq, w, w.modes, sample_b=(0, 9, 15))
+
+
+def test_k8v4_32k(oq):
+    w = wl.K8V4_32K
+    _run(oq, w, w.modes, sample_b=(0, 15))
+
+
+def test_k4v4_32k(oq):
+    w = wl.K4V4_32K
+    _run(oq, w, w.modes, sample_b=(0, 31))
+
+
+def test_k4v4_window(oq):
+    w = wl.K4V4_WINDOW
+    _run(oq, w, w.modes, sample_b=(0, 13, 31))
+
+
+@pytest.mark.parametrize("mode", wl.MNIML.modes, ids=lambda m: m.name)
+def test_mniml_generation_loop(oq, mode):
+    """4-token prompt, then 252 steps of (append one row, attend); every
+    step's output against the oracle."""
+    kvq = need_gpu()
+    import torch
+    from workloads.device import positions, to_device
+    w = wl.MNIML
+    cache, gs = _alloc(kvq, w, mode)
+    K = wl.rows(w, wl.K_STREAM, 0, 0, w.n_pos)
+    V = wl.rows(w, wl.V_STREAM, 0, 0, w.n_pos)
+    kvq.kvq_append(cache, to_device(K[None, :, :w.prompt]), to_device(V[None, :, :w.prompt]), w.prompt,
+                   positions([0]))
+    ws_bytes = kvq.kvq_workspace_bytes(cache, w.n_q_heads, w.capacity, 0)
+    ws = torch.empty(ws_bytes // 4 + 64, device="cuda")
+    out = torch.empty((1, w.n_q_heads, w.head_dim), device="cuda")
+    worst = 0.0
+    for step in range(w.n_pos - w.prompt):
+        pos = w.prompt + step
+        kvq.kvq_append(cache, to_device(np.ascontiguousarray(K[None, :, pos:pos + 1])),
+                       to_device(np.ascontiguousarray(V[None, :, pos:pos + 1])), 1, positions([pos]))
+        q = wl.query(w, 0, 0, step)
+        kvq.kvq_decode_attn(cache, to_device(q[None]), w.n_q_heads, positions([pos + 1]), w.capacity, 0.0, 0, out,
+                            ws, ws_bytes)
+        got = out.cpu().numpy()[0]
+        want = oq.decode_step(mode.k_bits, mode.v_bits, gs, 0, 0, K[:, :pos + 1], V[:, :pos + 1], q,
+                              1.0 / np.sqrt(w.head_dim))
+        worst = max(worst, assert_close(got, want, f"mniml {mode.name} step {step}")[0])
+    check_codes(oq, cache, K[None], V[None], linear_slots(w.n_pos, w.capacity))

@@ -1,0 +1,218 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle at
+sizes the oracle finishes in seconds: several chunks, a ragged tail, every
+kernel instantiation (widths x head_dim x GQA group), windows, groups."""
+import numpy as np
+import pytest
+
+from gpu_util import (assert_close, check_codes, group_size_of, linear_slots, need_gpu, softmax_default,
+                      window_slots)
+
+pytestmark = pytest.mark.gpu
+
+MODES = [(32, 32, 0), (16, 16, 0), (8, 8, 0), (8, 4, 0), (4, 4, 0), (4, 8, 0)]
+
+
+def _data(B, H, n_pos, HD, Hq, seed, outliers=False):
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((B, H, n_pos, HD)).astype(np.float32)
+    if outliers:
+        K[:, :, :, ::23] *= np.float32(10.0)
+    V = rng.standard_normal((B, H, n_pos, HD)).astype(np.float32)
+    q = rng.standard_normal((B, Hq, HD)).astype(np.float32)
+    return K, V, q
+
+
+def run_case(oq, kb, vb, group, B=2, H=2, G=4, HD=128, n_pos=700, n_anchor=0, window=0, pieces=(1.0,),
+             seq_lens=None, chunk=0, seed=0, outliers=False, check_all_codes=True):
+    kvq = need_gpu()
+    import torch
+    from workloads.device import decode, positions, to_device
+
+    Hq = H * G
+    K, V, q = _data(B, H, n_pos, HD, Hq, seed, outliers)
+    cap = n_anchor + window if window else n_pos
+    gs = group_size_of(kb, vb, group, H, HD)
+    cache = kvq.alloc_cache(B, H, HD, cap, kb, vb, gs, n_anchor, window)
+    # append in pieces (fractions of n_pos), all sequences per call
+    p0 = 0
+    for i, frac in enumerate(pieces):
+        n = n_pos - p0 if i == len(pieces) - 1 else max(1, int(round(frac * n_pos)))
+        kvq.kvq_append(cache, to_device(K[:, :, p0:p0 + n]), to_device(V[:, :, p0:p0 + n]), n,
+                       positions([p0] * B))
+        p0 += n
+    assert p0 == n_pos
+    lens = seq_lens if seq_lens is not None else [n_pos] * B
+    out = decode(cache, to_device(q), Hq, positions(lens), max(max(lens), 1), 0.0, chunk)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+
+    if check_all_codes:
+        slots = window_slots(oq, n_pos, n_anchor, window) if window else linear_slots(n_pos, cap)
+        check_codes(oq, cache, K, V, slots)
+    sc = softmax_default(HD)
+    for b in range(B):
+        L = min(max(lens[b], 0), cap) if not window else n_pos
+        if L == 0:
+            assert np.all(got[b] == 0)
+            continue
+        want = oq.decode_step(kb, vb, gs, n_anchor, window, K[b][:, :L], V[b][:, :L], q[b], sc)
+        assert_close(got[b], want, f"kb={kb} vb={vb} g={gs} HD={HD} G={G} b={b} L={L}")
+    return cache, got
+
+
+@pytest.mark.parametrize("kb,vb,group", MODES)
+@pytest.mark.parametrize("HD", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_every_instantiation(oq, kb, vb, group, HD, G):
+    run_case(oq, kb, vb, group, B=2, H=2, G=G, HD=HD, n_pos=333, seed=kb * 100 + vb + HD + G)
+
+
+@pytest.mark.parametrize("kb,vb", [(8, 8), (8, 4), (4, 4), (4, 8)])
+@pytest.mark.parametrize("group", [32, 64])
+def test_group_scales(oq, kb, vb, group):
+    """Several fp16 scales per head row (the KVSplit-style group layout)."""
+    run_case(oq, kb, vb, group, B=2, H=2, G=4, HD=128, n_pos=515, seed=7 + group, outliers=True)
+
+
+def test_per_row_scale(oq):
+    """One scale per position over all KV heads (mni-ml's per-tensor INT8)."""
+    run_case(oq, 8, 8, -1, B=2, H=4, G=1, HD=64, n_pos=300, seed=3)
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 512, 4096])
+def test_chunk_sizes(oq, chunk):
+    run_case(oq, 4, 4, 0, B=1, H=2, G=4, HD=128, n_pos=3001, chunk=chunk, seed=11)
+
+
+def test_ragged_lengths(oq):
+    """Different lengths per sequence, zero length, and lengths past capacity."""
+    run_case(oq, 8, 4, 0, B=4, H=2, G=4, HD=128, n_pos=1000, seq_lens=[1000, 1, 0, 777], seed=5)
+    run_case(oq, 16, 16, 0, B=3, H=1, G=2, HD=64, n_pos=130, seq_lens=[65, 5000, 129], seed=6)
+
+
+def test_pieces_equal_one_call(oq):
+    c1, o1 = run_case(oq, 4, 4, 0, B=2, H=2, G=2, HD=128, n_pos=500, pieces=(1.0,), seed=9)
+    c2, o2 = run_case(oq, 4, 4, 0, B=2, H=2, G=2, HD=128, n_pos=500, pieces=(0.3, 0.002, 0.5, 1.0), seed=9)
+    assert np.array_equal(o1, o2)
+    assert np.array_equal(c1.k_codes.cpu().numpy(), c2.k_codes.cpu().numpy())
+
+
+@pytest.mark.parametrize("n_pos", [5, 11, 12, 13, 40, 101])
+def test_window_edges(oq, n_pos):
+    """Anchors 3 + window 9 (capacity 12): before filling, exactly full, one
+    past, and many wraps, with single-row and multi-row appends."""
+    run_case(oq, 4, 4, 0, B=2, H=1, G=4, HD=64, n_pos=n_pos, n_anchor=3, window=9, seed=n_pos)
+    run_case(oq, 8, 8, 0, B=1, H=1, G=1, HD=64, n_pos=n_pos, n_anchor=3, window=9, seed=n_pos,
+             pieces=tuple([1.0 / n_pos] * (n_pos - 1) + [1.0]))
+
+
+def test_window_page_shape(oq):
+    """64 anchors + 1536 recent (on-device page), 5000 positions in mixed calls."""
+    run_case(oq, 4, 4, 0, B=2, H=2, G=4, HD=128, n_pos=5000, n_anchor=64, window=1536,
+             pieces=(0.01, 0.4, 0.0002, 1.0), seed=21)
+
+
+def test_determinism(oq):
+    _, a = run_case(oq, 4, 4, 0, B=2, H=2, G=4, HD=128, n_pos=2000, seed=13)
+    _, b = run_case(oq, 4, 4, 0, B=2, H=2, G=4, HD=128, n_pos=2000, seed=13)
+    assert np.array_equal(a, b)
+
+
+def test_special_rows(oq):
+    """All-zero rows, tiny rows (subnormal or zero scale), huge rows (scale
+    saturation), exact ties."""
+    kvq = need_gpu()
+    import torch
+    from workloads.device import decode, positions, to_device
+    B, H, HD, n = 1, 2, 64, 8
+    K = np.random.default_rng(1).standard_normal((B, H, n, HD)).astype(np.float32)
+    K[0, 0, 0] = 0.0
+    K[0, 0, 1] *= np.float32(1e-6)
+    K[0, 0, 2] *= np.float32(1e-4)
+    K[0, 0, 3] *= np.float32(1e6)
+    s = np.float32(0.142822265625)            # fp16 scale of amax 1, qmax 7
+    K[0, 1, 4] = 0.0
+    K[0, 1, 4, 0] = 1.0
+    K[0, 1, 4, 1:4] = [s / 2, 1.5 * s, 2.5 * s]
+    V = K.copy()
+    for kb, vb in [(8, 8), (4, 4), (16, 16)]:
+        cache = kvq.alloc_cache(B, H, HD, n, kb, vb, HD)
+        kvq.kvq_append(cache, to_device(K), to_device(V), n, positions([0]))
+        torch.cuda.synchronize()
+        check_codes(oq, cache, K, V, linear_slots(n, n))
+
+
+def test_append_skips_out_of_range(oq):
+    """Rows at negative positions or at/after capacity are not stored."""
+    kvq = need_gpu()
+    import torch
+    from workloads.device import positions, to_device
+    B, H, HD, cap = 2, 1, 64, 10
+    cache = kvq.alloc_cache(B, H, HD, cap, 8, 8, HD)
+    cache.k_codes.fill_(0x5A)
+    x = np.ones((B, H, 4, HD), np.float32)
+    kvq.kvq_append(cache, to_device(x), to_device(x), 4, positions([-2, 8]))
+    torch.cuda.synchronize()
+    kc = cache.k_codes.cpu().numpy().reshape(B, H, cap, HD)
+    assert np.all(kc[0, 0, :2] == 127) and np.all(kc[0, 0, 2:] == 0x5A)
+    assert np.all(kc[1, 0, 8:] == 127) and np.all(kc[1, 0, :8] == 0x5A)
+
+
+def test_guard_bands_untouched(oq):
+    """Buffers placed between guard bytes: append and decode write only
+    their own ranges."""
+    kvq = need_gpu()
+    import torch
+    from workloads.device import positions, to_device
+    B, H, HD, cap, G = 2, 2, 128, 300, 4
+    d0 = kvq.alloc_cache(B, H, HD, cap, 4, 4, HD)
+    sizes = kvq.kvq_cache_sizes(d0)
+    guard = 4096
+    big = [torch.full((s + 2 * guard,), 0xA5, dtype=torch.uint8, device="cuda") for s in sizes]
+    d = kvq.kvq_cache.from_buffer_copy(d0.desc)
+    d.k_codes, d.v_codes, d.k_scales, d.v_scales = (t.data_ptr() + guard for t in big)
+    K, V, q = _data(B, H, cap, HD, H * G, 4)
+    kvq.kvq_append(d, to_device(K), to_device(V), cap, positions([0, 0]))
+    ws_bytes = kvq.kvq_workspace_bytes(d, H * G, cap, 64)
+    ws = torch.full((ws_bytes + 2 * guard,), 0xA5, dtype=torch.uint8, device="cuda")
+    out = torch.full((B * H * G * HD + 2 * 64,), 7.0, device="cuda")
+    kvq.kvq_decode_attn(d, to_device(q), H * G, positions([cap, cap]), cap, 0.0, 64, out.data_ptr() + 256,
+                        ws.data_ptr() + guard, ws_bytes)
+    torch.cuda.synchronize()
+    for t in big + [ws]:
+        a = t.cpu().numpy()
+        assert np.all(a[:guard] == 0xA5) and np.all(a[-guard:] == 0xA5)
+    o = out.cpu().numpy()
+    assert np.all(o[:64] == 7.0) and np.all(o[-64:] == 7.0)
+
+
+def test_combine_matches_single_chunk(oq):
+    """Split-K partials merged by kvq_combine equal a one-chunk run."""
+    _, a = run_case(oq, 8, 8, 0, B=1, H=1, G=2, HD=128, n_pos=4000, chunk=64, seed=17)
+    _, b = run_case(oq, 8, 8, 0, B=1, H=1, G=2, HD=128, n_pos=4000, chunk=4096, seed=17)
+    np.testing.assert_allclose(a, b, rtol=0, atol=2e-4)
+
+
+def test_fp16_conversion_exhaustive():
+    """The FP16 cache mode stores fp16(x) for every float32 pattern exactly as
+    numpy's nearest-even cast does (any NaN stands for any NaN)."""
+    kvq = need_gpu()
+    import torch
+    from workloads.device import positions
+    HD = 128
+    n_rows = 1 << 18                    # 2^25 patterns per call
+    cache = kvq.alloc_cache(1, 1, HD, n_rows, 16, 16, HD)
+    step = n_rows * HD
+    sp = positions([0])
+    for hi in range(0, 1 << 32, step):
+        u = torch.arange(hi, hi + step, dtype=torch.int64, device="cuda").to(torch.int32)
+        x = u.view(torch.float32)
+        kvq.kvq_append(cache, x, x, n_rows, sp)
+        got = cache.k_codes.view(torch.int16).cpu().numpy().view(np.uint16)
+        xs = (np.arange(hi, hi + step, dtype=np.uint64).astype(np.uint32)).view(np.float32)
+        with np.errstate(over="ignore", invalid="ignore"):
+            ref = xs.astype(np.float16).view(np.uint16)
+        ref_nan = ((ref & 0x7C00) == 0x7C00) & ((ref & 0x3FF) != 0)
+        got_nan = ((got & 0x7C00) == 0x7C00) & ((got & 0x3FF) != 0)
+        assert np.array_equal(ref_nan, got_nan), hex(hi)
+        assert np.array_equal(got[~ref_nan], ref[~ref_nan]), hex(hi)
