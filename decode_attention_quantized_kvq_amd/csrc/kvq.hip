@@ -10,6 +10,7 @@
 #include "../../include/kvq.h"
 #include "kvq_append.hpp"
 #include "kvq_decode.hpp"
+#include "kvq_decode_quant.hpp"
 
 using namespace kvq;
 
@@ -45,7 +46,8 @@ bool bits_pair_ok(int kb, int vb)
 
 bool per_row(const kvq_cache *c) { return c->group_size == c->n_kv_heads * c->head_dim && c->group_size != c->head_dim; }
 
-constexpr size_t kMaxLds = 64 * 1024;
+constexpr size_t kMaxLds = 64 * 1024;    // largest workgroup LDS accepted
+constexpr size_t kAutoLds = 40 * 1024;   // the library's choice keeps 4 workgroups per CU
 
 // Geometry checks shared by every entry point (no pointer is read).
 int check_geometry(const kvq_cache *c)
@@ -100,11 +102,17 @@ int check_heads(const kvq_cache *c, int n_q_heads)
     return KVQ_OK;
 }
 
+bool quant_modes(const kvq_cache *c) { return quantized(c->k_bits); }   // both sides quantized (bits_pair_ok)
+
+int cap4_of(const kvq_cache *c) { return (c->capacity + 3) & ~3; }
+
 size_t lds_bytes(const kvq_cache *c, int G, int chunk)
 {
-    const int kg = quantized(c->k_bits) ? groups_per_head(c) : 1;
-    const int vg = quantized(c->v_bits) ? groups_per_head(c) : 1;
-    return (size_t)decode_smem(G, c->head_dim, c->k_bits, c->v_bits, chunk, kg, vg).total;
+    if (quant_modes(c)) {
+        const int vg = groups_per_head(c);
+        return (size_t)quant_smem(G, c->head_dim, chunk, vg).total;
+    }
+    return (size_t)float_smem(G, c->head_dim, chunk).total;
 }
 
 int max_len_of(const kvq_cache *c, int max_seq_len) { return max_seq_len < c->capacity ? max_seq_len : c->capacity; }
@@ -118,49 +126,112 @@ int auto_chunk(const kvq_cache *c, int n_q_heads, int max_seq_len)
     // workgroups per CU over 256 CUs; when even 64-slot chunks cannot, the
     // smallest chunk (most workgroups).
     for (int ch = 4096; ch >= 64; ch >>= 1) {
-        if (lds_bytes(c, G, ch) > kMaxLds) continue;
+        if (lds_bytes(c, G, ch) > kAutoLds) continue;
         if (units * ((L + ch - 1) / ch) >= 2048) return ch;
     }
     return 64;
 }
 
-using DecodeFn = void (*)(DecodeParams);
+using FloatFn = void (*)(FloatParams);
+using QuantFn = void (*)(QuantParams);
+using PrepFn = void (*)(const float *, int32_t *, float *, float);
 
-template <int KB, int VB, int HD>
-DecodeFn pick_g(int G)
+template <int B, int HD>
+FloatFn pick_float_g(int G)
 {
     switch (G) {
-    case 1: return decode_split_kernel<KB, VB, HD, 1, 4, 4>;
-    case 2: return decode_split_kernel<KB, VB, HD, 2, 4, 4>;
-    case 4: return decode_split_kernel<KB, VB, HD, 4, 4, 4>;
-    case 8: return decode_split_kernel<KB, VB, HD, 8, 4, 4>;
+    case 1: return decode_float_kernel<B, B, HD, 1, 4, 4>;
+    case 2: return decode_float_kernel<B, B, HD, 2, 4, 4>;
+    case 4: return decode_float_kernel<B, B, HD, 4, 4, 4>;
+    case 8: return decode_float_kernel<B, B, HD, 8, 4, 4>;
+    }
+    return nullptr;
+}
+
+FloatFn pick_float(int bits, int hd, int G)
+{
+    if (bits == 32) return hd == 64 ? pick_float_g<32, 64>(G) : pick_float_g<32, 128>(G);
+    return hd == 64 ? pick_float_g<16, 64>(G) : pick_float_g<16, 128>(G);
+}
+
+template <int KB, int VB, int HD, int KGM>
+QuantFn pick_quant_g(int G)
+{
+    switch (G) {
+    case 1: return decode_quant_kernel<KB, VB, HD, 1, KGM>;
+    case 2: return decode_quant_kernel<KB, VB, HD, 2, KGM>;
+    case 4: return decode_quant_kernel<KB, VB, HD, 4, KGM>;
+    case 8: return decode_quant_kernel<KB, VB, HD, 8, KGM>;
     }
     return nullptr;
 }
 
 template <int KB, int VB>
-DecodeFn pick_hd(int hd, int G)
+QuantFn pick_quant_hd(int hd, int G, bool grouped)
 {
-    return hd == 64 ? pick_g<KB, VB, 64>(G) : pick_g<KB, VB, 128>(G);
+    if (hd == 64) return grouped ? pick_quant_g<KB, VB, 64, 4>(G) : pick_quant_g<KB, VB, 64, 1>(G);
+    return grouped ? pick_quant_g<KB, VB, 128, 4>(G) : pick_quant_g<KB, VB, 128, 1>(G);
 }
 
-DecodeFn pick_decode(int kb, int vb, int hd, int G)
+// grouped: more than one key scale per row (group_size < head_dim)
+QuantFn pick_quant(int kb, int vb, int hd, int G, bool grouped)
 {
-    if (kb == 32) return pick_hd<32, 32>(hd, G);
-    if (kb == 16) return pick_hd<16, 16>(hd, G);
-    if (kb == 8 && vb == 8) return pick_hd<8, 8>(hd, G);
-    if (kb == 8 && vb == 4) return pick_hd<8, 4>(hd, G);
-    if (kb == 4 && vb == 4) return pick_hd<4, 4>(hd, G);
-    if (kb == 4 && vb == 8) return pick_hd<4, 8>(hd, G);
+    if (kb == 8 && vb == 8) return pick_quant_hd<8, 8>(hd, G, grouped);
+    if (kb == 8 && vb == 4) return pick_quant_hd<8, 4>(hd, G, grouped);
+    if (kb == 4 && vb == 4) return pick_quant_hd<4, 4>(hd, G, grouped);
+    if (kb == 4 && vb == 8) return pick_quant_hd<4, 8>(hd, G, grouped);
     return nullptr;
+}
+
+template <int KB, int HD>
+PrepFn pick_prep_g(int G)
+{
+    switch (G) {
+    case 1: return qprep_kernel<KB, HD, 1>;
+    case 2: return qprep_kernel<KB, HD, 2>;
+    case 4: return qprep_kernel<KB, HD, 4>;
+    case 8: return qprep_kernel<KB, HD, 8>;
+    }
+    return nullptr;
+}
+
+PrepFn pick_prep(int kb, int hd, int G)
+{
+    if (kb == 4) return hd == 64 ? pick_prep_g<4, 64>(G) : pick_prep_g<4, 128>(G);
+    return hd == 64 ? pick_prep_g<8, 64>(G) : pick_prep_g<8, 128>(G);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t ws_bytes(int batch, int n_q_heads, int head_dim, int n_chunks)
+// Workspace: ml [P][C][2] | acc [P][C][HD] | (quantized keys) query digits
+// [B*Hkv][K_COLS][ND][G] int32 | query scales [P] float.
+struct WsLayout {
+    size_t ml, acc, qdig, qsc, total;
+};
+
+WsLayout ws_layout(int batch, int n_q_heads, int head_dim, int n_chunks, int n_kv_heads, int k_bits)
 {
     const size_t P = (size_t)batch * n_q_heads;
-    return align256(P * n_chunks * 2 * sizeof(float)) + P * n_chunks * head_dim * sizeof(float);
+    WsLayout w;
+    w.ml = 0;
+    w.acc = align256(P * n_chunks * 2 * sizeof(float));
+    size_t off = w.acc + P * n_chunks * head_dim * sizeof(float);
+    w.qdig = w.qsc = 0;
+    if (quantized(k_bits)) {
+        const size_t cols = (size_t)head_dim * k_bits / 32;
+        const size_t nd = k_bits == 4 ? 4 : 2;
+        w.qdig = align256(off);
+        off = w.qdig + (size_t)batch * n_kv_heads * cols * nd * (n_q_heads / n_kv_heads) * 4;
+        w.qsc = align256(off);
+        off = w.qsc + P * sizeof(float);
+    }
+    w.total = off;
+    return w;
+}
+
+size_t ws_bytes(int batch, int n_q_heads, int head_dim, int n_chunks)
+{
+    return ws_layout(batch, n_q_heads, head_dim, n_chunks, 1, 32).total;
 }
 
 int hip_status(const char *what)
@@ -199,7 +270,10 @@ int kvq_cache_sizes(const kvq_cache *c, size_t *kc, size_t *vc, size_t *ksb, siz
     const size_t rows = (size_t)c->batch * c->n_kv_heads * c->capacity;
     const size_t sc = per_row(c) ? (size_t)c->batch * c->capacity : rows * groups_per_head(c);
     if (kc) *kc = rows * c->head_dim * c->k_bits / 8;
-    if (vc) *vc = rows * c->head_dim * c->v_bits / 8;
+    if (vc) {
+        const size_t vrows = quantized(c->v_bits) ? (size_t)c->batch * c->n_kv_heads * cap4_of(c) : rows;
+        *vc = vrows * c->head_dim * c->v_bits / 8;
+    }
     if (ksb) *ksb = quantized(c->k_bits) ? sc * 2 : 0;
     if (vsb) *vsb = quantized(c->v_bits) ? sc * 2 : 0;
     return ok();
@@ -232,6 +306,7 @@ int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n
     p.n_kv_heads = c->n_kv_heads;
     p.head_dim = c->head_dim;
     p.capacity = c->capacity;
+    p.cap4 = cap4_of(c);
     p.n_new = n_new;
     p.n_anchor = c->n_anchor;
     p.window = c->window;
@@ -273,12 +348,17 @@ static int resolve_chunk(const kvq_cache *c, int n_q_heads, int max_seq_len, int
     return KVQ_OK;
 }
 
+static size_t cache_ws_bytes(const kvq_cache *c, int n_q_heads, int n_chunks)
+{
+    return ws_layout(c->batch, n_q_heads, c->head_dim, n_chunks, c->n_kv_heads, c->k_bits).total;
+}
+
 size_t kvq_workspace_bytes(const kvq_cache *c, int n_q_heads, int max_seq_len, int chunk_tokens)
 {
     int ch, nc;
     if (resolve_chunk(c, n_q_heads, max_seq_len, chunk_tokens, &ch, &nc)) return 0;
     ok();
-    return ws_bytes(c->batch, n_q_heads, c->head_dim, nc);
+    return cache_ws_bytes(c, n_q_heads, nc);
 }
 
 int kvq_decode_partials(const kvq_cache *c, const float *q, int n_q_heads, const int32_t *seq_len, int max_seq_len,
@@ -292,35 +372,68 @@ int kvq_decode_partials(const kvq_cache *c, const float *q, int n_q_heads, const
     if (!aligned(q, 16)) return fail(KVQ_ERR_ALIGN, "q must be 16-byte aligned");
     if (!aligned(seq_len, 4)) return fail(KVQ_ERR_ALIGN, "seq_len must be 4-byte aligned");
     if (!aligned(workspace, 256)) return fail(KVQ_ERR_ALIGN, "workspace must be 256-byte aligned");
-    const size_t need = ws_bytes(c->batch, n_q_heads, c->head_dim, nc);
+    const size_t need = cache_ws_bytes(c, n_q_heads, nc);
     if (workspace_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
     if (!std::isfinite(softmax_scale) || softmax_scale < 0.0f)
         return fail(KVQ_ERR_ARG, "softmax_scale must be finite and >= 0");
     const float scale = softmax_scale == 0.0f ? 1.0f / std::sqrt((float)c->head_dim) : softmax_scale;
+    const float qk_scale = scale * 1.4426950408889634f;   // log2(e): scores kept in log2 units
     const int G = n_q_heads / c->n_kv_heads;
-    DecodeFn fn = pick_decode(c->k_bits, c->v_bits, c->head_dim, G);
-    if (!fn) return fail(KVQ_ERR_BITS, "no kernel for k_bits=%d v_bits=%d", c->k_bits, c->v_bits);
+    const WsLayout wl = ws_layout(c->batch, n_q_heads, c->head_dim, nc, c->n_kv_heads, c->k_bits);
+    char *ws = static_cast<char *>(workspace);
+    hipStream_t st_ = static_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)nc, (unsigned)(c->batch * c->n_kv_heads));
+    const size_t lds = lds_bytes(c, G, ch);
 
-    const size_t P = (size_t)c->batch * n_q_heads;
-    DecodeParams p;
+    if (!quant_modes(c)) {
+        FloatFn fn = pick_float(c->k_bits, c->head_dim, G);
+        if (!fn) return fail(KVQ_ERR_BITS, "no kernel for k_bits=%d", c->k_bits);
+        FloatParams p;
+        p.k_codes = static_cast<const uint8_t *>(c->k_codes);
+        p.v_codes = static_cast<const uint8_t *>(c->v_codes);
+        p.q = q;
+        p.seq_len = seq_len;
+        p.ws_ml = reinterpret_cast<float *>(ws + wl.ml);
+        p.ws_acc = reinterpret_cast<float *>(ws + wl.acc);
+        p.n_kv_heads = c->n_kv_heads;
+        p.capacity = c->capacity;
+        p.max_len = max_len_of(c, max_seq_len);
+        p.chunk = ch;
+        p.n_chunks = nc;
+        p.qk_scale = qk_scale;
+        hipLaunchKernelGGL(fn, grid, dim3(DEC_THREADS), lds, st_, p);
+        return hip_status("decode_float_kernel launch");
+    }
+
+    QuantFn fn = pick_quant(c->k_bits, c->v_bits, c->head_dim, G, groups_per_head(c) > 1);
+    PrepFn prep = pick_prep(c->k_bits, c->head_dim, G);
+    if (!fn || !prep) return fail(KVQ_ERR_BITS, "no kernel for k_bits=%d v_bits=%d", c->k_bits, c->v_bits);
+    int32_t *qdig = reinterpret_cast<int32_t *>(ws + wl.qdig);
+    float *qsc = reinterpret_cast<float *>(ws + wl.qsc);
+    hipLaunchKernelGGL(prep, dim3((unsigned)(c->batch * c->n_kv_heads)), dim3(256), 0, st_, q, qdig, qsc, qk_scale);
+    int hs = hip_status("qprep_kernel launch");
+    if (hs) return hs;
+
+    QuantParams p;
     p.k_codes = static_cast<const uint8_t *>(c->k_codes);
     p.v_codes = static_cast<const uint8_t *>(c->v_codes);
     p.k_scales = static_cast<const uint16_t *>(c->k_scales);
     p.v_scales = static_cast<const uint16_t *>(c->v_scales);
-    p.q = q;
+    p.qdig = qdig;
+    p.qsc = qsc;
     p.seq_len = seq_len;
-    p.ws_ml = static_cast<float *>(workspace);
-    p.ws_acc = reinterpret_cast<float *>(static_cast<char *>(workspace) + align256(P * nc * 2 * sizeof(float)));
+    p.ws_ml = reinterpret_cast<float *>(ws + wl.ml);
+    p.ws_acc = reinterpret_cast<float *>(ws + wl.acc);
     p.n_kv_heads = c->n_kv_heads;
     p.capacity = c->capacity;
+    p.cap4 = cap4_of(c);
     p.max_len = max_len_of(c, max_seq_len);
     p.chunk = ch;
     p.n_chunks = nc;
     const bool pr = per_row(c);
     const int gph = groups_per_head(c);
-    p.kg = quantized(c->k_bits) ? gph : 1;
-    p.vg = quantized(c->v_bits) ? gph : 1;
-    p.k_group = p.v_group = pr ? c->n_kv_heads * c->head_dim : (quantized(c->k_bits) ? c->group_size : c->head_dim);
+    p.kg = p.vg = gph;
+    p.k_group = p.v_group = pr ? c->n_kv_heads * c->head_dim : c->group_size;
     if (pr) {
         p.k_sc_b = p.v_sc_b = c->capacity;
         p.k_sc_h = p.v_sc_h = 0;
@@ -330,11 +443,8 @@ int kvq_decode_partials(const kvq_cache *c, const float *q, int n_q_heads, const
         p.k_sc_h = p.v_sc_h = (long long)c->capacity * gph;
         p.k_sc_t = p.v_sc_t = gph;
     }
-    p.qk_scale = scale * 1.4426950408889634f;   // log2(e): scores kept in log2 units
-    const size_t lds = lds_bytes(c, G, ch);
-    dim3 grid((unsigned)nc, (unsigned)(c->batch * c->n_kv_heads));
-    hipLaunchKernelGGL(fn, grid, dim3(DEC_THREADS), lds, static_cast<hipStream_t>(stream), p);
-    return hip_status("decode_split_kernel launch");
+    hipLaunchKernelGGL(fn, grid, dim3(QD_THREADS), lds, st_, p);
+    return hip_status("decode_quant_kernel launch");
 }
 
 int kvq_combine(int batch, int n_q_heads, int head_dim, int n_chunks, const void *workspace, size_t workspace_bytes,

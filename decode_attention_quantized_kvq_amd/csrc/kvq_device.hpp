@@ -49,7 +49,21 @@ __device__ __forceinline__ float wave_sum(float v)
 }
 
 // ------------------------------------------------------ vector memory ops
-__device__ __forceinline__ uint4 ld_u4(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
-__device__ __forceinline__ uint2 ld_u2(const void *p) { return *reinterpret_cast<const uint2 *>(p); }
+// Loads through the global address space (global_load_*, not flat_load_*).
+#define KVQ_GLOBAL __attribute__((address_space(1)))
+#define KVQ_CONST __attribute__((address_space(4)))
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_u4(const void *p)
+{
+    const u32x4_t v = *(const KVQ_GLOBAL u32x4_t *)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_u2(const void *p)
+{
+    const u32x2_t v = *(const KVQ_GLOBAL u32x2_t *)p;
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint16_t ld_u16(const void *p) { return *(const KVQ_GLOBAL uint16_t *)p; }
 
 } // namespace kvq

@@ -84,7 +84,13 @@ extern "C" {
  *   the anchors and the `window` most recent positions.
  *
  * Layouts (row-major, innermost last; R = head_dim * bits / 8 bytes):
- *   k_codes / v_codes : [batch][n_kv_heads][capacity][R] bytes, 16-byte aligned
+ *   k_codes, and v_codes of a 16/32-bit value side:
+ *       [batch][n_kv_heads][capacity][R] bytes, 16-byte aligned
+ *   v_codes of an 8/4-bit value side, four positions interleaved per byte:
+ *       [batch][n_kv_heads][cap4 / 4][R][4] bytes, cap4 = capacity rounded up
+ *       to a multiple of 4: byte j of the row of slot s sits at
+ *       ((s & ~3) * R + 4 * j + (s & 3)) within its (sequence, head), so one
+ *       32-bit word holds byte j of four consecutive slots.
  *   k_scales / v_scales (quantized sides only, NULL otherwise), fp16 bits:
  *       groups inside a head : [batch][n_kv_heads][capacity][head_dim/group_size]
  *       one scale per position: [batch][capacity]
@@ -185,8 +191,9 @@ int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n
  * workspace    : device memory of at least kvq_workspace_bytes(...) bytes,
  *                256-byte aligned.  Layout, for P = batch * n_q_heads rows
  *                and C chunks: float ml[P][C][2] = (m, l) at offset 0, then
- *                float acc[P][C][head_dim] at offset round_up(8*P*C, 256).
- *                An empty chunk has m = -inf, l = 0, acc = 0.
+ *                float acc[P][C][head_dim] at offset round_up(8*P*C, 256);
+ *                with 8/4-bit keys, scratch for the query's fixed-point form
+ *                follows.  An empty chunk has m = -inf, l = 0, acc = 0.
  * Results are deterministic: no atomics, fixed chunk partition and order.
  */
 int kvq_chunk_tokens(const kvq_cache *c, int n_q_heads, int max_seq_len);

@@ -47,7 +47,15 @@ def cache_arrays(cache):
     d = cache.desc
     B, H, HD, cap = d.batch, d.n_kv_heads, d.head_dim, d.capacity
     kc = cache.k_codes.cpu().numpy().reshape(B, H, cap, HD * d.k_bits // 8)
-    vc = cache.v_codes.cpu().numpy().reshape(B, H, cap, HD * d.v_bits // 8)
+    vraw = cache.v_codes.cpu().numpy()
+    R = HD * d.v_bits // 8
+    if d.v_bits < 16:
+        # 8/4-bit values: four positions interleaved per byte (kvq.h):
+        # byte j of slot s at ((s & ~3) * R + 4 * j + (s & 3)) within a (b, head)
+        cap4 = (cap + 3) // 4 * 4
+        vc = vraw.reshape(B, H, cap4 // 4, R, 4).transpose(0, 1, 2, 4, 3).reshape(B, H, cap4, R)[:, :, :cap]
+    else:
+        vc = vraw.reshape(B, H, cap, R)
     out = [kc, vc]
     per_row = d.group_size == H * HD and H > 1
     for t in (cache.k_scales, cache.v_scales):

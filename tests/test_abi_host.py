@@ -170,9 +170,17 @@ def test_workspace_and_chunks(kvq):
     n_chunks = -(-32768 // ch)
     assert 32 * 8 * n_chunks >= 2048                     # enough workgroups for 256 CUs
     P = 32 * 32
-    want = ((P * n_chunks * 8 + 255) // 256) * 256 + P * n_chunks * 128 * 4
-    assert kvq.kvq_workspace_bytes(d, 32, 32768, 0) == want
-    assert kvq.kvq_workspace_bytes(d, 32, 32768, 64) == ((P * 512 * 8 + 255) // 256) * 256 + P * 512 * 512
+    partials = ((P * n_chunks * 8 + 255) // 256) * 256 + P * n_chunks * 128 * 4
+    # int4 keys: the query's fixed-point digits (4 per value) and scales follow the partials
+    digits = 32 * 8 * 16 * 4 * 4 * 4 + P * 4
+    ws = kvq.kvq_workspace_bytes(d, 32, 32768, 0)
+    assert partials + digits <= ws <= partials + digits + 512
+    ws64 = kvq.kvq_workspace_bytes(d, 32, 32768, 64)
+    assert ws64 >= ((P * 512 * 8 + 255) // 256) * 256 + P * 512 * 512
+    # float caches need the partials only
+    f = _desc(kvq, batch=2, n_kv_heads=2, capacity=1000, k_bits=16, v_bits=16)
+    nc = -(-1000 // kvq.kvq_chunk_tokens(f, 8, 1000))
+    assert kvq.kvq_workspace_bytes(f, 8, 1000, 0) == ((16 * nc * 8 + 255) // 256) * 256 + 16 * nc * 128 * 4
     # max_seq_len beyond capacity sizes by capacity
     assert kvq.kvq_workspace_bytes(d, 32, 10 ** 9, 1024) == kvq.kvq_workspace_bytes(d, 32, 32768, 1024)
     # short contexts use the smallest chunk
