@@ -154,32 +154,38 @@ FloatFn pick_float(int bits, int hd, int G)
     return hd == 64 ? pick_float_g<16, 64>(G) : pick_float_g<16, 128>(G);
 }
 
-template <int KB, int VB, int HD, int KGM>
+template <int KB, int VB, int HD, int KG>
 QuantFn pick_quant_g(int G)
 {
     switch (G) {
-    case 1: return decode_quant_kernel<KB, VB, HD, 1, KGM>;
-    case 2: return decode_quant_kernel<KB, VB, HD, 2, KGM>;
-    case 4: return decode_quant_kernel<KB, VB, HD, 4, KGM>;
-    case 8: return decode_quant_kernel<KB, VB, HD, 8, KGM>;
+    case 1: return decode_quant_kernel<KB, VB, HD, 1, KG>;
+    case 2: return decode_quant_kernel<KB, VB, HD, 2, KG>;
+    case 4: return decode_quant_kernel<KB, VB, HD, 4, KG>;
+    case 8: return decode_quant_kernel<KB, VB, HD, 8, KG>;
     }
     return nullptr;
 }
 
 template <int KB, int VB>
-QuantFn pick_quant_hd(int hd, int G, bool grouped)
+QuantFn pick_quant_hd(int hd, int G, int kg)
 {
-    if (hd == 64) return grouped ? pick_quant_g<KB, VB, 64, 4>(G) : pick_quant_g<KB, VB, 64, 1>(G);
-    return grouped ? pick_quant_g<KB, VB, 128, 4>(G) : pick_quant_g<KB, VB, 128, 1>(G);
+    if (hd == 64) return kg == 2 ? pick_quant_g<KB, VB, 64, 2>(G) : kg == 1 ? pick_quant_g<KB, VB, 64, 1>(G) : nullptr;
+    switch (kg) {
+    case 1: return pick_quant_g<KB, VB, 128, 1>(G);
+    case 2: return pick_quant_g<KB, VB, 128, 2>(G);
+    case 4: return pick_quant_g<KB, VB, 128, 4>(G);
+    }
+    return nullptr;
 }
 
-// grouped: more than one key scale per row (group_size < head_dim)
-QuantFn pick_quant(int kb, int vb, int hd, int G, bool grouped)
+// kg: scale groups per head row (head_dim / group_size; 1 for one scale per
+// position shared by all heads)
+QuantFn pick_quant(int kb, int vb, int hd, int G, int kg)
 {
-    if (kb == 8 && vb == 8) return pick_quant_hd<8, 8>(hd, G, grouped);
-    if (kb == 8 && vb == 4) return pick_quant_hd<8, 4>(hd, G, grouped);
-    if (kb == 4 && vb == 4) return pick_quant_hd<4, 4>(hd, G, grouped);
-    if (kb == 4 && vb == 8) return pick_quant_hd<4, 8>(hd, G, grouped);
+    if (kb == 8 && vb == 8) return pick_quant_hd<8, 8>(hd, G, kg);
+    if (kb == 8 && vb == 4) return pick_quant_hd<8, 4>(hd, G, kg);
+    if (kb == 4 && vb == 4) return pick_quant_hd<4, 4>(hd, G, kg);
+    if (kb == 4 && vb == 8) return pick_quant_hd<4, 8>(hd, G, kg);
     return nullptr;
 }
 
@@ -405,7 +411,7 @@ int kvq_decode_partials(const kvq_cache *c, const float *q, int n_q_heads, const
         return hip_status("decode_float_kernel launch");
     }
 
-    QuantFn fn = pick_quant(c->k_bits, c->v_bits, c->head_dim, G, groups_per_head(c) > 1);
+    QuantFn fn = pick_quant(c->k_bits, c->v_bits, c->head_dim, G, groups_per_head(c));
     PrepFn prep = pick_prep(c->k_bits, c->head_dim, G);
     if (!fn || !prep) return fail(KVQ_ERR_BITS, "no kernel for k_bits=%d v_bits=%d", c->k_bits, c->v_bits);
     int32_t *qdig = reinterpret_cast<int32_t *>(ws + wl.qdig);
@@ -432,8 +438,6 @@ int kvq_decode_partials(const kvq_cache *c, const float *q, int n_q_heads, const
     p.n_chunks = nc;
     const bool pr = per_row(c);
     const int gph = groups_per_head(c);
-    p.kg = p.vg = gph;
-    p.k_group = p.v_group = pr ? c->n_kv_heads * c->head_dim : c->group_size;
     if (pr) {
         p.k_sc_b = p.v_sc_b = c->capacity;
         p.k_sc_h = p.v_sc_h = 0;

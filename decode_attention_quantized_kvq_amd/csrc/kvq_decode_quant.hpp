@@ -79,8 +79,6 @@ struct QuantParams {
     int n_kv_heads, capacity, cap4;
     int max_len;
     int chunk, n_chunks;
-    int kg, vg;                // scale groups per head row
-    int k_group, v_group;      // values per scale
     long long k_sc_b, k_sc_h;
     int k_sc_t;
     long long v_sc_b, v_sc_h;
@@ -125,7 +123,8 @@ __host__ __device__ inline QuantSmem quant_smem(int G, int HD, int chunk, int vg
 // s_q = max|q| / 30000 and q_int = rint(q / s_q) in [-30000, 30000], split
 // into ND balanced digits; digit j of the channels of key dword `col` is
 // packed like the codes (int4: channel 8col+i in nibble i; int8: channel
-// 4col+i in byte i) at qdig[unit][j][col][h].
+// 4col+i in byte i) at qdig[unit][col][j][h], so the ND * G digit words of
+// one key dword are contiguous (one scalar load).
 // ---------------------------------------------------------------------------
 template <int KB, int HD, int G>
 __global__ __launch_bounds__(256) void qprep_kernel(const float *__restrict__ q, int32_t *__restrict__ qdig,
@@ -165,7 +164,7 @@ __global__ __launch_bounds__(256) void qprep_kernel(const float *__restrict__ q,
             }
         }
 #pragma unroll
-        for (int j = 0; j < ND; j++) qdig[(((size_t)unit * ND + j) * K_COLS + col) * G + h] = (int32_t)d[j];
+        for (int j = 0; j < ND; j++) qdig[(((size_t)unit * K_COLS + col) * ND + j) * G + h] = (int32_t)d[j];
     }
     if (tid < G) qsc[unit * G + tid] = amax[tid] / (float)Q_RANGE * qk_scale;
 }
@@ -177,48 +176,48 @@ __device__ __forceinline__ int kdot(int qd, int k, int acc)
     else return __builtin_amdgcn_sdot4(qd, k, acc, false);
 }
 
+// First dot of a sum: the three-operand form with an inline zero accumulator
+// (the two-operand form accumulates into its destination, which the compiler
+// would first clear with a move).
+template <int KB>
+__device__ __forceinline__ int kdot0(int qd, int k)
+{
+    int r;
+    if constexpr (KB == 4) asm("v_dot8_i32_i4 %0, %1, %2, 0" : "=v"(r) : "s"(qd), "v"(k));
+    else asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "s"(qd), "v"(k));
+    return r;
+}
+
 __device__ __forceinline__ uint32_t kword(const uint4 &r, int i)
 {
     return (i & 3) == 0 ? r.x : (i & 3) == 1 ? r.y : (i & 3) == 2 ? r.z : r.w;
 }
 
-// Exact sum_c q_int[h][c] * code[c] over key dwords [c0, c1) of one row,
-// digit-major Horner (highest digit first, acc *= base between digits).
-// c0, c1 are compile-time constants after unrolling at every call.
-template <int KB, int VB, int HD, int G>
-__device__ __forceinline__ void key_dots(const uint4 (&kr)[QT<KB, VB, HD, G>::K_U4], const KVQ_CONST int32_t *qd,
-                                         int c0, int c1, int (&acc)[G])
+// Pack the low and high bytes of four 16-bit weights (each held as the bits
+// of 1.5 * 2^23 + w, i.e. w in the low mantissa bits) into two words, byte k
+// of each word belonging to position k.
+__device__ __forceinline__ void pack_w(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, uint32_t &lo, uint32_t &hi)
 {
-    using T = QT<KB, VB, HD, G>;
-#pragma unroll
-    for (int h = 0; h < G; h++) acc[h] = 0;
-#pragma unroll
-    for (int j = T::ND - 1; j >= 0; j--) {
-        if (j < T::ND - 1) {
-#pragma unroll
-            for (int h = 0; h < G; h++) acc[h] *= T::DBASE;
-        }
-#pragma unroll
-        for (int col = 0; col < T::K_COLS; col++) {
-            if (col < c0 || col >= c1) continue;
-            if (((col - c0) & 1) == 0)
-                asm volatile("" : "+s"(qd));         // at most two digit columns in SGPRs at once
-            const int kw = (int)kword(kr[col / 4], col);
-#pragma unroll
-            for (int h = 0; h < G; h++) acc[h] = kdot<KB>(qd[(j * T::K_COLS + col) * G + h], kw, acc[h]);
-        }
-    }
+    const uint32_t x01 = __builtin_amdgcn_perm(w1, w0, 0x05010400u);   // w0.b0 w1.b0 w0.b1 w1.b1
+    const uint32_t x23 = __builtin_amdgcn_perm(w3, w2, 0x05010400u);   // w2.b0 w3.b0 w2.b1 w3.b1
+    lo = __builtin_amdgcn_perm(x23, x01, 0x05040100u);
+    hi = __builtin_amdgcn_perm(x23, x01, 0x07060302u);
 }
 
-// KGM = 1: one key scale per row (groups of head_dim or per-position scales);
-// KGM = 4: up to 4 scale groups per row, summed per 32-channel block.
-template <int KB, int VB, int HD, int G, int KGM>
+// KG = scale groups per head row for both keys and values (1: groups of
+// head_dim, or one scale per position shared by all heads; 2 or 4: groups of
+// head_dim / KG channels); key dots are summed per group.
+// per 32-channel block.
+template <int KB, int VB, int HD, int G, int KG>
 __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
 {
     using T = QT<KB, VB, HD, G>;
     extern __shared__ __align__(16) unsigned char smem[];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index as a wave-uniform (scalar) value, so that everything derived
+    // from it (the wave's range, its buffer descriptors) stays in SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int chunk_id = blockIdx.x;
     const int bh = blockIdx.y;
     const int b = bh / p.n_kv_heads;
@@ -246,7 +245,7 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
         return;
     }
 
-    const QuantSmem lay = quant_smem(G, HD, CH, p.vg);
+    const QuantSmem lay = quant_smem(G, HD, CH, KG);
     float *zs = reinterpret_cast<float *>(smem + lay.zs);
     float *vs = reinterpret_cast<float *>(smem + lay.vs);
     float *red = reinterpret_cast<float *>(smem + lay.red);
@@ -261,94 +260,100 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
 
     const int sub = CH / QD_WAVES;                   // positions per wave (multiple of 16)
     const int s0 = wave * sub;
-    const int s1 = min(s0 + sub, n_tok);             // may be <= s0
+    const int nw = max(min(sub, n_tok - s0), 0);     // positions of this wave
     // this wave's weight words: over its own scores when there is one value group
     uint32_t *wdw = lay.wd_alias ? reinterpret_cast<uint32_t *>(zs + (size_t)s0 * G)
-                                 : reinterpret_cast<uint32_t *>(smem + lay.wd) + (size_t)wave * p.vg * (sub / 4) * G * 2;
+                                 : reinterpret_cast<uint32_t *>(smem + lay.wd) + (size_t)wave * KG * (sub / 4) * G * 2;
 
     float qs[G];
 #pragma unroll
     for (int h = 0; h < G; h++) qs[h] = p.qsc[row0 + h];
 
-    // ---------------- pass 1: scores ------------------------------------
+    // ---------------- pass 1: scores (unscaled: z = sum q_int * code * s_k) ----
     float mloc[G];
 #pragma unroll
     for (int h = 0; h < G; h++) mloc[h] = -INFINITY;
-    float vmloc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float vmloc[KG];
+#pragma unroll
+    for (int g = 0; g < KG; g++) vmloc[g] = 0.0f;
     {
-        const uint8_t *kbase = p.k_codes + ((size_t)bh * p.capacity + t0) * T::K_ROW;
-        const uint16_t *ksrc = p.k_scales + b * p.k_sc_b + kvh * p.k_sc_h + (size_t)t0 * p.k_sc_t;
-        const uint16_t *vsrc = p.v_scales + b * p.v_sc_b + kvh * p.v_sc_h + (size_t)t0 * p.v_sc_t;
-        const KVQ_CONST int32_t *qd = (const KVQ_CONST int32_t *)(p.qdig + (size_t)bh * T::ND * T::K_COLS * G);
-        // Everything a tile needs (key row, key scales, value scales) is
-        // loaded one tile ahead, so the loads of tile i+1 are in flight while
-        // tile i computes: the vector-memory counter retires loads in order,
-        // and consuming a load issued in the same iteration would wait for
-        // the prefetch too.
-        constexpr int NKS = KGM;                     // key scales per row loaded
-        uint4 kr[T::K_U4];
-        // (scales kept one per 32-bit register: packing two 16-bit loads into
-        // one register would make the compiler wait for them at once)
-        uint32_t ksr[NKS], vsr[4];
-        // Loads are unconditional (positions past the end read the last
-        // valid row and are ignored), so the code stays straight-line and the
-        // compiler can wait for exactly the previous tile's loads.
-        const int t_last = s1 - 1;                   // >= 0: the chunk has a position
-        auto load_tile = [&](int t, uint4 (&k)[T::K_U4], uint32_t (&ks)[NKS], uint32_t (&vv)[4]) {
-            const int ts = min(t, t_last);
-#pragma unroll
-            for (int u = 0; u < T::K_U4; u++) k[u] = ld_u4(kbase + (size_t)ts * T::K_ROW + u * 16);
-#pragma unroll
-            for (int g = 0; g < NKS; g++) ks[g] = ld_u16(ksrc + (size_t)ts * p.k_sc_t + min(g, p.kg - 1));
-#pragma unroll
-            for (int g = 0; g < 4; g++) vv[g] = ld_u16(vsrc + (size_t)ts * p.v_sc_t + min(g, p.vg - 1));
+        const uint8_t *kb0 = p.k_codes + ((size_t)bh * p.capacity + t0 + s0) * T::K_ROW;
+        const uint16_t *ks0 = p.k_scales + b * p.k_sc_b + kvh * p.k_sc_h + (size_t)(t0 + s0) * p.k_sc_t;
+        const uint16_t *vs0 = p.v_scales + b * p.v_sc_b + kvh * p.v_sc_h + (size_t)(t0 + s0) * p.v_sc_t;
+        const KVQ_CONST int32_t *qd = (const KVQ_CONST int32_t *)(p.qdig + (size_t)bh * T::K_COLS * T::ND * G);
+        const uint32_t ko = lane * T::K_ROW;         // this lane's row within a tile
+        const uint32_t kso = lane * p.k_sc_t * 2, vso = lane * p.v_sc_t * 2;
+        constexpr int CPB = T::K_COLS / KG;                    // key dwords per scale group
+        struct Tile {
+            uint4 k[T::K_U4];
+            uint32_t ks[KG], vs[KG];
         };
-        load_tile(s0 + lane, kr, ksr, vsr);
-        for (int tb = s0; tb < s1; tb += 64) {
-            const int t = tb + lane;
-            const bool valid = t < s1;
-            uint4 kn[T::K_U4];
-            uint32_t ksn[NKS], vsn[4];
-            load_tile(t + 64, kn, ksn, vsn);
+        // Everything a tile needs is loaded one tile ahead into the other of
+        // two register sets (the loop is unrolled twice, so no copies and no
+        // waits on the newer loads); past the wave's range the buffer loads
+        // return zeros.
+        // (the descriptors move with the tile, so the per-lane offsets are
+        // loop-invariant and the pieces of a row use immediate offsets)
+        auto load = [&](int tb, Tile &d) {
+            const uint32_t rem = (uint32_t)max(nw - tb, 0);
+            const rsrc_t krs = make_rsrc(kb0 + (size_t)tb * T::K_ROW, rem * T::K_ROW);
+            const rsrc_t ksrs = make_rsrc(ks0 + (size_t)tb * p.k_sc_t, rem * p.k_sc_t * 2);
+            const rsrc_t vsrs = make_rsrc(vs0 + (size_t)tb * p.v_sc_t, rem * p.v_sc_t * 2);
+#pragma unroll
+            for (int u = 0; u < T::K_U4; u++) d.k[u] = bld_u4(krs, ko + u * 16);
+#pragma unroll
+            for (int g = 0; g < KG; g++) {
+                d.ks[g] = bld_u16(ksrs, kso + 2 * g);
+                d.vs[g] = bld_u16(vsrs, vso + 2 * g);
+            }
+        };
+        auto compute = [&](int tb, const Tile &c) {
+            const int t = tb + lane;                           // position within the wave
+            const bool valid = t < nw;
             // value scales of this position -> LDS, running max per group
 #pragma unroll
-            for (int g = 0; g < 4; g++) {
-                if (g < p.vg) {
-                    const float sv = valid ? f16_bits_to_f32((uint16_t)vsr[g]) : 0.0f;
-                    if (valid) vs[t * p.vg + g] = sv;
-                    vmloc[g] = fmaxf(vmloc[g], sv);
-                }
+            for (int g = 0; g < KG; g++) {
+                // (zero past the wave's range: the load returned zero)
+                const float sv = f16_bits_to_f32((uint16_t)c.vs[g]);
+                if (valid) vs[(s0 + t) * KG + g] = sv;
+                vmloc[g] = fmax_nc(vmloc[g], sv);
             }
-            const KVQ_CONST int32_t *qdl = qd;
-            asm volatile("" : "+s"(qdl));            // keep the digit loads inside the loop
+            // an opaque zero offset, redefined every tile, keeps the digit
+            // loads inside the loop (hoisted, they would need 256 SGPRs)
+            int qz;
+            asm volatile("s_mov_b32 %0, 0" : "=s"(qz));
+            const KVQ_CONST int32_t *qdl = qd + qz;
             float z[G];
-            if constexpr (KGM == 1) {
-                int acc[G];
-                key_dots<KB, VB, HD, G>(kr, qdl, 0, T::K_COLS, acc);
-                const float sk = f16_bits_to_f32((uint16_t)ksr[0]);
 #pragma unroll
-                for (int h = 0; h < G; h++) z[h] = (float)acc[h] * sk;
-            } else {
+            for (int blk = 0; blk < KG; blk++) {
+                int acc[T::ND][G];
 #pragma unroll
-                for (int h = 0; h < G; h++) z[h] = 0.0f;
+                for (int cc = 0; cc < CPB; cc++) {
+                    const int col = blk * CPB + cc;
+                    const int kw = (int)kword(c.k[col / 4], col);
+                    const KVQ_CONST int32_t *qc = qdl + col * T::ND * G;
 #pragma unroll
-                for (int blk = 0; blk < HD / 32; blk++) {
-                    int acc[G];
-                    key_dots<KB, VB, HD, G>(kr, qdl, blk * T::BLK_COLS, (blk + 1) * T::BLK_COLS, acc);
-                    const int grp = (blk * 32) / p.k_group;
-                    const float sk = f16_bits_to_f32((uint16_t)(grp == 0 ? ksr[0] : grp == 1 ? ksr[NKS > 1 ? 1 : 0]
-                                                     : grp == 2 ? ksr[NKS > 2 ? 2 : 0] : ksr[NKS > 3 ? 3 : 0]));
+                    for (int j = 0; j < T::ND; j++)
 #pragma unroll
-                    for (int h = 0; h < G; h++) z[h] = fmaf((float)acc[h], sk, z[h]);
+                        for (int h = 0; h < G; h++)
+                            acc[j][h] = cc == 0 ? kdot0<KB>(qc[j * G + h], kw) : kdot<KB>(qc[j * G + h], kw, acc[j][h]);
                 }
+                // Horner over the digits: exact int32 sum of q_int * code
+                int tot[G];
+#pragma unroll
+                for (int h = 0; h < G; h++) {
+                    tot[h] = acc[T::ND - 1][h];
+#pragma unroll
+                    for (int j = T::ND - 2; j >= 0; j--) tot[h] = tot[h] * T::DBASE + acc[j][h];
+                }
+                const float sk = f16_bits_to_f32((uint16_t)c.ks[blk]);
+#pragma unroll
+                for (int h = 0; h < G; h++) z[h] = blk == 0 ? (float)tot[h] * sk : fmaf((float)tot[h], sk, z[h]);
             }
             if (valid) {
 #pragma unroll
-                for (int h = 0; h < G; h++) {
-                    z[h] *= qs[h];
-                    mloc[h] = fmaxf(mloc[h], z[h]);
-                }
-                float *dst = zs + (size_t)t * G;
+                for (int h = 0; h < G; h++) mloc[h] = fmax_nc(mloc[h], z[h]);
+                float *dst = zs + (size_t)(s0 + t) * G;
                 if constexpr (G % 4 == 0) {
 #pragma unroll
                     for (int h = 0; h < G; h += 4)
@@ -359,26 +364,29 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
                     dst[0] = z[0];
                 }
             }
-#pragma unroll
-            for (int u = 0; u < T::K_U4; u++) kr[u] = kn[u];
-#pragma unroll
-            for (int g = 0; g < NKS; g++) ksr[g] = ksn[g];
-#pragma unroll
-            for (int g = 0; g < 4; g++) vsr[g] = vsn[g];
+        };
+        // (both halves run unconditionally: a half past the end sees only
+        // invalid lanes and zero rows, and the code stays free of a merge
+        // point that would send the two register sets through memory)
+        Tile ta, tb_;
+        load(0, ta);
+        for (int tb = 0; tb < nw; tb += 128) {
+            load(tb + 64, tb_);
+            compute(tb, ta);
+            load(tb + 128, ta);
+            compute(tb + 64, tb_);
         }
     }
     // chunk maxima of the scores (per head) and of the value scales (per group)
 #pragma unroll
     for (int h = 0; h < G; h++) {
-        const float v = wave_max(mloc[h]);
+        const float v = wave_max_u(mloc[h]);
         if (lane == 0) part[wave * G + h] = v;
     }
 #pragma unroll
-    for (int g = 0; g < 4; g++) {
-        if (g < p.vg) {
-            const float v = wave_max(vmloc[g]);
-            if (lane == 0) vpart[wave * 4 + g] = v;
-        }
+    for (int g = 0; g < KG; g++) {
+        const float v = wave_max_u(vmloc[g]);
+        if (lane == 0) vpart[wave * 4 + g] = v;
     }
     __syncthreads();
     if (tid < G) {
@@ -386,7 +394,7 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
 #pragma unroll
         for (int w = 1; w < QD_WAVES; w++) v = fmaxf(v, part[w * G + tid]);
         m_sh[tid] = v;
-    } else if (tid >= 64 && tid < 64 + p.vg) {
+    } else if (tid >= 64 && tid < 64 + KG) {
         const int g = tid - 64;
         float v = vpart[g];
 #pragma unroll
@@ -396,32 +404,38 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
     __syncthreads();
 
     // ---------------- pass 2: weights, one lane per 4 positions ---------------
+    // p = 2^(qs * (z - m)) <= 1; w_int = rint(p * s_v * 32767 / max s_v),
+    // rounded by one fma onto 1.5 * 2^23 (the integer lands in the low
+    // mantissa bits); bytes packed four positions per word.
     {
-        float mh[G], lloc[G];
+        constexpr float MAGIC = 12582912.0f;         // 1.5 * 2^23
+        float nqm[G], lloc[G];
 #pragma unroll
         for (int h = 0; h < G; h++) {
-            mh[h] = m_sh[h];
+            nqm[h] = -m_sh[h] * qs[h];
             lloc[h] = 0.0f;
         }
-        int wsl[4][G];
+        int wsl[KG][G];
 #pragma unroll
-        for (int g = 0; g < 4; g++)
+        for (int g = 0; g < KG; g++)
 #pragma unroll
             for (int h = 0; h < G; h++) wsl[g][h] = 0;
-        float fsc[4];
+        float fsc[KG];
 #pragma unroll
-        for (int g = 0; g < 4; g++) {
-            const float vmax = g < p.vg ? vmax_sh[g] : 0.0f;
-            fsc[g] = vmax > 0.0f ? (float)W_RANGE / vmax : 0.0f;
+        for (int g = 0; g < KG; g++) {
+            const float vmax = vmax_sh[g];
+            fsc[g] = vmax > 0.0f ? (float)W_RANGE * __builtin_amdgcn_rcpf(vmax) : 0.0f;
         }
-        for (int tb = s0; tb < s1; tb += 256) {
-            const int tq = tb + 4 * lane;                // first position of this lane's group
-            if (tq < s1) {
+        const int ngw = (nw + 3) >> 2;               // groups of 4 positions
+        for (int gb = 0; gb < ngw; gb += 64) {
+            const int grp = gb + lane;
+            if (grp < ngw) {
+                const int tq = 4 * grp;              // first position of the group (within the wave)
                 float pr[4][G];
 #pragma unroll
                 for (int k = 0; k < 4; k++) {
-                    const bool valid = tq + k < s1;
-                    const float *src = zs + (size_t)(tq + k) * G;
+                    const bool valid = tq + k < nw;
+                    const float *src = zs + (size_t)(s0 + tq + k) * G;
                     float zz[G];
                     if constexpr (G % 4 == 0) {
 #pragma unroll
@@ -437,28 +451,26 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
                     }
 #pragma unroll
                     for (int h = 0; h < G; h++) {
-                        pr[k][h] = valid ? __builtin_amdgcn_exp2f(zz[h] - mh[h]) : 0.0f;
+                        pr[k][h] = valid ? __builtin_amdgcn_exp2f(fmaf(zz[h], qs[h], nqm[h])) : 0.0f;
                         lloc[h] += pr[k][h];
                     }
                 }
-                const int rg = (tq - s0) >> 2;           // group index within the wave
 #pragma unroll
-                for (int g = 0; g < 4; g++) {
-                    if (g < p.vg) {
+                for (int g = 0; g < KG; g++) {
+                    {
                         float sv[4];
 #pragma unroll
-                        for (int k = 0; k < 4; k++) sv[k] = tq + k < s1 ? vs[(tq + k) * p.vg + g] * fsc[g] : 0.0f;
-                        uint32_t *dst = wdw + ((size_t)g * (sub / 4) + rg) * G * 2;
+                        for (int k = 0; k < 4; k++) sv[k] = tq + k < nw ? vs[(s0 + tq + k) * KG + g] * fsc[g] : 0.0f;
+                        uint32_t *dst = wdw + ((size_t)g * (sub / 4) + grp) * G * 2;
 #pragma unroll
                         for (int h = 0; h < G; h++) {
-                            uint32_t lo = 0, hi = 0;
+                            uint32_t wb[4];
 #pragma unroll
-                            for (int k = 0; k < 4; k++) {
-                                const int wi = (int)rintf(fminf(pr[k][h] * sv[k], (float)W_RANGE));
-                                wsl[g][h] += wi;
-                                lo |= (uint32_t)(wi & 0xFF) << (8 * k);
-                                hi |= (uint32_t)(wi >> 8) << (8 * k);
-                            }
+                            for (int k = 0; k < 4; k++) wb[k] = __builtin_bit_cast(uint32_t, fmaf(pr[k][h], sv[k], MAGIC));
+                            uint32_t lo, hi;
+                            pack_w(wb[0], wb[1], wb[2], wb[3], lo, hi);
+                            wsl[g][h] += (int)__builtin_amdgcn_udot4(lo, 0x01010101u, 0u, false)
+                                       + 256 * (int)__builtin_amdgcn_udot4(hi, 0x01010101u, 0u, false);
                             dst[2 * h] = lo;
                             dst[2 * h + 1] = hi;
                         }
@@ -468,17 +480,15 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
         }
 #pragma unroll
         for (int h = 0; h < G; h++) {
-            const float v = wave_sum(lloc[h]);
+            const float v = wave_sum_u(lloc[h]);
             if (lane == 0) lpart[wave * G + h] = v;
         }
 #pragma unroll
-        for (int g = 0; g < 4; g++) {
-            if (g < p.vg) {
+        for (int g = 0; g < KG; g++) {
+            {
 #pragma unroll
                 for (int h = 0; h < G; h++) {
-                    int v = wsl[g][h];
-#pragma unroll
-                    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+                    const int v = wave_sum_ui(wsl[g][h]);
                     if (lane == 0) wsum[(wave * 4 + g) * G + h] = (float)v;
                 }
             }
@@ -495,31 +505,26 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
 #pragma unroll
         for (int c = 0; c < T::V_ACC; c++) accl[h][c] = acch[h][c] = 0u;
     {
-        constexpr int PF = 8;                        // group loads per lane in flight
-        const int ng = (s1 - s0 + 3) >> 2;           // groups of this wave with a valid position
-        const int vgrp = (qsl * T::V_DPL * T::V_CPD) / p.v_group;
+        constexpr uint32_t GSTEP = T::V_GPL * 4 * T::V_ROW;   // bytes per wave-wide group load
+        constexpr int PF = GSTEP * 16 <= 4096 ? 16 : 8;       // group loads in flight per lane
+        const int ng = (nw + 3) >> 2;                // groups of this wave with a valid position
+        const int vgrp = (qsl * T::V_DPL * T::V_CPD) / (HD / KG);   // value scale group of the lane
         const uint32_t *wdg = wdw + (size_t)vgrp * (sub / 4) * G * 2;
-        const uint8_t *vbase = p.v_codes + ((size_t)bh * p.cap4 + t0 + s0) * T::V_ROW + qsl * T::V_DPL * 4;
-        // unconditional loads (groups past the end re-read the last one and
-        // are skipped), one batch of PF groups ahead
-        const int g_last = ng - 1;
-        uint32_t cur[PF][T::V_DPL];
+        const uint8_t *vb0 = p.v_codes + ((size_t)bh * p.cap4 + t0 + s0) * T::V_ROW;
+        const uint32_t vo = gi * 4 * T::V_ROW + qsl * T::V_DPL * 4;   // loop-invariant lane offset
+        // rotating buffer: slot f is consumed, then reloaded one batch (PF
+        // loads) ahead; the descriptor moves with the batch
+        uint32_t buf[PF][T::V_DPL];
+        {
+            const rsrc_t vrs = make_rsrc(vb0, (uint32_t)ng * 4 * T::V_ROW);
 #pragma unroll
-        for (int f = 0; f < PF; f++) {
-            const int rg = max(min(f * T::V_GPL + gi, g_last), 0);
+            for (int f = 0; f < PF; f++)
 #pragma unroll
-            for (int d = 0; d < T::V_DPL; d++)
-                cur[f][d] = *(const KVQ_GLOBAL uint32_t *)(vbase + (size_t)rg * 4 * T::V_ROW + d * 4);
+                for (int d = 0; d < T::V_DPL; d++) buf[f][d] = bld_u32(vrs, vo + f * GSTEP + d * 4);
         }
         for (int rb = 0; rb < ng; rb += PF * T::V_GPL) {
-            uint32_t nxt[PF][T::V_DPL];
-#pragma unroll
-            for (int f = 0; f < PF; f++) {
-                const int rg = min(rb + (PF + f) * T::V_GPL + gi, g_last);
-#pragma unroll
-                for (int d = 0; d < T::V_DPL; d++)
-                    nxt[f][d] = *(const KVQ_GLOBAL uint32_t *)(vbase + (size_t)rg * 4 * T::V_ROW + d * 4);
-            }
+            const int nb = rb + PF * T::V_GPL;               // first group of the next batch
+            const rsrc_t vrs = make_rsrc(vb0 + (size_t)nb * 4 * T::V_ROW, (uint32_t)max(ng - nb, 0) * 4 * T::V_ROW);
 #pragma unroll
             for (int f = 0; f < PF; f++) {
                 const int rg = rb + f * T::V_GPL + gi;
@@ -534,7 +539,7 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
 #pragma unroll
                     for (int d = 0; d < T::V_DPL; d++) {
                         if constexpr (VB == 4) {
-                            const uint32_t u = cur[f][d] ^ 0x88888888u;   // offset binary per nibble
+                            const uint32_t u = buf[f][d] ^ 0x88888888u;    // offset binary per nibble
                             const uint32_t ulo = u & 0x0F0F0F0Fu;          // even channel, 4 positions
                             const uint32_t uhi = u & 0xF0F0F0F0u;          // odd channel, x16
 #pragma unroll
@@ -545,7 +550,7 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
                                 acch[h][2 * d + 1] = __builtin_amdgcn_udot4(wh[h], uhi, acch[h][2 * d + 1], false);
                             }
                         } else {
-                            const uint32_t u = cur[f][d] ^ 0x80808080u;   // offset binary per byte
+                            const uint32_t u = buf[f][d] ^ 0x80808080u;    // offset binary per byte
 #pragma unroll
                             for (int h = 0; h < G; h++) {
                                 accl[h][d] = __builtin_amdgcn_udot4(wl[h], u, accl[h][d], false);
@@ -554,11 +559,9 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
                         }
                     }
                 }
+#pragma unroll
+                for (int d = 0; d < T::V_DPL; d++) buf[f][d] = bld_u32(vrs, vo + f * GSTEP + d * 4);
             }
-#pragma unroll
-            for (int f = 0; f < PF; f++)
-#pragma unroll
-                for (int d = 0; d < T::V_DPL; d++) cur[f][d] = nxt[f][d];
         }
     }
 
@@ -579,7 +582,6 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
     }
     __syncthreads();                                 // every wave is done with scores and weights
     if (gi == 0) {
-        // lane's channels: byte positions qsl*V_DPL + d -> V4: channels 2(...), 2(...)+1; V8: (...)
 #pragma unroll
         for (int h = 0; h < G; h++)
 #pragma unroll
@@ -591,7 +593,7 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
         float s = 0.0f, wtot = 0.0f;
 #pragma unroll
         for (int w = 0; w < QD_WAVES; w++) s += red[(w * G + h) * HD + c];
-        const int g = p.vg == 1 ? 0 : c / p.v_group;  // scale group of channel c
+        const int g = c / (HD / KG);                 // scale group of channel c
 #pragma unroll
         for (int w = 0; w < QD_WAVES; w++) wtot += wsum[(w * 4 + g) * G + h];
         // V4 odd channels accumulated 16u; the codes are u - 8 (V4) or u - 128 (V8)
@@ -603,7 +605,7 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
         float lt = 0.0f;
 #pragma unroll
         for (int w = 0; w < QD_WAVES; w++) lt += lpart[w * G + tid];
-        ml0[tid * ml_hs] = m_sh[tid];
+        ml0[tid * ml_hs] = m_sh[tid] * p.qsc[row0 + tid];   // back to log2 units
         ml0[tid * ml_hs + 1] = lt;
     }
 }

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <limits.h>
 
 namespace kvq {
 
@@ -65,5 +66,91 @@ __device__ __forceinline__ uint2 ld_u2(const void *p)
     return make_uint2(v.x, v.y);
 }
 __device__ __forceinline__ uint16_t ld_u16(const void *p) { return *(const KVQ_GLOBAL uint16_t *)p; }
+
+// max of two floats as one v_max_f32 (fmaxf also quiets signalling NaNs
+// first, one extra instruction per operand; the values here are never NaN)
+__device__ __forceinline__ float fmax_nc(float a, float b)
+{
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+// ------------------------------------------------------- buffer resources
+// Raw buffer (stride 0) over [base, base + n_bytes): loads take a 32-bit
+// byte offset, and a load past n_bytes returns zero without touching memory,
+// so tails need neither clamping nor branches.  Third descriptor word as
+// documented for gfx9-family GPUs.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t n_bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n_bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bld_u4(rsrc_t r, uint32_t off)
+{
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t bld_u32(rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bld_u16(rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+
+// ------------------------------------------- DPP wave reductions (uniform)
+// In-row steps (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+// row_mirror) leave every lane with its 16-lane row total; row_bcast:15 into
+// rows 1 and 3, then row_bcast:31 into rows 2 and 3, leave the wave total in
+// lane 63, which is read back as a wave-uniform value.  Rows a broadcast
+// does not write keep the operation's identity.  All 64 lanes must be active.
+template <int CTRL, int ROWS = 0xF, bool BC = false>
+__device__ __forceinline__ int dpp_i(int old, int v)
+{
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xF, BC);
+}
+__device__ __forceinline__ int wave_max_ui(int v)
+{
+    v = max(v, dpp_i<0xB1, 0xF, true>(0, v));
+    v = max(v, dpp_i<0x4E, 0xF, true>(0, v));
+    v = max(v, dpp_i<0x141, 0xF, true>(0, v));
+    v = max(v, dpp_i<0x140, 0xF, true>(0, v));
+    v = max(v, dpp_i<0x142, 0xA>(INT_MIN, v));
+    v = max(v, dpp_i<0x143, 0xC>(INT_MIN, v));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ int wave_sum_ui(int v)
+{
+    v += dpp_i<0xB1, 0xF, true>(0, v);
+    v += dpp_i<0x4E, 0xF, true>(0, v);
+    v += dpp_i<0x141, 0xF, true>(0, v);
+    v += dpp_i<0x140, 0xF, true>(0, v);
+    v += dpp_i<0x142, 0xA>(0, v);
+    v += dpp_i<0x143, 0xC>(0, v);
+    return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ float wave_sum_u(float v)
+{
+    auto f = [](int x) { return __builtin_bit_cast(float, x); };
+    auto i = [](float x) { return __builtin_bit_cast(int, x); };
+    v += f(dpp_i<0xB1, 0xF, true>(0, i(v)));
+    v += f(dpp_i<0x4E, 0xF, true>(0, i(v)));
+    v += f(dpp_i<0x141, 0xF, true>(0, i(v)));
+    v += f(dpp_i<0x140, 0xF, true>(0, i(v)));
+    v += f(dpp_i<0x142, 0xA>(0, i(v)));
+    v += f(dpp_i<0x143, 0xC>(0, i(v)));
+    return f(__builtin_amdgcn_readlane(i(v), 63));
+}
+// Order-preserving map of non-NaN floats to int32 (an involution): flips the
+// magnitude bits of negative values, so integer max is float max.
+__device__ __forceinline__ int f2ord(float x)
+{
+    const int b = __builtin_bit_cast(int, x);
+    return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float ord2f(int k) { return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7FFFFFFF)); }
+__device__ __forceinline__ float wave_max_u(float v) { return ord2f(wave_max_ui(f2ord(v))); }
 
 } // namespace kvq
