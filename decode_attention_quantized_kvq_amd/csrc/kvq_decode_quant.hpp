@@ -113,7 +113,7 @@ __host__ __device__ inline QuantSmem quant_smem(int G, int HD, int chunk, int vg
         off += red;
     }
     s.misc = off;
-    off += (2 * G + 8 + QD_WAVES * G + QD_WAVES * 4 + QD_WAVES * G + QD_WAVES * 4 * G) * 4;
+    off += 2 * QD_WAVES * G * 4;                   // wave maxima and sums
     s.total = off;
     return s;
 }
@@ -250,13 +250,6 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
     float *vs = reinterpret_cast<float *>(smem + lay.vs);
     float *red = reinterpret_cast<float *>(smem + lay.red);
     float *misc = reinterpret_cast<float *>(smem + lay.misc);
-    float *m_sh = misc;                              // [G]
-    float *l_sh = m_sh + G;                          // [G]
-    float *vmax_sh = l_sh + G;                       // [4] (8 reserved)
-    float *part = vmax_sh + 8;                       // [QD_WAVES][G]
-    float *vpart = part + QD_WAVES * G;              // [QD_WAVES][4]
-    float *lpart = vpart + QD_WAVES * 4;             // [QD_WAVES][G]
-    float *wsum = lpart + QD_WAVES * G;              // [QD_WAVES][4][G]
 
     const int sub = CH / QD_WAVES;                   // positions per wave (multiple of 16)
     const int s0 = wave * sub;
@@ -324,6 +317,14 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
             asm volatile("s_mov_b32 %0, 0" : "=s"(qz));
             const KVQ_CONST int32_t *qdl = qd + qz;
             float z[G];
+            // The digits of column c come through a pointer that depends on
+            // every sum after column c - LAG, so about 96 digit words are in
+            // SGPRs at once (the scheduler would otherwise load them all early
+            // and spill).
+            constexpr int LAG = 96 / (T::ND * G) > 2 ? 96 / (T::ND * G) : 2;
+            const KVQ_CONST int32_t *ring[LAG];
+#pragma unroll
+            for (int i = 0; i < LAG; i++) ring[i] = qdl;
 #pragma unroll
             for (int blk = 0; blk < KG; blk++) {
                 int acc[T::ND][G];
@@ -331,12 +332,20 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
                 for (int cc = 0; cc < CPB; cc++) {
                     const int col = blk * CPB + cc;
                     const int kw = (int)kword(c.k[col / 4], col);
-                    const KVQ_CONST int32_t *qc = qdl + col * T::ND * G;
+                    const KVQ_CONST int32_t *qc = ring[0] + col * T::ND * G;
 #pragma unroll
                     for (int j = 0; j < T::ND; j++)
 #pragma unroll
                         for (int h = 0; h < G; h++)
                             acc[j][h] = cc == 0 ? kdot0<KB>(qc[j * G + h], kw) : kdot<KB>(qc[j * G + h], kw, acc[j][h]);
+#pragma unroll
+                    for (int i = 0; i + 1 < LAG; i++) ring[i] = ring[i + 1];
+                    const KVQ_CONST int32_t *qn = qdl;
+#pragma unroll
+                    for (int j = 0; j < T::ND; j++)
+#pragma unroll
+                        for (int h = 0; h < G; h++) asm("" : "+s"(qn) : "v"(acc[j][h]));
+                    ring[LAG - 1] = qn;
                 }
                 // Horner over the digits: exact int32 sum of q_int * code
                 int tot[G];
@@ -377,33 +386,46 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
             compute(tb + 64, tb_);
         }
     }
-    // chunk maxima of the scores (per head) and of the value scales (per group)
+    // ---------------- value prefetch ----------------------------------------
+    // The first batch of value loads is issued here, so that it is in flight
+    // during the reductions, the barrier and the weights pass.
+    // lane -> (group slot gi of a load, dword slice qsl of the group)
+    const int gi = lane / T::V_LPG;
+    const int qsl = lane % T::V_LPG;
+    constexpr uint32_t GSTEP = T::V_GPL * 4 * T::V_ROW;   // bytes per wave-wide group load
+    constexpr int PFH = GSTEP * 8 <= 4096 ? 8 : 4096 / GSTEP;     // loads per descriptor (offsets < 4 KiB)
+    constexpr int PF = 2 * PFH;                            // group loads in flight per lane
+    const int ng = (nw + 3) >> 2;                          // groups of this wave with a valid position
+    const uint8_t *vb0 = p.v_codes + ((size_t)bh * p.cap4 + t0 + s0) * T::V_ROW;
+    const uint32_t vo = gi * 4 * T::V_ROW + qsl * T::V_DPL * 4;   // loop-invariant lane offset
+    // descriptor half `hf` of the batch starting at group g0 (zero past the
+    // wave's groups)
+    auto vrsrc = [&](int g0, int hf) {
+        const int b0 = g0 * 4 * T::V_ROW + hf * PFH * (int)GSTEP;
+        return make_rsrc(vb0 + b0, (uint32_t)max(ng * 4 * T::V_ROW - b0, 0));
+    };
+    // rotating buffer: slot f is consumed, then reloaded one batch (PF loads)
+    // ahead; the descriptors move with the batch
+    uint32_t buf[PF][T::V_DPL];
+    {
+        const rsrc_t vra = vrsrc(0, 0), vrb = vrsrc(0, 1);
 #pragma unroll
-    for (int h = 0; h < G; h++) {
-        const float v = wave_max_u(mloc[h]);
-        if (lane == 0) part[wave * G + h] = v;
+        for (int f = 0; f < PF; f++)
+#pragma unroll
+            for (int d = 0; d < T::V_DPL; d++) buf[f][d] = bld_u32(f < PFH ? vra : vrb, vo + (f % PFH) * GSTEP + d * 4);
     }
+
+    // this wave's maxima of the scores (per head) and of the value scales
+    // (per group), wave-uniform; each wave weights its own positions against
+    // them and the waves are merged once, at the end
+    float mw[G], vmw[KG];
 #pragma unroll
-    for (int g = 0; g < KG; g++) {
-        const float v = wave_max_u(vmloc[g]);
-        if (lane == 0) vpart[wave * 4 + g] = v;
-    }
-    __syncthreads();
-    if (tid < G) {
-        float v = part[tid];
+    for (int h = 0; h < G; h++) mw[h] = wave_max_u(mloc[h]);
 #pragma unroll
-        for (int w = 1; w < QD_WAVES; w++) v = fmaxf(v, part[w * G + tid]);
-        m_sh[tid] = v;
-    } else if (tid >= 64 && tid < 64 + KG) {
-        const int g = tid - 64;
-        float v = vpart[g];
-#pragma unroll
-        for (int w = 1; w < QD_WAVES; w++) v = fmaxf(v, vpart[w * 4 + g]);
-        vmax_sh[g] = v;
-    }
-    __syncthreads();
+    for (int g = 0; g < KG; g++) vmw[g] = wave_max_u(vmloc[g]);
 
     // ---------------- pass 2: weights, one lane per 4 positions ---------------
+    float lw[G], wsw[KG][G];                         // this wave's sum of p and of w_int
     // p = 2^(qs * (z - m)) <= 1; w_int = rint(p * s_v * 32767 / max s_v),
     // rounded by one fma onto 1.5 * 2^23 (the integer lands in the low
     // mantissa bits); bytes packed four positions per word.
@@ -412,7 +434,7 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
         float nqm[G], lloc[G];
 #pragma unroll
         for (int h = 0; h < G; h++) {
-            nqm[h] = -m_sh[h] * qs[h];
+            nqm[h] = nw > 0 ? -mw[h] * qs[h] : 0.0f;
             lloc[h] = 0.0f;
         }
         int wsl[KG][G];
@@ -423,7 +445,7 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
         float fsc[KG];
 #pragma unroll
         for (int g = 0; g < KG; g++) {
-            const float vmax = vmax_sh[g];
+            const float vmax = vmw[g];
             fsc[g] = vmax > 0.0f ? (float)W_RANGE * __builtin_amdgcn_rcpf(vmax) : 0.0f;
         }
         const int ngw = (nw + 3) >> 2;               // groups of 4 positions
@@ -479,93 +501,83 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
             }
         }
 #pragma unroll
-        for (int h = 0; h < G; h++) {
-            const float v = wave_sum_u(lloc[h]);
-            if (lane == 0) lpart[wave * G + h] = v;
-        }
+        for (int h = 0; h < G; h++) lw[h] = wave_sum_u(lloc[h]);
 #pragma unroll
-        for (int g = 0; g < KG; g++) {
-            {
+        for (int g = 0; g < KG; g++)
 #pragma unroll
-                for (int h = 0; h < G; h++) {
-                    const int v = wave_sum_ui(wsl[g][h]);
-                    if (lane == 0) wsum[(wave * 4 + g) * G + h] = (float)v;
-                }
-            }
-        }
+            for (int h = 0; h < G; h++) wsw[g][h] = (float)wave_sum_ui(wsl[g][h]);
     }
 
     // ---------------- pass 3: values ---------------------------------------
-    // lane -> (group slot gi of the load, dword slice qsl of the group)
-    const int gi = lane / T::V_LPG;
-    const int qsl = lane % T::V_LPG;
     uint32_t accl[G][T::V_ACC], acch[G][T::V_ACC];
 #pragma unroll
     for (int h = 0; h < G; h++)
 #pragma unroll
         for (int c = 0; c < T::V_ACC; c++) accl[h][c] = acch[h][c] = 0u;
     {
-        constexpr uint32_t GSTEP = T::V_GPL * 4 * T::V_ROW;   // bytes per wave-wide group load
-        constexpr int PF = GSTEP * 16 <= 4096 ? 16 : 8;       // group loads in flight per lane
-        const int ng = (nw + 3) >> 2;                // groups of this wave with a valid position
         const int vgrp = (qsl * T::V_DPL * T::V_CPD) / (HD / KG);   // value scale group of the lane
         const uint32_t *wdg = wdw + (size_t)vgrp * (sub / 4) * G * 2;
-        const uint8_t *vb0 = p.v_codes + ((size_t)bh * p.cap4 + t0 + s0) * T::V_ROW;
-        const uint32_t vo = gi * 4 * T::V_ROW + qsl * T::V_DPL * 4;   // loop-invariant lane offset
-        // rotating buffer: slot f is consumed, then reloaded one batch (PF
-        // loads) ahead; the descriptor moves with the batch
-        uint32_t buf[PF][T::V_DPL];
-        {
-            const rsrc_t vrs = make_rsrc(vb0, (uint32_t)ng * 4 * T::V_ROW);
+        // one 4-position group: weight words of group rg (LDS broadcast) times
+        // the value codes this lane holds for it
+        auto group = [&](int rg, const uint32_t (&x)[T::V_DPL]) {
+            uint32_t wl[G], wh[G];
+            const uint32_t *src = wdg + (size_t)rg * G * 2;
 #pragma unroll
-            for (int f = 0; f < PF; f++)
+            for (int h = 0; h < G; h++) {
+                wl[h] = src[2 * h];
+                wh[h] = src[2 * h + 1];
+            }
 #pragma unroll
-                for (int d = 0; d < T::V_DPL; d++) buf[f][d] = bld_u32(vrs, vo + f * GSTEP + d * 4);
+            for (int d = 0; d < T::V_DPL; d++) {
+                if constexpr (VB == 4) {
+                    const uint32_t u = x[d] ^ 0x88888888u;        // offset binary per nibble
+                    const uint32_t ulo = u & 0x0F0F0F0Fu;          // even channel, 4 positions
+                    const uint32_t uhi = u & 0xF0F0F0F0u;          // odd channel, x16
+#pragma unroll
+                    for (int h = 0; h < G; h++) {
+                        accl[h][2 * d] = __builtin_amdgcn_udot4(wl[h], ulo, accl[h][2 * d], false);
+                        acch[h][2 * d] = __builtin_amdgcn_udot4(wh[h], ulo, acch[h][2 * d], false);
+                        accl[h][2 * d + 1] = __builtin_amdgcn_udot4(wl[h], uhi, accl[h][2 * d + 1], false);
+                        acch[h][2 * d + 1] = __builtin_amdgcn_udot4(wh[h], uhi, acch[h][2 * d + 1], false);
+                    }
+                } else {
+                    const uint32_t u = x[d] ^ 0x80808080u;        // offset binary per byte
+#pragma unroll
+                    for (int h = 0; h < G; h++) {
+                        accl[h][d] = __builtin_amdgcn_udot4(wl[h], u, accl[h][d], false);
+                        acch[h][d] = __builtin_amdgcn_udot4(wh[h], u, acch[h][d], false);
+                    }
+                }
+            }
+        };
+        // Full batches are straight-line code (the weight reads of later
+        // groups are issued early); the last, partial batch checks each group.
+        constexpr int PB = PF * T::V_GPL;                  // groups per batch
+        const int nfull = ng / PB * PB;
+        int rb = 0;
+        for (; rb < nfull; rb += PB) {
+            const int nb = rb + PB;                        // first group of the next batch
+            const rsrc_t vra = vrsrc(nb, 0), vrb = vrsrc(nb, 1);
+#pragma unroll
+            for (int f = 0; f < PF; f++) {
+                group(rb + f * T::V_GPL + gi, buf[f]);
+#pragma unroll
+                for (int d = 0; d < T::V_DPL; d++)
+                    buf[f][d] = bld_u32(f < PFH ? vra : vrb, vo + (f % PFH) * GSTEP + d * 4);
+            }
         }
-        for (int rb = 0; rb < ng; rb += PF * T::V_GPL) {
-            const int nb = rb + PF * T::V_GPL;               // first group of the next batch
-            const rsrc_t vrs = make_rsrc(vb0 + (size_t)nb * 4 * T::V_ROW, (uint32_t)max(ng - nb, 0) * 4 * T::V_ROW);
+        if (rb < ng) {
 #pragma unroll
             for (int f = 0; f < PF; f++) {
                 const int rg = rb + f * T::V_GPL + gi;
-                if (rg < ng) {
-                    uint32_t wl[G], wh[G];
-                    const uint32_t *src = wdg + (size_t)rg * G * 2;
-#pragma unroll
-                    for (int h = 0; h < G; h++) {
-                        wl[h] = src[2 * h];
-                        wh[h] = src[2 * h + 1];
-                    }
-#pragma unroll
-                    for (int d = 0; d < T::V_DPL; d++) {
-                        if constexpr (VB == 4) {
-                            const uint32_t u = buf[f][d] ^ 0x88888888u;    // offset binary per nibble
-                            const uint32_t ulo = u & 0x0F0F0F0Fu;          // even channel, 4 positions
-                            const uint32_t uhi = u & 0xF0F0F0F0u;          // odd channel, x16
-#pragma unroll
-                            for (int h = 0; h < G; h++) {
-                                accl[h][2 * d] = __builtin_amdgcn_udot4(wl[h], ulo, accl[h][2 * d], false);
-                                acch[h][2 * d] = __builtin_amdgcn_udot4(wh[h], ulo, acch[h][2 * d], false);
-                                accl[h][2 * d + 1] = __builtin_amdgcn_udot4(wl[h], uhi, accl[h][2 * d + 1], false);
-                                acch[h][2 * d + 1] = __builtin_amdgcn_udot4(wh[h], uhi, acch[h][2 * d + 1], false);
-                            }
-                        } else {
-                            const uint32_t u = buf[f][d] ^ 0x80808080u;    // offset binary per byte
-#pragma unroll
-                            for (int h = 0; h < G; h++) {
-                                accl[h][d] = __builtin_amdgcn_udot4(wl[h], u, accl[h][d], false);
-                                acch[h][d] = __builtin_amdgcn_udot4(wh[h], u, acch[h][d], false);
-                            }
-                        }
-                    }
-                }
-#pragma unroll
-                for (int d = 0; d < T::V_DPL; d++) buf[f][d] = bld_u32(vrs, vo + f * GSTEP + d * 4);
+                if (rg < ng) group(rg, buf[f]);
             }
         }
     }
 
-    // ---------------- pass 4: reduce, undo offsets, write ------------------
+    // ---------------- pass 4: per-wave values, merge the waves, write -------
+    // This wave's output (relative to its own maxima): undo the byte split,
+    // the x16 of odd V4 channels and the offset binary, then the fixed point.
     float af[G][T::V_ACC];
 #pragma unroll
     for (int h = 0; h < G; h++)
@@ -581,32 +593,54 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
                 for (int c = 0; c < T::V_ACC; c++) af[h][c] += __shfl_xor(af[h][c], m, 64);
     }
     __syncthreads();                                 // every wave is done with scores and weights
+    float *pm = misc;                                // [QD_WAVES][G] wave maxima
+    float *pl = pm + QD_WAVES * G;                   // [QD_WAVES][G] wave sums of p
     if (gi == 0) {
+        const float bias = VB == 4 ? 8.0f : 128.0f;
 #pragma unroll
-        for (int h = 0; h < G; h++)
+        for (int c = 0; c < T::V_ACC; c++) {
+            const int ch = qsl * T::V_ACC + c;       // channel
+            const int g = ch / (HD / KG);             // its scale group
 #pragma unroll
-            for (int c = 0; c < T::V_ACC; c++) red[(wave * G + h) * HD + qsl * T::V_ACC + c] = af[h][c];
+            for (int h = 0; h < G; h++) {
+                const float su = (VB == 4 && (c & 1)) ? af[h][c] * 0.0625f : af[h][c];
+                red[(wave * G + h) * HD + ch] = (su - bias * wsw[g][h]) * (vmw[g] * (1.0f / (float)W_RANGE));
+            }
+        }
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            pm[wave * G + h] = nw > 0 ? mw[h] * qs[h] : -INFINITY;   // log2 units
+            pl[wave * G + h] = lw[h];
+        }
     }
     __syncthreads();
     for (int i = tid; i < G * HD; i += QD_THREADS) {
         const int h = i / HD, c = i - h * HD;
-        float s = 0.0f, wtot = 0.0f;
+        float m = pm[h];
 #pragma unroll
-        for (int w = 0; w < QD_WAVES; w++) s += red[(w * G + h) * HD + c];
-        const int g = c / (HD / KG);                 // scale group of channel c
+        for (int w = 1; w < QD_WAVES; w++) m = fmaxf(m, pm[w * G + h]);
+        float s = 0.0f;
 #pragma unroll
-        for (int w = 0; w < QD_WAVES; w++) wtot += wsum[(w * 4 + g) * G + h];
-        // V4 odd channels accumulated 16u; the codes are u - 8 (V4) or u - 128 (V8)
-        const float su = (VB == 4 && (c & 1)) ? s * 0.0625f : s;
-        const float bias = VB == 4 ? 8.0f : 128.0f;
-        acc0[h * acc_hs + c] = (su - bias * wtot) * (vmax_sh[g] / (float)W_RANGE);
+        for (int w = 0; w < QD_WAVES; w++) {
+            const float mv = pm[w * G + h];
+            if (mv != -INFINITY) s = fmaf(__builtin_amdgcn_exp2f(mv - m), red[(w * G + h) * HD + c], s);
+        }
+        acc0[h * acc_hs + c] = s;
     }
     if (tid < G) {
-        float lt = 0.0f;
+        float m = pm[tid];
 #pragma unroll
-        for (int w = 0; w < QD_WAVES; w++) lt += lpart[w * G + tid];
-        ml0[tid * ml_hs] = m_sh[tid] * p.qsc[row0 + tid];   // back to log2 units
-        ml0[tid * ml_hs + 1] = lt;
+        for (int w = 1; w < QD_WAVES; w++) m = fmaxf(m, pm[w * G + tid]);
+        float l = 0.0f;
+#pragma unroll
+        for (int w = 0; w < QD_WAVES; w++) {
+            const float mv = pm[w * G + tid];
+            if (mv != -INFINITY) l = fmaf(__builtin_amdgcn_exp2f(mv - m), pl[w * G + tid], l);
+        }
+        ml0[tid * ml_hs] = m;
+        ml0[tid * ml_hs + 1] = l;
     }
 }
 
