@@ -47,7 +47,7 @@ bool bits_pair_ok(int kb, int vb)
 bool per_row(const kvq_cache *c) { return c->group_size == c->n_kv_heads * c->head_dim && c->group_size != c->head_dim; }
 
 constexpr size_t kMaxLds = 64 * 1024;    // largest workgroup LDS accepted
-constexpr size_t kAutoLds = 40 * 1024;   // the library's choice keeps 4 workgroups per CU
+constexpr size_t kAutoLds = 48 * 1024;   // the library's choice keeps 3 workgroups per CU
 
 // Geometry checks shared by every entry point (no pointer is read).
 int check_geometry(const kvq_cache *c)
@@ -465,8 +465,14 @@ int kvq_combine(int batch, int n_q_heads, int head_dim, int n_chunks, const void
     if (P > 0x7FFFFFFFull) return fail(KVQ_ERR_SHAPE, "too many rows");
     const float *ml = static_cast<const float *>(workspace);
     const float *acc = reinterpret_cast<const float *>(static_cast<const char *>(workspace) + align256(P * n_chunks * 2 * sizeof(float)));
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)P), dim3(head_dim), 0, static_cast<hipStream_t>(stream), ml, acc,
-                       out, n_chunks, head_dim);
+    const int rpb = 256 / head_dim;
+    const dim3 grid((unsigned)((P + rpb - 1) / rpb));
+    if (head_dim == 64)
+        hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(256), 0, static_cast<hipStream_t>(stream), ml, acc, out, n_chunks,
+                           (int)P);
+    else
+        hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(256), 0, static_cast<hipStream_t>(stream), ml, acc, out, n_chunks,
+                           (int)P);
     return hip_status("combine_kernel launch");
 }
 

@@ -317,10 +317,12 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
             asm volatile("s_mov_b32 %0, 0" : "=s"(qz));
             const KVQ_CONST int32_t *qdl = qd + qz;
             float z[G];
-            // The digits of column c come through a pointer that depends on
-            // every sum after column c - LAG, so about 96 digit words are in
-            // SGPRs at once (the scheduler would otherwise load them all early
-            // and spill).
+            // int4 keys: the digits of column c come through a pointer that
+            // depends on every sum after column c - LAG, so about 96 digit
+            // words are in SGPRs at once (the scheduler would otherwise load
+            // them all early and spill).  int8 keys (twice the columns, half
+            // the digits each) run faster with the scheduler's own deeper
+            // prefetch, spills included.
             constexpr int LAG = 96 / (T::ND * G) > 2 ? 96 / (T::ND * G) : 2;
             const KVQ_CONST int32_t *ring[LAG];
 #pragma unroll
@@ -344,7 +346,8 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
 #pragma unroll
                     for (int j = 0; j < T::ND; j++)
 #pragma unroll
-                        for (int h = 0; h < G; h++) asm("" : "+s"(qn) : "v"(acc[j][h]));
+                        for (int h = 0; h < G; h++)
+                            if constexpr (KB == 4) asm("" : "+s"(qn) : "v"(acc[j][h]));
                     ring[LAG - 1] = qn;
                 }
                 // Horner over the digits: exact int32 sum of q_int * code
