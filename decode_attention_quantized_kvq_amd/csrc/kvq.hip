@@ -110,7 +110,7 @@ size_t lds_bytes(const kvq_cache *c, int G, int chunk)
 {
     if (quant_modes(c)) {
         const int vg = groups_per_head(c);
-        return (size_t)quant_smem(G, c->head_dim, chunk, vg).total;
+        return (size_t)quant_smem(G, c->head_dim, vg).total;
     }
     return (size_t)float_smem(G, c->head_dim, chunk).total;
 }
@@ -123,13 +123,15 @@ int auto_chunk(const kvq_cache *c, int n_q_heads, int max_seq_len)
     const long long units = (long long)c->batch * c->n_kv_heads;
     const int L = max_len_of(c, max_seq_len);
     // The largest chunk that fits the LDS budget and still gives >= 8
-    // workgroups per CU over 256 CUs; when even 64-slot chunks cannot, the
-    // smallest chunk (most workgroups).
-    for (int ch = 4096; ch >= 64; ch >>= 1) {
+    // workgroups per CU over 256 CUs; when no chunk does, the smallest one
+    // (most workgroups): 64 slots, or 256 for integer caches, whose waves
+    // take 64 positions per step.
+    const int smallest = quant_modes(c) ? 256 : 64;
+    for (int ch = 4096; ch >= smallest; ch >>= 1) {
         if (lds_bytes(c, G, ch) > kAutoLds) continue;
         if (units * ((L + ch - 1) / ch) >= 2048) return ch;
     }
-    return 64;
+    return smallest;
 }
 
 using FloatFn = void (*)(FloatParams);

@@ -24,20 +24,22 @@
 // (|dw| <= max s_v / 65534); accumulation is exact in int32, then fp32.
 //
 // Workgroup = 4 waves = one context chunk of one (sequence, KV head); each
-// wave owns a quarter of the chunk.
-//   1. keys, one lane per position: scores (log2 units) -> LDS; the query
-//      digits are wave-uniform and come from SGPRs (prepared per (sequence,
-//      KV head) by qprep_kernel); value scales -> LDS; running maxima.
-//   -- workgroup barrier: chunk max of the scores and of the value scales --
-//   2. weights, one lane per four positions: p = 2^(z - max), l += p,
-//      w_int digits packed four positions per word -> LDS (over the wave's
-//      own scores).
+// wave owns a quarter of the chunk and streams it in sub-chunks of 256
+// positions, the key tiles and the value groups loaded ahead without a break
+// between sub-chunks.  Per sub-chunk:
+//   1. keys, one lane per position: scores -> LDS; the query digits are
+//      wave-uniform and come from SGPRs (prepared per (sequence, KV head) by
+//      qprep_kernel); value scales -> LDS; the sub-chunk's maxima (DPP).
+//   2. weights, one lane per four positions: p = 2^(z - max), w_int packed
+//      four positions per word -> LDS (over the sub-chunk's scores).
 //   3. values: a lane owns fixed byte positions (two channels) of every
-//      4-position group and accumulates v_dot4_u32_u8 over the wave's groups;
-//      the group's weight words are LDS broadcasts.
-//   -- workgroup barrier --
-//   4. sum the 4 waves, undo the offset binary and the fixed point, write the
-//      chunk's (m, l, acc).
+//      4-position group and accumulates v_dot4_u32_u8 over the sub-chunk's
+//      groups; the group's weight words are LDS broadcasts.
+//   4. the integer sums become floats (offset binary and fixed point undone)
+//      and are merged into the wave's running (max, sum, acc) with the usual
+//      2^(m - M) factors.
+// At the end the 4 waves are merged the same way through LDS and the chunk's
+// (m, l, acc) written.  LDS use does not depend on the chunk length.
 #pragma once
 
 #include "kvq_device.hpp"
@@ -46,6 +48,9 @@ namespace kvq {
 
 constexpr int QD_THREADS = 256;
 constexpr int QD_WAVES = QD_THREADS / 64;
+// positions per wave sub-chunk: 256, or 128 when many heads and scale
+// groups make the per-position LDS large
+__host__ __device__ constexpr int qd_sub(int G, int vg) { return G * vg >= 16 ? 128 : 256; }
 constexpr int Q_RANGE = 30000;
 constexpr int W_RANGE = 32767;
 
@@ -56,7 +61,6 @@ template <int KB, int VB, int HD, int G> struct QT {
     static constexpr int ND = KB == 4 ? 4 : 2;         // query digits
     static constexpr int DBASE = KB == 4 ? 16 : 256;   // digit base
     static constexpr int CPC = KB == 4 ? 8 : 4;        // channels per key dword
-    static constexpr int BLK_COLS = 32 / CPC;          // key dwords per 32-channel block
     static constexpr int V_ROW = HD * VB / 8;          // bytes per value row
     static constexpr int V_DW = V_ROW;                 // dwords per 4-position group
     static constexpr int V_DPL = V_DW >= 64 ? V_DW / 64 : 1;   // dwords per lane
@@ -71,7 +75,7 @@ struct QuantParams {
     const uint8_t *v_codes;    // [B][Hkv][cap4/4][V_ROW][4]  (4 positions interleaved per byte)
     const uint16_t *k_scales;
     const uint16_t *v_scales;
-    const int32_t *qdig;       // [B*Hkv][ND][K_COLS][G] packed query digits
+    const int32_t *qdig;       // [B*Hkv][ND][K_COLS][G] packed query digits (digit-major)
     const float *qsc;          // [B*Hq]: s_q * softmax_scale * log2(e)
     const int32_t *seq_len;
     float *ws_ml;
@@ -90,24 +94,29 @@ struct QuantSmem {
     bool wd_alias;             // weight words overwrite each wave's own scores
 };
 
-__host__ __device__ inline QuantSmem quant_smem(int G, int HD, int chunk, int vg)
+// Per wave: scores [S][G], value scales [S][vg], weight words
+// [vg][S/4][G][lo, hi] (over the scores when vg == 1); then the
+// cross-wave merge area (over the scores when it fits) and the wave maxima
+// and sums.
+__host__ __device__ inline QuantSmem quant_smem(int G, int HD, int vg)
 {
     QuantSmem s;
+    const int S = qd_sub(G, vg);
     int off = 0;
     s.zs = off;
-    off += chunk * G * 4;                          // scores [chunk][G]
+    off += QD_WAVES * S * G * 4;
     s.vs = off;
-    off += chunk * vg * 4;                         // value scales [chunk][vg]
+    off += QD_WAVES * S * vg * 4;
     s.wd_alias = vg == 1;
     if (s.wd_alias) {
         s.wd = s.zs;
     } else {
         s.wd = off;
-        off += vg * (chunk / 4) * G * 2 * 4;       // weight words [vg][chunk/4][G][lo, hi]
+        off += QD_WAVES * vg * (S / 4) * G * 2 * 4;
     }
     const int red = QD_WAVES * G * HD * 4;
-    if (chunk * G * 4 >= red) {
-        s.red = s.zs;                              // scores and weights are dead in pass 4
+    if (QD_WAVES * S * G * 4 >= red) {
+        s.red = s.zs;                              // scores and weights are dead by then
     } else {
         s.red = off;
         off += red;
@@ -123,8 +132,8 @@ __host__ __device__ inline QuantSmem quant_smem(int G, int HD, int chunk, int vg
 // s_q = max|q| / 30000 and q_int = rint(q / s_q) in [-30000, 30000], split
 // into ND balanced digits; digit j of the channels of key dword `col` is
 // packed like the codes (int4: channel 8col+i in nibble i; int8: channel
-// 4col+i in byte i) at qdig[unit][col][j][h], so the ND * G digit words of
-// one key dword are contiguous (one scalar load).
+// 4col+i in byte i) at qdig[unit][j][col][h] (digit-major, the order the
+// decode kernel reads them in).
 // ---------------------------------------------------------------------------
 template <int KB, int HD, int G>
 __global__ __launch_bounds__(256) void qprep_kernel(const float *__restrict__ q, int32_t *__restrict__ qdig,
@@ -164,7 +173,7 @@ __global__ __launch_bounds__(256) void qprep_kernel(const float *__restrict__ q,
             }
         }
 #pragma unroll
-        for (int j = 0; j < ND; j++) qdig[(((size_t)unit * K_COLS + col) * ND + j) * G + h] = (int32_t)d[j];
+        for (int j = 0; j < ND; j++) qdig[(((size_t)unit * ND + j) * K_COLS + col) * G + h] = (int32_t)d[j];
     }
     if (tid < G) qsc[unit * G + tid] = amax[tid] / (float)Q_RANGE * qk_scale;
 }
@@ -207,11 +216,11 @@ __device__ __forceinline__ void pack_w(uint32_t w0, uint32_t w1, uint32_t w2, ui
 // KG = scale groups per head row for both keys and values (1: groups of
 // head_dim, or one scale per position shared by all heads; 2 or 4: groups of
 // head_dim / KG channels); key dots are summed per group.
-// per 32-channel block.
 template <int KB, int VB, int HD, int G, int KG>
 __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
 {
     using T = QT<KB, VB, HD, G>;
+    constexpr int S = qd_sub(G, KG);
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -245,222 +254,255 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
         return;
     }
 
-    const QuantSmem lay = quant_smem(G, HD, CH, KG);
-    float *zs = reinterpret_cast<float *>(smem + lay.zs);
-    float *vs = reinterpret_cast<float *>(smem + lay.vs);
+    const QuantSmem lay = quant_smem(G, HD, KG);
+    float *zs = reinterpret_cast<float *>(smem + lay.zs) + wave * S * G;       // this wave's scores
+    float *vsl = reinterpret_cast<float *>(smem + lay.vs) + wave * S * KG;    // and value scales
+    uint32_t *wdw = lay.wd_alias ? reinterpret_cast<uint32_t *>(zs)
+                                 : reinterpret_cast<uint32_t *>(smem + lay.wd) + wave * KG * (S / 4) * G * 2;
     float *red = reinterpret_cast<float *>(smem + lay.red);
     float *misc = reinterpret_cast<float *>(smem + lay.misc);
 
-    const int sub = CH / QD_WAVES;                   // positions per wave (multiple of 16)
+    const int sub = CH / QD_WAVES;                   // positions per wave (multiple of 64)
     const int s0 = wave * sub;
     const int nw = max(min(sub, n_tok - s0), 0);     // positions of this wave
-    // this wave's weight words: over its own scores when there is one value group
-    uint32_t *wdw = lay.wd_alias ? reinterpret_cast<uint32_t *>(zs + (size_t)s0 * G)
-                                 : reinterpret_cast<uint32_t *>(smem + lay.wd) + (size_t)wave * KG * (sub / 4) * G * 2;
 
     float qs[G];
 #pragma unroll
     for (int h = 0; h < G; h++) qs[h] = p.qsc[row0 + h];
 
-    // ---------------- pass 1: scores (unscaled: z = sum q_int * code * s_k) ----
-    float mloc[G];
+    // ---- key stream: tiles of 64 positions, one lane per position, loaded
+    // one tile ahead into the other of two register sets; the descriptors
+    // move with the tile (past the wave's range the loads return zeros)
+    const uint8_t *kb0 = p.k_codes + ((size_t)bh * p.capacity + t0 + s0) * T::K_ROW;
+    const uint16_t *ks0 = p.k_scales + b * p.k_sc_b + kvh * p.k_sc_h + (size_t)(t0 + s0) * p.k_sc_t;
+    const uint16_t *vs0 = p.v_scales + b * p.v_sc_b + kvh * p.v_sc_h + (size_t)(t0 + s0) * p.v_sc_t;
+    const KVQ_CONST int32_t *qd = (const KVQ_CONST int32_t *)(p.qdig + (size_t)bh * T::ND * T::K_COLS * G);
+    const uint32_t ko = lane * T::K_ROW;
+    const uint32_t kso = lane * p.k_sc_t * 2, vso = lane * p.v_sc_t * 2;
+    struct Tile {
+        uint4 k[T::K_U4];
+        uint32_t ks[KG], vs[KG];
+    };
+    auto load = [&](int tb, Tile &d) {
+        const uint32_t rem = (uint32_t)max(nw - tb, 0);
+        const rsrc_t krs = make_rsrc(kb0 + (size_t)tb * T::K_ROW, rem * T::K_ROW);
+        const rsrc_t ksrs = make_rsrc(ks0 + (size_t)tb * p.k_sc_t, rem * p.k_sc_t * 2);
+        const rsrc_t vsrs = make_rsrc(vs0 + (size_t)tb * p.v_sc_t, rem * p.v_sc_t * 2);
 #pragma unroll
-    for (int h = 0; h < G; h++) mloc[h] = -INFINITY;
-    float vmloc[KG];
+        for (int u = 0; u < T::K_U4; u++) d.k[u] = bld_u4(krs, ko + u * 16);
 #pragma unroll
-    for (int g = 0; g < KG; g++) vmloc[g] = 0.0f;
-    {
-        const uint8_t *kb0 = p.k_codes + ((size_t)bh * p.capacity + t0 + s0) * T::K_ROW;
-        const uint16_t *ks0 = p.k_scales + b * p.k_sc_b + kvh * p.k_sc_h + (size_t)(t0 + s0) * p.k_sc_t;
-        const uint16_t *vs0 = p.v_scales + b * p.v_sc_b + kvh * p.v_sc_h + (size_t)(t0 + s0) * p.v_sc_t;
-        const KVQ_CONST int32_t *qd = (const KVQ_CONST int32_t *)(p.qdig + (size_t)bh * T::K_COLS * T::ND * G);
-        const uint32_t ko = lane * T::K_ROW;         // this lane's row within a tile
-        const uint32_t kso = lane * p.k_sc_t * 2, vso = lane * p.v_sc_t * 2;
-        constexpr int CPB = T::K_COLS / KG;                    // key dwords per scale group
-        struct Tile {
-            uint4 k[T::K_U4];
-            uint32_t ks[KG], vs[KG];
-        };
-        // Everything a tile needs is loaded one tile ahead into the other of
-        // two register sets (the loop is unrolled twice, so no copies and no
-        // waits on the newer loads); past the wave's range the buffer loads
-        // return zeros.
-        // (the descriptors move with the tile, so the per-lane offsets are
-        // loop-invariant and the pieces of a row use immediate offsets)
-        auto load = [&](int tb, Tile &d) {
-            const uint32_t rem = (uint32_t)max(nw - tb, 0);
-            const rsrc_t krs = make_rsrc(kb0 + (size_t)tb * T::K_ROW, rem * T::K_ROW);
-            const rsrc_t ksrs = make_rsrc(ks0 + (size_t)tb * p.k_sc_t, rem * p.k_sc_t * 2);
-            const rsrc_t vsrs = make_rsrc(vs0 + (size_t)tb * p.v_sc_t, rem * p.v_sc_t * 2);
+        for (int g = 0; g < KG; g++) {
+            d.ks[g] = bld_u16(ksrs, kso + 2 * g);
+            d.vs[g] = bld_u16(vsrs, vso + 2 * g);
+        }
+    };
+    float mloc[G], vmloc[KG];                        // per-lane maxima of the current sub-chunk
+    // scores of one tile (tb: first position of the tile within the wave;
+    // sc0: first position of the sub-chunk)
+    auto compute = [&](int tb, int sc0, const Tile &c) {
+        const int t = tb + lane;
+        const bool valid = t < nw;
 #pragma unroll
-            for (int u = 0; u < T::K_U4; u++) d.k[u] = bld_u4(krs, ko + u * 16);
+        for (int g = 0; g < KG; g++) {
+            // (zero past the wave's range: the load returned zero)
+            const float sv = f16_bits_to_f32((uint16_t)c.vs[g]);
+            if (valid) vsl[(t - sc0) * KG + g] = sv;
+            vmloc[g] = fmax_nc(vmloc[g], sv);
+        }
+        // an opaque zero offset, redefined every tile, keeps the digit loads
+        // inside the loop (hoisted, they would need hundreds of SGPRs)
+        int qz;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(qz));
+        const KVQ_CONST int32_t *qdl = qd + qz;
+        // int4 keys: the digits of step i come through a pointer that depends
+        // on the sums after step i - LAG, which bounds the digit words held in
+        // SGPRs (the scheduler would otherwise load them all early and spill).
+        // int8 keys (twice the columns) run faster with the scheduler's own
+        // deeper prefetch, spills included.
+        constexpr int LAG = 64 / G > 2 ? 64 / G : 2;
+        const KVQ_CONST int32_t *ring[LAG];
 #pragma unroll
-            for (int g = 0; g < KG; g++) {
-                d.ks[g] = bld_u16(ksrs, kso + 2 * g);
-                d.vs[g] = bld_u16(vsrs, vso + 2 * g);
-            }
-        };
-        auto compute = [&](int tb, const Tile &c) {
-            const int t = tb + lane;                           // position within the wave
-            const bool valid = t < nw;
-            // value scales of this position -> LDS, running max per group
+        for (int i = 0; i < LAG; i++) ring[i] = qdl;
+        constexpr int CPB = T::K_COLS / KG;          // key dwords per scale group
+        float z[G];
 #pragma unroll
-            for (int g = 0; g < KG; g++) {
-                // (zero past the wave's range: the load returned zero)
-                const float sv = f16_bits_to_f32((uint16_t)c.vs[g]);
-                if (valid) vs[(s0 + t) * KG + g] = sv;
-                vmloc[g] = fmax_nc(vmloc[g], sv);
-            }
-            // an opaque zero offset, redefined every tile, keeps the digit
-            // loads inside the loop (hoisted, they would need 256 SGPRs)
-            int qz;
-            asm volatile("s_mov_b32 %0, 0" : "=s"(qz));
-            const KVQ_CONST int32_t *qdl = qd + qz;
-            float z[G];
-            // int4 keys: the digits of column c come through a pointer that
-            // depends on every sum after column c - LAG, so about 96 digit
-            // words are in SGPRs at once (the scheduler would otherwise load
-            // them all early and spill).  int8 keys (twice the columns, half
-            // the digits each) run faster with the scheduler's own deeper
-            // prefetch, spills included.
-            constexpr int LAG = 96 / (T::ND * G) > 2 ? 96 / (T::ND * G) : 2;
-            const KVQ_CONST int32_t *ring[LAG];
+        for (int blk = 0; blk < KG; blk++) {
+            // digit-major Horner: acc = sum_j DBASE^j sum_col digit_j * code,
+            // the exact int32 sum of q_int * code over the group's channels
+            int acc[G];
 #pragma unroll
-            for (int i = 0; i < LAG; i++) ring[i] = qdl;
+            for (int j = T::ND - 1; j >= 0; j--) {
+                if (j < T::ND - 1) {
 #pragma unroll
-            for (int blk = 0; blk < KG; blk++) {
-                int acc[T::ND][G];
+                    for (int h = 0; h < G; h++) acc[h] *= T::DBASE;
+                }
 #pragma unroll
                 for (int cc = 0; cc < CPB; cc++) {
                     const int col = blk * CPB + cc;
                     const int kw = (int)kword(c.k[col / 4], col);
-                    const KVQ_CONST int32_t *qc = ring[0] + col * T::ND * G;
+                    const KVQ_CONST int32_t *qc = ring[0] + (j * T::K_COLS + col) * G;
 #pragma unroll
-                    for (int j = 0; j < T::ND; j++)
-#pragma unroll
-                        for (int h = 0; h < G; h++)
-                            acc[j][h] = cc == 0 ? kdot0<KB>(qc[j * G + h], kw) : kdot<KB>(qc[j * G + h], kw, acc[j][h]);
+                    for (int h = 0; h < G; h++)
+                        acc[h] = (j == T::ND - 1 && cc == 0) ? kdot0<KB>(qc[h], kw) : kdot<KB>(qc[h], kw, acc[h]);
 #pragma unroll
                     for (int i = 0; i + 1 < LAG; i++) ring[i] = ring[i + 1];
                     const KVQ_CONST int32_t *qn = qdl;
 #pragma unroll
-                    for (int j = 0; j < T::ND; j++)
-#pragma unroll
-                        for (int h = 0; h < G; h++)
-                            if constexpr (KB == 4) asm("" : "+s"(qn) : "v"(acc[j][h]));
+                    for (int h = 0; h < G; h++)
+                        if constexpr (KB == 4) asm("" : "+s"(qn) : "v"(acc[h]));
                     ring[LAG - 1] = qn;
                 }
-                // Horner over the digits: exact int32 sum of q_int * code
-                int tot[G];
+            }
+            const float sk = f16_bits_to_f32((uint16_t)c.ks[blk]);
+#pragma unroll
+            for (int h = 0; h < G; h++) z[h] = blk == 0 ? (float)acc[h] * sk : fmaf((float)acc[h], sk, z[h]);
+        }
+        if (valid) {
+#pragma unroll
+            for (int h = 0; h < G; h++) mloc[h] = fmax_nc(mloc[h], z[h]);
+            float *dst = zs + (size_t)(t - sc0) * G;
+            if constexpr (G % 4 == 0) {
+#pragma unroll
+                for (int h = 0; h < G; h += 4)
+                    *reinterpret_cast<float4 *>(dst + h) = make_float4(z[h], z[h + 1], z[h + 2], z[h + 3]);
+            } else if constexpr (G == 2) {
+                *reinterpret_cast<float2 *>(dst) = make_float2(z[0], z[1]);
+            } else {
+                dst[0] = z[0];
+            }
+        }
+    };
+
+    // ---- value stream: 4-position groups, a lane owns fixed byte positions
+    // of each group; rotating buffer, slot f consumed then reloaded one batch
+    // (PF loads) ahead, the descriptors moving with the batch
+    const int gi = lane / T::V_LPG;                  // group slot of a wave load
+    const int qsl = lane % T::V_LPG;                 // dword slice of the group
+    constexpr uint32_t GSTEP = T::V_GPL * 4 * T::V_ROW;   // bytes per wave-wide group load
+    constexpr int PFH = GSTEP * 8 <= 4096 ? 8 : 4096 / GSTEP;   // loads per descriptor (offsets < 4 KiB)
+    constexpr int PF = 2 * PFH;                      // group loads in flight per lane
+    constexpr int PB = PF * T::V_GPL;                // groups per batch (divides S / 4)
+    static_assert((S / 4) % PB == 0, "a sub-chunk holds whole batches");
+    const int ngw = (nw + 3) >> 2;                   // groups of this wave
+    const uint8_t *vb0 = p.v_codes + ((size_t)bh * p.cap4 + t0 + s0) * T::V_ROW;
+    const uint32_t vo = gi * 4 * T::V_ROW + qsl * T::V_DPL * 4;
+    auto vrsrc = [&](int g0, int hf) {
+        const int b0 = g0 * 4 * T::V_ROW + hf * PFH * (int)GSTEP;
+        return make_rsrc(vb0 + b0, (uint32_t)max(ngw * 4 * T::V_ROW - b0, 0));
+    };
+    uint32_t buf[PF][T::V_DPL];
+    auto vload = [&](int g0, int f, const rsrc_t &ra, const rsrc_t &rb) {
+#pragma unroll
+        for (int d = 0; d < T::V_DPL; d++) buf[f][d] = bld_u32(f < PFH ? ra : rb, vo + (f % PFH) * GSTEP + d * 4);
+    };
+    const int vgrp = (qsl * T::V_DPL * T::V_CPD) / (HD / KG);   // value scale group of the lane
+    const uint32_t *wdg = wdw + (size_t)vgrp * (S / 4) * G * 2;
+    uint32_t accl[G][T::V_ACC], acch[G][T::V_ACC];
+    // one 4-position group: weight words of local group rg (LDS broadcast)
+    // times the value codes this lane holds for it
+    auto group = [&](int rg, const uint32_t (&x)[T::V_DPL]) {
+        uint32_t wl[G], wh[G];
+        const uint32_t *src = wdg + (size_t)rg * G * 2;
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            wl[h] = src[2 * h];
+            wh[h] = src[2 * h + 1];
+        }
+#pragma unroll
+        for (int d = 0; d < T::V_DPL; d++) {
+            if constexpr (VB == 4) {
+                const uint32_t u = x[d] ^ 0x88888888u;        // offset binary per nibble
+                const uint32_t ulo = u & 0x0F0F0F0Fu;          // even channel, 4 positions
+                const uint32_t uhi = u & 0xF0F0F0F0u;          // odd channel, x16
 #pragma unroll
                 for (int h = 0; h < G; h++) {
-                    tot[h] = acc[T::ND - 1][h];
-#pragma unroll
-                    for (int j = T::ND - 2; j >= 0; j--) tot[h] = tot[h] * T::DBASE + acc[j][h];
+                    accl[h][2 * d] = __builtin_amdgcn_udot4(wl[h], ulo, accl[h][2 * d], false);
+                    acch[h][2 * d] = __builtin_amdgcn_udot4(wh[h], ulo, acch[h][2 * d], false);
+                    accl[h][2 * d + 1] = __builtin_amdgcn_udot4(wl[h], uhi, accl[h][2 * d + 1], false);
+                    acch[h][2 * d + 1] = __builtin_amdgcn_udot4(wh[h], uhi, acch[h][2 * d + 1], false);
                 }
-                const float sk = f16_bits_to_f32((uint16_t)c.ks[blk]);
+            } else {
+                const uint32_t u = x[d] ^ 0x80808080u;        // offset binary per byte
 #pragma unroll
-                for (int h = 0; h < G; h++) z[h] = blk == 0 ? (float)tot[h] * sk : fmaf((float)tot[h], sk, z[h]);
-            }
-            if (valid) {
-#pragma unroll
-                for (int h = 0; h < G; h++) mloc[h] = fmax_nc(mloc[h], z[h]);
-                float *dst = zs + (size_t)(s0 + t) * G;
-                if constexpr (G % 4 == 0) {
-#pragma unroll
-                    for (int h = 0; h < G; h += 4)
-                        *reinterpret_cast<float4 *>(dst + h) = make_float4(z[h], z[h + 1], z[h + 2], z[h + 3]);
-                } else if constexpr (G == 2) {
-                    *reinterpret_cast<float2 *>(dst) = make_float2(z[0], z[1]);
-                } else {
-                    dst[0] = z[0];
+                for (int h = 0; h < G; h++) {
+                    accl[h][d] = __builtin_amdgcn_udot4(wl[h], u, accl[h][d], false);
+                    acch[h][d] = __builtin_amdgcn_udot4(wh[h], u, acch[h][d], false);
                 }
             }
-        };
+        }
+    };
+
+    // ---- the wave's running result: max M (unscaled score units), per-lane
+    // partial sum of p, and the lane's output channels, all relative to M
+    float M[G], lsum[G], af[G][T::V_ACC];
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        M[h] = -INFINITY;
+        lsum[h] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < T::V_ACC; c++) af[h][c] = 0.0f;
+    }
+
+    Tile ta, tb_;
+    load(0, ta);
+    for (int sc0 = 0; sc0 < nw; sc0 += S) {
+        const int ns = min(S, nw - sc0);             // positions of this sub-chunk
+        // ---------------- pass 1: scores of the sub-chunk ----------------------
+#pragma unroll
+        for (int h = 0; h < G; h++) mloc[h] = -INFINITY;
+#pragma unroll
+        for (int g = 0; g < KG; g++) vmloc[g] = 0.0f;
         // (both halves run unconditionally: a half past the end sees only
         // invalid lanes and zero rows, and the code stays free of a merge
         // point that would send the two register sets through memory)
-        Tile ta, tb_;
-        load(0, ta);
-        for (int tb = 0; tb < nw; tb += 128) {
+        for (int tb = sc0; tb < sc0 + ns; tb += 128) {
             load(tb + 64, tb_);
-            compute(tb, ta);
-            load(tb + 128, ta);
-            compute(tb + 64, tb_);
+            compute(tb, sc0, ta);
+            if (tb + 128 < sc0 + ns) load(tb + 128, ta);
+            compute(tb + 64, sc0, tb_);
         }
-    }
-    // ---------------- value prefetch ----------------------------------------
-    // The first batch of value loads is issued here, so that it is in flight
-    // during the reductions, the barrier and the weights pass.
-    // lane -> (group slot gi of a load, dword slice qsl of the group)
-    const int gi = lane / T::V_LPG;
-    const int qsl = lane % T::V_LPG;
-    constexpr uint32_t GSTEP = T::V_GPL * 4 * T::V_ROW;   // bytes per wave-wide group load
-    constexpr int PFH = GSTEP * 8 <= 4096 ? 8 : 4096 / GSTEP;     // loads per descriptor (offsets < 4 KiB)
-    constexpr int PF = 2 * PFH;                            // group loads in flight per lane
-    const int ng = (nw + 3) >> 2;                          // groups of this wave with a valid position
-    const uint8_t *vb0 = p.v_codes + ((size_t)bh * p.cap4 + t0 + s0) * T::V_ROW;
-    const uint32_t vo = gi * 4 * T::V_ROW + qsl * T::V_DPL * 4;   // loop-invariant lane offset
-    // descriptor half `hf` of the batch starting at group g0 (zero past the
-    // wave's groups)
-    auto vrsrc = [&](int g0, int hf) {
-        const int b0 = g0 * 4 * T::V_ROW + hf * PFH * (int)GSTEP;
-        return make_rsrc(vb0 + b0, (uint32_t)max(ng * 4 * T::V_ROW - b0, 0));
-    };
-    // rotating buffer: slot f is consumed, then reloaded one batch (PF loads)
-    // ahead; the descriptors move with the batch
-    uint32_t buf[PF][T::V_DPL];
-    {
-        const rsrc_t vra = vrsrc(0, 0), vrb = vrsrc(0, 1);
+        // the sub-chunk's first batch of value loads, in flight during the
+        // weights pass
+        {
+            const rsrc_t ra = vrsrc(sc0 >> 2, 0), rb = vrsrc(sc0 >> 2, 1);
 #pragma unroll
-        for (int f = 0; f < PF; f++)
-#pragma unroll
-            for (int d = 0; d < T::V_DPL; d++) buf[f][d] = bld_u32(f < PFH ? vra : vrb, vo + (f % PFH) * GSTEP + d * 4);
-    }
-
-    // this wave's maxima of the scores (per head) and of the value scales
-    // (per group), wave-uniform; each wave weights its own positions against
-    // them and the waves are merged once, at the end
-    float mw[G], vmw[KG];
-#pragma unroll
-    for (int h = 0; h < G; h++) mw[h] = wave_max_u(mloc[h]);
-#pragma unroll
-    for (int g = 0; g < KG; g++) vmw[g] = wave_max_u(vmloc[g]);
-
-    // ---------------- pass 2: weights, one lane per 4 positions ---------------
-    float lw[G], wsw[KG][G];                         // this wave's sum of p and of w_int
-    // p = 2^(qs * (z - m)) <= 1; w_int = rint(p * s_v * 32767 / max s_v),
-    // rounded by one fma onto 1.5 * 2^23 (the integer lands in the low
-    // mantissa bits); bytes packed four positions per word.
-    {
-        constexpr float MAGIC = 12582912.0f;         // 1.5 * 2^23
-        float nqm[G], lloc[G];
-#pragma unroll
-        for (int h = 0; h < G; h++) {
-            nqm[h] = nw > 0 ? -mw[h] * qs[h] : 0.0f;
-            lloc[h] = 0.0f;
+            for (int f = 0; f < PF; f++) vload(0, f, ra, rb);
         }
+        float ms[G], vms[KG];                        // sub-chunk maxima, wave-uniform
+#pragma unroll
+        for (int h = 0; h < G; h++) ms[h] = wave_max_u(mloc[h]);
+#pragma unroll
+        for (int g = 0; g < KG; g++) vms[g] = wave_max_u(vmloc[g]);
+
+        // ---------------- pass 2: weights, one lane per 4 positions ---------------
+        // p = 2^(qs * (z - ms)) <= 1; w_int = rint(p * s_v * 32767 / vms),
+        // rounded by one fma onto 1.5 * 2^23 (the integer lands in the low
+        // mantissa bits); bytes packed four positions per word.
+        float lloc[G];
         int wsl[KG][G];
+        {
+            constexpr float MAGIC = 12582912.0f;     // 1.5 * 2^23
+            float nqm[G];
 #pragma unroll
-        for (int g = 0; g < KG; g++)
+            for (int h = 0; h < G; h++) {
+                nqm[h] = -ms[h] * qs[h];
+                lloc[h] = 0.0f;
+            }
 #pragma unroll
-            for (int h = 0; h < G; h++) wsl[g][h] = 0;
-        float fsc[KG];
+            for (int g = 0; g < KG; g++)
 #pragma unroll
-        for (int g = 0; g < KG; g++) {
-            const float vmax = vmw[g];
-            fsc[g] = vmax > 0.0f ? (float)W_RANGE * __builtin_amdgcn_rcpf(vmax) : 0.0f;
-        }
-        const int ngw = (nw + 3) >> 2;               // groups of 4 positions
-        for (int gb = 0; gb < ngw; gb += 64) {
-            const int grp = gb + lane;
-            if (grp < ngw) {
-                const int tq = 4 * grp;              // first position of the group (within the wave)
+                for (int h = 0; h < G; h++) wsl[g][h] = 0;
+            float fsc[KG];
+#pragma unroll
+            for (int g = 0; g < KG; g++) fsc[g] = vms[g] > 0.0f ? (float)W_RANGE * __builtin_amdgcn_rcpf(vms[g]) : 0.0f;
+            const int grp = lane;                    // S / 4 <= 64 groups, one per lane
+            const int tq = 4 * grp;                  // first position of the group (within the sub-chunk)
+            if (tq < ns) {
                 float pr[4][G];
 #pragma unroll
                 for (int k = 0; k < 4; k++) {
-                    const bool valid = tq + k < nw;
-                    const float *src = zs + (size_t)(s0 + tq + k) * G;
+                    const bool valid = tq + k < ns;
+                    const float *src = zs + (size_t)(tq + k) * G;
                     float zz[G];
                     if constexpr (G % 4 == 0) {
 #pragma unroll
@@ -482,110 +524,93 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
                 }
 #pragma unroll
                 for (int g = 0; g < KG; g++) {
-                    {
-                        float sv[4];
+                    float sv[4];
 #pragma unroll
-                        for (int k = 0; k < 4; k++) sv[k] = tq + k < nw ? vs[(s0 + tq + k) * KG + g] * fsc[g] : 0.0f;
-                        uint32_t *dst = wdw + ((size_t)g * (sub / 4) + grp) * G * 2;
+                    for (int k = 0; k < 4; k++) sv[k] = tq + k < ns ? vsl[(tq + k) * KG + g] * fsc[g] : 0.0f;
+                    uint32_t *dst = wdw + ((size_t)g * (S / 4) + grp) * G * 2;
 #pragma unroll
-                        for (int h = 0; h < G; h++) {
-                            uint32_t wb[4];
+                    for (int h = 0; h < G; h++) {
+                        uint32_t wb[4];
 #pragma unroll
-                            for (int k = 0; k < 4; k++) wb[k] = __builtin_bit_cast(uint32_t, fmaf(pr[k][h], sv[k], MAGIC));
-                            uint32_t lo, hi;
-                            pack_w(wb[0], wb[1], wb[2], wb[3], lo, hi);
-                            wsl[g][h] += (int)__builtin_amdgcn_udot4(lo, 0x01010101u, 0u, false)
-                                       + 256 * (int)__builtin_amdgcn_udot4(hi, 0x01010101u, 0u, false);
-                            dst[2 * h] = lo;
-                            dst[2 * h + 1] = hi;
-                        }
+                        for (int k = 0; k < 4; k++) wb[k] = __builtin_bit_cast(uint32_t, fmaf(pr[k][h], sv[k], MAGIC));
+                        uint32_t lo, hi;
+                        pack_w(wb[0], wb[1], wb[2], wb[3], lo, hi);
+                        wsl[g][h] += (int)__builtin_amdgcn_udot4(lo, 0x01010101u, 0u, false)
+                                   + 256 * (int)__builtin_amdgcn_udot4(hi, 0x01010101u, 0u, false);
+                        dst[2 * h] = lo;
+                        dst[2 * h + 1] = hi;
                     }
                 }
             }
         }
-#pragma unroll
-        for (int h = 0; h < G; h++) lw[h] = wave_sum_u(lloc[h]);
-#pragma unroll
-        for (int g = 0; g < KG; g++)
-#pragma unroll
-            for (int h = 0; h < G; h++) wsw[g][h] = (float)wave_sum_ui(wsl[g][h]);
-    }
 
-    // ---------------- pass 3: values ---------------------------------------
-    uint32_t accl[G][T::V_ACC], acch[G][T::V_ACC];
+        // ---------------- pass 3: values of the sub-chunk ------------------------
 #pragma unroll
-    for (int h = 0; h < G; h++)
+        for (int h = 0; h < G; h++)
 #pragma unroll
-        for (int c = 0; c < T::V_ACC; c++) accl[h][c] = acch[h][c] = 0u;
-    {
-        const int vgrp = (qsl * T::V_DPL * T::V_CPD) / (HD / KG);   // value scale group of the lane
-        const uint32_t *wdg = wdw + (size_t)vgrp * (sub / 4) * G * 2;
-        // one 4-position group: weight words of group rg (LDS broadcast) times
-        // the value codes this lane holds for it
-        auto group = [&](int rg, const uint32_t (&x)[T::V_DPL]) {
-            uint32_t wl[G], wh[G];
-            const uint32_t *src = wdg + (size_t)rg * G * 2;
+            for (int c = 0; c < T::V_ACC; c++) accl[h][c] = acch[h][c] = 0u;
+        {
+            // Full batches are straight-line code (the weight reads of later
+            // groups are issued early); a partial last batch checks each group.
+            const int g0 = sc0 >> 2;                 // first group of the sub-chunk (within the wave)
+            const int ngs = (ns + 3) >> 2;           // its groups
+            // (the last batch reloads nothing: the next sub-chunk starts its own)
+            const int nfull = (ngs - 1) / PB * PB;
+            int rb = 0;
+            for (; rb < nfull; rb += PB) {
+                const int nb = g0 + rb + PB;         // first group of the next batch
+                const rsrc_t ra = vrsrc(nb, 0), rb2 = vrsrc(nb, 1);
 #pragma unroll
-            for (int h = 0; h < G; h++) {
-                wl[h] = src[2 * h];
-                wh[h] = src[2 * h + 1];
-            }
-#pragma unroll
-            for (int d = 0; d < T::V_DPL; d++) {
-                if constexpr (VB == 4) {
-                    const uint32_t u = x[d] ^ 0x88888888u;        // offset binary per nibble
-                    const uint32_t ulo = u & 0x0F0F0F0Fu;          // even channel, 4 positions
-                    const uint32_t uhi = u & 0xF0F0F0F0u;          // odd channel, x16
-#pragma unroll
-                    for (int h = 0; h < G; h++) {
-                        accl[h][2 * d] = __builtin_amdgcn_udot4(wl[h], ulo, accl[h][2 * d], false);
-                        acch[h][2 * d] = __builtin_amdgcn_udot4(wh[h], ulo, acch[h][2 * d], false);
-                        accl[h][2 * d + 1] = __builtin_amdgcn_udot4(wl[h], uhi, accl[h][2 * d + 1], false);
-                        acch[h][2 * d + 1] = __builtin_amdgcn_udot4(wh[h], uhi, acch[h][2 * d + 1], false);
-                    }
-                } else {
-                    const uint32_t u = x[d] ^ 0x80808080u;        // offset binary per byte
-#pragma unroll
-                    for (int h = 0; h < G; h++) {
-                        accl[h][d] = __builtin_amdgcn_udot4(wl[h], u, accl[h][d], false);
-                        acch[h][d] = __builtin_amdgcn_udot4(wh[h], u, acch[h][d], false);
-                    }
+                for (int f = 0; f < PF; f++) {
+                    group(rb + f * T::V_GPL + gi, buf[f]);
+                    vload(nb, f, ra, rb2);
                 }
             }
-        };
-        // Full batches are straight-line code (the weight reads of later
-        // groups are issued early); the last, partial batch checks each group.
-        constexpr int PB = PF * T::V_GPL;                  // groups per batch
-        const int nfull = ng / PB * PB;
-        int rb = 0;
-        for (; rb < nfull; rb += PB) {
-            const int nb = rb + PB;                        // first group of the next batch
-            const rsrc_t vra = vrsrc(nb, 0), vrb = vrsrc(nb, 1);
-#pragma unroll
-            for (int f = 0; f < PF; f++) {
-                group(rb + f * T::V_GPL + gi, buf[f]);
-#pragma unroll
-                for (int d = 0; d < T::V_DPL; d++)
-                    buf[f][d] = bld_u32(f < PFH ? vra : vrb, vo + (f % PFH) * GSTEP + d * 4);
-            }
-        }
-        if (rb < ng) {
 #pragma unroll
             for (int f = 0; f < PF; f++) {
                 const int rg = rb + f * T::V_GPL + gi;
-                if (rg < ng) group(rg, buf[f]);
+                if (rg < ngs) group(rg, buf[f]);
+            }
+            // the next sub-chunk's first key tile
+            if (sc0 + S < nw) load(sc0 + S, ta);
+        }
+
+        // ---------------- merge the sub-chunk into the wave's running result -----
+        // integer sums -> floats: undo the byte split, the x16 of odd V4
+        // channels and the offset binary (sum of w_int over the sub-chunk, a
+        // wave total), then the fixed point; scale both parts to the new max.
+        {
+            float wsw[KG][G];
+#pragma unroll
+            for (int g = 0; g < KG; g++)
+#pragma unroll
+                for (int h = 0; h < G; h++) wsw[g][h] = (float)wave_sum_ui(wsl[g][h]);
+            // (lanes of the other group slots hold partial sums of the same
+            // channels, added to slot 0 at the end: the offset is removed once)
+            const float bias = gi == 0 ? (VB == 4 ? 8.0f : 128.0f) : 0.0f;
+#pragma unroll
+            for (int h = 0; h < G; h++) {
+                const float Mn = fmaxf(M[h], ms[h]);
+                const float fo = M[h] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(qs[h] * (M[h] - Mn));
+                const float fn = __builtin_amdgcn_exp2f(qs[h] * (ms[h] - Mn));
+                M[h] = Mn;
+                lsum[h] = fmaf(lsum[h], fo, lloc[h] * fn);
+#pragma unroll
+                for (int c = 0; c < T::V_ACC; c++) {
+                    const int g = ((qsl * T::V_ACC + c) / (HD / KG));   // scale group of the channel
+                    float v = 256.0f * (float)acch[h][c] + (float)accl[h][c];
+                    if (VB == 4 && (c & 1)) v *= 0.0625f;
+                    v = (v - bias * wsw[g][h]) * (vms[g] * (1.0f / (float)W_RANGE));
+                    af[h][c] = fmaf(af[h][c], fo, v * fn);
+                }
             }
         }
     }
 
-    // ---------------- pass 4: per-wave values, merge the waves, write -------
-    // This wave's output (relative to its own maxima): undo the byte split,
-    // the x16 of odd V4 channels and the offset binary, then the fixed point.
-    float af[G][T::V_ACC];
+    // ---------------- merge the 4 waves, write --------------------------------
+    float lw[G];
 #pragma unroll
-    for (int h = 0; h < G; h++)
-#pragma unroll
-        for (int c = 0; c < T::V_ACC; c++) af[h][c] = 256.0f * (float)acch[h][c] + (float)accl[h][c];
+    for (int h = 0; h < G; h++) lw[h] = wave_sum_u(lsum[h]);
     if constexpr (T::V_GPL > 1) {
         // lanes holding the same channels for different group slots
 #pragma unroll
@@ -596,25 +621,18 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
                 for (int c = 0; c < T::V_ACC; c++) af[h][c] += __shfl_xor(af[h][c], m, 64);
     }
     __syncthreads();                                 // every wave is done with scores and weights
-    float *pm = misc;                                // [QD_WAVES][G] wave maxima
+    float *pm = misc;                                // [QD_WAVES][G] wave maxima (log2 units)
     float *pl = pm + QD_WAVES * G;                   // [QD_WAVES][G] wave sums of p
     if (gi == 0) {
-        const float bias = VB == 4 ? 8.0f : 128.0f;
 #pragma unroll
-        for (int c = 0; c < T::V_ACC; c++) {
-            const int ch = qsl * T::V_ACC + c;       // channel
-            const int g = ch / (HD / KG);             // its scale group
+        for (int c = 0; c < T::V_ACC; c++)
 #pragma unroll
-            for (int h = 0; h < G; h++) {
-                const float su = (VB == 4 && (c & 1)) ? af[h][c] * 0.0625f : af[h][c];
-                red[(wave * G + h) * HD + ch] = (su - bias * wsw[g][h]) * (vmw[g] * (1.0f / (float)W_RANGE));
-            }
-        }
+            for (int h = 0; h < G; h++) red[(wave * G + h) * HD + qsl * T::V_ACC + c] = af[h][c];
     }
     if (lane == 0) {
 #pragma unroll
         for (int h = 0; h < G; h++) {
-            pm[wave * G + h] = nw > 0 ? mw[h] * qs[h] : -INFINITY;   // log2 units
+            pm[wave * G + h] = nw > 0 ? M[h] * qs[h] : -INFINITY;
             pl[wave * G + h] = lw[h];
         }
     }

@@ -183,9 +183,13 @@ def test_workspace_and_chunks(kvq):
     assert kvq.kvq_workspace_bytes(f, 8, 1000, 0) == ((16 * nc * 8 + 255) // 256) * 256 + 16 * nc * 128 * 4
     # max_seq_len beyond capacity sizes by capacity
     assert kvq.kvq_workspace_bytes(d, 32, 10 ** 9, 1024) == kvq.kvq_workspace_bytes(d, 32, 32768, 1024)
-    # short contexts use the smallest chunk
+    # short contexts use the smallest chunk: 256 slots for integer caches, 64 for float ones
     small = _desc(kvq, batch=1, n_kv_heads=4, head_dim=64, capacity=257, group_size=64)
-    assert kvq.kvq_chunk_tokens(small, 4, 257) == 64
+    assert kvq.kvq_chunk_tokens(small, 4, 257) == 256
+    small_f = _desc(kvq, batch=1, n_kv_heads=4, head_dim=64, capacity=257, k_bits=16, v_bits=16)
+    assert kvq.kvq_chunk_tokens(small_f, 4, 257) == 64
+    # integer caches: the chunk is no longer bounded by LDS (4096 at 32K x 256 units)
+    assert kvq.kvq_chunk_tokens(d, 32, 32768) == 4096
 
 
 def test_binding_has_no_fallback(kvq, monkeypatch, tmp_path):
