@@ -142,10 +142,11 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
     return res
 
 
-def cpu_baseline(w, mode, log=print) -> dict:
+def cpu_baseline(w, mode, log=print, budget_s: float = 12.0) -> dict:
     """The CPU oracle's decode step, untuned, on a bounded sample of the
     workload: whole sequences (every KV and query head, the full context),
-    one per thread."""
+    one per thread, repeated over the batch until about `budget_s` seconds of
+    wall time have been spent (at least one round)."""
     import numpy as np
 
     import oracle
@@ -153,34 +154,139 @@ def cpu_baseline(w, mode, log=print) -> dict:
 
     oracle.lib()
     cores = max(1, min(16, os.cpu_count() or 1, w.batch))
-    seqs = list(range(cores))
-    data = {}
-    for b in seqs:
-        data[b] = (wl.rows(w, wl.K_STREAM, 0, b, w.n_pos), wl.rows(w, wl.V_STREAM, 0, b, w.n_pos), wl.query(w, 0, b))
     g = _group(mode, w)
     scale = 1.0 / np.sqrt(w.head_dim)
+    seqs = list(range(cores))
+    data = {s_: (wl.rows(w, wl.K_STREAM, 0, s_, w.n_pos), wl.rows(w, wl.V_STREAM, 0, s_, w.n_pos),
+                 wl.query(w, 0, s_)) for s_ in seqs}
 
-    def work(b):
-        K, V, q = data[b]
+    def work(s_):
+        K, V, q = data[s_]
         oracle.decode_step(mode.k_bits, mode.v_bits, g, w.n_anchor, w.window, K, V, q, scale)
 
-    threads = [threading.Thread(target=work, args=(b,)) for b in seqs]
-    t0 = time.perf_counter()
-    for t in threads:
-        t.start()
-    for t in threads:
-        t.join()
-    dt = time.perf_counter() - t0
-    frac = len(seqs) / w.batch
-    sample_bytes = step_bytes(w, mode) * frac
-    log(f"[bench] cpu oracle: {len(seqs)} sequence(s) on {cores} thread(s) in {dt:.2f} s")
+    done = 0
+    t_work = 0.0
+    while done == 0 or t_work < budget_s:
+        threads = [threading.Thread(target=work, args=(s_,)) for s_ in seqs]
+        t0 = time.perf_counter()
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join()
+        t_work += time.perf_counter() - t0
+        done += len(seqs)
+    sample_bytes = step_bytes(w, mode) * done / w.batch
+    log(f"[bench] cpu oracle: {done} sequence-steps on {cores} thread(s) in {t_work:.2f} s")
     return {
-        "value": sample_bytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-        "sample": f"{len(seqs)} of {w.batch} sequences of {w.name} ({mode.name}), every head, "
-                  f"full {attended(w)}-position context, one sequence per thread; float64 oracle "
-                  f"(encode every row, then softmax attention); {dt:.2f} s wall",
-        "tokens_per_s": len(seqs) / dt,
+        "value": sample_bytes / t_work / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "sample": f"sequences 0-{cores - 1} of {w.name} ({mode.name}; {w.batch} per step), every head, full "
+                  f"{attended(w)}-position context, one sequence per thread, repeated to {done} sequence-steps; "
+                  f"float64 oracle (encode every row, then softmax attention); {t_work:.1f} s of oracle time "
+                  f"(input generation excluded)",
+        "tokens_per_s": done / t_work,
     }
+
+
+def traffic_record(w, mode):
+    """HBM bytes per launch of the split kernel from the committed counter
+    summary, if it was taken on the kernel sources as they are now."""
+    import hashlib
+    path = ROOT / "profiles" / "traffic.json"
+    if not path.exists():
+        return None
+    rec = json.loads(path.read_text())
+    h = hashlib.sha256()
+    for f in rec.get("sources", []):
+        h.update((ROOT / f).read_bytes())
+    entry = rec.get("workloads", {}).get(f"{w.name}/{mode.name}")
+    if entry is None or h.hexdigest() != rec.get("sha256"):
+        return None
+    return entry
+
+
+TRAFFIC_SOURCES = ["decode_attention_quantized_kvq_amd/csrc/kvq_decode_quant.hpp",
+                   "decode_attention_quantized_kvq_amd/csrc/kvq_device.hpp",
+                   "decode_attention_quantized_kvq_amd/csrc/kvq.hip"]
+
+
+def record_traffic(fetch_csv: str, write_csv: str, log=print) -> int:
+    """Turn the two counter runs of --probe-traffic into profiles/traffic.json:
+    each counter scaled by what it reads for the 1 GiB copy of the same run,
+    averaged over the three split launches."""
+    import csv
+    import hashlib
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)  # KiB -> bytes
+        return vals
+
+    w, mode = __import__("workloads").K4V4_32K, __import__("workloads").K4V4
+    out = {}
+    for name, path, counter, truth in (("fetch", fetch_csv, "FETCH_SIZE", 1 << 30), ("write", write_csv, "WRITE_SIZE", 1 << 30)):
+        vals = per_kernel(path, counter)
+        copy = max(v for k, v_ in vals.items() if "copyBuffer" in k or "copy" in k.lower() for v in v_)
+        factor = truth / copy
+        dec = [v for k, v_ in vals.items() if "decode_quant_kernel" in k for v in v_]
+        prep = [v for k, v_ in vals.items() if "qprep_kernel" in k for v in v_]
+        out[name] = {"counter": counter, "copy_reads": copy, "factor": factor,
+                     "decode_raw": sum(dec) / len(dec), "prep_raw": sum(prep) / len(prep) if prep else 0.0}
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        h.update((ROOT / f).read_bytes())
+    dec_bytes = out["fetch"]["decode_raw"] * out["fetch"]["factor"] + out["write"]["decode_raw"] * out["write"]["factor"]
+    rec = {
+        "sources": TRAFFIC_SOURCES, "sha256": h.hexdigest(),
+        "method": "rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, of `python bench.py --probe-traffic`; "
+                  "each counter scaled by its reading for a 1 GiB device copy in the same run",
+        "counters": out,
+        "workloads": {f"{w.name}/{mode.name}": {
+            "kernel": "decode_quant_kernel<4,4,128,4,1>",
+            "bytes_per_launch": round(dec_bytes),
+            "fetch_bytes": round(out["fetch"]["decode_raw"] * out["fetch"]["factor"]),
+            "write_bytes": round(out["write"]["decode_raw"] * out["write"]["factor"]),
+            "algorithmic_bytes": split_bytes(w, mode),
+            "ratio_to_algorithmic": dec_bytes / split_bytes(w, mode),
+        }},
+    }
+    (ROOT / "profiles").mkdir(exist_ok=True)
+    (ROOT / "profiles" / "traffic.json").write_text(json.dumps(rec, indent=1) + "\n")
+    log(json.dumps(rec["workloads"], indent=1))
+    return 0
+
+
+def probe_traffic(chunk: int, log=print) -> int:
+    """For a counter run (rocprofv3 --pmc FETCH_SIZE or WRITE_SIZE): a plain
+    device copy of 1 GiB (the calibration), then three split-kernel launches
+    of the headline workload."""
+    import torch
+
+    import decode_attention_quantized_kvq_amd as kvq
+    import workloads as wl
+    from workloads.device import fill, positions, queries
+
+    w, mode = wl.K4V4_32K, wl.K4V4
+    cache = kvq.alloc_cache(w.batch, w.n_kv_heads, w.head_dim, w.capacity, mode.k_bits, mode.v_bits,
+                            _group(mode, w), w.n_anchor, w.window)
+    fill([cache], w, 0, w.n_pos)
+    q = queries(w, 0)
+    ch = kvq.kvq_chunk_tokens(cache, w.n_q_heads, w.n_pos) if chunk == 0 else chunk
+    ws_bytes = kvq.kvq_workspace_bytes(cache, w.n_q_heads, w.n_pos, ch)
+    ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")
+    lens = positions([w.n_pos] * w.batch)
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)                                   # 1 GiB read, 1 GiB written
+    torch.cuda.synchronize()
+    for _ in range(3):
+        kvq.kvq_decode_partials(cache, q, w.n_q_heads, lens, w.n_pos, 0.0, ch, ws, ws_bytes)
+    torch.cuda.synchronize()
+    log(f"[bench] traffic probe: copy 1 GiB, 3 launches of {w.name}/{mode.name} (chunk {ch})")
+    return 0
 
 
 def main() -> int:
@@ -192,9 +298,15 @@ def main() -> int:
     ap.add_argument("--modes", choices=["headline", "targets", "all"], default="targets",
                     help="headline: the K4V4 32K line only; targets: + K8V4 at 32K; all: every workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe-traffic", action="store_true",
+                    help="copy 1 GiB then launch the headline split kernel 3 times (for counter runs)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from the two counter runs (CPU only)")
     ap.add_argument("--quiet", action="store_true")
     args = ap.parse_args()
 
+    if args.record_traffic:
+        return record_traffic(*args.record_traffic)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -212,6 +324,8 @@ def main() -> int:
     kvq.lib()
     dev = torch.cuda.get_device_properties(0)
     log(f"[bench] device: {dev.name} ({dev.multi_processor_count} CUs)")
+    if args.probe_traffic:
+        return probe_traffic(args.chunk, log=log)
 
     head_w, head_m = wl.K4V4_32K, wl.K4V4
     head = run_mode(head_w, head_m, args.steps, args.warmup, args.chunk, log=log)
@@ -229,6 +343,8 @@ def main() -> int:
             extra.append(run_mode(wl.TINY, m, args.steps, args.warmup, args.chunk, log=log))
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(head_w, head_m, log=log)
+    tr = traffic_record(head_w, head_m)
+    traffic = None if tr is None else tr["bytes_per_launch"]
 
     line = {
         "metric": METRIC,
@@ -241,7 +357,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 (i32 dot on K codes, f16->f32 on V codes)",
+        "dtype": "int4 K/V codes, int32 dot products (i4 x i4 keys, u8 x u8 values), f32 softmax",
         "data": "synthetic: seeded N(0,1) K/V/q (numpy PCG64), no model weights",
         "config": {"workload": head["workload"], "mode": head["mode"], "batch": head["batch"],
                    "n_q_heads": head["n_q_heads"], "n_kv_heads": head["n_kv_heads"], "head_dim": head["head_dim"],
@@ -251,12 +367,12 @@ def main() -> int:
         "pct_of_peak": round(100.0 * head["step_GBps"] / PEAK_HBM_GBS, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_split_kernel<4,4,128,4>",
+            "kernel": "decode_quant_kernel<4,4,128,4,1> (timed with its query-prep kernel)",
             "achieved": round(head["split_GBps"], 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(head["split_GBps"] / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "us_per_launch": round(head["us_split"], 3),
             "bytes_per_launch": head["split_bytes"],
         },
