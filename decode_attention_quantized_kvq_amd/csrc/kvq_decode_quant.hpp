@@ -216,8 +216,12 @@ __device__ __forceinline__ void pack_w(uint32_t w0, uint32_t w1, uint32_t w2, ui
 // KG = scale groups per head row for both keys and values (1: groups of
 // head_dim, or one scale per position shared by all heads; 2 or 4: groups of
 // head_dim / KG channels); key dots are summed per group.
+// waves per SIMD the register allocation aims at (5 = at most 96 VGPRs)
+__host__ __device__ constexpr int qd_waves_per_eu(int G, int KG) { return G * KG <= 4 ? 5 : 3; }
+
 template <int KB, int VB, int HD, int G, int KG>
-__global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
+__global__ __launch_bounds__(QD_THREADS)
+void decode_quant_kernel(QuantParams p)
 {
     using T = QT<KB, VB, HD, G>;
     constexpr int S = qd_sub(G, KG);
@@ -314,16 +318,18 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
         int qz;
         asm volatile("s_mov_b32 %0, 0" : "=s"(qz));
         const KVQ_CONST int32_t *qdl = qd + qz;
-        // int4 keys: the digits of step i come through a pointer that depends
-        // on the sums after step i - LAG, which bounds the digit words held in
-        // SGPRs (the scheduler would otherwise load them all early and spill).
-        // int8 keys (twice the columns) run faster with the scheduler's own
-        // deeper prefetch, spills included.
-        constexpr int LAG = 64 / G > 2 ? 64 / G : 2;
+        // int4 keys: the digits of a quad of columns come through a pointer
+        // that depends on the sums after the quad LAG quads earlier, which
+        // bounds the digit words held in SGPRs (the scheduler would otherwise
+        // load them all early and spill); a quad's 4G words are one scalar
+        // load per digit.  int8 keys (twice the columns) run faster with the
+        // scheduler's own deeper prefetch, spills included.
+        constexpr int LAG = 48 / (4 * G) > 2 ? 48 / (4 * G) : 2;
         const KVQ_CONST int32_t *ring[LAG];
 #pragma unroll
         for (int i = 0; i < LAG; i++) ring[i] = qdl;
-        constexpr int CPB = T::K_COLS / KG;          // key dwords per scale group
+        constexpr int CPB = T::K_COLS / KG;          // key dwords per scale group (a multiple of 4)
+        static_assert(CPB % 4 == 0, "scale groups hold whole quads of key dwords");
         float z[G];
 #pragma unroll
         for (int blk = 0; blk < KG; blk++) {
@@ -336,21 +342,25 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
 #pragma unroll
                     for (int h = 0; h < G; h++) acc[h] *= T::DBASE;
                 }
+                const KVQ_CONST int32_t *qp = qdl;
 #pragma unroll
                 for (int cc = 0; cc < CPB; cc++) {
                     const int col = blk * CPB + cc;
+                    if ((cc & 3) == 0) qp = ring[0];
                     const int kw = (int)kword(c.k[col / 4], col);
-                    const KVQ_CONST int32_t *qc = ring[0] + (j * T::K_COLS + col) * G;
+                    const KVQ_CONST int32_t *qc = qp + (j * T::K_COLS + col) * G;
 #pragma unroll
                     for (int h = 0; h < G; h++)
                         acc[h] = (j == T::ND - 1 && cc == 0) ? kdot0<KB>(qc[h], kw) : kdot<KB>(qc[h], kw, acc[h]);
+                    if ((cc & 3) == 3) {
 #pragma unroll
-                    for (int i = 0; i + 1 < LAG; i++) ring[i] = ring[i + 1];
-                    const KVQ_CONST int32_t *qn = qdl;
+                        for (int i = 0; i + 1 < LAG; i++) ring[i] = ring[i + 1];
+                        const KVQ_CONST int32_t *qn = qdl;
 #pragma unroll
-                    for (int h = 0; h < G; h++)
-                        if constexpr (KB == 4) asm("" : "+s"(qn) : "v"(acc[h]));
-                    ring[LAG - 1] = qn;
+                        for (int h = 0; h < G; h++)
+                            if constexpr (KB == 4) asm("" : "+s"(qn) : "v"(acc[h]));
+                        ring[LAG - 1] = qn;
+                    }
                 }
             }
             const float sk = f16_bits_to_f32((uint16_t)c.ks[blk]);
@@ -571,8 +581,9 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
                 const int rg = rb + f * T::V_GPL + gi;
                 if (rg < ngs) group(rg, buf[f]);
             }
-            // the next sub-chunk's first key tile
-            if (sc0 + S < nw) load(sc0 + S, ta);
+            // the next sub-chunk's first key tile (unconditional: past the end
+            // it reads zeros, and the old tile is then visibly dead)
+            load(sc0 + S, ta);
         }
 
         // ---------------- merge the sub-chunk into the wave's running result -----
@@ -580,14 +591,11 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
         // channels and the offset binary (sum of w_int over the sub-chunk, a
         // wave total), then the fixed point; scale both parts to the new max.
         {
-            float wsw[KG][G];
-#pragma unroll
-            for (int g = 0; g < KG; g++)
-#pragma unroll
-                for (int h = 0; h < G; h++) wsw[g][h] = (float)wave_sum_ui(wsl[g][h]);
+            // per (head, scale group) the wave-uniform factors: c = fn * vms / 32767
+            // (fn = 2^(q_s (m_s - M_new))), the offset -bias * sum(w_int) * c
             // (lanes of the other group slots hold partial sums of the same
             // channels, added to slot 0 at the end: the offset is removed once)
-            const float bias = gi == 0 ? (VB == 4 ? 8.0f : 128.0f) : 0.0f;
+            const float bias = VB == 4 ? 8.0f : 128.0f;
 #pragma unroll
             for (int h = 0; h < G; h++) {
                 const float Mn = fmaxf(M[h], ms[h]);
@@ -595,13 +603,21 @@ __global__ __launch_bounds__(QD_THREADS) void decode_quant_kernel(QuantParams p)
                 const float fn = __builtin_amdgcn_exp2f(qs[h] * (ms[h] - Mn));
                 M[h] = Mn;
                 lsum[h] = fmaf(lsum[h], fo, lloc[h] * fn);
+                float cg[KG], og[KG];
+#pragma unroll
+                for (int g = 0; g < KG; g++) {
+                    cg[g] = fn * vms[g] * (1.0f / (float)W_RANGE);
+                    const float wsum = (float)wave_sum_ui(wsl[g][h]);
+                    og[g] = (T::V_GPL == 1 || gi == 0) ? -bias * wsum * cg[g] : 0.0f;
+                }
 #pragma unroll
                 for (int c = 0; c < T::V_ACC; c++) {
                     const int g = ((qsl * T::V_ACC + c) / (HD / KG));   // scale group of the channel
-                    float v = 256.0f * (float)acch[h][c] + (float)accl[h][c];
-                    if (VB == 4 && (c & 1)) v *= 0.0625f;
-                    v = (v - bias * wsw[g][h]) * (vms[g] * (1.0f / (float)W_RANGE));
-                    af[h][c] = fmaf(af[h][c], fo, v * fn);
+                    // 256 * hi + lo is exact in uint32 (at most 64 groups a sub-chunk)
+                    const float v = (float)((acch[h][c] << 8) + accl[h][c]);
+                    // odd int4 channels were accumulated x16
+                    const float cs = (VB == 4 && (c & 1)) ? cg[g] * 0.0625f : cg[g];
+                    af[h][c] = fmaf(af[h][c], fo, fmaf(v, cs, og[g]));
                 }
             }
         }
