@@ -105,6 +105,7 @@ int check_heads(const kvq_cache *c, int n_q_heads)
 bool quant_modes(const kvq_cache *c) { return quantized(c->k_bits); }   // both sides quantized (bits_pair_ok)
 
 int cap4_of(const kvq_cache *c) { return (c->capacity + 3) & ~3; }
+int cap64_of(const kvq_cache *c) { return (c->capacity + 63) & ~63; }
 
 size_t lds_bytes(const kvq_cache *c, int G, int chunk)
 {
@@ -277,7 +278,10 @@ int kvq_cache_sizes(const kvq_cache *c, size_t *kc, size_t *vc, size_t *ksb, siz
     if (st) return st;
     const size_t rows = (size_t)c->batch * c->n_kv_heads * c->capacity;
     const size_t sc = per_row(c) ? (size_t)c->batch * c->capacity : rows * groups_per_head(c);
-    if (kc) *kc = rows * c->head_dim * c->k_bits / 8;
+    if (kc) {
+        const size_t krows = quantized(c->k_bits) ? (size_t)c->batch * c->n_kv_heads * cap64_of(c) : rows;
+        *kc = krows * c->head_dim * c->k_bits / 8;
+    }
     if (vc) {
         const size_t vrows = quantized(c->v_bits) ? (size_t)c->batch * c->n_kv_heads * cap4_of(c) : rows;
         *vc = vrows * c->head_dim * c->v_bits / 8;
@@ -315,6 +319,7 @@ int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n
     p.head_dim = c->head_dim;
     p.capacity = c->capacity;
     p.cap4 = cap4_of(c);
+    p.cap64 = cap64_of(c);
     p.n_new = n_new;
     p.n_anchor = c->n_anchor;
     p.window = c->window;
@@ -347,6 +352,8 @@ static int resolve_chunk(const kvq_cache *c, int n_q_heads, int max_seq_len, int
     if (ch == 0) ch = auto_chunk(c, n_q_heads, max_seq_len);
     if (ch < 64 || ch > 8192 || ch % 64 != 0)
         return fail(KVQ_ERR_ARG, "chunk_tokens %d must be a multiple of 64 in [64, 8192]", ch);
+    if (quant_modes(c) && ch % 256 != 0)
+        return fail(KVQ_ERR_ARG, "chunk_tokens %d must be a multiple of 256 for 8/4-bit caches", ch);
     const int G = n_q_heads / c->n_kv_heads;
     if (lds_bytes(c, G, ch) > kMaxLds)
         return fail(KVQ_ERR_ARG, "chunk_tokens %d needs %zu bytes of LDS (limit %zu)", ch, lds_bytes(c, G, ch), kMaxLds);
@@ -435,6 +442,7 @@ int kvq_decode_partials(const kvq_cache *c, const float *q, int n_q_heads, const
     p.n_kv_heads = c->n_kv_heads;
     p.capacity = c->capacity;
     p.cap4 = cap4_of(c);
+    p.cap64 = cap64_of(c);
     p.max_len = max_len_of(c, max_seq_len);
     p.chunk = ch;
     p.n_chunks = nc;

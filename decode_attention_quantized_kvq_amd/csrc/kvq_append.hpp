@@ -20,12 +20,13 @@ constexpr int APPEND_SPAN = APPEND_THREADS * APPEND_ELEMS;        // per block p
 
 struct AppendParams {
     const float *src[2];      // K, V: [batch][n_kv_heads][n_new][head_dim]
-    uint8_t *codes[2];        // K: [batch][n_kv_heads][capacity][row bytes]
+    uint8_t *codes[2];        // float sides: [batch][n_kv_heads][capacity][row bytes]
+                              // K (8/4-bit): [batch][n_kv_heads][cap64/64][row bytes/16][64][16]
                               // V (8/4-bit): [batch][n_kv_heads][cap4/4][row bytes][4]
     uint16_t *scales[2];      // see kvq.h
     int bits[2];
     const int32_t *start_pos; // [batch]
-    int n_kv_heads, head_dim, capacity, cap4, n_new, n_anchor, window;
+    int n_kv_heads, head_dim, capacity, cap4, cap64, n_new, n_anchor, window;
     int group;                // elements per scale
     int per_row;              // 1: one scale per position over all heads
 };
@@ -90,19 +91,24 @@ __device__ __forceinline__ void load8(const float *src, float (&x)[8])
 }
 
 // Store 8 encoded values (w0, w1 as packed by encode8) of row `slot`,
-// starting at value c0.  Keys, and values in float formats, are stored
-// row-major; 8/4-bit values are stored four positions interleaved per byte
-// (byte j of the row of slot s at ((s & ~3) * row + 4 * j + (s & 3))), so a
-// 32-bit word holds one byte position of four consecutive positions.
-__device__ __forceinline__ void store_codes(uint8_t *codes, size_t unit, int cap, int cap4, int slot, int row_bytes,
+// starting at value c0.  8/4-bit keys are stored in tiles of 64 slots,
+// slice-major (byte j of the row of slot s at ((s & ~63) * row + (j / 16) *
+// 1024 + (s & 63) * 16 + j % 16)), so one 16-byte slice of 64 consecutive
+// rows is contiguous; 8/4-bit values are stored four positions interleaved
+// per byte (byte j of the row of slot s at ((s & ~3) * row + 4 * j +
+// (s & 3))), so a 32-bit word holds one byte position of four consecutive
+// positions.
+__device__ __forceinline__ void store_codes(uint8_t *codes, size_t unit, int cap4, int cap64, int slot, int row_bytes,
                                             int c0, int bits, bool interleave, uint32_t w0, uint32_t w1)
 {
     if (!interleave) {
-        uint8_t *dst = codes + (unit * cap + slot) * (size_t)row_bytes;
+        const int j0 = bits == 8 ? c0 : c0 / 2;     // first byte (8 or 4 bytes, inside one 16-byte slice)
+        uint8_t *dst = codes + (unit * cap64 + (slot & ~63)) * (size_t)row_bytes + (j0 >> 4) * 1024 + (slot & 63) * 16 +
+                       (j0 & 15);
         if (bits == 8)
-            *reinterpret_cast<uint2 *>(dst + c0) = make_uint2(w0, w1);
+            *reinterpret_cast<uint2 *>(dst) = make_uint2(w0, w1);
         else
-            *reinterpret_cast<uint32_t *>(dst + c0 / 2) = w0;
+            *reinterpret_cast<uint32_t *>(dst) = w0;
         return;
     }
     uint8_t *grp = codes + (unit * cap4 + (slot & ~3)) * (size_t)row_bytes + (slot & 3);
@@ -169,7 +175,7 @@ __global__ __launch_bounds__(APPEND_THREADS) void append_kernel(AppendParams p)
             load8(src + (((size_t)(b * p.n_kv_heads + h) * p.n_new + i) * HD + c0), x);
             uint32_t w0, w1;
             encode8(x, s, qmax, bits, w0, w1);
-            store_codes(codes, (size_t)(b * p.n_kv_heads + h), p.capacity, p.cap4, slot, HD * bits / 8, c0, bits,
+            store_codes(codes, (size_t)(b * p.n_kv_heads + h), p.cap4, p.cap64, slot, HD * bits / 8, c0, bits,
                         side == 1, w0, w1);
         }
         return;
@@ -220,7 +226,7 @@ __global__ __launch_bounds__(APPEND_THREADS) void append_kernel(AppendParams p)
     encode8(x, s, qmax, bits, w0, w1);
     if (!active)
         return;
-    store_codes(codes, (size_t)(b * p.n_kv_heads + h), p.capacity, p.cap4, slot, HD * bits / 8, c0, bits, side == 1,
+    store_codes(codes, (size_t)(b * p.n_kv_heads + h), p.cap4, p.cap64, slot, HD * bits / 8, c0, bits, side == 1,
                 w0, w1);
     if (c0 % p.group == 0)
         scales[row * (size_t)(HD / p.group) + c0 / p.group] = sh;

@@ -71,7 +71,7 @@ template <int KB, int VB, int HD, int G> struct QT {
 };
 
 struct QuantParams {
-    const uint8_t *k_codes;    // [B][Hkv][cap][K_ROW]
+    const uint8_t *k_codes;    // [B][Hkv][cap64/64][K_ROW/16][64][16]  (tiles of 64 slots, slice-major)
     const uint8_t *v_codes;    // [B][Hkv][cap4/4][V_ROW][4]  (4 positions interleaved per byte)
     const uint16_t *k_scales;
     const uint16_t *v_scales;
@@ -80,7 +80,7 @@ struct QuantParams {
     const int32_t *seq_len;
     float *ws_ml;
     float *ws_acc;
-    int n_kv_heads, capacity, cap4;
+    int n_kv_heads, capacity, cap4, cap64;
     int max_len;
     int chunk, n_chunks;
     long long k_sc_b, k_sc_h;
@@ -276,12 +276,16 @@ void decode_quant_kernel(QuantParams p)
 
     // ---- key stream: tiles of 64 positions, one lane per position, loaded
     // one tile ahead into the other of two register sets; the descriptors
-    // move with the tile (past the wave's range the loads return zeros)
-    const uint8_t *kb0 = p.k_codes + ((size_t)bh * p.capacity + t0 + s0) * T::K_ROW;
+    // move with the tile.  A tile is stored slice-major, so load u (16 bytes
+    // per lane) reads 1 KiB of contiguous memory.  A tile with any position
+    // of the wave is read whole (lanes past the range see other rows and are
+    // masked); tiles past the range read zeros.  Scales past the range read
+    // zeros.
+    const uint8_t *kb0 = p.k_codes + ((size_t)bh * p.cap64 + t0 + s0) * T::K_ROW;   // t0 + s0: a multiple of 64
     const uint16_t *ks0 = p.k_scales + b * p.k_sc_b + kvh * p.k_sc_h + (size_t)(t0 + s0) * p.k_sc_t;
     const uint16_t *vs0 = p.v_scales + b * p.v_sc_b + kvh * p.v_sc_h + (size_t)(t0 + s0) * p.v_sc_t;
     const KVQ_CONST int32_t *qd = (const KVQ_CONST int32_t *)(p.qdig + (size_t)bh * T::ND * T::K_COLS * G);
-    const uint32_t ko = lane * T::K_ROW;
+    const uint32_t ko = lane * 16;
     const uint32_t kso = lane * p.k_sc_t * 2, vso = lane * p.v_sc_t * 2;
     struct Tile {
         uint4 k[T::K_U4];
@@ -289,11 +293,15 @@ void decode_quant_kernel(QuantParams p)
     };
     auto load = [&](int tb, Tile &d) {
         const uint32_t rem = (uint32_t)max(nw - tb, 0);
-        const rsrc_t krs = make_rsrc(kb0 + (size_t)tb * T::K_ROW, rem * T::K_ROW);
+        const uint32_t kbytes = rem > 0 ? 64 * T::K_ROW : 0;
+        const rsrc_t krs = make_rsrc(kb0 + (size_t)tb * T::K_ROW, kbytes);
         const rsrc_t ksrs = make_rsrc(ks0 + (size_t)tb * p.k_sc_t, rem * p.k_sc_t * 2);
         const rsrc_t vsrs = make_rsrc(vs0 + (size_t)tb * p.v_sc_t, rem * p.v_sc_t * 2);
+        // (immediate offsets reach 4 KiB: int8 rows use a second descriptor
+        // for slices 4..7)
+        const rsrc_t krs2 = make_rsrc(kb0 + (size_t)tb * T::K_ROW + 4096, kbytes > 4096 ? kbytes - 4096 : 0);
 #pragma unroll
-        for (int u = 0; u < T::K_U4; u++) d.k[u] = bld_u4(krs, ko + u * 16);
+        for (int u = 0; u < T::K_U4; u++) d.k[u] = bld_u4(u < 4 ? krs : krs2, ko + (u % 4) * 1024);
 #pragma unroll
         for (int g = 0; g < KG; g++) {
             d.ks[g] = bld_u16(ksrs, kso + 2 * g);

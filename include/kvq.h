@@ -84,8 +84,14 @@ extern "C" {
  *   the anchors and the `window` most recent positions.
  *
  * Layouts (row-major, innermost last; R = head_dim * bits / 8 bytes):
- *   k_codes, and v_codes of a 16/32-bit value side:
+ *   k_codes and v_codes of a 16/32-bit side:
  *       [batch][n_kv_heads][capacity][R] bytes, 16-byte aligned
+ *   k_codes of an 8/4-bit key side, tiles of 64 slots stored slice-major:
+ *       [batch][n_kv_heads][cap64 / 64][R / 16][64][16] bytes, cap64 =
+ *       capacity rounded up to a multiple of 64: byte j of the row of slot s
+ *       sits at ((s & ~63) * R + (j / 16) * 1024 + (s & 63) * 16 + j % 16)
+ *       within its (sequence, head), so the same 16-byte slice of 64
+ *       consecutive rows is 1 KiB of contiguous memory.
  *   v_codes of an 8/4-bit value side, four positions interleaved per byte:
  *       [batch][n_kv_heads][cap4 / 4][R][4] bytes, cap4 = capacity rounded up
  *       to a multiple of 4: byte j of the row of slot s sits at
@@ -186,8 +192,8 @@ int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n
  *                beyond it are not attended.
  * softmax_scale: > 0, or 0 for 1/sqrt(head_dim).
  * chunk_tokens : 0 for the library's choice (kvq_chunk_tokens()), or a
- *                multiple of 64 in [64, 8192] whose working set fits the
- *                device's LDS (else KVQ_ERR_ARG).
+ *                multiple of 64 (of 256 for 8/4-bit caches) in [64, 8192]
+ *                whose working set fits the device's LDS (else KVQ_ERR_ARG).
  * workspace    : device memory of at least kvq_workspace_bytes(...) bytes,
  *                256-byte aligned.  Layout, for P = batch * n_q_heads rows
  *                and C chunks: float ml[P][C][2] = (m, l) at offset 0, then

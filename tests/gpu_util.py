@@ -46,7 +46,16 @@ def cache_arrays(cache):
     [B][cap] for one scale per position."""
     d = cache.desc
     B, H, HD, cap = d.batch, d.n_kv_heads, d.head_dim, d.capacity
-    kc = cache.k_codes.cpu().numpy().reshape(B, H, cap, HD * d.k_bits // 8)
+    KR = HD * d.k_bits // 8
+    kraw = cache.k_codes.cpu().numpy()
+    if d.k_bits < 16:
+        # 8/4-bit keys: tiles of 64 slots, slice-major (kvq.h): byte j of slot s at
+        # ((s & ~63) * KR + (j // 16) * 1024 + (s & 63) * 16 + j % 16) within a (b, head)
+        cap64 = (cap + 63) // 64 * 64
+        kc = (kraw.reshape(B, H, cap64 // 64, KR // 16, 64, 16).transpose(0, 1, 2, 4, 3, 5)
+              .reshape(B, H, cap64, KR)[:, :, :cap])
+    else:
+        kc = kraw.reshape(B, H, cap, KR)
     vraw = cache.v_codes.cpu().numpy()
     R = HD * d.v_bits // 8
     if d.v_bits < 16:

@@ -72,6 +72,10 @@ def test_cache_sizes(kvq):
     kc, vc, ks, vs = kvq.kvq_cache_sizes(d)
     rows = 3 * 8 * 1600
     assert (kc, vc, ks, vs) == (rows * 64, rows * 128, rows * 4 * 2, rows * 4 * 2)
+    # integer keys pad each (sequence, head) to whole 64-slot tiles, integer values to 4 slots
+    d = _desc(kvq, batch=2, n_kv_heads=3, head_dim=64, capacity=1001, k_bits=8, v_bits=4, group_size=64)
+    kc, vc, _, _ = kvq.kvq_cache_sizes(d)
+    assert kc == 2 * 3 * 1024 * 64 and vc == 2 * 3 * 1004 * 32
     d = _desc(kvq, n_kv_heads=4, head_dim=64, group_size=256)           # one scale per position
     assert kvq.kvq_cache_sizes(d)[2] == 2 * 100 * 2
     d = _desc(kvq, k_bits=16, v_bits=16)
@@ -175,8 +179,12 @@ def test_workspace_and_chunks(kvq):
     digits = 32 * 8 * 16 * 4 * 4 * 4 + P * 4
     ws = kvq.kvq_workspace_bytes(d, 32, 32768, 0)
     assert partials + digits <= ws <= partials + digits + 512
-    ws64 = kvq.kvq_workspace_bytes(d, 32, 32768, 64)
-    assert ws64 >= ((P * 512 * 8 + 255) // 256) * 256 + P * 512 * 512
+    ws256 = kvq.kvq_workspace_bytes(d, 32, 32768, 256)
+    assert ws256 >= ((P * 128 * 8 + 255) // 256) * 256 + P * 128 * 512
+    # 8/4-bit caches take chunks in multiples of 256 slots
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_workspace_bytes(d, 32, 32768, 64)
+    assert e.value.status == -9
     # float caches need the partials only
     f = _desc(kvq, batch=2, n_kv_heads=2, capacity=1000, k_bits=16, v_bits=16)
     nc = -(-1000 // kvq.kvq_chunk_tokens(f, 8, 1000))

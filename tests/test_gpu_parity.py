@@ -4,7 +4,7 @@ kernel instantiation (widths x head_dim x GQA group), windows, groups."""
 import numpy as np
 import pytest
 
-from gpu_util import (assert_close, check_codes, group_size_of, linear_slots, need_gpu, softmax_default,
+from gpu_util import (assert_close, cache_arrays, check_codes, group_size_of, linear_slots, need_gpu, softmax_default,
                       window_slots)
 
 pytestmark = pytest.mark.gpu
@@ -79,9 +79,20 @@ def test_per_row_scale(oq):
     run_case(oq, 8, 8, -1, B=2, H=4, G=1, HD=64, n_pos=300, seed=3)
 
 
-@pytest.mark.parametrize("chunk", [64, 128, 512, 1024])
+@pytest.mark.parametrize("chunk", [256, 512, 1024, 2048])
 def test_chunk_sizes(oq, chunk):
     run_case(oq, 4, 4, 0, B=1, H=2, G=4, HD=128, n_pos=3001, chunk=chunk, seed=11)
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 512])
+def test_chunk_sizes_float(oq, chunk):
+    run_case(oq, 16, 16, 0, B=1, H=2, G=4, HD=128, n_pos=1001, chunk=chunk, seed=12)
+
+
+@pytest.mark.parametrize("chunk", [4096, 8192])
+def test_long_chunks(oq, chunk):
+    """Chunks of several sub-chunks per wave (running maxima merged), int8 keys."""
+    run_case(oq, 8, 4, 0, B=1, H=2, G=4, HD=128, n_pos=9000, chunk=chunk, seed=13, outliers=True)
 
 
 def test_ragged_lengths(oq):
@@ -153,7 +164,7 @@ def test_append_skips_out_of_range(oq):
     x = np.ones((B, H, 4, HD), np.float32)
     kvq.kvq_append(cache, to_device(x), to_device(x), 4, positions([-2, 8]))
     torch.cuda.synchronize()
-    kc = cache.k_codes.cpu().numpy().reshape(B, H, cap, HD)
+    kc = cache_arrays(cache)[0]
     assert np.all(kc[0, 0, :2] == 127) and np.all(kc[0, 0, 2:] == 0x5A)
     assert np.all(kc[1, 0, 8:] == 127) and np.all(kc[1, 0, :8] == 0x5A)
 
@@ -173,10 +184,10 @@ def test_guard_bands_untouched(oq):
     d.k_codes, d.v_codes, d.k_scales, d.v_scales = (t.data_ptr() + guard for t in big)
     K, V, q = _data(B, H, cap, HD, H * G, 4)
     kvq.kvq_append(d, to_device(K), to_device(V), cap, positions([0, 0]))
-    ws_bytes = kvq.kvq_workspace_bytes(d, H * G, cap, 64)
+    ws_bytes = kvq.kvq_workspace_bytes(d, H * G, cap, 256)
     ws = torch.full((ws_bytes + 2 * guard,), 0xA5, dtype=torch.uint8, device="cuda")
     out = torch.full((B * H * G * HD + 2 * 64,), 7.0, device="cuda")
-    kvq.kvq_decode_attn(d, to_device(q), H * G, positions([cap, cap]), cap, 0.0, 64, out.data_ptr() + 256,
+    kvq.kvq_decode_attn(d, to_device(q), H * G, positions([cap, cap]), cap, 0.0, 256, out.data_ptr() + 256,
                         ws.data_ptr() + guard, ws_bytes)
     torch.cuda.synchronize()
     for t in big + [ws]:
@@ -188,7 +199,7 @@ def test_guard_bands_untouched(oq):
 
 def test_combine_matches_single_chunk(oq):
     """Split-K partials merged by kvq_combine equal a one-chunk run."""
-    _, a = run_case(oq, 8, 8, 0, B=1, H=1, G=2, HD=128, n_pos=4000, chunk=64, seed=17)
+    _, a = run_case(oq, 8, 8, 0, B=1, H=1, G=2, HD=128, n_pos=4000, chunk=256, seed=17)
     _, b = run_case(oq, 8, 8, 0, B=1, H=1, G=2, HD=128, n_pos=4000, chunk=2048, seed=17)
     np.testing.assert_allclose(a, b, rtol=0, atol=2e-4)
 
