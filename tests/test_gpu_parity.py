@@ -248,3 +248,43 @@ def test_fp16_conversion_exhaustive():
     step = 1 << 25
     for hi in range(0, 1 << 32, step):
         _fp16_patterns(kvq, np.arange(hi, hi + step, dtype=np.uint64).astype(np.uint32))
+
+
+def test_graph_replay_matches_eager(oq):
+    """A step captured in a HIP graph (append + decode + combine) gives the
+    eager result bit for bit on every replay, with eager work in between."""
+    kvq = need_gpu()
+    import torch
+    from workloads.device import positions, to_device
+    B, H, G, HD, n = 2, 2, 4, 128, 700
+    cache = kvq.alloc_cache(B, H, HD, n, 4, 4, HD)
+    K, V, q = _data(B, H, n, HD, H * G, 21)
+    kvq.kvq_append(cache, to_device(K[:, :, : n - 1]), to_device(V[:, :, : n - 1]), n - 1, positions([0, 0]))
+    k1, v1, qd = to_device(K[:, :, n - 1:]), to_device(V[:, :, n - 1:]), to_device(q)
+    pos, lens = positions([n - 1] * B), positions([n] * B)
+    ws_bytes = kvq.kvq_workspace_bytes(cache, H * G, n, 0)
+    ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")
+    out = torch.zeros((B, H * G, HD), dtype=torch.float32, device="cuda")
+
+    def step(st):
+        kvq.kvq_append(cache, k1, v1, 1, pos, st)
+        kvq.kvq_decode_attn(cache, qd, H * G, lens, n, 0.0, 0, out, ws, ws_bytes, st)
+
+    step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    want = out.clone()
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        step(cs)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cs):
+        step(cs)
+    for r in range(3):
+        out.zero_()
+        ws.fill_(float(r + 1))                       # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), f"replay {r}"
