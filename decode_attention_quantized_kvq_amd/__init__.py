@@ -33,7 +33,7 @@ KVQ_ERR_ARG = -9
 
 EXPORTED = (
     "kvq_bytes_per_token", "kvq_cache_sizes", "kvq_append", "kvq_chunk_tokens", "kvq_workspace_bytes",
-    "kvq_decode_partials", "kvq_combine", "kvq_decode_attn", "kvq_status_str", "kvq_last_error",
+    "kvq_decode_partials", "kvq_combine", "kvq_decode_attn", "kvq_decode_step", "kvq_status_str", "kvq_last_error",
 )
 
 
@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_combine.restype = I
         L.kvq_decode_attn.argtypes = [C, P, I, P, I, ctypes.c_float, I, P, P, S, P]
         L.kvq_decode_attn.restype = I
+        L.kvq_decode_step.argtypes = [C, P, P, I, P, P, I, P, I, ctypes.c_float, I, P, P, S, P]
+        L.kvq_decode_step.restype = I
         L.kvq_status_str.argtypes = [I]
         L.kvq_status_str.restype = ctypes.c_char_p
         L.kvq_last_error.argtypes = []
@@ -174,6 +176,14 @@ def kvq_decode_attn(cache, q, n_q_heads: int, seq_len, max_seq_len: int, softmax
     _check(lib().kvq_decode_attn(ctypes.byref(_desc(cache)), _ptr(q), n_q_heads, _ptr(seq_len), max_seq_len,
                                  float(softmax_scale), chunk_tokens, _ptr(out), _ptr(workspace), int(workspace_bytes),
                                  _stream(stream)))
+
+
+def kvq_decode_step(cache, k_new, v_new, n_new: int, start_pos, q, n_q_heads: int, seq_len, max_seq_len: int,
+                    softmax_scale: float, chunk_tokens: int, out, workspace, workspace_bytes: int,
+                    stream=None) -> None:
+    _check(lib().kvq_decode_step(ctypes.byref(_desc(cache)), _ptr(k_new), _ptr(v_new), int(n_new), _ptr(start_pos),
+                                 _ptr(q), n_q_heads, _ptr(seq_len), max_seq_len, float(softmax_scale), chunk_tokens,
+                                 _ptr(out), _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
 def kvq_status_str(status: int) -> str:

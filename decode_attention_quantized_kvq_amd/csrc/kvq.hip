@@ -11,6 +11,7 @@
 #include "kvq_append.hpp"
 #include "kvq_decode.hpp"
 #include "kvq_decode_quant.hpp"
+#include "kvq_step.hpp"
 
 using namespace kvq;
 
@@ -123,14 +124,15 @@ int auto_chunk(const kvq_cache *c, int n_q_heads, int max_seq_len)
     const int G = n_q_heads / c->n_kv_heads;
     const long long units = (long long)c->batch * c->n_kv_heads;
     const int L = max_len_of(c, max_seq_len);
-    // The largest chunk that fits the LDS budget and still gives >= 8
-    // workgroups per CU over 256 CUs; when no chunk does, the smallest one
-    // (most workgroups): 64 slots, or 256 for integer caches, whose waves
-    // take 64 positions per step.
+    // The largest chunk that fits the LDS budget and still gives >= 16
+    // workgroups per CU over 256 CUs (four rounds of the four that fit at
+    // once, so the last round's stragglers cost less); when no chunk does,
+    // the smallest one (most workgroups): 64 slots, or 256 for integer
+    // caches, whose waves take 64 positions per step.
     const int smallest = quant_modes(c) ? 256 : 64;
     for (int ch = 4096; ch >= smallest; ch >>= 1) {
         if (lds_bytes(c, G, ch) > kAutoLds) continue;
-        if (units * ((L + ch - 1) / ch) >= 2048) return ch;
+        if (units * ((L + ch - 1) / ch) >= 4096) return ch;
     }
     return smallest;
 }
@@ -208,6 +210,26 @@ PrepFn pick_prep(int kb, int hd, int G)
 {
     if (kb == 4) return hd == 64 ? pick_prep_g<4, 64>(G) : pick_prep_g<4, 128>(G);
     return hd == 64 ? pick_prep_g<8, 64>(G) : pick_prep_g<8, 128>(G);
+}
+
+using StepPrepFn = void (*)(AppendParams, int, int, const float *, int32_t *, float *, float);
+
+template <int KB, int HD>
+StepPrepFn pick_step_g(int G)
+{
+    switch (G) {
+    case 1: return step_prep_kernel<KB, HD, 1>;
+    case 2: return step_prep_kernel<KB, HD, 2>;
+    case 4: return step_prep_kernel<KB, HD, 4>;
+    case 8: return step_prep_kernel<KB, HD, 8>;
+    }
+    return nullptr;
+}
+
+StepPrepFn pick_step(int kb, int hd, int G)
+{
+    if (kb == 4) return hd == 64 ? pick_step_g<4, 64>(G) : pick_step_g<4, 128>(G);
+    return hd == 64 ? pick_step_g<8, 64>(G) : pick_step_g<8, 128>(G);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -291,12 +313,17 @@ int kvq_cache_sizes(const kvq_cache *c, size_t *kc, size_t *vc, size_t *ksb, siz
     return ok();
 }
 
-int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n_new, const int32_t *start_pos,
-               void *stream)
+} // extern "C"
+
+// Validates an append and fills its parameters and grid (grid.x == 0: nothing
+// to store).  Launches nothing.
+static int prepare_append(const kvq_cache *c, const float *k_new, const float *v_new, int n_new,
+                          const int32_t *start_pos, AppendParams *p, dim3 *grid)
 {
     int st = check_geometry(c);
     if (st) return st;
     if (n_new < 0) return fail(KVQ_ERR_SHAPE, "n_new %d < 0", n_new);
+    *grid = dim3(0, 1, 1);
     if (n_new == 0) return ok();
     if ((st = check_pointers(c))) return st;
     if (!k_new || !v_new || !start_pos) return fail(KVQ_ERR_NULL, "k_new / v_new / start_pos is NULL");
@@ -305,29 +332,40 @@ int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n
     const long long rows = (long long)c->batch * n_new;
     if (rows > 0x7FFFFFFFLL) return fail(KVQ_ERR_SHAPE, "batch * n_new too large");
 
-    AppendParams p;
-    p.src[0] = k_new;
-    p.src[1] = v_new;
-    p.codes[0] = static_cast<uint8_t *>(c->k_codes);
-    p.codes[1] = static_cast<uint8_t *>(c->v_codes);
-    p.scales[0] = static_cast<uint16_t *>(c->k_scales);
-    p.scales[1] = static_cast<uint16_t *>(c->v_scales);
-    p.bits[0] = c->k_bits;
-    p.bits[1] = c->v_bits;
-    p.start_pos = start_pos;
-    p.n_kv_heads = c->n_kv_heads;
-    p.head_dim = c->head_dim;
-    p.capacity = c->capacity;
-    p.cap4 = cap4_of(c);
-    p.cap64 = cap64_of(c);
-    p.n_new = n_new;
-    p.n_anchor = c->n_anchor;
-    p.window = c->window;
-    p.per_row = per_row(c) && quantized(c->k_bits) ? 1 : 0;
-    p.group = p.per_row ? c->n_kv_heads * c->head_dim : (quantized(c->k_bits) ? c->group_size : c->head_dim);
+    p->src[0] = k_new;
+    p->src[1] = v_new;
+    p->codes[0] = static_cast<uint8_t *>(c->k_codes);
+    p->codes[1] = static_cast<uint8_t *>(c->v_codes);
+    p->scales[0] = static_cast<uint16_t *>(c->k_scales);
+    p->scales[1] = static_cast<uint16_t *>(c->v_scales);
+    p->bits[0] = c->k_bits;
+    p->bits[1] = c->v_bits;
+    p->start_pos = start_pos;
+    p->n_kv_heads = c->n_kv_heads;
+    p->head_dim = c->head_dim;
+    p->capacity = c->capacity;
+    p->cap4 = cap4_of(c);
+    p->cap64 = cap64_of(c);
+    p->n_new = n_new;
+    p->n_anchor = c->n_anchor;
+    p->window = c->window;
+    p->per_row = per_row(c) && quantized(c->k_bits) ? 1 : 0;
+    p->group = p->per_row ? c->n_kv_heads * c->head_dim : (quantized(c->k_bits) ? c->group_size : c->head_dim);
     const int R = c->n_kv_heads * c->head_dim;
-    const int passes = p.per_row ? 1 : (R + APPEND_SPAN - 1) / APPEND_SPAN;
-    dim3 grid((unsigned)rows, (unsigned)passes, 2);
+    const int passes = p->per_row ? 1 : (R + APPEND_SPAN - 1) / APPEND_SPAN;
+    *grid = dim3((unsigned)rows, (unsigned)passes, 2);
+    return KVQ_OK;
+}
+
+extern "C" {
+
+int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n_new, const int32_t *start_pos,
+               void *stream)
+{
+    AppendParams p;
+    dim3 grid;
+    int st = prepare_append(c, k_new, v_new, n_new, start_pos, &p, &grid);
+    if (st || grid.x == 0) return st;
     hipLaunchKernelGGL(append_kernel, grid, dim3(APPEND_THREADS), 0, static_cast<hipStream_t>(stream), p);
     return hip_status("append_kernel launch");
 }
@@ -376,8 +414,15 @@ size_t kvq_workspace_bytes(const kvq_cache *c, int n_q_heads, int max_seq_len, i
     return cache_ws_bytes(c, n_q_heads, nc);
 }
 
-int kvq_decode_partials(const kvq_cache *c, const float *q, int n_q_heads, const int32_t *seq_len, int max_seq_len,
-                        float softmax_scale, int chunk_tokens, void *workspace, size_t workspace_bytes, void *stream)
+} // extern "C"
+
+// Query prep + split kernel (the float path: the split kernel alone).  With
+// `ap` (a decode step), the step's append runs first: in the same launch as
+// the query prep on an integer cache, as its own launch otherwise.  Every
+// check runs before anything is enqueued.
+static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, const int32_t *seq_len,
+                            int max_seq_len, float softmax_scale, int chunk_tokens, void *workspace,
+                            size_t workspace_bytes, void *stream, const AppendParams *ap, dim3 ap_grid)
 {
     int ch, nc;
     int st = resolve_chunk(c, n_q_heads, max_seq_len, chunk_tokens, &ch, &nc);
@@ -416,17 +461,32 @@ int kvq_decode_partials(const kvq_cache *c, const float *q, int n_q_heads, const
         p.chunk = ch;
         p.n_chunks = nc;
         p.qk_scale = qk_scale;
+        if (ap && ap_grid.x > 0) {
+            hipLaunchKernelGGL(append_kernel, ap_grid, dim3(APPEND_THREADS), 0, st_, *ap);
+            const int hs = hip_status("append_kernel launch");
+            if (hs) return hs;
+        }
         hipLaunchKernelGGL(fn, grid, dim3(DEC_THREADS), lds, st_, p);
         return hip_status("decode_float_kernel launch");
     }
 
     QuantFn fn = pick_quant(c->k_bits, c->v_bits, c->head_dim, G, groups_per_head(c));
     PrepFn prep = pick_prep(c->k_bits, c->head_dim, G);
-    if (!fn || !prep) return fail(KVQ_ERR_BITS, "no kernel for k_bits=%d v_bits=%d", c->k_bits, c->v_bits);
+    StepPrepFn sprep = pick_step(c->k_bits, c->head_dim, G);
+    if (!fn || !prep || !sprep) return fail(KVQ_ERR_BITS, "no kernel for k_bits=%d v_bits=%d", c->k_bits, c->v_bits);
     int32_t *qdig = reinterpret_cast<int32_t *>(ws + wl.qdig);
     float *qsc = reinterpret_cast<float *>(ws + wl.qsc);
-    hipLaunchKernelGGL(prep, dim3((unsigned)(c->batch * c->n_kv_heads)), dim3(256), 0, st_, q, qdig, qsc, qk_scale);
-    int hs = hip_status("qprep_kernel launch");
+    const unsigned units = (unsigned)(c->batch * c->n_kv_heads);
+    if (ap && ap_grid.x > 0) {
+        if ((unsigned long long)ap_grid.x * ap_grid.y * 2 + units > 0x7FFFFFFFull)
+            return fail(KVQ_ERR_SHAPE, "batch * n_new too large for a fused step");
+        const unsigned n_app = ap_grid.x * ap_grid.y * 2;
+        hipLaunchKernelGGL(sprep, dim3(n_app + units), dim3(256), 0, st_, *ap, (int)ap_grid.x, (int)ap_grid.y, q, qdig,
+                           qsc, qk_scale);
+    } else {
+        hipLaunchKernelGGL(prep, dim3(units), dim3(256), 0, st_, q, qdig, qsc, qk_scale);
+    }
+    int hs = hip_status("query prep launch");
     if (hs) return hs;
 
     QuantParams p;
@@ -459,6 +519,15 @@ int kvq_decode_partials(const kvq_cache *c, const float *q, int n_q_heads, const
     }
     hipLaunchKernelGGL(fn, grid, dim3(QD_THREADS), lds, st_, p);
     return hip_status("decode_quant_kernel launch");
+}
+
+extern "C" {
+
+int kvq_decode_partials(const kvq_cache *c, const float *q, int n_q_heads, const int32_t *seq_len, int max_seq_len,
+                        float softmax_scale, int chunk_tokens, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return enqueue_partials(c, q, n_q_heads, seq_len, max_seq_len, softmax_scale, chunk_tokens, workspace,
+                            workspace_bytes, stream, nullptr, dim3(0, 1, 1));
 }
 
 int kvq_combine(int batch, int n_q_heads, int head_dim, int n_chunks, const void *workspace, size_t workspace_bytes,
@@ -496,6 +565,24 @@ int kvq_decode_attn(const kvq_cache *c, const float *q, int n_q_heads, const int
     if (!out) return fail(KVQ_ERR_NULL, "out is NULL");
     if (!aligned(out, 16)) return fail(KVQ_ERR_ALIGN, "out must be 16-byte aligned");
     st = kvq_decode_partials(c, q, n_q_heads, seq_len, max_seq_len, softmax_scale, ch, workspace, workspace_bytes, stream);
+    if (st) return st;
+    return kvq_combine(c->batch, n_q_heads, c->head_dim, nc, workspace, workspace_bytes, out, stream);
+}
+
+int kvq_decode_step(const kvq_cache *c, const float *k_new, const float *v_new, int n_new, const int32_t *start_pos,
+                    const float *q, int n_q_heads, const int32_t *seq_len, int max_seq_len, float softmax_scale,
+                    int chunk_tokens, float *out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    int ch, nc;
+    int st = resolve_chunk(c, n_q_heads, max_seq_len, chunk_tokens, &ch, &nc);
+    if (st) return st;
+    if (!out) return fail(KVQ_ERR_NULL, "out is NULL");
+    if (!aligned(out, 16)) return fail(KVQ_ERR_ALIGN, "out must be 16-byte aligned");
+    AppendParams ap;
+    dim3 ag;
+    if ((st = prepare_append(c, k_new, v_new, n_new, start_pos, &ap, &ag))) return st;
+    st = enqueue_partials(c, q, n_q_heads, seq_len, max_seq_len, softmax_scale, ch, workspace, workspace_bytes, stream,
+                          &ap, ag);
     if (st) return st;
     return kvq_combine(c->batch, n_q_heads, c->head_dim, nc, workspace, workspace_bytes, out, stream);
 }

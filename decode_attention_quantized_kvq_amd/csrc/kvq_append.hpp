@@ -94,10 +94,10 @@ __device__ __forceinline__ void load8(const float *src, float (&x)[8])
 // starting at value c0.  8/4-bit keys are stored in tiles of 64 slots,
 // slice-major (byte j of the row of slot s at ((s & ~63) * row + (j / 16) *
 // 1024 + (s & 63) * 16 + j % 16)), so one 16-byte slice of 64 consecutive
-// rows is contiguous; 8/4-bit values are stored four positions interleaved
-// per byte (byte j of the row of slot s at ((s & ~3) * row + 4 * j +
-// (s & 3))), so a 32-bit word holds one byte position of four consecutive
-// positions.
+// rows is contiguous; 8/4-bit values are stored offset binary (code + 128
+// per byte, code + 8 per nibble) and four positions interleaved per byte
+// (byte j of the row of slot s at ((s & ~3) * row + 4 * j + (s & 3))), so a
+// 32-bit word holds one byte position of four consecutive positions.
 __device__ __forceinline__ void store_codes(uint8_t *codes, size_t unit, int cap4, int cap64, int slot, int row_bytes,
                                             int c0, int bits, bool interleave, uint32_t w0, uint32_t w1)
 {
@@ -111,6 +111,9 @@ __device__ __forceinline__ void store_codes(uint8_t *codes, size_t unit, int cap
             *reinterpret_cast<uint32_t *>(dst) = w0;
         return;
     }
+    const uint32_t ob = bits == 8 ? 0x80808080u : 0x88888888u;   // offset binary
+    w0 ^= ob;
+    w1 ^= ob;
     uint8_t *grp = codes + (unit * cap4 + (slot & ~3)) * (size_t)row_bytes + (slot & 3);
     const int j0 = bits == 8 ? c0 : c0 / 2;
     const int nb = bits == 8 ? 8 : 4;
@@ -123,12 +126,12 @@ __device__ __forceinline__ void store_codes(uint8_t *codes, size_t unit, int cap
     }
 }
 
-// grid: x = batch * n_new rows, y = passes over the row (groups inside a
-// head) or 1 (per-row scale), z = side (0 = K, 1 = V).  block: 256.
-__global__ __launch_bounds__(APPEND_THREADS) void append_kernel(AppendParams p)
+// One block of the append grid: x = batch * n_new rows, y = passes over the
+// row (groups inside a head) or 1 (per-row scale), z = side (0 = K, 1 = V).
+// 256 threads; block-uniform early exits only.
+__device__ __forceinline__ void append_block(const AppendParams &p, int bx, int by, int side)
 {
-    const int side = blockIdx.z;
-    const int r = blockIdx.x;
+    const int r = bx;
     const int b = r / p.n_new;
     const int i = r - b * p.n_new;
     const int start = p.start_pos[b];
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(APPEND_THREADS) void append_kernel(AppendParams p)
         return;
     }
 
-    const int e0 = (blockIdx.y * APPEND_THREADS + tid) * APPEND_ELEMS;
+    const int e0 = (by * APPEND_THREADS + tid) * APPEND_ELEMS;
     const bool active = e0 < R;
     const int h = active ? e0 / HD : 0;
     const int c0 = active ? e0 - h * HD : 0;
@@ -230,6 +233,11 @@ __global__ __launch_bounds__(APPEND_THREADS) void append_kernel(AppendParams p)
                 w0, w1);
     if (c0 % p.group == 0)
         scales[row * (size_t)(HD / p.group) + c0 / p.group] = sh;
+}
+
+__global__ __launch_bounds__(APPEND_THREADS) void append_kernel(AppendParams p)
+{
+    append_block(p, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 } // namespace kvq

@@ -19,7 +19,9 @@
 //  * the value weights w = 2^(z - max z) * s_v, per chunk, as
 //    w_int = rint(w * 32767 / max s_v) split into two unsigned bytes, so
 //    v_dot4_u32_u8 runs over four positions at once against value codes
-//    stored four positions interleaved (offset binary after one XOR).
+//    stored four positions interleaved and offset binary (code + 8 or
+//    code + 128, never negative); the offset's share, bias * sum(w), is
+//    subtracted once at the end.
 // Rounding happens only in q_int (|dq| <= s_q / 2) and in w_int
 // (|dw| <= max s_v / 65534); accumulation is exact in int32, then fp32.
 //
@@ -34,8 +36,9 @@
 //      four positions per word -> LDS (over the sub-chunk's scores).
 //   3. values: a lane owns fixed byte positions (two channels) of every
 //      4-position group and accumulates v_dot4_u32_u8 over the sub-chunk's
-//      groups; the group's weight words are LDS broadcasts.
-//   4. the integer sums become floats (offset binary and fixed point undone)
+//      groups (int4: the even channel's nibbles and the whole bytes, even +
+//      16 * odd); the group's weight words are LDS broadcasts.
+//   4. the integer sums become floats (byte split and fixed point undone)
 //      and are merged into the wave's running (max, sum, acc) with the usual
 //      2^(m - M) factors.
 // At the end the 4 waves are merged the same way through LDS and the chunk's
@@ -52,6 +55,7 @@ constexpr int QD_WAVES = QD_THREADS / 64;
 // groups make the per-position LDS large
 __host__ __device__ constexpr int qd_sub(int G, int vg) { return G * vg >= 16 ? 128 : 256; }
 constexpr int Q_RANGE = 30000;
+constexpr int QD_PF = 16;       // value group loads in flight per lane
 constexpr int W_RANGE = 32767;
 
 template <int KB, int VB, int HD, int G> struct QT {
@@ -136,14 +140,14 @@ __host__ __device__ inline QuantSmem quant_smem(int G, int HD, int vg)
 // decode kernel reads them in).
 // ---------------------------------------------------------------------------
 template <int KB, int HD, int G>
-__global__ __launch_bounds__(256) void qprep_kernel(const float *__restrict__ q, int32_t *__restrict__ qdig,
-                                                    float *__restrict__ qsc, float qk_scale)
+__device__ __forceinline__ void qprep_block(const float *__restrict__ q, int32_t *__restrict__ qdig,
+                                            float *__restrict__ qsc, float qk_scale, int unit)
 {
     constexpr int K_COLS = HD * KB / 32;
     constexpr int ND = KB == 4 ? 4 : 2;
     constexpr int CPC = KB == 4 ? 8 : 4;
     constexpr int BITS = KB == 4 ? 4 : 8;
-    const int unit = blockIdx.x;                         // b * Hkv + kvh
+    // unit = b * Hkv + kvh
     const float *qh = q + (size_t)unit * G * HD;         // query heads unit*G .. unit*G+G-1
     __shared__ float amax[G];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -176,6 +180,13 @@ __global__ __launch_bounds__(256) void qprep_kernel(const float *__restrict__ q,
         for (int j = 0; j < ND; j++) qdig[(((size_t)unit * ND + j) * K_COLS + col) * G + h] = (int32_t)d[j];
     }
     if (tid < G) qsc[unit * G + tid] = amax[tid] / (float)Q_RANGE * qk_scale;
+}
+
+template <int KB, int HD, int G>
+__global__ __launch_bounds__(256) void qprep_kernel(const float *__restrict__ q, int32_t *__restrict__ qdig,
+                                                    float *__restrict__ qsc, float qk_scale)
+{
+    qprep_block<KB, HD, G>(q, qdig, qsc, qk_scale, blockIdx.x);
 }
 
 template <int KB>
@@ -397,21 +408,34 @@ void decode_quant_kernel(QuantParams p)
     const int gi = lane / T::V_LPG;                  // group slot of a wave load
     const int qsl = lane % T::V_LPG;                 // dword slice of the group
     constexpr uint32_t GSTEP = T::V_GPL * 4 * T::V_ROW;   // bytes per wave-wide group load
-    constexpr int PFH = GSTEP * 8 <= 4096 ? 8 : 4096 / GSTEP;   // loads per descriptor (offsets < 4 KiB)
-    constexpr int PF = 2 * PFH;                      // group loads in flight per lane
+    // group loads in flight per lane (at most one sub-chunk's groups)
+    constexpr int PF_WANT = QD_PF;
+    constexpr int PF = PF_WANT < (S / 4) / T::V_GPL ? PF_WANT : (S / 4) / T::V_GPL;
+    constexpr int NPF = PF < 4096 / (int)GSTEP ? PF : 4096 / (int)GSTEP;   // loads per descriptor (offsets < 4 KiB)
+    constexpr int NR = PF / NPF;                     // descriptors per batch
+    static_assert(PF % NPF == 0, "whole descriptors per batch");
     constexpr int PB = PF * T::V_GPL;                // groups per batch (divides S / 4)
     static_assert((S / 4) % PB == 0, "a sub-chunk holds whole batches");
     const int ngw = (nw + 3) >> 2;                   // groups of this wave
     const uint8_t *vb0 = p.v_codes + ((size_t)bh * p.cap4 + t0 + s0) * T::V_ROW;
     const uint32_t vo = gi * 4 * T::V_ROW + qsl * T::V_DPL * 4;
-    auto vrsrc = [&](int g0, int hf) {
-        const int b0 = g0 * 4 * T::V_ROW + hf * PFH * (int)GSTEP;
-        return make_rsrc(vb0 + b0, (uint32_t)max(ngw * 4 * T::V_ROW - b0, 0));
+    struct VRs {
+        rsrc_t r[NR];
+    };
+    // descriptors of the batch starting at group g0
+    auto vrsrc = [&](int g0) {
+        VRs d;
+#pragma unroll
+        for (int r = 0; r < NR; r++) {
+            const int b0 = g0 * 4 * T::V_ROW + r * NPF * (int)GSTEP;
+            d.r[r] = make_rsrc(vb0 + b0, (uint32_t)max(ngw * 4 * T::V_ROW - b0, 0));
+        }
+        return d;
     };
     uint32_t buf[PF][T::V_DPL];
-    auto vload = [&](int g0, int f, const rsrc_t &ra, const rsrc_t &rb) {
+    auto vload = [&](int f, const VRs &rs) {
 #pragma unroll
-        for (int d = 0; d < T::V_DPL; d++) buf[f][d] = bld_u32(f < PFH ? ra : rb, vo + (f % PFH) * GSTEP + d * 4);
+        for (int d = 0; d < T::V_DPL; d++) buf[f][d] = bld_u32(rs.r[f / NPF], vo + (f % NPF) * GSTEP + d * 4);
     };
     const int vgrp = (qsl * T::V_DPL * T::V_CPD) / (HD / KG);   // value scale group of the lane
     const uint32_t *wdg = wdw + (size_t)vgrp * (S / 4) * G * 2;
@@ -429,18 +453,19 @@ void decode_quant_kernel(QuantParams p)
 #pragma unroll
         for (int d = 0; d < T::V_DPL; d++) {
             if constexpr (VB == 4) {
-                const uint32_t u = x[d] ^ 0x88888888u;        // offset binary per nibble
-                const uint32_t ulo = u & 0x0F0F0F0Fu;          // even channel, 4 positions
-                const uint32_t uhi = u & 0xF0F0F0F0u;          // odd channel, x16
+                // (codes are stored offset binary) the even channel's nibbles,
+                // and whole bytes: even + 16 * odd channel
+                const uint32_t u = x[d];
+                const uint32_t ulo = u & 0x0F0F0F0Fu;
 #pragma unroll
                 for (int h = 0; h < G; h++) {
                     accl[h][2 * d] = __builtin_amdgcn_udot4(wl[h], ulo, accl[h][2 * d], false);
                     acch[h][2 * d] = __builtin_amdgcn_udot4(wh[h], ulo, acch[h][2 * d], false);
-                    accl[h][2 * d + 1] = __builtin_amdgcn_udot4(wl[h], uhi, accl[h][2 * d + 1], false);
-                    acch[h][2 * d + 1] = __builtin_amdgcn_udot4(wh[h], uhi, acch[h][2 * d + 1], false);
+                    accl[h][2 * d + 1] = __builtin_amdgcn_udot4(wl[h], u, accl[h][2 * d + 1], false);
+                    acch[h][2 * d + 1] = __builtin_amdgcn_udot4(wh[h], u, acch[h][2 * d + 1], false);
                 }
             } else {
-                const uint32_t u = x[d] ^ 0x80808080u;        // offset binary per byte
+                const uint32_t u = x[d];                       // offset binary per byte
 #pragma unroll
                 for (int h = 0; h < G; h++) {
                     accl[h][d] = __builtin_amdgcn_udot4(wl[h], u, accl[h][d], false);
@@ -452,11 +477,13 @@ void decode_quant_kernel(QuantParams p)
 
     // ---- the wave's running result: max M (unscaled score units), per-lane
     // partial sum of p, and the lane's output channels, all relative to M
-    float M[G], lsum[G], af[G][T::V_ACC];
+    float M[G], lsum[G], af[G][T::V_ACC], bsum[KG][G];
 #pragma unroll
     for (int h = 0; h < G; h++) {
         M[h] = -INFINITY;
         lsum[h] = 0.0f;
+#pragma unroll
+        for (int g = 0; g < KG; g++) bsum[g][h] = 0.0f;
 #pragma unroll
         for (int c = 0; c < T::V_ACC; c++) af[h][c] = 0.0f;
     }
@@ -470,22 +497,27 @@ void decode_quant_kernel(QuantParams p)
         for (int h = 0; h < G; h++) mloc[h] = -INFINITY;
 #pragma unroll
         for (int g = 0; g < KG; g++) vmloc[g] = 0.0f;
-        // (both halves run unconditionally: a half past the end sees only
-        // invalid lanes and zero rows, and the code stays free of a merge
-        // point that would send the two register sets through memory)
-        for (int tb = sc0; tb < sc0 + ns; tb += 128) {
+        // (tiles run in pairs, both halves unconditionally: a half past the
+        // end sees only invalid lanes and zero rows, and the code stays free
+        // of a merge point that would send the two register sets through
+        // memory; the last pair is peeled to start the value loads early)
+        int tb = sc0;
+        for (; tb + 128 < sc0 + ns; tb += 128) {
             load(tb + 64, tb_);
             compute(tb, sc0, ta);
-            if (tb + 128 < sc0 + ns) load(tb + 128, ta);
+            load(tb + 128, ta);
             compute(tb + 64, sc0, tb_);
         }
+        load(tb + 64, tb_);
+        compute(tb, sc0, ta);
         // the sub-chunk's first batch of value loads, in flight during the
-        // weights pass
+        // last key tile and the weights pass
         {
-            const rsrc_t ra = vrsrc(sc0 >> 2, 0), rb = vrsrc(sc0 >> 2, 1);
+            const VRs rs = vrsrc(sc0 >> 2);
 #pragma unroll
-            for (int f = 0; f < PF; f++) vload(0, f, ra, rb);
+            for (int f = 0; f < PF; f++) vload(f, rs);
         }
+        compute(tb + 64, sc0, tb_);
         float ms[G], vms[KG];                        // sub-chunk maxima, wave-uniform
 #pragma unroll
         for (int h = 0; h < G; h++) ms[h] = wave_max_u(mloc[h]);
@@ -577,11 +609,11 @@ void decode_quant_kernel(QuantParams p)
             int rb = 0;
             for (; rb < nfull; rb += PB) {
                 const int nb = g0 + rb + PB;         // first group of the next batch
-                const rsrc_t ra = vrsrc(nb, 0), rb2 = vrsrc(nb, 1);
+                const VRs rs = vrsrc(nb);
 #pragma unroll
                 for (int f = 0; f < PF; f++) {
                     group(rb + f * T::V_GPL + gi, buf[f]);
-                    vload(nb, f, ra, rb2);
+                    vload(f, rs);
                 }
             }
 #pragma unroll
@@ -595,15 +627,12 @@ void decode_quant_kernel(QuantParams p)
         }
 
         // ---------------- merge the sub-chunk into the wave's running result -----
-        // integer sums -> floats: undo the byte split, the x16 of odd V4
-        // channels and the offset binary (sum of w_int over the sub-chunk, a
-        // wave total), then the fixed point; scale both parts to the new max.
+        // integer sums -> floats: undo the byte split and (int4) the even
+        // channel inside the whole-byte sums, then the fixed point; scale both
+        // parts to the new max.  The offset binary's share (bias * sum of
+        // w_int, the same for every channel) is kept as per-lane partial sums
+        // and taken out once at the end.
         {
-            // per (head, scale group) the wave-uniform factors: c = fn * vms / 32767
-            // (fn = 2^(q_s (m_s - M_new))), the offset -bias * sum(w_int) * c
-            // (lanes of the other group slots hold partial sums of the same
-            // channels, added to slot 0 at the end: the offset is removed once)
-            const float bias = VB == 4 ? 8.0f : 128.0f;
 #pragma unroll
             for (int h = 0; h < G; h++) {
                 const float Mn = fmaxf(M[h], ms[h]);
@@ -611,21 +640,26 @@ void decode_quant_kernel(QuantParams p)
                 const float fn = __builtin_amdgcn_exp2f(qs[h] * (ms[h] - Mn));
                 M[h] = Mn;
                 lsum[h] = fmaf(lsum[h], fo, lloc[h] * fn);
-                float cg[KG], og[KG];
+                float cg[KG];                        // c = fn * vms / 32767 per scale group
 #pragma unroll
                 for (int g = 0; g < KG; g++) {
                     cg[g] = fn * vms[g] * (1.0f / (float)W_RANGE);
-                    const float wsum = (float)wave_sum_ui(wsl[g][h]);
-                    og[g] = (T::V_GPL == 1 || gi == 0) ? -bias * wsum * cg[g] : 0.0f;
+                    bsum[g][h] = fmaf(bsum[g][h], fo, (float)wsl[g][h] * cg[g]);
+                }
+                // 256 * hi + lo is exact in uint32 (hi bytes <= 127, at most 64
+                // groups a sub-chunk)
+                uint32_t vi[T::V_ACC];
+#pragma unroll
+                for (int c = 0; c < T::V_ACC; c++) vi[c] = (acch[h][c] << 8) + accl[h][c];
+                if constexpr (VB == 4) {
+#pragma unroll
+                    for (int c = 1; c < T::V_ACC; c += 2) vi[c] -= vi[c - 1];   // 16 * odd channel
                 }
 #pragma unroll
                 for (int c = 0; c < T::V_ACC; c++) {
                     const int g = ((qsl * T::V_ACC + c) / (HD / KG));   // scale group of the channel
-                    // 256 * hi + lo is exact in uint32 (at most 64 groups a sub-chunk)
-                    const float v = (float)((acch[h][c] << 8) + accl[h][c]);
-                    // odd int4 channels were accumulated x16
                     const float cs = (VB == 4 && (c & 1)) ? cg[g] * 0.0625f : cg[g];
-                    af[h][c] = fmaf(af[h][c], fo, fmaf(v, cs, og[g]));
+                    af[h][c] = fmaf(af[h][c], fo, (float)vi[c] * cs);
                 }
             }
         }
@@ -643,6 +677,20 @@ void decode_quant_kernel(QuantParams p)
             for (int h = 0; h < G; h++)
 #pragma unroll
                 for (int c = 0; c < T::V_ACC; c++) af[h][c] += __shfl_xor(af[h][c], m, 64);
+    }
+    {
+        // the offset binary: code = stored - bias, so subtract bias * sum(w)
+        // (in the same fixed-point units) from every channel
+        const float bias = VB == 4 ? 8.0f : 128.0f;
+#pragma unroll
+        for (int g = 0; g < KG; g++)
+#pragma unroll
+            for (int h = 0; h < G; h++) {
+                const float ob = bias * wave_sum_u(bsum[g][h]);
+#pragma unroll
+                for (int c = 0; c < T::V_ACC; c++)
+                    if ((qsl * T::V_ACC + c) / (HD / KG) == g) af[h][c] -= ob;
+            }
     }
     __syncthreads();                                 // every wave is done with scores and weights
     float *pm = misc;                                // [QD_WAVES][G] wave maxima (log2 units)

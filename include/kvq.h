@@ -67,7 +67,9 @@ extern "C" {
  * Widths (k_bits, v_bits), per side:
  *   32 = float32 rows, 16 = fp16 rows (round to nearest even),
  *    8 = int8 codes in [-127, 127], 4 = int4 codes in [-7, 7], two per byte,
- *        element 2j in the low nibble of byte j, two's complement.
+ *        element 2j in the low nibble of byte j.  Key codes are stored two's
+ *        complement; value codes offset binary (code + 128 per byte, code + 8
+ *        per nibble, so the stored field is never negative).
  *   Supported pairs: (32,32), (16,16) and any pair from {8,4} x {8,4}.
  *
  * group_size: values per fp16 scale on the quantized sides.  Either a
@@ -220,6 +222,22 @@ int kvq_combine(int batch, int n_q_heads, int head_dim, int n_chunks, const void
                 size_t workspace_bytes, float *out, void *stream);
 
 int kvq_decode_attn(const kvq_cache *c, const float *q, int n_q_heads, const int32_t *seq_len,
+                    int max_seq_len, float softmax_scale, int chunk_tokens, float *out,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step (mni-ml page, how the KV cache gives its speed: a step
+ * adds only the new token's K and V to the cache, then attends over it):
+ * exactly kvq_append(c, k_new, v_new, n_new, start_pos, stream) followed by
+ * kvq_decode_attn(c, q, ..., stream), with the same arguments, rules and
+ * results.  A step is three launches: on an 8/4-bit cache the append and
+ * the query's fixed-point preparation share the first one, then the split
+ * kernel and the combine; on a 16/32-bit cache append, split, combine.
+ * Every argument is checked before anything is enqueued; on an error
+ * nothing is.
+ */
+int kvq_decode_step(const kvq_cache *c, const float *k_new, const float *v_new, int n_new,
+                    const int32_t *start_pos, const float *q, int n_q_heads, const int32_t *seq_len,
                     int max_seq_len, float softmax_scale, int chunk_tokens, float *out,
                     void *workspace, size_t workspace_bytes, void *stream);
 

@@ -61,8 +61,10 @@ def cache_arrays(cache):
     if d.v_bits < 16:
         # 8/4-bit values: four positions interleaved per byte (kvq.h):
         # byte j of slot s at ((s & ~3) * R + 4 * j + (s & 3)) within a (b, head)
+        # stored offset binary: code + 128 per byte (8-bit), code + 8 per nibble (4-bit)
         cap4 = (cap + 3) // 4 * 4
         vc = vraw.reshape(B, H, cap4 // 4, R, 4).transpose(0, 1, 2, 4, 3).reshape(B, H, cap4, R)[:, :, :cap]
+        vc = vc ^ np.uint8(0x80 if d.v_bits == 8 else 0x88)
     else:
         vc = vraw.reshape(B, H, cap, R)
     out = [kc, vc]

@@ -150,6 +150,34 @@ def test_decode_argument_errors(kvq):
         assert e.value.status == code, over
 
 
+def test_decode_step_argument_errors(kvq):
+    """The fused step checks the append's and the decode's arguments alike,
+    before it enqueues anything."""
+    d = _desc(kvq)
+    ws_need = kvq.kvq_workspace_bytes(d, 8, 100, 0)
+    ok = 0x40000
+    base = dict(k_new=ok, v_new=ok, n_new=1, start_pos=ok, q=ok, n_q_heads=8, seq_len=ok, max_seq_len=100,
+                scale=0.0, chunk=0, out=ok, ws=ok, ws_bytes=ws_need)
+    cases = [
+        (dict(n_new=-1), -3), (dict(k_new=None), -1), (dict(start_pos=None), -1), (dict(v_new=ok + 4), -7),
+        (dict(start_pos=ok + 2), -7),
+        (dict(n_q_heads=6), -3), (dict(q=None), -1), (dict(seq_len=None), -1), (dict(ws=None), -1),
+        (dict(out=None), -1), (dict(q=ok + 8), -7), (dict(ws=ok + 128), -7), (dict(out=ok + 4), -7),
+        (dict(ws_bytes=ws_need - 1), -6), (dict(max_seq_len=0), -9), (dict(chunk=100), -9),
+        (dict(scale=float("nan")), -9),
+        # the decode's checks also hold when there is nothing to append
+        (dict(n_new=0, q=None), -1), (dict(n_new=0, ws_bytes=ws_need - 1), -6),
+    ]
+    for over, code in cases:
+        a = dict(base)
+        a.update(over)
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.kvq_decode_step(d, a["k_new"], a["v_new"], a["n_new"], a["start_pos"], a["q"], a["n_q_heads"],
+                                a["seq_len"], a["max_seq_len"], a["scale"], a["chunk"], a["out"], a["ws"],
+                                a["ws_bytes"], 0)
+        assert e.value.status == code, over
+
+
 def test_combine_argument_errors(kvq):
     need = 0
     with pytest.raises(kvq.KvqError) as e:
@@ -172,7 +200,7 @@ def test_workspace_and_chunks(kvq):
     ch = kvq.kvq_chunk_tokens(d, 32, 32768)
     assert ch % 64 == 0 and 64 <= ch <= 4096
     n_chunks = -(-32768 // ch)
-    assert 32 * 8 * n_chunks >= 2048                     # enough workgroups for 256 CUs
+    assert 32 * 8 * n_chunks >= 4096                     # 16 workgroups per CU over 256 CUs
     P = 32 * 32
     partials = ((P * n_chunks * 8 + 255) // 256) * 256 + P * n_chunks * 128 * 4
     # int4 keys: the query's fixed-point digits (4 per value) and scales follow the partials
@@ -196,8 +224,11 @@ def test_workspace_and_chunks(kvq):
     assert kvq.kvq_chunk_tokens(small, 4, 257) == 256
     small_f = _desc(kvq, batch=1, n_kv_heads=4, head_dim=64, capacity=257, k_bits=16, v_bits=16)
     assert kvq.kvq_chunk_tokens(small_f, 4, 257) == 64
-    # integer caches: the chunk is no longer bounded by LDS (4096 at 32K x 256 units)
-    assert kvq.kvq_chunk_tokens(d, 32, 32768) == 4096
+    # integer caches: the chunk is not bounded by LDS; 2048 at 32K x 256 units
+    # (16 chunks per unit), 1024 at 32K x 128 units
+    assert kvq.kvq_chunk_tokens(d, 32, 32768) == 2048
+    d8 = _desc(kvq, batch=16, n_kv_heads=8, capacity=32768, k_bits=8, v_bits=4)
+    assert kvq.kvq_chunk_tokens(d8, 32, 32768) == 1024
 
 
 def test_binding_has_no_fallback(kvq, monkeypatch, tmp_path):

@@ -250,9 +250,47 @@ def test_fp16_conversion_exhaustive():
         _fp16_patterns(kvq, np.arange(hi, hi + step, dtype=np.uint64).astype(np.uint32))
 
 
-def test_graph_replay_matches_eager(oq):
-    """A step captured in a HIP graph (append + decode + combine) gives the
-    eager result bit for bit on every replay, with eager work in between."""
+@pytest.mark.parametrize("kb,vb,group", MODES)
+@pytest.mark.parametrize("n_new", [0, 1, 3])
+def test_decode_step_matches_separate_calls(oq, kb, vb, group, n_new):
+    """kvq_decode_step leaves the cache and the output bit for bit as
+    kvq_append followed by kvq_decode_attn does, and matches the oracle."""
+    kvq = need_gpu()
+    import torch
+    from workloads.device import positions, to_device
+    B, H, G, HD, n0 = 2, 2, 4, 128, 650
+    n = n0 + n_new
+    gs = group_size_of(kb, vb, group, H, HD)
+    K, V, q = _data(B, H, n, HD, H * G, 31 + n_new)
+    caches = [kvq.alloc_cache(B, H, HD, n, kb, vb, gs) for _ in range(2)]
+    for c in caches:
+        kvq.kvq_append(c, to_device(K[:, :, :n0]), to_device(V[:, :, :n0]), n0, positions([0] * B))
+    kn, vn, qd = to_device(K[:, :, n0:]), to_device(V[:, :, n0:]), to_device(q)
+    pos, lens = positions([n0] * B), positions([n] * B)
+    ws_bytes = kvq.kvq_workspace_bytes(caches[0], H * G, n, 0)
+    outs = [torch.full((B, H * G, HD), 7.0, dtype=torch.float32, device="cuda") for _ in range(2)]
+    wss = [torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda") for _ in range(2)]
+    kvq.kvq_decode_step(caches[0], kn, vn, n_new, pos, qd, H * G, lens, n, 0.0, 0, outs[0], wss[0], ws_bytes)
+    kvq.kvq_append(caches[1], kn, vn, n_new, pos)
+    kvq.kvq_decode_attn(caches[1], qd, H * G, lens, n, 0.0, 0, outs[1], wss[1], ws_bytes)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    for name in ("k_codes", "v_codes", "k_scales", "v_scales"):
+        a, b = getattr(caches[0], name), getattr(caches[1], name)
+        if a is not None:
+            assert torch.equal(a, b), name
+    got = outs[0].cpu().numpy()
+    sc = softmax_default(HD)
+    for b in range(B):
+        want = oq.decode_step(kb, vb, gs, 0, 0, K[b], V[b], q[b], sc)
+        assert_close(got[b], want, f"step kb={kb} vb={vb} n_new={n_new} b={b}")
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_replay_matches_eager(oq, fused):
+    """A step captured in a HIP graph (append + decode + combine, as separate
+    calls or as one kvq_decode_step) gives the eager result bit for bit on
+    every replay, with eager work in between."""
     kvq = need_gpu()
     import torch
     from workloads.device import positions, to_device
@@ -267,8 +305,11 @@ def test_graph_replay_matches_eager(oq):
     out = torch.zeros((B, H * G, HD), dtype=torch.float32, device="cuda")
 
     def step(st):
-        kvq.kvq_append(cache, k1, v1, 1, pos, st)
-        kvq.kvq_decode_attn(cache, qd, H * G, lens, n, 0.0, 0, out, ws, ws_bytes, st)
+        if fused:
+            kvq.kvq_decode_step(cache, k1, v1, 1, pos, qd, H * G, lens, n, 0.0, 0, out, ws, ws_bytes, st)
+        else:
+            kvq.kvq_append(cache, k1, v1, 1, pos, st)
+            kvq.kvq_decode_attn(cache, qd, H * G, lens, n, 0.0, 0, out, ws, ws_bytes, st)
 
     step(torch.cuda.current_stream())
     torch.cuda.synchronize()
