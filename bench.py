@@ -1,10 +1,14 @@
 #!/usr/bin/env python3
 """Decode-attention throughput over a quantized KV cache on one MI355X.
 
-One step = the whole hot path for one batch: quantize-append the step's new
-K/V row of every sequence and KV head into the cache (kvq_append), split-K
-decode attention over the cache (kvq_decode_partials) and the merge of the
-chunk partials (kvq_combine).  Inputs are resident in HBM before timing.
+One step = the whole hot path for one batch, one kvq_decode_step call per
+layer: quantize-append the step's new K/V row of every sequence and KV head
+into the cache, split-K decode attention over the cache and the merge of the
+chunk partials (three launches).  Inputs are resident in HBM before timing.
+The K timed steps run as one HIP graph of K steps (the way a model's layers
+follow each other inside one decode step); the line also reports a graph of
+one step replayed K times, eager steps, and the separate calls timed with
+events between them.
 
 The headline workload is 32 sequences x 32 query heads / 8 KV heads x
 head_dim 128 at a 32K-token context with nibble-packed int4 K and V
@@ -63,7 +67,8 @@ def step_bytes(w, mode) -> float:
     return split_bytes(w, mode) + w.batch * w.n_q_heads * w.head_dim * 4 + append
 
 
-def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = False, log=print) -> dict:
+def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = False, log=print,
+             settle_ms: float = 100.0) -> dict:
     import torch
 
     import decode_attention_quantized_kvq_amd as kvq
@@ -92,60 +97,96 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps * w.n_layers)]
 
-    def one_step(record, st):
-        for li, (cache, k_last, v_last, q) in enumerate(layers):
-            e = ev[record * w.n_layers + li] if record is not None else None
+    def one_step(st):
+        # the whole hot path of a decode step: one call per layer
+        for cache, k_last, v_last, q in layers:
             if scrub is not None:
                 scrub.zero_()
-            if e: e[0].record(st)
+            kvq.kvq_decode_step(cache, k_last, v_last, 1, pos, q, w.n_q_heads, lens, max_len, 0.0, ch, out, ws,
+                                ws_bytes, st)
+
+    def parts_step(record, st):
+        # the same work as separate calls, with events between them
+        for li, (cache, k_last, v_last, q) in enumerate(layers):
+            e = ev[record * w.n_layers + li]
+            if scrub is not None:
+                scrub.zero_()
+            e[0].record(st)
             kvq.kvq_append(cache, k_last, v_last, 1, pos, st)
-            if e: e[1].record(st)
+            e[1].record(st)
             kvq.kvq_decode_partials(cache, q, w.n_q_heads, lens, max_len, 0.0, ch, ws, ws_bytes, st)
-            if e: e[2].record(st)
+            e[2].record(st)
             kvq.kvq_combine(w.batch, w.n_q_heads, w.head_dim, n_chunks, ws, ws_bytes, out, st)
-            if e: e[3].record(st)
+            e[3].record(st)
 
     for _ in range(warmup):
-        one_step(None, stream)
+        one_step(stream)
     torch.cuda.synchronize()
     # (1) per-kernel breakdown: events around each call, eager launches
     t0 = time.perf_counter()
     for s_ in range(steps):
-        one_step(s_, stream)
+        parts_step(s_, stream)
     torch.cuda.synchronize()
     wall_eager = time.perf_counter() - t0
     t_app = sum(e[0].elapsed_time(e[1]) for e in ev) / len(ev)
     t_split = sum(e[1].elapsed_time(e[2]) for e in ev) / len(ev)
     t_comb = sum(e[2].elapsed_time(e[3]) for e in ev) / len(ev)
-    # (2) the split launch alone, back to back, events only around the loop
+    # (2) the split launch alone, back to back, events only around the loop.
+    # After an idle pause the first few dozen launches of a busy GPU run up to
+    # 40% slower for some milliseconds (a power-management transient; clocks
+    # and temperatures stay flat), so launches run untimed for `settle_ms`
+    # first and the timed loop is long enough to average over what remains.
     cache0, _, _, q0 = layers[0]
     ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ea.record(stream)
-    for _ in range(steps):
-        kvq.kvq_decode_partials(cache0, q0, w.n_q_heads, lens, max_len, 0.0, ch, ws, ws_bytes, stream)
-    eb.record(stream)
-    torch.cuda.synchronize()
-    t_split_loop = ea.elapsed_time(eb) / steps
-    # (3) the whole step as a replayed HIP graph (no launch gaps from the host,
-    # no event records between the kernels): the timed number
-    ms_step_graph = None
+
+    def timed(fn, n, st=stream):
+        ea.record(st)
+        for _ in range(n):
+            fn()
+        eb.record(st)
+        torch.cuda.synchronize()
+        return ea.elapsed_time(eb)
+
+    split = lambda: kvq.kvq_decode_partials(cache0, q0, w.n_q_heads, lens, max_len, 0.0, ch, ws, ws_bytes, stream)
+    settled = 0.0
+    while settled < settle_ms:
+        settled += timed(split, 50)
+    n_split = max(steps, 200)
+    t_split_loop = timed(split, n_split) / n_split
+    # (3) eager fused steps, back to back
+    ms_step_eager = timed(lambda: one_step(stream), steps) / steps
+    # (4) the step as HIP graphs: one step per replay, and `steps` steps in
+    # one graph (as the layers of a model's decode step run: no host launch
+    # between them); the latter is the timed number
+    ms_step_graph1 = ms_step_graph = None
     if scrub is None:
-        g = torch.cuda.CUDAGraph()
         cs = torch.cuda.Stream()
         cs.wait_stream(stream)
         with torch.cuda.stream(cs):
-            one_step(None, cs)                       # warm the capture stream
+            one_step(cs)                             # warm the capture stream
         torch.cuda.synchronize()
-        with torch.cuda.graph(g, stream=cs):
-            one_step(None, cs)
-        g.replay()
+        g1 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g1, stream=cs):
+            one_step(cs)
+        gk = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gk, stream=cs):
+            for _ in range(steps):
+                one_step(cs)
+        for _ in range(warmup):
+            g1.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(steps):
-            g.replay()
+            g1.replay()
+        torch.cuda.synchronize()
+        ms_step_graph1 = (time.perf_counter() - t0) / steps * 1e3
+        gk.replay()                                  # untimed: the graph's first launch
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        gk.replay()
         torch.cuda.synchronize()
         ms_step_graph = (time.perf_counter() - t0) / steps * 1e3
-        del g
+        del g1, gk
     ms_step_wall = wall_eager / steps * 1e3
     ms_step_gpu = (t_app + t_split + t_comb) * w.n_layers
     sbytes = step_bytes(w, mode) * w.n_layers
@@ -156,8 +197,10 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
         "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "context": attended(w), "n_layers": w.n_layers,
         "capacity": w.capacity, "n_anchor": w.n_anchor, "window": w.window, "group_size": _group(mode, w),
         "chunk_tokens": ch, "n_chunks": n_chunks, "mall_scrub": flush,
-        "ms_per_step": ms_step, "ms_per_step_graph": ms_step_graph, "ms_per_step_eager_with_events": ms_step_wall,
+        "ms_per_step": ms_step, "ms_per_step_graph": ms_step_graph, "ms_per_step_graph_1step": ms_step_graph1,
+        "ms_per_step_eager": ms_step_eager, "ms_per_step_eager_parts_with_events": ms_step_wall,
         "ms_per_step_kernels": ms_step_gpu, "us_split_back_to_back": t_split_loop * 1e3,
+        "split_launches_timed": n_split, "split_settle_ms": settled,
         "step_GBps": sbytes / (ms_step * 1e-3) / 1e9,
         "tokens_per_s": w.batch / (ms_step * 1e-3),
         "us_append": t_app * 1e3, "us_split": t_split * 1e3, "us_combine": t_comb * 1e3,
@@ -165,7 +208,8 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
     }
     res["split_pct_of_peak"] = 100.0 * res["split_GBps"] / PEAK_HBM_GBS
     log(f"[bench] {w.name} {mode.name}: step {ms_step * 1e3:.1f} us ({res['step_GBps']:.0f} GB/s, "
-        f"{res['tokens_per_s']:.0f} tok/s); split {t_split_loop * 1e3:.1f} us = {res['split_GBps']:.0f} GB/s "
+        f"{res['tokens_per_s']:.0f} tok/s; 1-step graph {(ms_step_graph1 or 0) * 1e3:.1f} us, eager "
+        f"{ms_step_eager * 1e3:.1f} us); split {t_split_loop * 1e3:.1f} us = {res['split_GBps']:.0f} GB/s "
         f"({res['split_pct_of_peak']:.1f}% of peak); append {t_app * 1e3:.1f} us, combine {t_comb * 1e3:.1f} us")
     del layers, ws, out, scrub
     torch.cuda.empty_cache()
@@ -322,8 +366,8 @@ def probe_traffic(chunk: int, log=print) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--chunk", type=int, default=0, help="split-K chunk (0 = the library's choice)")
     ap.add_argument("--modes", choices=["headline", "targets", "all"], default="targets",
                     help="headline: the K4V4 32K line only; targets: + K8V4 at 32K; all: every workload")
