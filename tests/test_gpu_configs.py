@@ -75,6 +75,37 @@ def test_k4v4_32k(oq):
     _run(oq, w, w.modes, sample_b=(0, 31))
 
 
+def test_k4v4_32k_ragged(oq):
+    """The library's chunks over a 32K context with per-sequence lengths that
+    end inside a chunk, on a chunk boundary, in the last chunk, or at 0 and
+    1 (empty chunks write empty partials)."""
+    kvq = need_gpu()
+    import torch
+    from workloads.device import decode, fill, positions, queries
+    w = wl.K4V4_32K
+    (cache, gs), mode = _alloc(kvq, w, wl.K4V4), wl.K4V4
+    fill([cache], w, 0, w.n_pos)
+    q = queries(w, 0)
+    qn = q.cpu().numpy()
+    lens = [w.n_pos - 97 * b for b in range(w.batch)]
+    special = {1: 30001, 2: 24577, 3: 24576, 4: 20000, 5: 513, 6: 1, 7: 0, 8: 4096}
+    for b, L in special.items():
+        lens[b] = L
+    out = decode(cache, q, w.n_q_heads, positions(lens), w.n_pos).cpu().numpy()
+    sc = 1.0 / np.sqrt(w.head_dim)
+    for b in sorted(special) + [20]:
+        L = lens[b]
+        if L == 0:
+            assert np.all(out[b] == 0)
+            continue
+        K = wl.rows(w, wl.K_STREAM, 0, b, L)
+        V = wl.rows(w, wl.V_STREAM, 0, b, L)
+        want = oq.decode_step(mode.k_bits, mode.v_bits, gs, 0, 0, K, V, qn[b], sc)
+        assert_close(out[b], want, f"ragged b={b} L={L}")
+    del cache
+    torch.cuda.empty_cache()
+
+
 def test_k4v4_window(oq):
     w = wl.K4V4_WINDOW
     _run(oq, w, w.modes, sample_b=(0, 13, 31))
