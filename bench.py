@@ -216,6 +216,34 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
     return res
 
 
+def read_probe(log=print, gib: int = 2, launches: int = 50) -> dict:
+    """The bandwidth a plain read stream reaches on this device
+    (kvq_read_probe over `gib` GiB, larger than the 256 MB MALL), after a
+    settle period, timed with HIP events over `launches` launches."""
+    import torch
+
+    import decode_attention_quantized_kvq_amd as kvq
+    nbytes = gib << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty(8192, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(20):
+        kvq.kvq_read_probe(buf, nbytes, sink, 8192 * 4, stream)
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ea.record(stream)
+    for _ in range(launches):
+        kvq.kvq_read_probe(buf, nbytes, sink, 8192 * 4, stream)
+    eb.record(stream)
+    torch.cuda.synchronize()
+    us = ea.elapsed_time(eb) / launches * 1e3
+    gbs = nbytes / us / 1e3
+    log(f"[bench] read probe: {gib} GiB in {us:.1f} us = {gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% of peak)")
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"GBps": round(gbs, 1), "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2), "bytes": nbytes,
+            "us_per_launch": round(us, 2), "kernel": "read_probe_kernel (8 x 16-byte nontemporal loads per thread)"}
+
+
 def cpu_baseline(w, mode, log=print, budget_s: float = 12.0) -> dict:
     """The CPU oracle's decode step, untuned, on a bounded sample of the
     workload: whole sequences (every KV and query head, the full context),
@@ -251,6 +279,14 @@ def cpu_baseline(w, mode, log=print, budget_s: float = 12.0) -> dict:
         done += len(seqs)
     sample_bytes = step_bytes(w, mode) * done / w.batch
     log(f"[bench] cpu oracle: {done} sequence-steps on {cores} thread(s) in {t_work:.2f} s")
+    # the same oracle on one core: one sequence, at least 2 s
+    one, t_one = 0, 0.0
+    while one == 0 or t_one < 2.0:
+        t0 = time.perf_counter()
+        work(0)
+        t_one += time.perf_counter() - t0
+        one += 1
+    log(f"[bench] cpu oracle, one core: {one} sequence-steps in {t_one:.2f} s")
     return {
         "value": sample_bytes / t_work / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
         "sample": f"sequences 0-{cores - 1} of {w.name} ({mode.name}; {w.batch} per step), every head, full "
@@ -258,6 +294,8 @@ def cpu_baseline(w, mode, log=print, budget_s: float = 12.0) -> dict:
                   f"float64 oracle (encode every row, then softmax attention); {t_work:.1f} s of oracle time "
                   f"(input generation excluded)",
         "tokens_per_s": done / t_work,
+        "one_core": {"value": step_bytes(w, mode) * one / w.batch / t_one / 1e9, "unit": "GB/s",
+                     "tokens_per_s": one / t_one, "sample": f"sequence 0, {one} sequence-steps, {t_one:.1f} s"},
     }
 
 
@@ -416,6 +454,7 @@ def main() -> int:
         for m in wl.TINY.modes:
             extra.append(run_mode(wl.TINY, m, args.steps, args.warmup, args.chunk, log=log))
 
+    probe = read_probe(log=log)
     cpu = None if args.no_cpu_baseline else cpu_baseline(head_w, head_m, log=log)
     tr = traffic_record(head_w, head_m)
     traffic = None if tr is None else tr["bytes_per_launch"]
@@ -449,7 +488,9 @@ def main() -> int:
             "traffic": traffic,
             "us_per_launch": round(head["us_split_back_to_back"], 3),
             "bytes_per_launch": head["split_bytes"],
+            "frac_of_read_probe": round(head["split_GBps"] / probe["GBps"], 4),
         },
+        "read_probe": probe,
         "cpu_baseline": cpu,
         "modes": {f"{r['workload']}/{r['mode']}": {k: (round(v, 4) if isinstance(v, float) else v)
                                                    for k, v in r.items()} for r in [head] + extra},

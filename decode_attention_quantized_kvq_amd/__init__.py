@@ -33,7 +33,8 @@ KVQ_ERR_ARG = -9
 
 EXPORTED = (
     "kvq_bytes_per_token", "kvq_cache_sizes", "kvq_append", "kvq_chunk_tokens", "kvq_workspace_bytes",
-    "kvq_decode_partials", "kvq_combine", "kvq_decode_attn", "kvq_decode_step", "kvq_status_str", "kvq_last_error",
+    "kvq_decode_partials", "kvq_combine", "kvq_decode_attn", "kvq_decode_step", "kvq_read_probe", "kvq_status_str",
+    "kvq_last_error",
 )
 
 
@@ -94,6 +95,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_decode_attn.restype = I
         L.kvq_decode_step.argtypes = [C, P, P, I, P, P, I, P, I, ctypes.c_float, I, P, P, S, P]
         L.kvq_decode_step.restype = I
+        L.kvq_read_probe.argtypes = [P, S, P, S, P]
+        L.kvq_read_probe.restype = I
         L.kvq_status_str.argtypes = [I]
         L.kvq_status_str.restype = ctypes.c_char_p
         L.kvq_last_error.argtypes = []
@@ -184,6 +187,10 @@ def kvq_decode_step(cache, k_new, v_new, n_new: int, start_pos, q, n_q_heads: in
     _check(lib().kvq_decode_step(ctypes.byref(_desc(cache)), _ptr(k_new), _ptr(v_new), int(n_new), _ptr(start_pos),
                                  _ptr(q), n_q_heads, _ptr(seq_len), max_seq_len, float(softmax_scale), chunk_tokens,
                                  _ptr(out), _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def kvq_read_probe(buf, nbytes: int, sink, sink_bytes: int, stream=None) -> None:
+    _check(lib().kvq_read_probe(_ptr(buf), int(nbytes), _ptr(sink), int(sink_bytes), _stream(stream)))
 
 
 def kvq_status_str(status: int) -> str:

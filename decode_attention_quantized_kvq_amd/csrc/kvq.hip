@@ -12,6 +12,7 @@
 #include "kvq_decode.hpp"
 #include "kvq_decode_quant.hpp"
 #include "kvq_step.hpp"
+#include "kvq_probe.hpp"
 
 using namespace kvq;
 
@@ -585,6 +586,19 @@ int kvq_decode_step(const kvq_cache *c, const float *k_new, const float *v_new, 
                           &ap, ag);
     if (st) return st;
     return kvq_combine(c->batch, n_q_heads, c->head_dim, nc, workspace, workspace_bytes, out, stream);
+}
+
+int kvq_read_probe(const void *buf, size_t bytes, void *sink, size_t sink_bytes, void *stream)
+{
+    const size_t blk = (size_t)PROBE_THREADS * PROBE_UNROLL * 16;
+    if (!buf || !sink) return fail(KVQ_ERR_NULL, "buf / sink is NULL");
+    if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(KVQ_ERR_ALIGN, "buf must be 16-byte, sink 4-byte aligned");
+    if (bytes < blk || bytes % blk != 0) return fail(KVQ_ERR_ARG, "bytes must be a positive multiple of %zu", blk);
+    const size_t grid = sink_bytes / 4 < 8192 ? sink_bytes / 4 : 8192;
+    if (grid < 1) return fail(KVQ_ERR_ARG, "sink must hold at least one 4-byte word");
+    hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)grid), dim3(PROBE_THREADS), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const probe_u4 *>(buf), (long long)(bytes / blk), static_cast<uint32_t *>(sink));
+    return hip_status("read_probe_kernel launch");
 }
 
 const char *kvq_status_str(int status)

@@ -242,6 +242,16 @@ int kvq_decode_step(const kvq_cache *c, const float *k_new, const float *v_new, 
                     void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---- diagnostics ------------------------------------------------------- */
+/*
+ * Not part of the attention path: stream `bytes` of device memory at `buf`
+ * once with 16-byte loads (a grid of min(sink_bytes / 4, 8192) workgroups,
+ * each writing one word to `sink`), so that a caller timing it learns the
+ * read bandwidth this device reaches in practice.  bytes must be a positive
+ * multiple of 32768; buf 16-byte aligned, sink 4-byte aligned.  Asynchronous
+ * on `stream`.
+ */
+int kvq_read_probe(const void *buf, size_t bytes, void *sink, size_t sink_bytes, void *stream);
+
 /* Static text for a status code. */
 const char *kvq_status_str(int status);
 

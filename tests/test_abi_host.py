@@ -178,6 +178,16 @@ def test_decode_step_argument_errors(kvq):
         assert e.value.status == code, over
 
 
+def test_read_probe_argument_errors(kvq):
+    ok = 0x40000
+    for args, code in [((None, 32768, ok, 64), -1), ((ok, 32768, None, 64), -1), ((ok + 8, 32768, ok, 64), -7),
+                       ((ok, 32768, ok + 2, 64), -7), ((ok, 1000, ok, 64), -9), ((ok, 0, ok, 64), -9),
+                       ((ok, 32768, ok, 3), -9)]:
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.kvq_read_probe(*args, 0)
+        assert e.value.status == code, args
+
+
 def test_combine_argument_errors(kvq):
     need = 0
     with pytest.raises(kvq.KvqError) as e:

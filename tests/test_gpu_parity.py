@@ -329,3 +329,17 @@ def test_graph_replay_matches_eager(oq, fused):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, want), f"replay {r}"
+
+
+def test_read_probe_runs():
+    """The read-bandwidth probe reads every block it is given (an all-zero
+    buffer folds to zero in every workgroup) and rejects bad sizes."""
+    kvq = need_gpu()
+    import torch
+    buf = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.full((64,), -1, dtype=torch.int32, device="cuda")
+    kvq.kvq_read_probe(buf, buf.numel(), sink, sink.numel() * 4)
+    torch.cuda.synchronize()
+    assert torch.all(sink == 0)
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_read_probe(buf, 1000, sink, sink.numel() * 4)
