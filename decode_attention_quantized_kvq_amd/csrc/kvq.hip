@@ -125,15 +125,16 @@ int auto_chunk(const kvq_cache *c, int n_q_heads, int max_seq_len)
     const int G = n_q_heads / c->n_kv_heads;
     const long long units = (long long)c->batch * c->n_kv_heads;
     const int L = max_len_of(c, max_seq_len);
-    // The largest chunk that fits the LDS budget and still gives >= 16
-    // workgroups per CU over 256 CUs (four rounds of the four that fit at
-    // once, so the last round's stragglers cost less); when no chunk does,
+    // The largest chunk of at most 2048 slots that fits the LDS budget and
+    // still gives >= 8 workgroups per CU over 256 CUs; when no chunk does,
     // the smallest one (most workgroups): 64 slots, or 256 for integer
-    // caches, whose waves take 64 positions per step.
+    // caches, whose waves take 64 positions per step.  (Measured at 32K
+    // contexts: 4096-slot chunks leave a longer ragged last round, 1024-slot
+    // ones pay each workgroup's start and final merge twice as often.)
     const int smallest = quant_modes(c) ? 256 : 64;
-    for (int ch = 4096; ch >= smallest; ch >>= 1) {
+    for (int ch = 2048; ch >= smallest; ch >>= 1) {
         if (lds_bytes(c, G, ch) > kAutoLds) continue;
-        if (units * ((L + ch - 1) / ch) >= 4096) return ch;
+        if (units * ((L + ch - 1) / ch) >= 2048) return ch;
     }
     return smallest;
 }

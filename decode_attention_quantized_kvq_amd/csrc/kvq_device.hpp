@@ -86,14 +86,21 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t n_bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n_bytes, 0x00020000);
 }
+// Cache policy of a load (the instruction's cache-policy bits): 0 plain,
+// CP_NT nontemporal.  A stream read exactly once, such as the cache codes,
+// reaches a markedly higher HBM bandwidth with CP_NT on this device (a plain
+// read stream ~79 % of peak, the same stream nontemporal ~88 %).
+constexpr int CP_NT = 2;
+template <int CP = 0>
 __device__ __forceinline__ uint4 bld_u4(rsrc_t r, uint32_t off)
 {
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CP);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+template <int CP = 0>
 __device__ __forceinline__ uint32_t bld_u32(rsrc_t r, uint32_t off)
 {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, CP);
 }
 __device__ __forceinline__ uint32_t bld_u16(rsrc_t r, uint32_t off)
 {

@@ -210,7 +210,7 @@ def test_workspace_and_chunks(kvq):
     ch = kvq.kvq_chunk_tokens(d, 32, 32768)
     assert ch % 64 == 0 and 64 <= ch <= 4096
     n_chunks = -(-32768 // ch)
-    assert 32 * 8 * n_chunks >= 4096                     # 16 workgroups per CU over 256 CUs
+    assert 32 * 8 * n_chunks >= 2048                     # 8 workgroups per CU over 256 CUs
     P = 32 * 32
     partials = ((P * n_chunks * 8 + 255) // 256) * 256 + P * n_chunks * 128 * 4
     # int4 keys: the query's fixed-point digits (4 per value) and scales follow the partials
@@ -234,11 +234,13 @@ def test_workspace_and_chunks(kvq):
     assert kvq.kvq_chunk_tokens(small, 4, 257) == 256
     small_f = _desc(kvq, batch=1, n_kv_heads=4, head_dim=64, capacity=257, k_bits=16, v_bits=16)
     assert kvq.kvq_chunk_tokens(small_f, 4, 257) == 64
-    # integer caches: the chunk is not bounded by LDS; 2048 at 32K x 256 units
-    # (16 chunks per unit), 1024 at 32K x 128 units
+    # integer caches: the chunk is not bounded by LDS; 2048 at 32K for 256 and
+    # for 128 units, 1024 for 64 units
     assert kvq.kvq_chunk_tokens(d, 32, 32768) == 2048
     d8 = _desc(kvq, batch=16, n_kv_heads=8, capacity=32768, k_bits=8, v_bits=4)
-    assert kvq.kvq_chunk_tokens(d8, 32, 32768) == 1024
+    assert kvq.kvq_chunk_tokens(d8, 32, 32768) == 2048
+    d4 = _desc(kvq, batch=8, n_kv_heads=8, capacity=32768, k_bits=8, v_bits=4)
+    assert kvq.kvq_chunk_tokens(d4, 32, 32768) == 1024
 
 
 def test_binding_has_no_fallback(kvq, monkeypatch, tmp_path):
