@@ -33,8 +33,8 @@ KVQ_ERR_ARG = -9
 
 EXPORTED = (
     "kvq_bytes_per_token", "kvq_cache_sizes", "kvq_append", "kvq_chunk_tokens", "kvq_workspace_bytes",
-    "kvq_decode_partials", "kvq_combine", "kvq_decode_attn", "kvq_decode_step", "kvq_read_probe", "kvq_status_str",
-    "kvq_last_error",
+    "kvq_decode_partials", "kvq_prepare_query", "kvq_decode_partials_prepared", "kvq_combine", "kvq_decode_attn",
+    "kvq_decode_step", "kvq_read_probe", "kvq_status_str", "kvq_last_error",
 )
 
 
@@ -89,6 +89,10 @@ def lib() -> ctypes.CDLL:
         L.kvq_workspace_bytes.restype = S
         L.kvq_decode_partials.argtypes = [C, P, I, P, I, ctypes.c_float, I, P, S, P]
         L.kvq_decode_partials.restype = I
+        L.kvq_prepare_query.argtypes = [C, P, I, I, ctypes.c_float, I, P, S, P]
+        L.kvq_prepare_query.restype = I
+        L.kvq_decode_partials_prepared.argtypes = [C, I, P, I, I, P, S, P]
+        L.kvq_decode_partials_prepared.restype = I
         L.kvq_combine.argtypes = [I, I, I, I, P, S, P, P]
         L.kvq_combine.restype = I
         L.kvq_decode_attn.argtypes = [C, P, I, P, I, ctypes.c_float, I, P, P, S, P]
@@ -166,6 +170,18 @@ def kvq_decode_partials(cache, q, n_q_heads: int, seq_len, max_seq_len: int, sof
     _check(lib().kvq_decode_partials(ctypes.byref(_desc(cache)), _ptr(q), n_q_heads, _ptr(seq_len), max_seq_len,
                                      float(softmax_scale), chunk_tokens, _ptr(workspace), int(workspace_bytes),
                                      _stream(stream)))
+
+
+def kvq_prepare_query(cache, q, n_q_heads: int, max_seq_len: int, softmax_scale: float, chunk_tokens: int,
+                      workspace, workspace_bytes: int, stream=None) -> None:
+    _check(lib().kvq_prepare_query(ctypes.byref(_desc(cache)), _ptr(q), n_q_heads, max_seq_len, float(softmax_scale),
+                                   chunk_tokens, _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def kvq_decode_partials_prepared(cache, n_q_heads: int, seq_len, max_seq_len: int, chunk_tokens: int, workspace,
+                                 workspace_bytes: int, stream=None) -> None:
+    _check(lib().kvq_decode_partials_prepared(ctypes.byref(_desc(cache)), n_q_heads, _ptr(seq_len), max_seq_len,
+                                              chunk_tokens, _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
 def kvq_combine(batch: int, n_q_heads: int, head_dim: int, n_chunks: int, workspace, workspace_bytes: int, out,

@@ -422,17 +422,23 @@ size_t kvq_workspace_bytes(const kvq_cache *c, int n_q_heads, int max_seq_len, i
 // `ap` (a decode step), the step's append runs first: in the same launch as
 // the query prep on an integer cache, as its own launch otherwise.  Every
 // check runs before anything is enqueued.
+enum { PHASE_PREP = 1, PHASE_SPLIT = 2 };
+
 static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, const int32_t *seq_len,
                             int max_seq_len, float softmax_scale, int chunk_tokens, void *workspace,
-                            size_t workspace_bytes, void *stream, const AppendParams *ap, dim3 ap_grid)
+                            size_t workspace_bytes, void *stream, const AppendParams *ap, dim3 ap_grid,
+                            int phases = PHASE_PREP | PHASE_SPLIT)
 {
     int ch, nc;
     int st = resolve_chunk(c, n_q_heads, max_seq_len, chunk_tokens, &ch, &nc);
     if (st) return st;
     if ((st = check_pointers(c))) return st;
-    if (!q || !seq_len || !workspace) return fail(KVQ_ERR_NULL, "q / seq_len / workspace is NULL");
-    if (!aligned(q, 16)) return fail(KVQ_ERR_ALIGN, "q must be 16-byte aligned");
-    if (!aligned(seq_len, 4)) return fail(KVQ_ERR_ALIGN, "seq_len must be 4-byte aligned");
+    if (phases != (PHASE_PREP | PHASE_SPLIT) && !quant_modes(c))
+        return fail(KVQ_ERR_BITS, "only 8/4-bit caches have a separate query preparation");
+    if (((phases & PHASE_PREP) && !q) || ((phases & PHASE_SPLIT) && !seq_len) || !workspace)
+        return fail(KVQ_ERR_NULL, "q / seq_len / workspace is NULL");
+    if ((phases & PHASE_PREP) && !aligned(q, 16)) return fail(KVQ_ERR_ALIGN, "q must be 16-byte aligned");
+    if ((phases & PHASE_SPLIT) && !aligned(seq_len, 4)) return fail(KVQ_ERR_ALIGN, "seq_len must be 4-byte aligned");
     if (!aligned(workspace, 256)) return fail(KVQ_ERR_ALIGN, "workspace must be 256-byte aligned");
     const size_t need = cache_ws_bytes(c, n_q_heads, nc);
     if (workspace_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
@@ -479,17 +485,20 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
     int32_t *qdig = reinterpret_cast<int32_t *>(ws + wl.qdig);
     float *qsc = reinterpret_cast<float *>(ws + wl.qsc);
     const unsigned units = (unsigned)(c->batch * c->n_kv_heads);
-    if (ap && ap_grid.x > 0) {
-        if ((unsigned long long)ap_grid.x * ap_grid.y * 2 + units > 0x7FFFFFFFull)
-            return fail(KVQ_ERR_SHAPE, "batch * n_new too large for a fused step");
-        const unsigned n_app = ap_grid.x * ap_grid.y * 2;
-        hipLaunchKernelGGL(sprep, dim3(n_app + units), dim3(256), 0, st_, *ap, (int)ap_grid.x, (int)ap_grid.y, q, qdig,
-                           qsc, qk_scale);
-    } else {
-        hipLaunchKernelGGL(prep, dim3(units), dim3(256), 0, st_, q, qdig, qsc, qk_scale);
+    if (ap && ap_grid.x > 0 && (unsigned long long)ap_grid.x * ap_grid.y * 2 + units > 0x7FFFFFFFull)
+        return fail(KVQ_ERR_SHAPE, "batch * n_new too large for a fused step");
+    if (phases & PHASE_PREP) {
+        if (ap && ap_grid.x > 0) {
+            const unsigned n_app = ap_grid.x * ap_grid.y * 2;
+            hipLaunchKernelGGL(sprep, dim3(n_app + units), dim3(256), 0, st_, *ap, (int)ap_grid.x, (int)ap_grid.y, q,
+                               qdig, qsc, qk_scale);
+        } else {
+            hipLaunchKernelGGL(prep, dim3(units), dim3(256), 0, st_, q, qdig, qsc, qk_scale);
+        }
+        const int hs = hip_status("query prep launch");
+        if (hs) return hs;
     }
-    int hs = hip_status("query prep launch");
-    if (hs) return hs;
+    if (!(phases & PHASE_SPLIT)) return KVQ_OK;
 
     QuantParams p;
     p.k_codes = static_cast<const uint8_t *>(c->k_codes);
@@ -530,6 +539,20 @@ int kvq_decode_partials(const kvq_cache *c, const float *q, int n_q_heads, const
 {
     return enqueue_partials(c, q, n_q_heads, seq_len, max_seq_len, softmax_scale, chunk_tokens, workspace,
                             workspace_bytes, stream, nullptr, dim3(0, 1, 1));
+}
+
+int kvq_prepare_query(const kvq_cache *c, const float *q, int n_q_heads, int max_seq_len, float softmax_scale,
+                      int chunk_tokens, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return enqueue_partials(c, q, n_q_heads, nullptr, max_seq_len, softmax_scale, chunk_tokens, workspace,
+                            workspace_bytes, stream, nullptr, dim3(0, 1, 1), PHASE_PREP);
+}
+
+int kvq_decode_partials_prepared(const kvq_cache *c, int n_q_heads, const int32_t *seq_len, int max_seq_len,
+                                 int chunk_tokens, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return enqueue_partials(c, nullptr, n_q_heads, seq_len, max_seq_len, 0.0f, chunk_tokens, workspace,
+                            workspace_bytes, stream, nullptr, dim3(0, 1, 1), PHASE_SPLIT);
 }
 
 int kvq_combine(int batch, int n_q_heads, int head_dim, int n_chunks, const void *workspace, size_t workspace_bytes,

@@ -213,6 +213,25 @@ int kvq_decode_partials(const kvq_cache *c, const float *q, int n_q_heads, const
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The two halves of kvq_decode_partials() on an 8/4-bit cache (KVQ_ERR_BITS
+ * on a 16/32-bit one), same arguments: kvq_prepare_query() writes the
+ * query's fixed-point form (per head a scale and the integer digits the
+ * split kernel multiplies the codes with) into the workspace;
+ * kvq_decode_partials_prepared() runs the split kernel on it and writes the
+ * partials.  The prepared form stays valid until the workspace is written
+ * again, so one preparation can serve several split launches for the same
+ * query, n_q_heads, max_seq_len and chunk_tokens (e.g. to time the split
+ * kernel alone).  kvq_decode_partials() = both, in order.
+ */
+int kvq_prepare_query(const kvq_cache *c, const float *q, int n_q_heads, int max_seq_len,
+                      float softmax_scale, int chunk_tokens, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+int kvq_decode_partials_prepared(const kvq_cache *c, int n_q_heads, const int32_t *seq_len,
+                                 int max_seq_len, int chunk_tokens, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+/*
  * Merge the partials of `n_chunks` chunks for P = batch * n_q_heads rows
  * (layout as above) into out[P][head_dim]:
  *   M = max_i m_i,  out = sum_i acc_i * 2^(m_i - M) / sum_i l_i * 2^(m_i - M),

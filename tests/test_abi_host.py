@@ -178,6 +178,29 @@ def test_decode_step_argument_errors(kvq):
         assert e.value.status == code, over
 
 
+def test_prepared_halves_argument_errors(kvq):
+    d = _desc(kvq)
+    ws = kvq.kvq_workspace_bytes(d, 8, 100, 0)
+    ok = 0x40000
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_prepare_query(d, None, 8, 100, 0.0, 0, ok, ws, 0)
+    assert e.value.status == -1
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_decode_partials_prepared(d, 8, None, 100, 0, ok, ws, 0)
+    assert e.value.status == -1
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_decode_partials_prepared(d, 8, ok, 100, 0, ok, ws - 1, 0)
+    assert e.value.status == -6
+    # 16/32-bit caches have no separate query preparation
+    f = _desc(kvq, k_bits=16, v_bits=16)
+    wf = kvq.kvq_workspace_bytes(f, 8, 100, 0)
+    for call in (lambda: kvq.kvq_prepare_query(f, ok, 8, 100, 0.0, 0, ok, wf, 0),
+                 lambda: kvq.kvq_decode_partials_prepared(f, 8, ok, 100, 0, ok, wf, 0)):
+        with pytest.raises(kvq.KvqError) as e:
+            call()
+        assert e.value.status == -2
+
+
 def test_read_probe_argument_errors(kvq):
     ok = 0x40000
     for args, code in [((None, 32768, ok, 64), -1), ((ok, 32768, None, 64), -1), ((ok + 8, 32768, ok, 64), -7),

@@ -343,3 +343,26 @@ def test_read_probe_runs():
     assert torch.all(sink == 0)
     with pytest.raises(kvq.KvqError):
         kvq.kvq_read_probe(buf, 1000, sink, sink.numel() * 4)
+
+
+@pytest.mark.parametrize("kb,vb", [(4, 4), (8, 4), (8, 8), (4, 8)])
+def test_prepared_halves_match_partials(oq, kb, vb):
+    """kvq_prepare_query + kvq_decode_partials_prepared (run twice on one
+    preparation) write the same partials, bit for bit, as
+    kvq_decode_partials."""
+    kvq = need_gpu()
+    import torch
+    from workloads.device import positions, to_device
+    B, H, G, HD, n = 2, 2, 4, 128, 900
+    cache = kvq.alloc_cache(B, H, HD, n, kb, vb, HD)
+    K, V, q = _data(B, H, n, HD, H * G, 41)
+    kvq.kvq_append(cache, to_device(K), to_device(V), n, positions([0] * B))
+    qd, lens = to_device(q), positions([n, n - 301])
+    ws_bytes = kvq.kvq_workspace_bytes(cache, H * G, n, 0)
+    ws = [torch.full((ws_bytes // 4 + 64,), 3.0, dtype=torch.float32, device="cuda") for _ in range(2)]
+    kvq.kvq_decode_partials(cache, qd, H * G, lens, n, 0.0, 0, ws[0], ws_bytes)
+    kvq.kvq_prepare_query(cache, qd, H * G, n, 0.0, 0, ws[1], ws_bytes)
+    for _ in range(2):
+        kvq.kvq_decode_partials_prepared(cache, H * G, lens, n, 0, ws[1], ws_bytes)
+    torch.cuda.synchronize()
+    assert torch.equal(ws[0], ws[1])
