@@ -365,4 +365,5 @@ def test_prepared_halves_match_partials(oq, kb, vb):
     for _ in range(2):
         kvq.kvq_decode_partials_prepared(cache, H * G, lens, n, 0, ws[1], ws_bytes)
     torch.cuda.synchronize()
-    assert torch.equal(ws[0], ws[1])
+    # (raw words: the workspace also holds the query's integer digits)
+    assert torch.equal(ws[0].view(torch.int32), ws[1].view(torch.int32))
