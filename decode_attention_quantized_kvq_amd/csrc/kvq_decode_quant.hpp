@@ -26,9 +26,10 @@
 // (|dw| <= max s_v / 65534); accumulation is exact in int32, then fp32.
 //
 // Workgroup = 4 waves = one context chunk of one (sequence, KV head); each
-// wave owns a quarter of the chunk and streams it in sub-chunks of 256
-// positions, the key tiles and the value groups loaded ahead without a break
-// between sub-chunks.  Per sub-chunk:
+// wave owns a quarter of the chunk and streams it in sub-chunks of 512
+// positions (fewer with many heads or scale groups), the key tiles and the
+// value groups loaded ahead without a break between sub-chunks.  Per
+// sub-chunk:
 //   1. keys, one lane per position: scores -> LDS; the query digits are
 //      wave-uniform and come from SGPRs (prepared per (sequence, KV head) by
 //      qprep_kernel); value scales -> LDS; the sub-chunk's maxima (DPP).
@@ -51,9 +52,10 @@ namespace kvq {
 
 constexpr int QD_THREADS = 256;
 constexpr int QD_WAVES = QD_THREADS / 64;
-// positions per wave sub-chunk: 256, or 128 when many heads and scale
-// groups make the per-position LDS large
-__host__ __device__ constexpr int qd_sub(int G, int vg) { return G * vg >= 16 ? 128 : 256; }
+// positions per wave sub-chunk: 512, or 256 / 128 when many heads and scale
+// groups make the per-position LDS large.  (A sub-chunk's value sums stay
+// exact in uint32: at most 512 * 32767 * 255 < 2^32.)
+__host__ __device__ constexpr int qd_sub(int G, int vg) { return G * vg >= 16 ? 128 : G * vg >= 8 ? 256 : 512; }
 constexpr int Q_RANGE = 30000;
 constexpr int QD_PF = 16;       // value group loads in flight per lane
 constexpr int W_RANGE = 32767;
@@ -102,7 +104,7 @@ struct QuantSmem {
     bool wd_alias;             // weight words overwrite each wave's own scores
 };
 
-// Per wave: scores [S][G], value scales [S][vg], weight words
+// Per wave: scores [S][G] fp32, value scales [S][vg] fp16 bits, weight words
 // [vg][S/4][G][lo, hi] (over the scores when vg == 1); then the
 // cross-wave merge area (over the scores when it fits) and the wave maxima
 // and sums.
@@ -114,7 +116,7 @@ __host__ __device__ inline QuantSmem quant_smem(int G, int HD, int vg)
     s.zs = off;
     off += QD_WAVES * S * G * 4;
     s.vs = off;
-    off += QD_WAVES * S * vg * 4;
+    off += QD_WAVES * S * vg * 2;
     s.wd_alias = vg == 1;
     if (s.wd_alias) {
         s.wd = s.zs;
@@ -275,7 +277,7 @@ void decode_quant_kernel(QuantParams p)
 
     const QuantSmem lay = quant_smem(G, HD, KG);
     float *zs = reinterpret_cast<float *>(smem + lay.zs) + wave * S * G;       // this wave's scores
-    float *vsl = reinterpret_cast<float *>(smem + lay.vs) + wave * S * KG;    // and value scales
+    uint16_t *vsl = reinterpret_cast<uint16_t *>(smem + lay.vs) + wave * S * KG;   // and value scales
     uint32_t *wdw = lay.wd_alias ? reinterpret_cast<uint32_t *>(zs)
                                  : reinterpret_cast<uint32_t *>(smem + lay.wd) + wave * KG * (S / 4) * G * 2;
     float *red = reinterpret_cast<float *>(smem + lay.red);
@@ -323,7 +325,9 @@ void decode_quant_kernel(QuantParams p)
             d.vs[g] = bld_u16(vsrs, vso + 2 * g);
         }
     };
-    float mloc[G], vmloc[KG];                        // per-lane maxima of the current sub-chunk
+    float mloc[G];                                   // per-lane maxima of the current sub-chunk:
+    uint32_t vmloc[KG];                              // scores; value scales as fp16 bits (>= 0, so
+                                                     // the largest bits are the largest value)
     // scores of one tile (tb: first position of the tile within the wave;
     // sc0: first position of the sub-chunk)
     auto compute = [&](int tb, int sc0, const Tile &c) {
@@ -332,9 +336,8 @@ void decode_quant_kernel(QuantParams p)
 #pragma unroll
         for (int g = 0; g < KG; g++) {
             // (zero past the wave's range: the load returned zero)
-            const float sv = f16_bits_to_f32((uint16_t)c.vs[g]);
-            if (valid) vsl[(t - sc0) * KG + g] = sv;
-            vmloc[g] = fmax_nc(vmloc[g], sv);
+            if (valid) vsl[(t - sc0) * KG + g] = (uint16_t)c.vs[g];
+            vmloc[g] = max(vmloc[g], c.vs[g]);
         }
         // an opaque zero offset, redefined every tile, keeps the digit loads
         // inside the loop (hoisted, they would need hundreds of SGPRs)
@@ -500,7 +503,7 @@ void decode_quant_kernel(QuantParams p)
 #pragma unroll
         for (int h = 0; h < G; h++) mloc[h] = -INFINITY;
 #pragma unroll
-        for (int g = 0; g < KG; g++) vmloc[g] = 0.0f;
+        for (int g = 0; g < KG; g++) vmloc[g] = 0u;
         // (tiles run in pairs, both halves unconditionally: a half past the
         // end sees only invalid lanes and zero rows, and the code stays free
         // of a merge point that would send the two register sets through
@@ -526,7 +529,7 @@ void decode_quant_kernel(QuantParams p)
 #pragma unroll
         for (int h = 0; h < G; h++) ms[h] = wave_max_u(mloc[h]);
 #pragma unroll
-        for (int g = 0; g < KG; g++) vms[g] = wave_max_u(vmloc[g]);
+        for (int g = 0; g < KG; g++) vms[g] = f16_bits_to_f32((uint16_t)wave_max_ui((int)vmloc[g]));
 
         // ---------------- pass 2: weights, one lane per 4 positions ---------------
         // p = 2^(qs * (z - ms)) <= 1; w_int = rint(p * s_v * 32767 / vms),
@@ -549,7 +552,12 @@ void decode_quant_kernel(QuantParams p)
             float fsc[KG];
 #pragma unroll
             for (int g = 0; g < KG; g++) fsc[g] = vms[g] > 0.0f ? (float)W_RANGE * __builtin_amdgcn_rcpf(vms[g]) : 0.0f;
-            const int grp = lane;                    // S / 4 <= 64 groups, one per lane
+            // S / 4 groups of 4 positions, one per lane and turn (the weight
+            // words go over the scores: a turn writes only rows it or an
+            // earlier turn has read)
+#pragma unroll
+            for (int gq = 0; gq < S / 4; gq += 64) {
+            const int grp = gq + lane;
             const int tq = 4 * grp;                  // first position of the group (within the sub-chunk)
             if (tq < ns) {
                 float pr[4][G];
@@ -580,7 +588,8 @@ void decode_quant_kernel(QuantParams p)
                 for (int g = 0; g < KG; g++) {
                     float sv[4];
 #pragma unroll
-                    for (int k = 0; k < 4; k++) sv[k] = tq + k < ns ? vsl[(tq + k) * KG + g] * fsc[g] : 0.0f;
+                    for (int k = 0; k < 4; k++)
+                        sv[k] = tq + k < ns ? f16_bits_to_f32(vsl[(tq + k) * KG + g]) * fsc[g] : 0.0f;
                     uint32_t *dst = wdw + ((size_t)g * (S / 4) + grp) * G * 2;
 #pragma unroll
                     for (int h = 0; h < G; h++) {
@@ -595,6 +604,7 @@ void decode_quant_kernel(QuantParams p)
                         dst[2 * h + 1] = hi;
                     }
                 }
+            }
             }
         }
 
@@ -650,8 +660,8 @@ void decode_quant_kernel(QuantParams p)
                     cg[g] = fn * vms[g] * (1.0f / (float)W_RANGE);
                     bsum[g][h] = fmaf(bsum[g][h], fo, (float)wsl[g][h] * cg[g]);
                 }
-                // 256 * hi + lo is exact in uint32 (hi bytes <= 127, at most 64
-                // groups a sub-chunk)
+                // 256 * hi + lo is exact in uint32 (hi bytes <= 127, at most
+                // 128 groups a sub-chunk: <= 512 * 32767 * 255 < 2^32)
                 uint32_t vi[T::V_ACC];
 #pragma unroll
                 for (int c = 0; c < T::V_ACC; c++) vi[c] = (acch[h][c] << 8) + accl[h][c];
