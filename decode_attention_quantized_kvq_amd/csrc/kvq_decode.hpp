@@ -249,7 +249,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_float_kernel(FloatParams p
 #pragma unroll
             for (int u = 0; u < UA; u++) {
                 const int t = base + u * TPP + tr;
-                raw[u] = t < n_tok ? ld_u4(kbase + (size_t)t * K_ROW) : make_uint4(0, 0, 0, 0);
+                raw[u] = t < n_tok ? ld_u4_nt(kbase + (size_t)t * K_ROW) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int u = 0; u < UA; u++) {
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_float_kernel(FloatParams p
 #pragma unroll
             for (int u = 0; u < UC; u++) {
                 const int t = base + u * TPP + tr;
-                raw[u] = t < n_tok ? ld_u4(vbase + (size_t)t * V_ROW) : make_uint4(0, 0, 0, 0);
+                raw[u] = t < n_tok ? ld_u4_nt(vbase + (size_t)t * V_ROW) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int u = 0; u < UC; u++) {

@@ -60,6 +60,12 @@ __device__ __forceinline__ uint4 ld_u4(const void *p)
     const u32x4_t v = *(const KVQ_GLOBAL u32x4_t *)p;
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+// the same load, nontemporal (data streamed once)
+__device__ __forceinline__ uint4 ld_u4_nt(const void *p)
+{
+    const u32x4_t v = __builtin_nontemporal_load((const KVQ_GLOBAL u32x4_t *)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ uint2 ld_u2(const void *p)
 {
     const u32x2_t v = *(const KVQ_GLOBAL u32x2_t *)p;
