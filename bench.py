@@ -451,6 +451,8 @@ def main() -> int:
         extra.append(run_mode(wl.K8V4_32K, wl.K8V4, args.steps, args.warmup, args.chunk, log=log))
     if args.modes == "all":
         extra.append(run_mode(wl.K4V4_32K, wl.FP16, args.steps, args.warmup, args.chunk, log=log))
+        extra.append(run_mode(wl.K4V4_32K, wl.K4V4_G32, args.steps, args.warmup, args.chunk, log=log))
+        extra.append(run_mode(wl.K4V4_32K, wl.K4V8, args.steps, args.warmup, args.chunk, log=log))
         extra.append(run_mode(wl.K4V4_WINDOW, wl.K4V4, args.steps, args.warmup, args.chunk, flush=True, log=log))
         for m in wl.K8V4_8K.modes:
             extra.append(run_mode(wl.K8V4_8K, m, args.steps, args.warmup, args.chunk, flush=True, log=log))

@@ -53,6 +53,7 @@ K8V4 = Mode("k8v4", 8, 4)
 K4V4 = Mode("k4v4", 4, 4)
 K4V8 = Mode("k4v8", 4, 8)
 K8V8_ROW = Mode("k8v8-row", 8, 8, -1)
+K4V4_G32 = Mode("k4v4-g32", 4, 4, 32)      # one scale per 32 codes (KVSplit's footprint ratios)
 
 
 @dataclass(frozen=True)
