@@ -60,6 +60,9 @@ class kvq_cache(ctypes.Structure):
         ("v_codes", ctypes.c_void_p),
         ("k_scales", ctypes.c_void_p),
         ("v_scales", ctypes.c_void_p),
+        ("page_size", ctypes.c_int32),
+        ("n_pages", ctypes.c_int32),
+        ("block_table", ctypes.c_void_p),
     ]
 
 
@@ -233,9 +236,13 @@ class Cache:
         return self.desc.batch
 
     def sequence(self, b: int) -> "Cache":
-        """Descriptor of sequence b alone (batch 1), sharing the buffers."""
+        """Descriptor of sequence b alone (batch 1), sharing the buffers.  A
+        paged cache keeps its pools and points at row b of the block table."""
         d = kvq_cache.from_buffer_copy(self.desc)
         d.batch = 1
+        if d.page_size:
+            d.block_table = self.desc.block_table + 4 * b * (d.capacity // d.page_size)
+            return Cache(d, self.k_codes, self.v_codes, self.k_scales, self.v_scales, keep=[self])
         per_seq = lambda t: None if t is None else t.view(self.desc.batch, -1)[b]
         kc, vc, ks, vs = (per_seq(t) for t in (self.k_codes, self.v_codes, self.k_scales, self.v_scales))
         d.k_codes, d.v_codes = kc.data_ptr(), vc.data_ptr()
@@ -245,13 +252,25 @@ class Cache:
 
 
 def alloc_cache(batch: int, n_kv_heads: int, head_dim: int, capacity: int, k_bits: int, v_bits: int,
-                group_size: int = 0, n_anchor: int = 0, window: int = 0, device="cuda") -> Cache:
+                group_size: int = 0, n_anchor: int = 0, window: int = 0, device="cuda",
+                page_size: int = 0, n_pages: int = 0, block_table=None) -> Cache:
     """Allocate the four cache buffers with torch (zero-filled) and describe them.
 
-    group_size 0 means one scale per head (group_size = head_dim)."""
+    group_size 0 means one scale per head (group_size = head_dim).  page_size > 0
+    allocates pools of n_pages pages of page_size slots instead of one region per
+    sequence; block_table is then an int32 device tensor of batch x
+    (capacity / page_size) page indices, kept alive by the returned Cache."""
     import torch
     d = kvq_cache(batch, n_kv_heads, head_dim, capacity, k_bits, v_bits, group_size or head_dim, n_anchor, window,
-                  None, None, None, None)
+                  None, None, None, None, page_size, n_pages, None)
+    keep = []
+    if page_size:
+        if block_table is None:
+            raise ValueError("a paged cache needs a block table")
+        if block_table.dtype != torch.int32 or not block_table.is_contiguous():
+            raise ValueError("block_table must be a contiguous int32 tensor")
+        d.block_table = block_table.data_ptr()
+        keep.append(block_table)
     kc, vc, ks, vs = kvq_cache_sizes(d)
     k_codes = torch.zeros(max(kc, 16), dtype=torch.uint8, device=device)
     v_codes = torch.zeros(max(vc, 16), dtype=torch.uint8, device=device)
@@ -260,7 +279,7 @@ def alloc_cache(batch: int, n_kv_heads: int, head_dim: int, capacity: int, k_bit
     d.k_codes, d.v_codes = k_codes.data_ptr(), v_codes.data_ptr()
     d.k_scales = k_scales.data_ptr() if k_scales is not None else None
     d.v_scales = v_scales.data_ptr() if v_scales is not None else None
-    return Cache(d, k_codes, v_codes, k_scales, v_scales)
+    return Cache(d, k_codes, v_codes, k_scales, v_scales, keep=keep)
 
 
 def default_scale(head_dim: int) -> float:

@@ -77,6 +77,16 @@ int check_geometry(const kvq_cache *c)
         return fail(KVQ_ERR_WINDOW, "n_anchor %d without a window", c->n_anchor);
     if (c->window > 0 && (long long)c->n_anchor + c->window != c->capacity)
         return fail(KVQ_ERR_WINDOW, "capacity %d != n_anchor %d + window %d", c->capacity, c->n_anchor, c->window);
+    if (c->page_size != 0) {
+        const int P = c->page_size;
+        if (P < 64 || P > 4096 || (P & (P - 1)) != 0)
+            return fail(KVQ_ERR_SHAPE, "page_size %d must be a power of two in [64, 4096] (or 0)", P);
+        if (c->capacity % P != 0)
+            return fail(KVQ_ERR_SHAPE, "capacity %d is not a multiple of page_size %d", c->capacity, P);
+        if (c->n_pages < 1) return fail(KVQ_ERR_SHAPE, "n_pages %d must be >= 1", c->n_pages);
+        if ((long long)c->n_pages * c->n_kv_heads * P > 0x7FFFFFFFLL)
+            return fail(KVQ_ERR_SHAPE, "n_pages * n_kv_heads * page_size exceeds 2^31 - 1 slots");
+    }
     return KVQ_OK;
 }
 
@@ -89,6 +99,10 @@ int check_pointers(const kvq_cache *c)
     if (quantized(c->v_bits) && !c->v_scales) return fail(KVQ_ERR_NULL, "v_scales is NULL for a quantized value side");
     if ((c->k_scales && !aligned(c->k_scales, 2)) || (c->v_scales && !aligned(c->v_scales, 2)))
         return fail(KVQ_ERR_ALIGN, "scale buffers must be 2-byte aligned");
+    if (c->page_size != 0) {
+        if (!c->block_table) return fail(KVQ_ERR_NULL, "block_table is NULL for paged storage");
+        if (!aligned(c->block_table, 4)) return fail(KVQ_ERR_ALIGN, "block_table must be 4-byte aligned");
+    }
     return KVQ_OK;
 }
 
@@ -106,8 +120,18 @@ int check_heads(const kvq_cache *c, int n_q_heads)
 
 bool quant_modes(const kvq_cache *c) { return quantized(c->k_bits); }   // both sides quantized (bits_pair_ok)
 
-int cap4_of(const kvq_cache *c) { return (c->capacity + 3) & ~3; }
-int cap64_of(const kvq_cache *c) { return (c->capacity + 63) & ~63; }
+// storage units (sequences, or pages) and the slots each holds
+bool paged(const kvq_cache *c) { return c->page_size != 0; }
+int units_of(const kvq_cache *c) { return paged(c) ? c->n_pages : c->batch; }
+int cap_u(const kvq_cache *c) { return paged(c) ? c->page_size : c->capacity; }
+int cap4_of(const kvq_cache *c) { return (cap_u(c) + 3) & ~3; }
+int cap64_of(const kvq_cache *c) { return (cap_u(c) + 63) & ~63; }
+int log2i(int x)
+{
+    int r = 0;
+    while ((1 << r) < x) r++;
+    return r;
+}
 
 size_t lds_bytes(const kvq_cache *c, int G, int chunk)
 {
@@ -143,57 +167,70 @@ using FloatFn = void (*)(FloatParams);
 using QuantFn = void (*)(QuantParams);
 using PrepFn = void (*)(const float *, int32_t *, float *, float);
 
-template <int B, int HD>
+template <int B, int HD, bool PG>
 FloatFn pick_float_g(int G)
 {
     switch (G) {
-    case 1: return decode_float_kernel<B, B, HD, 1, 4, 4>;
-    case 2: return decode_float_kernel<B, B, HD, 2, 4, 4>;
-    case 4: return decode_float_kernel<B, B, HD, 4, 4, 4>;
-    case 8: return decode_float_kernel<B, B, HD, 8, 4, 4>;
+    case 1: return decode_float_kernel<B, B, HD, 1, 4, 4, PG>;
+    case 2: return decode_float_kernel<B, B, HD, 2, 4, 4, PG>;
+    case 4: return decode_float_kernel<B, B, HD, 4, 4, 4, PG>;
+    case 8: return decode_float_kernel<B, B, HD, 8, 4, 4, PG>;
     }
     return nullptr;
 }
 
-FloatFn pick_float(int bits, int hd, int G)
+template <bool PG>
+FloatFn pick_float_p(int bits, int hd, int G)
 {
-    if (bits == 32) return hd == 64 ? pick_float_g<32, 64>(G) : pick_float_g<32, 128>(G);
-    return hd == 64 ? pick_float_g<16, 64>(G) : pick_float_g<16, 128>(G);
+    if (bits == 32) return hd == 64 ? pick_float_g<32, 64, PG>(G) : pick_float_g<32, 128, PG>(G);
+    return hd == 64 ? pick_float_g<16, 64, PG>(G) : pick_float_g<16, 128, PG>(G);
 }
 
-template <int KB, int VB, int HD, int KG>
+FloatFn pick_float(int bits, int hd, int G, bool pg)
+{
+    return pg ? pick_float_p<true>(bits, hd, G) : pick_float_p<false>(bits, hd, G);
+}
+
+template <int KB, int VB, int HD, int KG, bool PG>
 QuantFn pick_quant_g(int G)
 {
     switch (G) {
-    case 1: return decode_quant_kernel<KB, VB, HD, 1, KG>;
-    case 2: return decode_quant_kernel<KB, VB, HD, 2, KG>;
-    case 4: return decode_quant_kernel<KB, VB, HD, 4, KG>;
-    case 8: return decode_quant_kernel<KB, VB, HD, 8, KG>;
+    case 1: return decode_quant_kernel<KB, VB, HD, 1, KG, PG>;
+    case 2: return decode_quant_kernel<KB, VB, HD, 2, KG, PG>;
+    case 4: return decode_quant_kernel<KB, VB, HD, 4, KG, PG>;
+    case 8: return decode_quant_kernel<KB, VB, HD, 8, KG, PG>;
     }
     return nullptr;
 }
 
-template <int KB, int VB>
+template <int KB, int VB, bool PG>
 QuantFn pick_quant_hd(int hd, int G, int kg)
 {
-    if (hd == 64) return kg == 2 ? pick_quant_g<KB, VB, 64, 2>(G) : kg == 1 ? pick_quant_g<KB, VB, 64, 1>(G) : nullptr;
+    if (hd == 64)
+        return kg == 2 ? pick_quant_g<KB, VB, 64, 2, PG>(G) : kg == 1 ? pick_quant_g<KB, VB, 64, 1, PG>(G) : nullptr;
     switch (kg) {
-    case 1: return pick_quant_g<KB, VB, 128, 1>(G);
-    case 2: return pick_quant_g<KB, VB, 128, 2>(G);
-    case 4: return pick_quant_g<KB, VB, 128, 4>(G);
+    case 1: return pick_quant_g<KB, VB, 128, 1, PG>(G);
+    case 2: return pick_quant_g<KB, VB, 128, 2, PG>(G);
+    case 4: return pick_quant_g<KB, VB, 128, 4, PG>(G);
     }
+    return nullptr;
+}
+
+template <bool PG>
+QuantFn pick_quant_p(int kb, int vb, int hd, int G, int kg)
+{
+    if (kb == 8 && vb == 8) return pick_quant_hd<8, 8, PG>(hd, G, kg);
+    if (kb == 8 && vb == 4) return pick_quant_hd<8, 4, PG>(hd, G, kg);
+    if (kb == 4 && vb == 4) return pick_quant_hd<4, 4, PG>(hd, G, kg);
+    if (kb == 4 && vb == 8) return pick_quant_hd<4, 8, PG>(hd, G, kg);
     return nullptr;
 }
 
 // kg: scale groups per head row (head_dim / group_size; 1 for one scale per
-// position shared by all heads)
-QuantFn pick_quant(int kb, int vb, int hd, int G, int kg)
+// position shared by all heads); pg: paged storage
+QuantFn pick_quant(int kb, int vb, int hd, int G, int kg, bool pg)
 {
-    if (kb == 8 && vb == 8) return pick_quant_hd<8, 8>(hd, G, kg);
-    if (kb == 8 && vb == 4) return pick_quant_hd<8, 4>(hd, G, kg);
-    if (kb == 4 && vb == 4) return pick_quant_hd<4, 4>(hd, G, kg);
-    if (kb == 4 && vb == 8) return pick_quant_hd<4, 8>(hd, G, kg);
-    return nullptr;
+    return pg ? pick_quant_p<true>(kb, vb, hd, G, kg) : pick_quant_p<false>(kb, vb, hd, G, kg);
 }
 
 template <int KB, int HD>
@@ -300,14 +337,15 @@ int kvq_cache_sizes(const kvq_cache *c, size_t *kc, size_t *vc, size_t *ksb, siz
 {
     int st = check_geometry(c);
     if (st) return st;
-    const size_t rows = (size_t)c->batch * c->n_kv_heads * c->capacity;
-    const size_t sc = per_row(c) ? (size_t)c->batch * c->capacity : rows * groups_per_head(c);
+    const size_t U = (size_t)units_of(c);
+    const size_t rows = U * c->n_kv_heads * cap_u(c);
+    const size_t sc = per_row(c) ? U * cap_u(c) : rows * groups_per_head(c);
     if (kc) {
-        const size_t krows = quantized(c->k_bits) ? (size_t)c->batch * c->n_kv_heads * cap64_of(c) : rows;
+        const size_t krows = quantized(c->k_bits) ? U * c->n_kv_heads * cap64_of(c) : rows;
         *kc = krows * c->head_dim * c->k_bits / 8;
     }
     if (vc) {
-        const size_t vrows = quantized(c->v_bits) ? (size_t)c->batch * c->n_kv_heads * cap4_of(c) : rows;
+        const size_t vrows = quantized(c->v_bits) ? U * c->n_kv_heads * cap4_of(c) : rows;
         *vc = vrows * c->head_dim * c->v_bits / 8;
     }
     if (ksb) *ksb = quantized(c->k_bits) ? sc * 2 : 0;
@@ -348,6 +386,11 @@ static int prepare_append(const kvq_cache *c, const float *k_new, const float *v
     p->capacity = c->capacity;
     p->cap4 = cap4_of(c);
     p->cap64 = cap64_of(c);
+    p->cap_u = cap_u(c);
+    p->page_shift = paged(c) ? log2i(c->page_size) : 0;
+    p->pages_per_seq = paged(c) ? c->capacity / c->page_size : 0;
+    p->n_pages = c->n_pages;
+    p->block_table = c->block_table;
     p->n_new = n_new;
     p->n_anchor = c->n_anchor;
     p->window = c->window;
@@ -454,7 +497,7 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
     const size_t lds = lds_bytes(c, G, ch);
 
     if (!quant_modes(c)) {
-        FloatFn fn = pick_float(c->k_bits, c->head_dim, G);
+        FloatFn fn = pick_float(c->k_bits, c->head_dim, G, paged(c));
         if (!fn) return fail(KVQ_ERR_BITS, "no kernel for k_bits=%d", c->k_bits);
         FloatParams p;
         p.k_codes = static_cast<const uint8_t *>(c->k_codes);
@@ -464,8 +507,12 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
         p.ws_ml = reinterpret_cast<float *>(ws + wl.ml);
         p.ws_acc = reinterpret_cast<float *>(ws + wl.acc);
         p.n_kv_heads = c->n_kv_heads;
-        p.capacity = c->capacity;
+        p.capacity = cap_u(c);
         p.max_len = max_len_of(c, max_seq_len);
+        p.block_table = c->block_table;
+        p.page_shift = paged(c) ? log2i(c->page_size) : 0;
+        p.pages_per_seq = paged(c) ? c->capacity / c->page_size : 0;
+        p.n_pages = c->n_pages;
         p.chunk = ch;
         p.n_chunks = nc;
         p.qk_scale = qk_scale;
@@ -478,7 +525,7 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
         return hip_status("decode_float_kernel launch");
     }
 
-    QuantFn fn = pick_quant(c->k_bits, c->v_bits, c->head_dim, G, groups_per_head(c));
+    QuantFn fn = pick_quant(c->k_bits, c->v_bits, c->head_dim, G, groups_per_head(c), paged(c));
     PrepFn prep = pick_prep(c->k_bits, c->head_dim, G);
     StepPrepFn sprep = pick_step(c->k_bits, c->head_dim, G);
     if (!fn || !prep || !sprep) return fail(KVQ_ERR_BITS, "no kernel for k_bits=%d v_bits=%d", c->k_bits, c->v_bits);
@@ -511,21 +558,25 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
     p.ws_ml = reinterpret_cast<float *>(ws + wl.ml);
     p.ws_acc = reinterpret_cast<float *>(ws + wl.acc);
     p.n_kv_heads = c->n_kv_heads;
-    p.capacity = c->capacity;
+    p.capacity = cap_u(c);
     p.cap4 = cap4_of(c);
     p.cap64 = cap64_of(c);
+    p.block_table = c->block_table;
+    p.page_shift = paged(c) ? log2i(c->page_size) : 0;
+    p.pages_per_seq = paged(c) ? c->capacity / c->page_size : 0;
+    p.n_pages = c->n_pages;
     p.max_len = max_len_of(c, max_seq_len);
     p.chunk = ch;
     p.n_chunks = nc;
     const bool pr = per_row(c);
     const int gph = groups_per_head(c);
-    if (pr) {
-        p.k_sc_b = p.v_sc_b = c->capacity;
+    if (pr) {                                        // strides per storage unit (sequence or page)
+        p.k_sc_b = p.v_sc_b = cap_u(c);
         p.k_sc_h = p.v_sc_h = 0;
         p.k_sc_t = p.v_sc_t = 1;
     } else {
-        p.k_sc_b = p.v_sc_b = (long long)c->n_kv_heads * c->capacity * gph;
-        p.k_sc_h = p.v_sc_h = (long long)c->capacity * gph;
+        p.k_sc_b = p.v_sc_b = (long long)c->n_kv_heads * cap_u(c) * gph;
+        p.k_sc_h = p.v_sc_h = (long long)cap_u(c) * gph;
         p.k_sc_t = p.v_sc_t = gph;
     }
     hipLaunchKernelGGL(fn, grid, dim3(QD_THREADS), lds, st_, p);

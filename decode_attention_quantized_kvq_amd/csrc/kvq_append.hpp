@@ -27,6 +27,10 @@ struct AppendParams {
     int bits[2];
     const int32_t *start_pos; // [batch]
     int n_kv_heads, head_dim, capacity, cap4, cap64, n_new, n_anchor, window;
+    // storage: cap_u slots per storage unit (a sequence, or a page of
+    // 1 << page_shift slots when page_shift > 0, found through block_table)
+    int cap_u, page_shift, pages_per_seq, n_pages;
+    const int32_t *block_table;
     int group;                // elements per scale
     int per_row;              // 1: one scale per position over all heads
 };
@@ -135,9 +139,17 @@ __device__ __forceinline__ void append_block(const AppendParams &p, int bx, int 
     const int b = r / p.n_new;
     const int i = r - b * p.n_new;
     const int start = p.start_pos[b];
-    const int slot = append_slot(p, start, start + i);
-    if (slot < 0)
+    const int lslot = append_slot(p, start, start + i);
+    if (lslot < 0)
         return;                                        // uniform over the block
+    // storage unit (sequence or page) and slot inside it
+    int ub = b, slot = lslot;
+    if (p.page_shift > 0) {
+        ub = p.block_table[(size_t)b * p.pages_per_seq + (lslot >> p.page_shift)];
+        if (ub < 0 || ub >= p.n_pages)
+            return;                                    // no page: not stored
+        slot = lslot & ((1 << p.page_shift) - 1);
+    }
 
     const int bits = p.bits[side];
     const int HD = p.head_dim;
@@ -171,14 +183,14 @@ __device__ __forceinline__ void append_block(const AppendParams &p, int bx, int 
         const uint16_t sh = scale_bits_from_amax(amax, qmax);
         const float s = f16_bits_to_f32(sh);
         if (tid == 0)
-            scales[(size_t)b * p.capacity + slot] = sh;
+            scales[(size_t)ub * p.cap_u + slot] = sh;
         for (int e0 = tid * APPEND_ELEMS; e0 < R; e0 += APPEND_SPAN) {
             const int h = e0 / HD, c0 = e0 - h * HD;
             float x[8];
             load8(src + (((size_t)(b * p.n_kv_heads + h) * p.n_new + i) * HD + c0), x);
             uint32_t w0, w1;
             encode8(x, s, qmax, bits, w0, w1);
-            store_codes(codes, (size_t)(b * p.n_kv_heads + h), p.cap4, p.cap64, slot, HD * bits / 8, c0, bits,
+            store_codes(codes, (size_t)ub * p.n_kv_heads + h, p.cap4, p.cap64, slot, HD * bits / 8, c0, bits,
                         side == 1, w0, w1);
         }
         return;
@@ -194,7 +206,7 @@ __device__ __forceinline__ void append_block(const AppendParams &p, int bx, int 
     else
 #pragma unroll
         for (int j = 0; j < 8; j++) x[j] = 0.0f;
-    const size_t row = (size_t)(b * p.n_kv_heads + h) * p.capacity + slot;
+    const size_t row = ((size_t)ub * p.n_kv_heads + h) * p.cap_u + slot;
 
     if (bits == 32) {
         if (active) {
@@ -229,7 +241,7 @@ __device__ __forceinline__ void append_block(const AppendParams &p, int bx, int 
     encode8(x, s, qmax, bits, w0, w1);
     if (!active)
         return;
-    store_codes(codes, (size_t)(b * p.n_kv_heads + h), p.cap4, p.cap64, slot, HD * bits / 8, c0, bits, side == 1,
+    store_codes(codes, (size_t)ub * p.n_kv_heads + h, p.cap4, p.cap64, slot, HD * bits / 8, c0, bits, side == 1,
                 w0, w1);
     if (c0 % p.group == 0)
         scales[row * (size_t)(HD / p.group) + c0 / p.group] = sh;

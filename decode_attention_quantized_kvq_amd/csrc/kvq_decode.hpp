@@ -33,16 +33,22 @@ struct FloatParams {
     const int32_t *seq_len;    // [batch]
     float *ws_ml;              // [batch*n_q_heads][n_chunks][2]
     float *ws_acc;             // [batch*n_q_heads][n_chunks][head_dim]
-    int n_kv_heads, capacity;
-    int max_len;               // min(max_seq_len, capacity)
+    int n_kv_heads, capacity;  // capacity: slots per storage unit (a sequence, or a page)
+    int max_len;               // min(max_seq_len, logical capacity)
     int chunk, n_chunks;
     float qk_scale;            // softmax_scale * log2(e)
+    // paged storage: slot s of sequence b in page block_table[b * pages_per_seq
+    // + (s >> page_shift)] (paged kernels only)
+    const int32_t *block_table;
+    int page_shift, pages_per_seq, n_pages;
 };
 
 // LDS layout (byte offsets), shared by the host (launch size) and the kernel.
 struct FloatSmem {
-    int zs, red, misc, total;
+    int zs, red, misc, pages, total;
 };
+
+constexpr int FLOAT_MAX_PAGES = 132;             // pages a chunk can touch (<= 8192 / 64 + 1)
 
 __host__ __device__ inline FloatSmem float_smem(int G, int HD, int chunk)
 {
@@ -54,6 +60,8 @@ __host__ __device__ inline FloatSmem float_smem(int G, int HD, int chunk)
     off += DEC_WAVES * G * HD * 4;               // cross-wave reduction of acc
     s.misc = off;
     off += (2 * G + 2 * DEC_WAVES * G) * 4;      // m, l, wave partials
+    s.pages = off;
+    off += FLOAT_MAX_PAGES * 4;                  // paged storage: the chunk's pages
     s.total = off;
     return s;
 }
@@ -188,7 +196,7 @@ __device__ __forceinline__ void reduce_and_store(float (&acc)[G][CPL], float *re
     }
 }
 
-template <int KB, int VB, int HD, int G, int UA, int UC>
+template <int KB, int VB, int HD, int G, int UA, int UC, bool PAGED>
 __global__ __launch_bounds__(DEC_THREADS) void decode_float_kernel(FloatParams p)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -229,6 +237,29 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_float_kernel(FloatParams p
 
     const FloatSmem lay = float_smem(G, HD, CH);
     float *zs = reinterpret_cast<float *>(smem + lay.zs);
+    // paged storage: the pages of the chunk's slots (-1: none, read as zero)
+    int *pg = reinterpret_cast<int *>(smem + lay.pages);
+    const int pg0 = PAGED ? (t0 >> p.page_shift) : 0;
+    if constexpr (PAGED) {
+        const int npg = ((t0 + n_tok - 1) >> p.page_shift) - pg0 + 1;
+        for (int i = tid; i < npg; i += DEC_THREADS) {
+            const int e = p.block_table[(size_t)b * p.pages_per_seq + pg0 + i];
+            pg[i] = (e >= 0 && e < p.n_pages) ? e : -1;
+        }
+        __syncthreads();
+    }
+    // address of slot t0 + t of this KV head's rows (nullptr: no page)
+    auto row_ptr = [&](const uint8_t *base, int t, int row_bytes) -> const uint8_t * {
+        if constexpr (PAGED) {
+            const int pos = t0 + t;
+            const int u = pg[(pos >> p.page_shift) - pg0];
+            if (u < 0) return nullptr;
+            return base + (((size_t)u * p.n_kv_heads + kvh) * p.capacity + (pos & ((1 << p.page_shift) - 1))) *
+                              (size_t)row_bytes;
+        } else {
+            return base + ((size_t)bh * p.capacity + t0 + t) * (size_t)row_bytes;
+        }
+    };
     float *red = reinterpret_cast<float *>(smem + lay.red);
     float *m_sh = reinterpret_cast<float *>(smem + lay.misc);
     float *l_sh = m_sh + G;
@@ -243,13 +274,13 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_float_kernel(FloatParams p
         const int sl = tid % LPT, tr = tid / LPT;
         KS kside;
         kside.init(qh, sl);
-        const uint8_t *kbase = p.k_codes + ((size_t)bh * p.capacity + t0) * K_ROW + sl * 16;
         for (int base = 0; base < n_tok; base += TPP * UA) {
             uint4 raw[UA];
 #pragma unroll
             for (int u = 0; u < UA; u++) {
                 const int t = base + u * TPP + tr;
-                raw[u] = t < n_tok ? ld_u4_nt(kbase + (size_t)t * K_ROW) : make_uint4(0, 0, 0, 0);
+                const uint8_t *r = t < n_tok ? row_ptr(p.k_codes, t, K_ROW) : nullptr;
+                raw[u] = r ? ld_u4_nt(r + sl * 16) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int u = 0; u < UA; u++) {
@@ -328,13 +359,13 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_float_kernel(FloatParams p
         constexpr int LPT = VS::LPT;
         constexpr int TPP = DEC_THREADS / LPT;
         const int sl = tid % LPT, tr = tid / LPT;
-        const uint8_t *vbase = p.v_codes + ((size_t)bh * p.capacity + t0) * V_ROW + sl * 16;
         for (int base = 0; base < n_tok; base += TPP * UC) {
             uint4 raw[UC];
 #pragma unroll
             for (int u = 0; u < UC; u++) {
                 const int t = base + u * TPP + tr;
-                raw[u] = t < n_tok ? ld_u4_nt(vbase + (size_t)t * V_ROW) : make_uint4(0, 0, 0, 0);
+                const uint8_t *r = t < n_tok ? row_ptr(p.v_codes, t, V_ROW) : nullptr;
+                raw[u] = r ? ld_u4_nt(r + sl * 16) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int u = 0; u < UC; u++) {

@@ -90,7 +90,11 @@ struct QuantParams {
     const int32_t *seq_len;
     float *ws_ml;
     float *ws_acc;
-    int n_kv_heads, capacity, cap4, cap64;
+    int n_kv_heads, capacity, cap4, cap64;   // capacity, cap4, cap64: per storage unit (sequence or page)
+    // paged storage: slot s of sequence b in page block_table[b * pages_per_seq
+    // + (s >> page_shift)] (paged kernels only)
+    const int32_t *block_table;
+    int page_shift, pages_per_seq, n_pages;
     int max_len;
     int chunk, n_chunks;
     long long k_sc_b, k_sc_h;
@@ -236,7 +240,7 @@ __device__ __forceinline__ void pack_w(uint32_t w0, uint32_t w1, uint32_t w2, ui
 // waves per SIMD the register allocation aims at (5 = at most 96 VGPRs)
 __host__ __device__ constexpr int qd_waves_per_eu(int G, int KG) { return G * KG <= 4 ? 5 : 3; }
 
-template <int KB, int VB, int HD, int G, int KG>
+template <int KB, int VB, int HD, int G, int KG, bool PAGED>
 __global__ __launch_bounds__(QD_THREADS)
 void decode_quant_kernel(QuantParams p)
 {
@@ -298,9 +302,32 @@ void decode_quant_kernel(QuantParams p)
     // of the wave is read whole (lanes past the range see other rows and are
     // masked); tiles past the range read zeros.  Scales past the range read
     // zeros.
-    const uint8_t *kb0 = p.k_codes + ((size_t)bh * p.cap64 + t0 + s0) * T::K_ROW;   // t0 + s0: a multiple of 64
-    const uint16_t *ks0 = p.k_scales + b * p.k_sc_b + kvh * p.k_sc_h + (size_t)(t0 + s0) * p.k_sc_t;
-    const uint16_t *vs0 = p.v_scales + b * p.v_sc_b + kvh * p.v_sc_h + (size_t)(t0 + s0) * p.v_sc_t;
+    // Storage unit (the sequence, or with paged storage the page) of the
+    // wave-relative position tw, and tw's slot inside it.  Paged: lane i holds
+    // the page of the wave's i-th logical page (a wave's range touches at most
+    // 2048 / 64 + 1 pages); -1 marks a missing page, whose slots read as zero.
+    const int w0 = t0 + s0;                          // a multiple of 64
+    int pg_lane = -1, pg_first = 0;
+    if constexpr (PAGED) {
+        pg_first = w0 >> p.page_shift;
+        const int npg = nw > 0 ? ((w0 + nw - 1) >> p.page_shift) - pg_first + 1 : 0;
+        if (lane < npg) {
+            const int e = p.block_table[(size_t)b * p.pages_per_seq + pg_first + lane];
+            pg_lane = (e >= 0 && e < p.n_pages) ? e : -1;
+        }
+    }
+    auto unit_of = [&](int tw) -> int {
+        if constexpr (PAGED) {
+            const int i = min(((w0 + tw) >> p.page_shift) - pg_first, 63);
+            return __builtin_amdgcn_readlane(pg_lane, i);
+        } else {
+            return b;
+        }
+    };
+    auto slot_of = [&](int tw) -> int {
+        if constexpr (PAGED) return (w0 + tw) & ((1 << p.page_shift) - 1);
+        else return w0 + tw;
+    };
     const KVQ_CONST int32_t *qd = (const KVQ_CONST int32_t *)(p.qdig + (size_t)bh * T::ND * T::K_COLS * G);
     const uint32_t ko = lane * 16;
     const uint32_t kso = lane * p.k_sc_t * 2, vso = lane * p.v_sc_t * 2;
@@ -309,16 +336,22 @@ void decode_quant_kernel(QuantParams p)
         uint32_t ks[KG], vs[KG];
     };
     auto load = [&](int tb, Tile &d) {
-        const uint32_t rem = (uint32_t)max(nw - tb, 0);
+        const int u = unit_of(tb);
+        const int sl = slot_of(tb);
+        const uint32_t rem = u < 0 ? 0u : (uint32_t)max(nw - tb, 0);
         const uint32_t kbytes = rem > 0 ? 64 * T::K_ROW : 0;
-        const rsrc_t krs = make_rsrc(kb0 + (size_t)tb * T::K_ROW, kbytes);
-        const rsrc_t ksrs = make_rsrc(ks0 + (size_t)tb * p.k_sc_t, rem * p.k_sc_t * 2);
-        const rsrc_t vsrs = make_rsrc(vs0 + (size_t)tb * p.v_sc_t, rem * p.v_sc_t * 2);
+        const int uu = u < 0 ? 0 : u;
+        const uint8_t *kb = p.k_codes + (((size_t)uu * p.n_kv_heads + kvh) * p.cap64 + sl) * T::K_ROW;
+        const rsrc_t krs = make_rsrc(kb, kbytes);
+        const rsrc_t ksrs = make_rsrc(p.k_scales + uu * p.k_sc_b + kvh * p.k_sc_h + (size_t)sl * p.k_sc_t,
+                                      rem * p.k_sc_t * 2);
+        const rsrc_t vsrs = make_rsrc(p.v_scales + uu * p.v_sc_b + kvh * p.v_sc_h + (size_t)sl * p.v_sc_t,
+                                      rem * p.v_sc_t * 2);
         // (immediate offsets reach 4 KiB: int8 rows use a second descriptor
         // for slices 4..7)
-        const rsrc_t krs2 = make_rsrc(kb0 + (size_t)tb * T::K_ROW + 4096, kbytes > 4096 ? kbytes - 4096 : 0);
+        const rsrc_t krs2 = make_rsrc(kb + 4096, kbytes > 4096 ? kbytes - 4096 : 0);
 #pragma unroll
-        for (int u = 0; u < T::K_U4; u++) d.k[u] = bld_u4<CP_NT>(u < 4 ? krs : krs2, ko + (u % 4) * 1024);
+        for (int u4 = 0; u4 < T::K_U4; u4++) d.k[u4] = bld_u4<CP_NT>(u4 < 4 ? krs : krs2, ko + (u4 % 4) * 1024);
 #pragma unroll
         for (int g = 0; g < KG; g++) {
             d.ks[g] = bld_u16(ksrs, kso + 2 * g);
@@ -415,27 +448,34 @@ void decode_quant_kernel(QuantParams p)
     const int gi = lane / T::V_LPG;                  // group slot of a wave load
     const int qsl = lane % T::V_LPG;                 // dword slice of the group
     constexpr uint32_t GSTEP = T::V_GPL * 4 * T::V_ROW;   // bytes per wave-wide group load
-    // group loads in flight per lane (at most one sub-chunk's groups)
-    constexpr int PF_WANT = QD_PF;
+    // group loads in flight per lane (at most one sub-chunk's groups; paged
+    // storage keeps a batch to 64 positions, so that it lies in one page)
+    constexpr int PF_WANT = PAGED && QD_PF * T::V_GPL > 16 ? 16 / T::V_GPL : QD_PF;
     constexpr int PF = PF_WANT < (S / 4) / T::V_GPL ? PF_WANT : (S / 4) / T::V_GPL;
     constexpr int NPF = PF < 4096 / (int)GSTEP ? PF : 4096 / (int)GSTEP;   // loads per descriptor (offsets < 4 KiB)
     constexpr int NR = PF / NPF;                     // descriptors per batch
     static_assert(PF % NPF == 0, "whole descriptors per batch");
     constexpr int PB = PF * T::V_GPL;                // groups per batch (divides S / 4)
     static_assert((S / 4) % PB == 0, "a sub-chunk holds whole batches");
+    static_assert(!PAGED || PB <= 16, "a paged batch lies in one 64-slot block");
     const int ngw = (nw + 3) >> 2;                   // groups of this wave
-    const uint8_t *vb0 = p.v_codes + ((size_t)bh * p.cap4 + t0 + s0) * T::V_ROW;
     const uint32_t vo = gi * 4 * T::V_ROW + qsl * T::V_DPL * 4;
     struct VRs {
         rsrc_t r[NR];
     };
-    // descriptors of the batch starting at group g0
+    // descriptors of the batch starting at group g0 (paged storage: a batch
+    // is at most 64 positions, aligned to its size within the 64-aligned
+    // range of the wave, so it lies in one page)
     auto vrsrc = [&](int g0) {
         VRs d;
+        const int u = unit_of(4 * g0);
+        const int uu = u < 0 ? 0 : u;
+        const uint8_t *vb = p.v_codes + (((size_t)uu * p.n_kv_heads + kvh) * p.cap4 + slot_of(4 * g0)) * T::V_ROW;
+        const int left = u < 0 ? 0 : (ngw - g0) * 4 * T::V_ROW;   // bytes of the wave's range from the batch on
 #pragma unroll
         for (int r = 0; r < NR; r++) {
-            const int b0 = g0 * 4 * T::V_ROW + r * NPF * (int)GSTEP;
-            d.r[r] = make_rsrc(vb0 + b0, (uint32_t)max(ngw * 4 * T::V_ROW - b0, 0));
+            const int b0 = r * NPF * (int)GSTEP;
+            d.r[r] = make_rsrc(vb + b0, (uint32_t)max(left - b0, 0));
         }
         return d;
     };

@@ -104,6 +104,19 @@ extern "C" {
  *       one scale per position: [batch][capacity]
  *     2-byte aligned.
  * kvq_cache_sizes() returns the byte size of each buffer.
+ *
+ * Paged storage (page_size != 0): the four buffers are pools of n_pages
+ * pages, each holding page_size consecutive slots of every KV head, laid out
+ * exactly as above with [batch] replaced by [n_pages] and capacity by
+ * page_size (so cap4 = cap64 = page_size).  Slot s of sequence b lives in
+ * page block_table[b * (capacity / page_size) + s / page_size], at slot
+ * s % page_size of that page.  page_size is a power of two in [64, 4096]
+ * that divides capacity; block_table is device memory, int32 [batch]
+ * [capacity / page_size], 4-byte aligned, read by the kernels.  Pages may be
+ * shared, reordered or reused between sequences as the caller manages them;
+ * an entry outside [0, n_pages) is never written (the append skips the row)
+ * and its slots read as zero codes.  page_size == 0: contiguous storage,
+ * n_pages and block_table ignored.
  */
 typedef struct kvq_cache {
     int32_t batch;
@@ -119,6 +132,9 @@ typedef struct kvq_cache {
     void *v_codes;
     void *k_scales;
     void *v_scales;
+    int32_t page_size;    /* 0 = contiguous */
+    int32_t n_pages;
+    const int32_t *block_table;
 } kvq_cache;
 
 /* ---- accounting ------------------------------------------------------ */

@@ -97,6 +97,59 @@ def test_geometry_errors(kvq, kw, code):
     assert kvq.kvq_last_error()
 
 
+def test_paged_cache_sizes(kvq):
+    """Paged storage: each buffer is a pool of n_pages pages laid out as
+    page_size-slot sequences of every KV head."""
+    d = _desc(kvq, batch=3, n_kv_heads=8, head_dim=128, capacity=1024, k_bits=4, v_bits=8, group_size=32,
+              page_size=256, n_pages=13)
+    d.block_table = 0x50000
+    kc, vc, ks, vs = kvq.kvq_cache_sizes(d)
+    rows = 13 * 8 * 256
+    assert (kc, vc, ks, vs) == (rows * 64, rows * 128, rows * 4 * 2, rows * 4 * 2)
+    d = _desc(kvq, n_kv_heads=4, head_dim=64, capacity=128, group_size=256, page_size=64, n_pages=5)
+    d.block_table = 0x50000
+    assert kvq.kvq_cache_sizes(d)[2] == 5 * 64 * 2           # one scale per slot of each page
+    d = _desc(kvq, k_bits=16, v_bits=16, capacity=4096, page_size=4096, n_pages=1)
+    d.block_table = 0x50000
+    assert kvq.kvq_cache_sizes(d) == (1 * 2 * 4096 * 256, 1 * 2 * 4096 * 256, 0, 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(page_size=100, capacity=200), -3), (dict(page_size=32, capacity=64), -3),
+    (dict(page_size=8192, capacity=8192), -3), (dict(page_size=-64), -3),
+    (dict(page_size=64, capacity=100), -3), (dict(page_size=64, capacity=128, n_pages=0), -3),
+    (dict(page_size=4096, capacity=4096, n_pages=300000), -3),
+])
+def test_paged_geometry_errors(kvq, kw, code):
+    d = _desc(kvq, **kw)
+    d.block_table = 0x50000
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_cache_sizes(d)
+    assert e.value.status == code
+    assert kvq.kvq_last_error()
+
+
+def test_paged_pointer_errors(kvq):
+    """A paged cache needs a 4-byte aligned block table; contiguous storage
+    ignores it."""
+    ok = 0x30000
+    d = _desc(kvq, capacity=128, page_size=64, n_pages=4)
+    with pytest.raises(kvq.KvqError) as e:                    # no block table
+        kvq.kvq_append(d, ok, ok, 1, ok, 0)
+    assert e.value.status == -1
+    d.block_table = 0x50002
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_append(d, ok, ok, 1, ok, 0)
+    assert e.value.status == -7
+    ws = kvq.kvq_workspace_bytes(d, 8, 128, 0)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_decode_attn(d, ok, 8, ok, 128, 0.0, 0, ok, ok, ws, 0)
+    assert e.value.status == -7
+    c = _desc(kvq)
+    c.n_pages, c.block_table = 0, None                        # page_size 0: both ignored
+    assert kvq.kvq_cache_sizes(c)[0] == 2 * 2 * 128 * 128
+
+
 def test_append_argument_errors(kvq):
     d = _desc(kvq)
     ok = 0x30000

@@ -1,0 +1,247 @@
+"""Paged storage on the GPU: a cache whose buffers are pools of pages,
+addressed through a block table, holds bit for bit what a contiguous cache
+holds once its pages are gathered in table order, and decodes to the same
+outputs bit for bit (and within tolerance of the oracle), for every kernel
+instantiation, window mode, ragged lengths, appends that cross pages, the
+fused step, and table entries that name no page."""
+import numpy as np
+import pytest
+
+from gpu_util import assert_close, group_size_of, need_gpu, softmax_default
+
+pytestmark = pytest.mark.gpu
+
+MODES = [(32, 32, 0), (16, 16, 0), (8, 8, 0), (8, 4, 0), (4, 4, 0), (4, 8, 0)]
+BUFFERS = ("k_codes", "v_codes", "k_scales", "v_scales")
+
+
+def _data(B, H, n_pos, HD, Hq, seed):
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((B, H, n_pos, HD)).astype(np.float32)
+    V = rng.standard_normal((B, H, n_pos, HD)).astype(np.float32)
+    q = rng.standard_normal((B, Hq, HD)).astype(np.float32)
+    return K, V, q
+
+
+def _table(B, pps, n_pages, seed):
+    """A random assignment of distinct pool pages to the logical pages."""
+    rng = np.random.default_rng(1000 + seed)
+    return rng.permutation(n_pages)[: B * pps].reshape(B, pps).astype(np.int32)
+
+
+def _paged(kvq, table, n_pages, B, H, HD, cap, kb, vb, gs, P, n_anchor=0, window=0):
+    from workloads.device import to_device
+    bt = to_device(np.ascontiguousarray(table, np.int32))
+    return kvq.alloc_cache(B, H, HD, cap, kb, vb, gs, n_anchor, window, page_size=P, n_pages=n_pages,
+                           block_table=bt)
+
+
+def _unit_view(cache, name):
+    """The pool `name` as [n_pages][heads][elements per page and head]
+    (heads 1 for one scale per slot over all heads)."""
+    kvq = need_gpu()
+    d = cache.desc
+    t = getattr(cache, name)
+    size = kvq.kvq_cache_sizes(d)[BUFFERS.index(name)] // t.element_size()
+    per_row = name.endswith("scales") and d.group_size == d.n_kv_heads * d.head_dim and d.n_kv_heads > 1
+    return t[:size].view(d.n_pages, 1 if per_row else d.n_kv_heads, -1)
+
+
+def _gathered(cache, table, name):
+    """Pool `name` gathered in table order: the contiguous cache's layout,
+    [batch][heads][elements per sequence and head]."""
+    import torch
+    u = _unit_view(cache, name)
+    B, pps = table.shape
+    g = u[torch.as_tensor(table.reshape(-1).astype(np.int64), device=u.device)]
+    return g.view(B, pps, u.shape[1], -1).permute(0, 2, 1, 3).reshape(B, u.shape[1], -1)
+
+
+def _contig_view(cache, name, heads):
+    kvq = need_gpu()
+    d = cache.desc
+    t = getattr(cache, name)
+    size = kvq.kvq_cache_sizes(d)[BUFFERS.index(name)] // t.element_size()
+    return t[:size].view(d.batch, heads, -1)
+
+
+def _assert_same_storage(paged, table, contig):
+    import torch
+    for name in BUFFERS:
+        if getattr(contig, name) is None:
+            assert getattr(paged, name) is None
+            continue
+        g = _gathered(paged, table, name)
+        c = _contig_view(contig, name, g.shape[1])
+        assert torch.equal(g, c), f"{name}: gathered pages differ from the contiguous cache"
+        spare = sorted(set(range(paged.desc.n_pages)) - set(table.reshape(-1).tolist()))
+        if spare:
+            u = _unit_view(paged, name)
+            assert not torch.any(u[torch.as_tensor(spare, device=u.device)]), f"{name}: a spare page was written"
+
+
+def _append_pieces(kvq, caches, K, V, pieces):
+    from workloads.device import positions, to_device
+    B, n_pos = K.shape[0], K.shape[2]
+    p0 = 0
+    for i, frac in enumerate(pieces):
+        n = n_pos - p0 if i == len(pieces) - 1 else max(1, int(round(frac * n_pos)))
+        kk, vv = to_device(K[:, :, p0:p0 + n]), to_device(V[:, :, p0:p0 + n])
+        for c in caches:
+            kvq.kvq_append(c, kk, vv, n, positions([p0] * B))
+        p0 += n
+    assert p0 == n_pos
+
+
+def run_paged(oq, kb, vb, group, B=3, H=2, G=4, HD=128, P=64, n_pos=700, pieces=(0.3, 0.002, 0.5, 1.0),
+              seq_lens=None, chunk=0, n_anchor=0, window=0, spare=5, seed=0):
+    kvq = need_gpu()
+    import torch
+    from workloads.device import decode, positions, to_device
+    Hq = H * G
+    K, V, q = _data(B, H, n_pos, HD, Hq, seed)
+    cap = n_anchor + window if window else (n_pos + P - 1) // P * P
+    assert cap % P == 0
+    pps = cap // P
+    n_pages = B * pps + spare
+    table = _table(B, pps, n_pages, seed)
+    gs = group_size_of(kb, vb, group, H, HD)
+    contig = kvq.alloc_cache(B, H, HD, cap, kb, vb, gs, n_anchor, window)
+    paged = _paged(kvq, table, n_pages, B, H, HD, cap, kb, vb, gs, P, n_anchor, window)
+    _append_pieces(kvq, [contig, paged], K, V, pieces)
+    torch.cuda.synchronize()
+    _assert_same_storage(paged, table, contig)
+
+    lens = seq_lens if seq_lens is not None else [n_pos] * B
+    qd = to_device(q)
+    outs = [decode(c, qd, Hq, positions(lens), max(max(lens), 1), 0.0, chunk) for c in (contig, paged)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]), "paged output differs from the contiguous cache's"
+    got = outs[1].cpu().numpy()
+    sc = softmax_default(HD)
+    for b in range(B):
+        L = n_pos if window else min(max(lens[b], 0), cap)
+        if L == 0:
+            assert np.all(got[b] == 0)
+            continue
+        want = oq.decode_step(kb, vb, gs, n_anchor, window, K[b][:, :L], V[b][:, :L], q[b], sc)
+        assert_close(got[b], want, f"paged P={P} kb={kb} vb={vb} HD={HD} G={G} b={b} L={L}")
+
+
+@pytest.mark.parametrize("kb,vb,group", MODES)
+@pytest.mark.parametrize("HD", [64, 128])
+@pytest.mark.parametrize("P", [64, 256])
+def test_paged_matches_contiguous(oq, kb, vb, group, HD, P):
+    run_paged(oq, kb, vb, group, HD=HD, P=P, seq_lens=[700, 333, 1], seed=kb * 10 + vb + HD + P)
+
+
+@pytest.mark.parametrize("kb,vb", [(4, 4), (8, 4), (16, 16)])
+@pytest.mark.parametrize("G", [1, 2, 8])
+def test_paged_gqa_groups(oq, kb, vb, G):
+    run_paged(oq, kb, vb, 0, B=2, H=2, G=G, HD=128, P=128, n_pos=901, seed=G + kb)
+
+
+@pytest.mark.parametrize("chunk", [256, 512, 2048])
+def test_paged_chunks(oq, chunk):
+    """Chunks smaller, equal and larger than the page; the wave ranges start
+    inside pages and span several."""
+    run_paged(oq, 4, 4, 0, B=2, H=2, G=4, HD=128, P=512, n_pos=3001, chunk=chunk, seq_lens=[3001, 2050],
+              seed=chunk)
+    run_paged(oq, 8, 4, 0, B=2, H=2, G=4, HD=64, P=64, n_pos=3001, chunk=chunk, seed=chunk + 1)
+
+
+@pytest.mark.parametrize("kb,vb", [(8, 8), (4, 4)])
+def test_paged_group_scales(oq, kb, vb):
+    run_paged(oq, kb, vb, 32, B=2, H=2, G=4, HD=128, P=64, n_pos=515, seed=40 + kb)
+
+
+def test_paged_per_row_scale(oq):
+    run_paged(oq, 8, 8, -1, B=2, H=4, G=1, HD=64, P=64, n_pos=300, seed=41)
+
+
+@pytest.mark.parametrize("kb,vb", [(4, 4), (16, 16)])
+def test_paged_window(oq, kb, vb):
+    """Anchors and a ring over pages: capacity 64 + 192 slots in 64-slot
+    pages, a context that wraps the ring several times."""
+    run_paged(oq, kb, vb, 0, B=2, H=2, G=4, HD=128, P=64, n_pos=700, n_anchor=64, window=192, seed=50 + kb)
+
+
+@pytest.mark.parametrize("kb,vb,group", [(4, 4, 0), (8, 8, 0), (16, 16, 0), (8, 4, 0)])
+def test_paged_invalid_entries(oq, kb, vb, group):
+    """Table entries outside [0, n_pages) are skipped by the append and read
+    as zero codes and scales: the cache and the output equal those of a
+    cache whose entries name pages that are zeroed after the append."""
+    kvq = need_gpu()
+    import torch
+    from workloads.device import decode, positions, to_device
+    B, H, G, HD, P, n_pos = 2, 2, 4, 128, 64, 450
+    K, V, q = _data(B, H, n_pos, HD, H * G, 60 + kb)
+    cap = 512
+    pps, n_pages = cap // P, B * (cap // P) + 4
+    table = _table(B, pps, n_pages, 60 + kb)
+    used = set(table.reshape(-1).tolist())
+    spare = [u for u in range(n_pages) if u not in used]
+    bad = table.copy()
+    bad[1, 2], bad[1, 5], bad[0, 0] = -1, n_pages, -7
+    good = table.copy()
+    good[1, 2], good[1, 5], good[0, 0] = spare[0], spare[1], spare[2]
+    gs = group_size_of(kb, vb, group, H, HD)
+    cx = _paged(kvq, bad, n_pages, B, H, HD, cap, kb, vb, gs, P)
+    cy = _paged(kvq, good, n_pages, B, H, HD, cap, kb, vb, gs, P)
+    _append_pieces(kvq, [cx, cy], K, V, (0.5, 1.0))
+    for name in BUFFERS:
+        if getattr(cy, name) is not None:
+            _unit_view(cy, name)[torch.as_tensor(spare[:3], device="cuda")] = 0
+    torch.cuda.synchronize()
+    for name in BUFFERS:
+        if getattr(cx, name) is not None:
+            assert torch.equal(getattr(cx, name), getattr(cy, name)), f"{name}: an invalid page entry was written"
+    qd = to_device(q)
+    lens = positions([n_pos, n_pos - 10])
+    ox, oy = (decode(c, qd, H * G, lens, n_pos) for c in (cx, cy))
+    torch.cuda.synchronize()
+    assert torch.equal(ox, oy)
+    assert torch.all(torch.isfinite(ox))
+
+
+@pytest.mark.parametrize("kb,vb,group", [(4, 4, 0), (8, 4, 0), (16, 16, 0)])
+@pytest.mark.parametrize("n_new", [1, 3])
+def test_paged_decode_step(oq, kb, vb, group, n_new):
+    """kvq_decode_step on a paged cache, its new rows crossing a page
+    boundary, equals the separate calls on the same pages and on a
+    contiguous cache."""
+    kvq = need_gpu()
+    import torch
+    from workloads.device import positions, to_device
+    B, H, G, HD, P = 2, 2, 4, 128, 64
+    n0 = 3 * P - 1
+    n = n0 + n_new
+    cap = 4 * P
+    pps, n_pages = 4, 2 * 4 + 3
+    table = _table(B, pps, n_pages, 70 + n_new)
+    gs = group_size_of(kb, vb, group, H, HD)
+    K, V, q = _data(B, H, n, HD, H * G, 70 + n_new + kb)
+    ps = [_paged(kvq, table, n_pages, B, H, HD, cap, kb, vb, gs, P) for _ in range(2)]
+    contig = kvq.alloc_cache(B, H, HD, cap, kb, vb, gs)
+    caches = ps + [contig]
+    for c in caches:
+        kvq.kvq_append(c, to_device(K[:, :, :n0]), to_device(V[:, :, :n0]), n0, positions([0] * B))
+    kn, vn, qd = to_device(K[:, :, n0:]), to_device(V[:, :, n0:]), to_device(q)
+    pos, lens = positions([n0] * B), positions([n] * B)
+    ws_bytes = kvq.kvq_workspace_bytes(contig, H * G, n, 0)
+    outs = [torch.full((B, H * G, HD), 7.0, dtype=torch.float32, device="cuda") for _ in range(3)]
+    wss = [torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda") for _ in range(3)]
+    kvq.kvq_decode_step(ps[0], kn, vn, n_new, pos, qd, H * G, lens, n, 0.0, 0, outs[0], wss[0], ws_bytes)
+    for i in (1, 2):
+        kvq.kvq_append(caches[i], kn, vn, n_new, pos)
+        kvq.kvq_decode_attn(caches[i], qd, H * G, lens, n, 0.0, 0, outs[i], wss[i], ws_bytes)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    for name in BUFFERS:
+        if getattr(contig, name) is not None:
+            assert torch.equal(getattr(ps[0], name), getattr(ps[1], name)), name
+    _assert_same_storage(ps[0], table, contig)
+    got = outs[0].cpu().numpy()
+    for b in range(B):
+        want = oq.decode_step(kb, vb, gs, 0, 0, K[b], V[b], q[b], softmax_default(HD))
+        assert_close(got[b], want, f"paged step kb={kb} vb={vb} n_new={n_new} b={b}")
