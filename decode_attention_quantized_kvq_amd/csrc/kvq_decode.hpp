@@ -45,10 +45,8 @@ struct FloatParams {
 
 // LDS layout (byte offsets), shared by the host (launch size) and the kernel.
 struct FloatSmem {
-    int zs, red, misc, pages, total;
+    int zs, red, misc, total;
 };
-
-constexpr int FLOAT_MAX_PAGES = 132;             // pages a chunk can touch (<= 8192 / 64 + 1)
 
 __host__ __device__ inline FloatSmem float_smem(int G, int HD, int chunk)
 {
@@ -60,8 +58,6 @@ __host__ __device__ inline FloatSmem float_smem(int G, int HD, int chunk)
     off += DEC_WAVES * G * HD * 4;               // cross-wave reduction of acc
     s.misc = off;
     off += (2 * G + 2 * DEC_WAVES * G) * 4;      // m, l, wave partials
-    s.pages = off;
-    off += FLOAT_MAX_PAGES * 4;                  // paged storage: the chunk's pages
     s.total = off;
     return s;
 }
@@ -237,27 +233,39 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_float_kernel(FloatParams p
 
     const FloatSmem lay = float_smem(G, HD, CH);
     float *zs = reinterpret_cast<float *>(smem + lay.zs);
-    // paged storage: the pages of the chunk's slots (-1: none, read as zero)
-    int *pg = reinterpret_cast<int *>(smem + lay.pages);
+    // paged storage: the pages of the chunk's slots (-1: none, read as zero),
+    // entry i in lane i % 64 of pgv[i / 64] of every wave.  A chunk (at most
+    // 8192 slots, a multiple of 64 from a multiple of 64) touches at most 128
+    // pages of at least 64 slots.
     const int pg0 = PAGED ? (t0 >> p.page_shift) : 0;
+    int pgv[2] = {-1, -1};
     if constexpr (PAGED) {
         const int npg = ((t0 + n_tok - 1) >> p.page_shift) - pg0 + 1;
-        for (int i = tid; i < npg; i += DEC_THREADS) {
-            const int e = p.block_table[(size_t)b * p.pages_per_seq + pg0 + i];
-            pg[i] = (e >= 0 && e < p.n_pages) ? e : -1;
+        const int lane = tid & 63;
+#pragma unroll
+        for (int k = 0; k < 2; k++) {
+            const int i = k * 64 + lane;
+            if (i < npg) {
+                const int e = p.block_table[(size_t)b * p.pages_per_seq + pg0 + i];
+                pgv[k] = (e >= 0 && e < p.n_pages) ? e : -1;
+            }
         }
-        __syncthreads();
     }
-    // address of slot t0 + t of this KV head's rows (nullptr: no page)
-    auto row_ptr = [&](const uint8_t *base, int t, int row_bytes) -> const uint8_t * {
+    // block-uniform address of row t0 + t1 of this KV head, t1 a multiple of
+    // 64 or the first row of a load batch inside one 64-row block (nullptr:
+    // no page).  A page holds whole 64-row blocks, so the rows of the block
+    // from t1 on follow at row_bytes each; the lookup is a readlane.
+    auto block_ptr = [&](const uint8_t *base, int t1, int row_bytes) -> const uint8_t * {
         if constexpr (PAGED) {
-            const int pos = t0 + t;
-            const int u = pg[(pos >> p.page_shift) - pg0];
+            const int pos = t0 + t1;
+            const int i = (pos >> p.page_shift) - pg0;
+            const int lo = __builtin_amdgcn_readlane(pgv[0], i & 63), hi = __builtin_amdgcn_readlane(pgv[1], i & 63);
+            const int u = i < 64 ? lo : hi;
             if (u < 0) return nullptr;
             return base + (((size_t)u * p.n_kv_heads + kvh) * p.capacity + (pos & ((1 << p.page_shift) - 1))) *
                               (size_t)row_bytes;
         } else {
-            return base + ((size_t)bh * p.capacity + t0 + t) * (size_t)row_bytes;
+            return base + ((size_t)bh * p.capacity + t0 + t1) * (size_t)row_bytes;
         }
     };
     float *red = reinterpret_cast<float *>(smem + lay.red);
@@ -271,16 +279,21 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_float_kernel(FloatParams p
     {
         constexpr int LPT = KS::LPT;
         constexpr int TPP = DEC_THREADS / LPT;
+        constexpr int S64 = 64 / TPP;           // load steps per 64-row block
+        static_assert(TPP <= 64 && 64 % TPP == 0, "a load step lies in one 64-row block");
         const int sl = tid % LPT, tr = tid / LPT;
         KS kside;
         kside.init(qh, sl);
         for (int base = 0; base < n_tok; base += TPP * UA) {
             uint4 raw[UA];
+            // one address per 64 rows (S64 steps of TPP rows), then 32-bit offsets
+            const uint8_t *blk = nullptr;
 #pragma unroll
             for (int u = 0; u < UA; u++) {
                 const int t = base + u * TPP + tr;
-                const uint8_t *r = t < n_tok ? row_ptr(p.k_codes, t, K_ROW) : nullptr;
-                raw[u] = r ? ld_u4_nt(r + sl * 16) : make_uint4(0, 0, 0, 0);
+                if (u % S64 == 0) blk = block_ptr(p.k_codes, base + u * TPP, K_ROW);
+                const uint32_t off = (uint32_t)(((u % S64) * TPP + tr) * K_ROW + sl * 16);
+                raw[u] = blk && t < n_tok ? ld_u4_nt(blk + off) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int u = 0; u < UA; u++) {
@@ -358,14 +371,19 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_float_kernel(FloatParams p
     {
         constexpr int LPT = VS::LPT;
         constexpr int TPP = DEC_THREADS / LPT;
+        constexpr int S64 = 64 / TPP;           // load steps per 64-row block
+        static_assert(TPP <= 64 && 64 % TPP == 0, "a load step lies in one 64-row block");
         const int sl = tid % LPT, tr = tid / LPT;
         for (int base = 0; base < n_tok; base += TPP * UC) {
             uint4 raw[UC];
+            // one address per 64 rows (S64 steps of TPP rows), then 32-bit offsets
+            const uint8_t *blk = nullptr;
 #pragma unroll
             for (int u = 0; u < UC; u++) {
                 const int t = base + u * TPP + tr;
-                const uint8_t *r = t < n_tok ? row_ptr(p.v_codes, t, V_ROW) : nullptr;
-                raw[u] = r ? ld_u4_nt(r + sl * 16) : make_uint4(0, 0, 0, 0);
+                if (u % S64 == 0) blk = block_ptr(p.v_codes, base + u * TPP, V_ROW);
+                const uint32_t off = (uint32_t)(((u % S64) * TPP + tr) * V_ROW + sl * 16);
+                raw[u] = blk && t < n_tok ? ld_u4_nt(blk + off) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int u = 0; u < UC; u++) {

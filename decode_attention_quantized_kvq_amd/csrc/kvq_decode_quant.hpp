@@ -237,11 +237,17 @@ __device__ __forceinline__ void pack_w(uint32_t w0, uint32_t w1, uint32_t w2, ui
 // KG = scale groups per head row for both keys and values (1: groups of
 // head_dim, or one scale per position shared by all heads; 2 or 4: groups of
 // head_dim / KG channels); key dots are summed per group.
-// waves per SIMD the register allocation aims at (5 = at most 96 VGPRs)
-__host__ __device__ constexpr int qd_waves_per_eu(int G, int KG) { return G * KG <= 4 ? 5 : 3; }
+// waves per SIMD the register allocation must allow: the contiguous int4
+// key and value instances with G x KG <= 4 fit 128 VGPRs (4 waves) by
+// themselves; their paged instances would miss it by a register or two, so
+// they ask for it (the others take what they need)
+__host__ __device__ constexpr int qd_min_waves(int KB, int VB, int G, int KG, bool paged)
+{
+    return paged && KB == 4 && VB == 4 && G * KG <= 4 ? 4 : 1;
+}
 
 template <int KB, int VB, int HD, int G, int KG, bool PAGED>
-__global__ __launch_bounds__(QD_THREADS)
+__global__ __launch_bounds__(QD_THREADS) __attribute__((amdgpu_waves_per_eu(qd_min_waves(KB, VB, G, KG, PAGED))))
 void decode_quant_kernel(QuantParams p)
 {
     using T = QT<KB, VB, HD, G>;
