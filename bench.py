@@ -17,7 +17,7 @@ GB/s of algorithmic bytes (the bytes the method must move: the cache it
 streams, q in, out, and the appended rows); `roofline` prices the split-K
 kernel alone against MI355X's 8 TB/s HBM peak.
 
-    python bench.py [--steps K] [--warmup W] [--modes headline|targets|all]
+    python bench.py [--steps K] [--warmup W] [--modes headline|targets|paged|all]
 
 Prints one JSON line.
 """
@@ -68,7 +68,9 @@ def step_bytes(w, mode) -> float:
 
 
 def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = False, log=print,
-             settle_ms: float = 100.0) -> dict:
+             settle_ms: float = 100.0, page_size: int = 0) -> dict:
+    """One bench line.  page_size > 0 stores the cache in a pool of pages of
+    that many slots, assigned to the sequences in a seeded random order."""
     import torch
 
     import decode_attention_quantized_kvq_amd as kvq
@@ -77,12 +79,20 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
     t_fill = time.perf_counter()
     layers = []
     for layer in range(w.n_layers):
+        paging = {}
+        if page_size:
+            pps = w.capacity // page_size
+            n_pages = w.batch * pps
+            order = torch.randperm(n_pages, generator=torch.Generator().manual_seed(w.seed + layer))
+            paging = dict(page_size=page_size, n_pages=n_pages,
+                          block_table=order.to(torch.int32).view(w.batch, pps).to("cuda"))
         cache = kvq.alloc_cache(w.batch, w.n_kv_heads, w.head_dim, w.capacity, mode.k_bits, mode.v_bits,
-                                _group(mode, w), w.n_anchor, w.window)
+                                _group(mode, w), w.n_anchor, w.window, **paging)
         k_last, v_last = fill([cache], w, layer, w.n_pos)
         q = queries(w, layer)
         layers.append((cache, k_last, v_last, q))
-    log(f"[bench] {w.name} {mode.name}: {w.n_layers} layer(s) filled in {time.perf_counter() - t_fill:.1f} s")
+    name = f"{w.name}-paged{page_size}" if page_size else w.name
+    log(f"[bench] {name} {mode.name}: {w.n_layers} layer(s) filled in {time.perf_counter() - t_fill:.1f} s")
 
     max_len = w.n_pos
     ch = kvq.kvq_chunk_tokens(layers[0][0], w.n_q_heads, max_len) if chunk == 0 else chunk
@@ -198,7 +208,7 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
     # with the MALL scrub inside the loop, wall time includes it: rate from kernel events then
     ms_step = ms_step_gpu if flush else ms_step_graph
     res = {
-        "workload": w.name, "mode": mode.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
+        "workload": name, "mode": mode.name, "page_size": page_size, "batch": w.batch, "n_q_heads": w.n_q_heads,
         "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "context": attended(w), "n_layers": w.n_layers,
         "capacity": w.capacity, "n_anchor": w.n_anchor, "window": w.window, "group_size": _group(mode, w),
         "chunk_tokens": ch, "n_chunks": n_chunks, "mall_scrub": flush,
@@ -212,7 +222,7 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
         "split_bytes": split_bytes(w, mode), "split_GBps": split_bytes(w, mode) / (t_split_loop * 1e-3) / 1e9,
     }
     res["split_pct_of_peak"] = 100.0 * res["split_GBps"] / PEAK_HBM_GBS
-    log(f"[bench] {w.name} {mode.name}: step {ms_step * 1e3:.1f} us ({res['step_GBps']:.0f} GB/s, "
+    log(f"[bench] {name} {mode.name}: step {ms_step * 1e3:.1f} us ({res['step_GBps']:.0f} GB/s, "
         f"{res['tokens_per_s']:.0f} tok/s; 1-step graph {(ms_step_graph1 or 0) * 1e3:.1f} us, eager "
         f"{ms_step_eager * 1e3:.1f} us); split {t_split_loop * 1e3:.1f} us = {res['split_GBps']:.0f} GB/s "
         f"({res['split_pct_of_peak']:.1f}% of peak); append {t_app * 1e3:.1f} us, combine {t_comb * 1e3:.1f} us")
@@ -361,7 +371,7 @@ def record_traffic(fetch_csv: str, write_csv: str, log=print) -> int:
                   "each counter scaled by its reading for a 1 GiB device copy in the same run",
         "counters": out,
         "workloads": {f"{w.name}/{mode.name}": {
-            "kernel": "decode_quant_kernel<4,4,128,4,1>",
+            "kernel": "decode_quant_kernel<4,4,128,4,1,false>",
             "bytes_per_launch": round(dec_bytes),
             "fetch_bytes": round(out["fetch"]["decode_raw"] * out["fetch"]["factor"]),
             "write_bytes": round(out["write"]["decode_raw"] * out["write"]["factor"]),
@@ -412,8 +422,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--chunk", type=int, default=0, help="split-K chunk (0 = the library's choice)")
-    ap.add_argument("--modes", choices=["headline", "targets", "all"], default="targets",
-                    help="headline: the K4V4 32K line only; targets: + K8V4 at 32K; all: every workload")
+    ap.add_argument("--modes", choices=["headline", "targets", "paged", "all"], default="targets",
+                    help="headline: the K4V4 32K line only; targets: + K8V4 at 32K; paged: + both 32K "
+                         "workloads in 256-slot pages; all: every workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe-traffic", action="store_true",
                     help="copy 1 GiB then launch the headline split kernel 3 times (for counter runs)")
@@ -449,6 +460,9 @@ def main() -> int:
     extra = []
     if args.modes in ("targets", "all"):
         extra.append(run_mode(wl.K8V4_32K, wl.K8V4, args.steps, args.warmup, args.chunk, log=log))
+    if args.modes in ("paged", "all"):
+        extra.append(run_mode(wl.K4V4_32K, wl.K4V4, args.steps, args.warmup, args.chunk, log=log, page_size=256))
+        extra.append(run_mode(wl.K8V4_32K, wl.K8V4, args.steps, args.warmup, args.chunk, log=log, page_size=256))
     if args.modes == "all":
         extra.append(run_mode(wl.K4V4_32K, wl.FP16, args.steps, args.warmup, args.chunk, log=log))
         extra.append(run_mode(wl.K4V4_32K, wl.K4V4_G32, args.steps, args.warmup, args.chunk, log=log))
@@ -487,7 +501,7 @@ def main() -> int:
         "pct_of_peak": round(100.0 * head["step_GBps"] / PEAK_HBM_GBS, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_quant_kernel<4,4,128,4,1>",
+            "kernel": "decode_quant_kernel<4,4,128,4,1,false>",
             "achieved": round(head["split_GBps"], 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

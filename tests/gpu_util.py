@@ -118,3 +118,57 @@ def window_slots(oq, n_pos, A, W):
 
 def softmax_default(hd):
     return 1.0 / math.sqrt(hd)
+
+
+# ---------------------------------------------------------------- paged caches
+BUFFERS = ("k_codes", "v_codes", "k_scales", "v_scales")
+
+
+def paged_table(B, pps, n_pages, seed):
+    """A random assignment of distinct pool pages to the logical pages."""
+    rng = np.random.default_rng(1000 + seed)
+    return rng.permutation(n_pages)[: B * pps].reshape(B, pps).astype(np.int32)
+
+
+def unit_view(cache, name):
+    """The pool `name` as [n_pages][heads][elements per page and head]
+    (heads 1 for one scale per slot over all heads)."""
+    import decode_attention_quantized_kvq_amd as kvq
+    d = cache.desc
+    t = getattr(cache, name)
+    size = kvq.kvq_cache_sizes(d)[BUFFERS.index(name)] // t.element_size()
+    per_row = name.endswith("scales") and d.group_size == d.n_kv_heads * d.head_dim and d.n_kv_heads > 1
+    return t[:size].view(d.n_pages, 1 if per_row else d.n_kv_heads, -1)
+
+
+def gathered(cache, table, name):
+    """Pool `name` gathered in table order: the contiguous cache's layout,
+    [batch][heads][elements per sequence and head]."""
+    import torch
+    u = unit_view(cache, name)
+    B, pps = table.shape
+    g = u[torch.as_tensor(table.reshape(-1).astype(np.int64), device=u.device)]
+    return g.view(B, pps, u.shape[1], -1).permute(0, 2, 1, 3).reshape(B, u.shape[1], -1)
+
+
+def _contig_view(cache, name, heads):
+    import decode_attention_quantized_kvq_amd as kvq
+    d = cache.desc
+    t = getattr(cache, name)
+    size = kvq.kvq_cache_sizes(d)[BUFFERS.index(name)] // t.element_size()
+    return t[:size].view(d.batch, heads, -1)
+
+
+def assert_same_storage(paged, table, contig):
+    import torch
+    for name in BUFFERS:
+        if getattr(contig, name) is None:
+            assert getattr(paged, name) is None
+            continue
+        g = gathered(paged, table, name)
+        c = _contig_view(contig, name, g.shape[1])
+        assert torch.equal(g, c), f"{name}: gathered pages differ from the contiguous cache"
+        spare = sorted(set(range(paged.desc.n_pages)) - set(table.reshape(-1).tolist()))
+        if spare:
+            u = unit_view(paged, name)
+            assert not torch.any(u[torch.as_tensor(spare, device=u.device)]), f"{name}: a spare page was written"

@@ -7,7 +7,8 @@ import numpy as np
 import pytest
 
 import workloads as wl
-from gpu_util import assert_close, cache_arrays, check_codes, group_size_of, linear_slots, need_gpu, window_slots
+from gpu_util import (assert_close, assert_same_storage, cache_arrays, check_codes, group_size_of, linear_slots, need_gpu,
+                      paged_table, window_slots)
 
 pytestmark = pytest.mark.gpu
 
@@ -103,6 +104,38 @@ def test_k4v4_32k_ragged(oq):
         want = oq.decode_step(mode.k_bits, mode.v_bits, gs, 0, 0, K, V, qn[b], sc)
         assert_close(out[b], want, f"ragged b={b} L={L}")
     del cache
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("w,mode", [(wl.K4V4_32K, wl.K4V4), (wl.K8V4_32K, wl.K8V4)], ids=["k4v4-32k", "k8v4-32k"])
+def test_32k_paged(oq, w, mode):
+    """The 32K workloads in 256-slot pages, assigned in a random order (as
+    the paged bench lines run them): the pages hold bit for bit what the
+    contiguous cache holds, the outputs are bit for bit the contiguous
+    cache's, and sampled sequences match the oracle."""
+    kvq = need_gpu()
+    import torch
+    from workloads.device import decode, fill, positions, queries, to_device
+    P = 256
+    pps = w.capacity // P
+    table = paged_table(w.batch, pps, w.batch * pps, 90)
+    (contig, gs) = _alloc(kvq, w, mode)
+    paged = kvq.alloc_cache(w.batch, w.n_kv_heads, w.head_dim, w.capacity, mode.k_bits, mode.v_bits, gs,
+                            page_size=P, n_pages=w.batch * pps, block_table=to_device(table))
+    fill([contig, paged], w, 0, w.n_pos)
+    assert_same_storage(paged, table, contig)
+    q = queries(w, 0)
+    lens = positions([w.n_pos] * w.batch)
+    oc, op = (decode(c, q, w.n_q_heads, lens, w.n_pos) for c in (contig, paged))
+    torch.cuda.synchronize()
+    assert torch.equal(oc, op)
+    out, qn = op.cpu().numpy(), q.cpu().numpy()
+    for b in (0, w.batch - 1):
+        K = wl.rows(w, wl.K_STREAM, 0, b, w.n_pos)
+        V = wl.rows(w, wl.V_STREAM, 0, b, w.n_pos)
+        want = oq.decode_step(mode.k_bits, mode.v_bits, gs, 0, 0, K, V, qn[b], 1.0 / np.sqrt(w.head_dim))
+        assert_close(out[b], want, f"{w.name} paged b={b}")
+    del contig, paged
     torch.cuda.empty_cache()
 
 

@@ -7,12 +7,12 @@ fused step, and table entries that name no page."""
 import numpy as np
 import pytest
 
-from gpu_util import assert_close, group_size_of, need_gpu, softmax_default
+from gpu_util import (BUFFERS, assert_close, assert_same_storage, group_size_of, need_gpu, paged_table,
+                      softmax_default, unit_view)
 
 pytestmark = pytest.mark.gpu
 
 MODES = [(32, 32, 0), (16, 16, 0), (8, 8, 0), (8, 4, 0), (4, 4, 0), (4, 8, 0)]
-BUFFERS = ("k_codes", "v_codes", "k_scales", "v_scales")
 
 
 def _data(B, H, n_pos, HD, Hq, seed):
@@ -23,61 +23,11 @@ def _data(B, H, n_pos, HD, Hq, seed):
     return K, V, q
 
 
-def _table(B, pps, n_pages, seed):
-    """A random assignment of distinct pool pages to the logical pages."""
-    rng = np.random.default_rng(1000 + seed)
-    return rng.permutation(n_pages)[: B * pps].reshape(B, pps).astype(np.int32)
-
-
 def _paged(kvq, table, n_pages, B, H, HD, cap, kb, vb, gs, P, n_anchor=0, window=0):
     from workloads.device import to_device
     bt = to_device(np.ascontiguousarray(table, np.int32))
     return kvq.alloc_cache(B, H, HD, cap, kb, vb, gs, n_anchor, window, page_size=P, n_pages=n_pages,
                            block_table=bt)
-
-
-def _unit_view(cache, name):
-    """The pool `name` as [n_pages][heads][elements per page and head]
-    (heads 1 for one scale per slot over all heads)."""
-    kvq = need_gpu()
-    d = cache.desc
-    t = getattr(cache, name)
-    size = kvq.kvq_cache_sizes(d)[BUFFERS.index(name)] // t.element_size()
-    per_row = name.endswith("scales") and d.group_size == d.n_kv_heads * d.head_dim and d.n_kv_heads > 1
-    return t[:size].view(d.n_pages, 1 if per_row else d.n_kv_heads, -1)
-
-
-def _gathered(cache, table, name):
-    """Pool `name` gathered in table order: the contiguous cache's layout,
-    [batch][heads][elements per sequence and head]."""
-    import torch
-    u = _unit_view(cache, name)
-    B, pps = table.shape
-    g = u[torch.as_tensor(table.reshape(-1).astype(np.int64), device=u.device)]
-    return g.view(B, pps, u.shape[1], -1).permute(0, 2, 1, 3).reshape(B, u.shape[1], -1)
-
-
-def _contig_view(cache, name, heads):
-    kvq = need_gpu()
-    d = cache.desc
-    t = getattr(cache, name)
-    size = kvq.kvq_cache_sizes(d)[BUFFERS.index(name)] // t.element_size()
-    return t[:size].view(d.batch, heads, -1)
-
-
-def _assert_same_storage(paged, table, contig):
-    import torch
-    for name in BUFFERS:
-        if getattr(contig, name) is None:
-            assert getattr(paged, name) is None
-            continue
-        g = _gathered(paged, table, name)
-        c = _contig_view(contig, name, g.shape[1])
-        assert torch.equal(g, c), f"{name}: gathered pages differ from the contiguous cache"
-        spare = sorted(set(range(paged.desc.n_pages)) - set(table.reshape(-1).tolist()))
-        if spare:
-            u = _unit_view(paged, name)
-            assert not torch.any(u[torch.as_tensor(spare, device=u.device)]), f"{name}: a spare page was written"
 
 
 def _append_pieces(kvq, caches, K, V, pieces):
@@ -104,13 +54,13 @@ def run_paged(oq, kb, vb, group, B=3, H=2, G=4, HD=128, P=64, n_pos=700, pieces=
     assert cap % P == 0
     pps = cap // P
     n_pages = B * pps + spare
-    table = _table(B, pps, n_pages, seed)
+    table = paged_table(B, pps, n_pages, seed)
     gs = group_size_of(kb, vb, group, H, HD)
     contig = kvq.alloc_cache(B, H, HD, cap, kb, vb, gs, n_anchor, window)
     paged = _paged(kvq, table, n_pages, B, H, HD, cap, kb, vb, gs, P, n_anchor, window)
     _append_pieces(kvq, [contig, paged], K, V, pieces)
     torch.cuda.synchronize()
-    _assert_same_storage(paged, table, contig)
+    assert_same_storage(paged, table, contig)
 
     lens = seq_lens if seq_lens is not None else [n_pos] * B
     qd = to_device(q)
@@ -178,7 +128,7 @@ def test_paged_invalid_entries(oq, kb, vb, group):
     K, V, q = _data(B, H, n_pos, HD, H * G, 60 + kb)
     cap = 512
     pps, n_pages = cap // P, B * (cap // P) + 4
-    table = _table(B, pps, n_pages, 60 + kb)
+    table = paged_table(B, pps, n_pages, 60 + kb)
     used = set(table.reshape(-1).tolist())
     spare = [u for u in range(n_pages) if u not in used]
     bad = table.copy()
@@ -191,7 +141,7 @@ def test_paged_invalid_entries(oq, kb, vb, group):
     _append_pieces(kvq, [cx, cy], K, V, (0.5, 1.0))
     for name in BUFFERS:
         if getattr(cy, name) is not None:
-            _unit_view(cy, name)[torch.as_tensor(spare[:3], device="cuda")] = 0
+            unit_view(cy, name)[torch.as_tensor(spare[:3], device="cuda")] = 0
     torch.cuda.synchronize()
     for name in BUFFERS:
         if getattr(cx, name) is not None:
@@ -218,7 +168,7 @@ def test_paged_decode_step(oq, kb, vb, group, n_new):
     n = n0 + n_new
     cap = 4 * P
     pps, n_pages = 4, 2 * 4 + 3
-    table = _table(B, pps, n_pages, 70 + n_new)
+    table = paged_table(B, pps, n_pages, 70 + n_new)
     gs = group_size_of(kb, vb, group, H, HD)
     K, V, q = _data(B, H, n, HD, H * G, 70 + n_new + kb)
     ps = [_paged(kvq, table, n_pages, B, H, HD, cap, kb, vb, gs, P) for _ in range(2)]
@@ -240,7 +190,7 @@ def test_paged_decode_step(oq, kb, vb, group, n_new):
     for name in BUFFERS:
         if getattr(contig, name) is not None:
             assert torch.equal(getattr(ps[0], name), getattr(ps[1], name)), name
-    _assert_same_storage(ps[0], table, contig)
+    assert_same_storage(ps[0], table, contig)
     got = outs[0].cpu().numpy()
     for b in range(B):
         want = oq.decode_step(kb, vb, gs, 0, 0, K[b], V[b], q[b], softmax_default(HD))
