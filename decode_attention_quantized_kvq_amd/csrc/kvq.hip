@@ -165,7 +165,7 @@ int auto_chunk(const kvq_cache *c, int n_q_heads, int max_seq_len)
 
 using FloatFn = void (*)(FloatParams);
 using QuantFn = void (*)(QuantParams);
-using PrepFn = void (*)(const float *, int32_t *, float *, float);
+using PrepFn = void (*)(const float *, int32_t *, float *, float, int *);
 
 template <int B, int HD, bool PG>
 FloatFn pick_float_g(int G)
@@ -251,7 +251,7 @@ PrepFn pick_prep(int kb, int hd, int G)
     return hd == 64 ? pick_prep_g<8, 64>(G) : pick_prep_g<8, 128>(G);
 }
 
-using StepPrepFn = void (*)(AppendParams, int, int, const float *, int32_t *, float *, float);
+using StepPrepFn = void (*)(AppendParams, int, int, const float *, int32_t *, float *, float, int *);
 
 template <int KB, int HD>
 StepPrepFn pick_step_g(int G)
@@ -276,7 +276,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Workspace: ml [P][C][2] | acc [P][C][HD] | (quantized keys) query digits
 // [B*Hkv][K_COLS][ND][G] int32 | query scales [P] float.
 struct WsLayout {
-    size_t ml, acc, qdig, qsc, total;
+    size_t ml, acc, qdig, qsc, cnt, total;
 };
 
 WsLayout ws_layout(int batch, int n_q_heads, int head_dim, int n_chunks, int n_kv_heads, int k_bits)
@@ -286,7 +286,7 @@ WsLayout ws_layout(int batch, int n_q_heads, int head_dim, int n_chunks, int n_k
     w.ml = 0;
     w.acc = align256(P * n_chunks * 2 * sizeof(float));
     size_t off = w.acc + P * n_chunks * head_dim * sizeof(float);
-    w.qdig = w.qsc = 0;
+    w.qdig = w.qsc = w.cnt = 0;
     if (quantized(k_bits)) {
         const size_t cols = (size_t)head_dim * k_bits / 32;
         const size_t nd = k_bits == 4 ? 4 : 2;
@@ -294,6 +294,8 @@ WsLayout ws_layout(int batch, int n_q_heads, int head_dim, int n_chunks, int n_k
         off = w.qdig + (size_t)batch * n_kv_heads * cols * nd * (n_q_heads / n_kv_heads) * 4;
         w.qsc = align256(off);
         off = w.qsc + P * sizeof(float);
+        w.cnt = align256(off);                       // the fused step's ticket counters
+        off = w.cnt + (size_t)batch * n_kv_heads * sizeof(int);
     }
     w.total = off;
     return w;
@@ -467,10 +469,15 @@ size_t kvq_workspace_bytes(const kvq_cache *c, int n_q_heads, int max_seq_len, i
 // check runs before anything is enqueued.
 enum { PHASE_PREP = 1, PHASE_SPLIT = 2 };
 
+// kvq_decode_step merges inside the split kernel up to this many chunks
+constexpr int FUSED_MERGE_MAX_CHUNKS = 4;
+
+// out != nullptr (integer caches, both phases): the split kernel's last
+// workgroup per (sequence, KV head) also merges the partials into out
 static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, const int32_t *seq_len,
                             int max_seq_len, float softmax_scale, int chunk_tokens, void *workspace,
                             size_t workspace_bytes, void *stream, const AppendParams *ap, dim3 ap_grid,
-                            int phases = PHASE_PREP | PHASE_SPLIT)
+                            int phases = PHASE_PREP | PHASE_SPLIT, float *out = nullptr)
 {
     int ch, nc;
     int st = resolve_chunk(c, n_q_heads, max_seq_len, chunk_tokens, &ch, &nc);
@@ -531,6 +538,8 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
     if (!fn || !prep || !sprep) return fail(KVQ_ERR_BITS, "no kernel for k_bits=%d v_bits=%d", c->k_bits, c->v_bits);
     int32_t *qdig = reinterpret_cast<int32_t *>(ws + wl.qdig);
     float *qsc = reinterpret_cast<float *>(ws + wl.qsc);
+    if (out && phases != (PHASE_PREP | PHASE_SPLIT)) return fail(KVQ_ERR_ARG, "a fused combine needs both phases");
+    int *cnt = out ? reinterpret_cast<int *>(ws + wl.cnt) : nullptr;
     const unsigned units = (unsigned)(c->batch * c->n_kv_heads);
     if (ap && ap_grid.x > 0 && (unsigned long long)ap_grid.x * ap_grid.y * 2 + units > 0x7FFFFFFFull)
         return fail(KVQ_ERR_SHAPE, "batch * n_new too large for a fused step");
@@ -538,9 +547,9 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
         if (ap && ap_grid.x > 0) {
             const unsigned n_app = ap_grid.x * ap_grid.y * 2;
             hipLaunchKernelGGL(sprep, dim3(n_app + units), dim3(256), 0, st_, *ap, (int)ap_grid.x, (int)ap_grid.y, q,
-                               qdig, qsc, qk_scale);
+                               qdig, qsc, qk_scale, cnt);
         } else {
-            hipLaunchKernelGGL(prep, dim3(units), dim3(256), 0, st_, q, qdig, qsc, qk_scale);
+            hipLaunchKernelGGL(prep, dim3(units), dim3(256), 0, st_, q, qdig, qsc, qk_scale, cnt);
         }
         const int hs = hip_status("query prep launch");
         if (hs) return hs;
@@ -568,6 +577,8 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
     p.max_len = max_len_of(c, max_seq_len);
     p.chunk = ch;
     p.n_chunks = nc;
+    p.cnt = cnt;
+    p.out = out;
     const bool pr = per_row(c);
     const int gph = groups_per_head(c);
     if (pr) {                                        // strides per storage unit (sequence or page)
@@ -657,6 +668,14 @@ int kvq_decode_step(const kvq_cache *c, const float *k_new, const float *v_new, 
     AppendParams ap;
     dim3 ag;
     if ((st = prepare_append(c, k_new, v_new, n_new, start_pos, &ap, &ag))) return st;
+    // Few chunks per (sequence, KV head): two launches, the split kernel's
+    // last workgroup of each merging the partials (a short split kernel, where
+    // a third launch costs more than that merge).  More chunks: the merge as a
+    // launch of its own (the in-kernel merge adds a store wait to every
+    // workgroup and a serial merge at the end).
+    if (quant_modes(c) && nc <= FUSED_MERGE_MAX_CHUNKS)
+        return enqueue_partials(c, q, n_q_heads, seq_len, max_seq_len, softmax_scale, ch, workspace, workspace_bytes,
+                                stream, &ap, ag, PHASE_PREP | PHASE_SPLIT, out);
     st = enqueue_partials(c, q, n_q_heads, seq_len, max_seq_len, softmax_scale, ch, workspace, workspace_bytes, stream,
                           &ap, ag);
     if (st) return st;

@@ -19,6 +19,8 @@
 
 #include <type_traits>
 
+#include "kvq_combine.hpp"
+
 #include "kvq_device.hpp"
 
 namespace kvq {
@@ -400,38 +402,6 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_float_kernel(FloatParams p
         ml0[tid * ml_hstride] = m_sh[tid];
         ml0[tid * ml_hstride + 1] = l_sh[tid];
     }
-}
-
-// ------------------------------------------------------------------------
-// Merge: for each (sequence, query head) row, M = max m_i,
-// out = sum acc_i 2^(m_i - M) / sum l_i 2^(m_i - M); 0 if every chunk is empty.
-// A block holds 256 / HD rows, one thread per output channel; the chunk loop
-// is unrolled so several partial loads are in flight per thread.
-// ------------------------------------------------------------------------
-template <int HD>
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ ml, const float *__restrict__ acc,
-                                                      float *__restrict__ out, int n_chunks, int n_rows)
-{
-    constexpr int RPB = 256 / HD;
-    const int r = threadIdx.x / HD, c = threadIdx.x - r * HD;
-    const size_t row = (size_t)blockIdx.x * RPB + r;
-    if (row >= (size_t)n_rows) return;
-    const float2 *mr = reinterpret_cast<const float2 *>(ml) + row * (size_t)n_chunks;
-    float M = -INFINITY;
-#pragma unroll 8
-    for (int i = 0; i < n_chunks; i++) M = fmaxf(M, mr[i].x);
-    float L = 0.0f, o = 0.0f;
-    if (M != -INFINITY) {
-        const float *ac = acc + row * (size_t)n_chunks * HD + c;
-#pragma unroll 8
-        for (int i = 0; i < n_chunks; i++) {
-            const float2 v = mr[i];
-            const float e = v.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(v.x - M);
-            L = fmaf(v.y, e, L);
-            o = fmaf(ac[(size_t)i * HD], e, o);
-        }
-    }
-    out[row * HD + c] = L > 0.0f ? o / L : 0.0f;
 }
 
 } // namespace kvq

@@ -46,6 +46,7 @@
 // (m, l, acc) written.  LDS use does not depend on the chunk length.
 #pragma once
 
+#include "kvq_combine.hpp"
 #include "kvq_device.hpp"
 
 namespace kvq {
@@ -97,6 +98,12 @@ struct QuantParams {
     int page_shift, pages_per_seq, n_pages;
     int max_len;
     int chunk, n_chunks;
+    // one decode step in one launch pair: after writing its partials each
+    // workgroup takes a ticket on cnt[b * Hkv + kvh] (zeroed by the query
+    // preparation before the launch) and the last one merges the G rows of
+    // its (sequence, KV head) into out.  cnt == nullptr: partials only.
+    int *cnt;
+    float *out;
     long long k_sc_b, k_sc_h;
     int k_sc_t;
     long long v_sc_b, v_sc_h;
@@ -151,7 +158,7 @@ __host__ __device__ inline QuantSmem quant_smem(int G, int HD, int vg)
 // ---------------------------------------------------------------------------
 template <int KB, int HD, int G>
 __device__ __forceinline__ void qprep_block(const float *__restrict__ q, int32_t *__restrict__ qdig,
-                                            float *__restrict__ qsc, float qk_scale, int unit)
+                                            float *__restrict__ qsc, float qk_scale, int unit, int *cnt)
 {
     constexpr int K_COLS = HD * KB / 32;
     constexpr int ND = KB == 4 ? 4 : 2;
@@ -190,13 +197,14 @@ __device__ __forceinline__ void qprep_block(const float *__restrict__ q, int32_t
         for (int j = 0; j < ND; j++) qdig[(((size_t)unit * ND + j) * K_COLS + col) * G + h] = (int32_t)d[j];
     }
     if (tid < G) qsc[unit * G + tid] = amax[tid] / (float)Q_RANGE * qk_scale;
+    if (cnt && tid == 0) cnt[unit] = 0;              // the fused step's ticket counter
 }
 
 template <int KB, int HD, int G>
 __global__ __launch_bounds__(256) void qprep_kernel(const float *__restrict__ q, int32_t *__restrict__ qdig,
-                                                    float *__restrict__ qsc, float qk_scale)
+                                                    float *__restrict__ qsc, float qk_scale, int *cnt)
 {
-    qprep_block<KB, HD, G>(q, qdig, qsc, qk_scale, blockIdx.x);
+    qprep_block<KB, HD, G>(q, qdig, qsc, qk_scale, blockIdx.x, cnt);
 }
 
 template <int KB>
@@ -276,12 +284,20 @@ void decode_quant_kernel(QuantParams p)
     const size_t ml_hs = (size_t)p.n_chunks * 2;
     const size_t acc_hs = (size_t)p.n_chunks * HD;
 
+    // (block-uniform; the ticket needs one int of LDS, free by then)
+    auto finish = [&]() {
+        if (p.cnt)
+            combine_if_last<HD, G, QD_THREADS>(p.ws_ml, p.ws_acc, p.out, p.cnt + bh, p.n_chunks, row0,
+                                               reinterpret_cast<int *>(smem));
+    };
+
     if (n_tok <= 0) {
-        for (int i = tid; i < G * HD; i += QD_THREADS) acc0[(i / HD) * acc_hs + (i % HD)] = 0.0f;
+        for (int i = tid; i < G * HD; i += QD_THREADS) store_partial(&acc0[(i / HD) * acc_hs + (i % HD)], 0.0f);
         if (tid < G) {
-            ml0[tid * ml_hs] = -INFINITY;
-            ml0[tid * ml_hs + 1] = 0.0f;
+            store_partial(&ml0[tid * ml_hs], -INFINITY);
+            store_partial(&ml0[tid * ml_hs + 1], 0.0f);
         }
+        finish();
         return;
     }
 
@@ -780,7 +796,7 @@ void decode_quant_kernel(QuantParams p)
             const float mv = pm[w * G + h];
             if (mv != -INFINITY) s = fmaf(__builtin_amdgcn_exp2f(mv - m), red[(w * G + h) * HD + c], s);
         }
-        acc0[h * acc_hs + c] = s;
+        store_partial(&acc0[h * acc_hs + c], s);
     }
     if (tid < G) {
         float m = pm[tid];
@@ -792,9 +808,10 @@ void decode_quant_kernel(QuantParams p)
             const float mv = pm[w * G + tid];
             if (mv != -INFINITY) l = fmaf(__builtin_amdgcn_exp2f(mv - m), pl[w * G + tid], l);
         }
-        ml0[tid * ml_hs] = m;
-        ml0[tid * ml_hs + 1] = l;
+        store_partial(&ml0[tid * ml_hs], m);
+        store_partial(&ml0[tid * ml_hs + 1], l);
     }
+    finish();
 }
 
 } // namespace kvq

@@ -11,10 +11,11 @@
 namespace kvq {
 
 // grid.x = app_x * app_y * 2 append blocks (row, pass, side), then one query
-// block per (sequence, KV head).  256 threads.
+// block per (sequence, KV head), which also zeroes that unit's ticket counter
+// when cnt is not null.  256 threads.
 template <int KB, int HD, int G>
 __global__ __launch_bounds__(256) void step_prep_kernel(AppendParams ap, int app_x, int app_y, const float *q,
-                                                        int32_t *qdig, float *qsc, float qk_scale)
+                                                        int32_t *qdig, float *qsc, float qk_scale, int *cnt)
 {
     const int n_app = app_x * app_y * 2;
     const int bid = blockIdx.x;
@@ -25,7 +26,7 @@ __global__ __launch_bounds__(256) void step_prep_kernel(AppendParams ap, int app
         append_block(ap, r % app_x, r / app_x, side);
         return;
     }
-    qprep_block<KB, HD, G>(q, qdig, qsc, qk_scale, bid - n_app);
+    qprep_block<KB, HD, G>(q, qdig, qsc, qk_scale, bid - n_app, cnt);
 }
 
 } // namespace kvq

@@ -265,9 +265,14 @@ int kvq_decode_attn(const kvq_cache *c, const float *q, int n_q_heads, const int
  * adds only the new token's K and V to the cache, then attends over it):
  * exactly kvq_append(c, k_new, v_new, n_new, start_pos, stream) followed by
  * kvq_decode_attn(c, q, ..., stream), with the same arguments, rules and
- * results.  A step is three launches: on an 8/4-bit cache the append and
- * the query's fixed-point preparation share the first one, then the split
- * kernel and the combine; on a 16/32-bit cache append, split, combine.
+ * results, bit for bit.  On an 8/4-bit cache the append and the query's
+ * fixed-point preparation share the first launch, then the split kernel,
+ * then the combine; when a sequence's context spans at most 4 chunks the
+ * split kernel's last workgroup per (sequence, KV head) merges the partials
+ * itself (same arithmetic, one launch fewer for short contexts, where the
+ * launches dominate).  On a 16/32-bit cache: append, split, combine.  The
+ * workspace holds the merge's ticket counters, which the first launch
+ * zeroes each step (no memset, so the step can be captured in a graph).
  * Every argument is checked before anything is enqueued; on an error
  * nothing is.
  */

@@ -286,6 +286,38 @@ def test_decode_step_matches_separate_calls(oq, kb, vb, group, n_new):
         assert_close(got[b], want, f"step kb={kb} vb={vb} n_new={n_new} b={b}")
 
 
+@pytest.mark.parametrize("kb,vb", [(4, 4), (8, 4)])
+@pytest.mark.parametrize("n", [1023, 1024, 1025, 2100])
+def test_decode_step_merge_rule(oq, kb, vb, n):
+    """Contexts of 4 chunks (merged inside the split kernel), 5 and 9 chunks
+    (merged by the combine launch), with one row appended by the step: both
+    forms equal the separate calls bit for bit."""
+    kvq = need_gpu()
+    import torch
+    from workloads.device import positions, to_device
+    B, H, G, HD, ch = 2, 2, 4, 128, 256
+    n0 = n - 1
+    K, V, q = _data(B, H, n, HD, H * G, 80 + n)
+    caches = [kvq.alloc_cache(B, H, HD, n, kb, vb, HD) for _ in range(2)]
+    for c in caches:
+        kvq.kvq_append(c, to_device(K[:, :, :n0]), to_device(V[:, :, :n0]), n0, positions([0] * B))
+    kn, vn, qd = to_device(K[:, :, n0:]), to_device(V[:, :, n0:]), to_device(q)
+    pos, lens = positions([n0] * B), positions([n, n - 300])
+    ws_bytes = kvq.kvq_workspace_bytes(caches[0], H * G, n, ch)
+    outs = [torch.full((B, H * G, HD), 7.0, dtype=torch.float32, device="cuda") for _ in range(2)]
+    wss = [torch.full((ws_bytes // 4 + 64,), 3.0, dtype=torch.float32, device="cuda") for _ in range(2)]
+    for _ in range(2):                                  # the second step reuses the workspace's counters
+        kvq.kvq_decode_step(caches[0], kn, vn, 1, pos, qd, H * G, lens, n, 0.0, ch, outs[0], wss[0], ws_bytes)
+    kvq.kvq_append(caches[1], kn, vn, 1, pos)
+    kvq.kvq_decode_attn(caches[1], qd, H * G, lens, n, 0.0, ch, outs[1], wss[1], ws_bytes)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    got = outs[0].cpu().numpy()
+    for b, L in ((0, n), (1, n - 300)):
+        want = oq.decode_step(kb, vb, HD, 0, 0, K[b][:, :L], V[b][:, :L], q[b], softmax_default(HD))
+        assert_close(got[b], want, f"merge rule n={n} b={b}")
+
+
 @pytest.mark.parametrize("fused", [False, True])
 def test_graph_replay_matches_eager(oq, fused):
     """A step captured in a HIP graph (append + decode + combine, as separate
