@@ -404,6 +404,26 @@ static int prepare_append(const kvq_cache *c, const float *k_new, const float *v
     return KVQ_OK;
 }
 
+// Bulk appends (n_new >= this) into 8/4-bit caches without a window and with
+// scales per head or group go through the 64-slot tile kernel.
+constexpr int APPEND_TILE_MIN_ROWS = 64;
+
+using AppendTileFn = void (*)(AppendParams);
+
+template <int HD>
+AppendTileFn pick_append_tile_hd(int kb, int vb)
+{
+    if (kb == 8) return vb == 8 ? append_tile_kernel<HD, 8, 8> : append_tile_kernel<HD, 8, 4>;
+    return vb == 8 ? append_tile_kernel<HD, 4, 8> : append_tile_kernel<HD, 4, 4>;
+}
+
+AppendTileFn pick_append_tile(const kvq_cache *c, int n_new)
+{
+    if (n_new < APPEND_TILE_MIN_ROWS || !quantized(c->k_bits) || c->window != 0 || per_row(c)) return nullptr;
+    return c->head_dim == 64 ? pick_append_tile_hd<64>(c->k_bits, c->v_bits)
+                             : pick_append_tile_hd<128>(c->k_bits, c->v_bits);
+}
+
 extern "C" {
 
 int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n_new, const int32_t *start_pos,
@@ -413,7 +433,16 @@ int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n
     dim3 grid;
     int st = prepare_append(c, k_new, v_new, n_new, start_pos, &p, &grid);
     if (st || grid.x == 0) return st;
-    hipLaunchKernelGGL(append_kernel, grid, dim3(APPEND_THREADS), 0, static_cast<hipStream_t>(stream), p);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (AppendTileFn tile = pick_append_tile(c, n_new)) {
+        // tiles of 64 slots from start & ~63 (start is read on the device)
+        const unsigned tiles = (unsigned)((n_new + 2 * TILE_ROWS - 2) / TILE_ROWS);
+        if ((unsigned long long)c->batch * c->n_kv_heads > 65535u)
+            return fail(KVQ_ERR_SHAPE, "batch * n_kv_heads too large for a bulk append");
+        hipLaunchKernelGGL(tile, dim3(tiles, (unsigned)(c->batch * c->n_kv_heads), 2), dim3(256), 0, s, p);
+        return hip_status("append_tile_kernel launch");
+    }
+    hipLaunchKernelGGL(append_kernel, grid, dim3(APPEND_THREADS), 0, s, p);
     return hip_status("append_kernel launch");
 }
 

@@ -61,16 +61,35 @@ __device__ __forceinline__ uint16_t scale_bits_from_amax(float amax, float qmax)
     return h;
 }
 
+// One code: clamp(rint_even(x / s), -qmax, qmax), decided by the IEEE fp32
+// quotient RN(x / s); a zero scale (an all-zero or vanishing group) gives
+// code 0.  rs = v_rcp_f32(s), relative error <= 2^-22, so q = RN(x * rs)
+// has relative error <= 2^-22 + 2^-24 < 3e-7 against x / s.  The stored scale
+// is the fp16 rounding of amax / qmax, so |x / s| <= 1.5 * qmax < 192 (the
+// worst case is an fp16 subnormal rounded down), q is within 5.8e-5 of x / s
+// and RN(x / s) within half an ulp (7.6e-6): q and RN(x / s) differ by less
+// than 6.6e-5, and unless q is within 1e-4 of a half-integer both round to
+// the same integer.  Those rare cases take the IEEE divide itself.  (A scale
+// saturated at 65504 allows larger quotients, but beyond 192 the code is
+// clamped either way.)
+__device__ __forceinline__ int code_of(float x, float s, float rs, float qmax)
+{
+    const float q = x * rs;
+    float r = rintf(q);
+    if (fabsf(q - r) > 0.5f - 1.0e-4f) r = rintf(x / (s > 0.0f ? s : 1.0f));
+    return (int)(s > 0.0f ? fminf(fmaxf(r, -qmax), qmax) : 0.0f);
+}
+
+// the reciprocal code_of takes (1 for a zero scale, whose codes are 0)
+__device__ __forceinline__ float code_rcp(float s) { return __builtin_amdgcn_rcpf(s > 0.0f ? s : 1.0f); }
+
 // 8 values -> 8 codes against stored scale s (s > 0), packed for `bits`.
 __device__ __forceinline__ void encode8(const float (&x)[8], float s, float qmax, int bits, uint32_t &w0, uint32_t &w1)
 {
     int c[8];
+    const float rs = code_rcp(s);
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-        float r = (s > 0.0f) ? rintf(x[j] / s) : 0.0f;   // IEEE divide, ties to even
-        r = fminf(fmaxf(r, -qmax), qmax);
-        c[j] = (int)r;
-    }
+    for (int j = 0; j < 8; j++) c[j] = code_of(x[j], s, rs, qmax);
     if (bits == 8) {
         w0 = (uint32_t)(c[0] & 0xFF) | ((uint32_t)(c[1] & 0xFF) << 8) | ((uint32_t)(c[2] & 0xFF) << 16) |
              ((uint32_t)(c[3] & 0xFF) << 24);
@@ -250,6 +269,123 @@ __device__ __forceinline__ void append_block(const AppendParams &p, int bx, int 
 __global__ __launch_bounds__(APPEND_THREADS) void append_kernel(AppendParams p)
 {
     append_block(p, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// ------------------------------------------------------------------------
+// Bulk appends (a prompt's rows in one call) into 8/4-bit caches without a
+// window and with scales per head or per group: one workgroup per 64-slot
+// tile of one (sequence, KV head, side).  The rows of a tile are contiguous
+// in the input and the tile is contiguous in the cache (keys: one tile;
+// values: 16 groups of four interleaved slots), so both streams move in
+// whole 16-byte pieces; the encoding is the row kernel's, value for value.
+// 256 threads = 64 rows x 4 quarters of a row.
+// grid: x = tiles (the call's slots from start & ~63), y = batch * n_kv_heads,
+// z = side.
+// ------------------------------------------------------------------------
+constexpr int TILE_ROWS = 64;
+
+template <int HD, int BITS>
+__device__ __forceinline__ void append_tile(const AppendParams &p, int tile, int bh, int side)
+{
+    constexpr int ROWB = HD * BITS / 8;            // code bytes per row
+    constexpr int V4 = TILE_ROWS * HD / 4;         // float4 pieces of the tile's input
+    constexpr int ROUNDS = V4 / 256;               // per thread
+    constexpr int LPR = HD / 4;                    // lanes per row in a round
+    static_assert(V4 % 256 == 0 && 64 % LPR == 0, "whole rows per wave and round");
+    __shared__ __align__(16) uint8_t tb[TILE_ROWS * ROWB];   // the tile's codes in their cache layout
+
+    const int b = bh / p.n_kv_heads, h = bh - b * p.n_kv_heads;
+    const int start = p.start_pos[b];
+    const int t0 = (start & ~(TILE_ROWS - 1)) + tile * TILE_ROWS;   // first slot (= position) of the tile
+    const int lo = max(max(t0, start), 0), hi = min(min(t0 + TILE_ROWS, start + p.n_new), p.capacity);
+    if (lo >= hi) return;                          // block-uniform
+    int ub = b, slot0 = t0;                        // storage unit and the tile's first slot in it
+    if (p.page_shift > 0) {
+        ub = p.block_table[(size_t)b * p.pages_per_seq + (t0 >> p.page_shift)];
+        if (ub < 0 || ub >= p.n_pages) return;     // no page: not stored
+        slot0 = t0 & ((1 << p.page_shift) - 1);
+    }
+    const int tid = threadIdx.x;
+    const float qmax = BITS == 8 ? 127.0f : 7.0f;
+    const int g = p.group;                         // >= 32 values, divides head_dim
+    // input rows t0 .. t0 + 63 are contiguous ([n_new][head_dim] per
+    // sequence and head): round k, thread tid holds float4 piece k * 256 + tid,
+    // row (k * 256 + tid) / LPR, channels 4 * ((k * 256 + tid) % LPR) ..
+    const float *src = p.src[side] + (size_t)bh * p.n_new * HD;      // this sequence and head
+    uint4 raw[ROUNDS];
+#pragma unroll
+    for (int k = 0; k < ROUNDS; k++) {
+        const int e = k * 256 + tid, t = t0 + e / LPR;
+        raw[k] = t >= lo && t < hi ? ld_u4_nt(src + (size_t)(t - start) * HD + 4 * (e % LPR)) : make_uint4(0, 0, 0, 0);
+    }
+    const uint32_t ob = side == 1 ? (BITS == 8 ? 0x80808080u : 0x88888888u) : 0u;   // values: offset binary
+#pragma unroll
+    for (int k = 0; k < ROUNDS; k++) {
+        const int e = k * 256 + tid, r = e / LPR, c = 4 * (e % LPR);
+        const float x[4] = {__uint_as_float(raw[k].x), __uint_as_float(raw[k].y), __uint_as_float(raw[k].z),
+                            __uint_as_float(raw[k].w)};
+        float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+        for (int m = 1; m < g / 4; m <<= 1) amax = fmaxf(amax, shfl_xor(amax, m));   // the group's lanes
+        const uint16_t sh = scale_bits_from_amax(amax, qmax);
+        const float sc = f16_bits_to_f32(sh), rs = code_rcp(sc);
+        const int t = t0 + r;
+        if (t >= lo && t < hi && c % g == 0)
+            p.scales[side][(((size_t)ub * p.n_kv_heads + h) * p.cap_u + slot0 + r) * (size_t)(HD / g) + c / g] = sh;
+        const int q0 = code_of(x[0], sc, rs, qmax), q1 = code_of(x[1], sc, rs, qmax);
+        const int q2 = code_of(x[2], sc, rs, qmax), q3 = code_of(x[3], sc, rs, qmax);
+        uint32_t w;                                // the 2 (int4) or 4 (int8) code bytes of c .. c + 3
+        if constexpr (BITS == 8)
+            w = (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
+                ((uint32_t)(q3 & 0xFF) << 24);
+        else
+            w = (uint32_t)(q0 & 0xF) | ((uint32_t)(q1 & 0xF) << 4) | ((uint32_t)(q2 & 0xF) << 8) |
+                ((uint32_t)(q3 & 0xF) << 12);
+        w ^= ob;
+        const int j = c * BITS / 8;                // first code byte in the row
+        if (side == 0) {
+            // keys: byte j of row r at (j / 16) * 1024 + r * 16 + j % 16
+            uint8_t *d = tb + (j >> 4) * 1024 + r * 16 + (j & 15);
+            if constexpr (BITS == 8) *reinterpret_cast<uint32_t *>(d) = w;
+            else *reinterpret_cast<uint16_t *>(d) = (uint16_t)w;
+        } else {
+            // values: byte j of row r at (r & ~3) * ROWB + 4 * j + (r & 3)
+            uint8_t *d = tb + (r & ~3) * ROWB + 4 * j + (r & 3);
+#pragma unroll
+            for (int m = 0; m < BITS / 2; m++) d[4 * m] = (uint8_t)(w >> (8 * m));
+        }
+    }
+    __syncthreads();
+    // the tile in the cache: keys one 64-slot tile, values 16 groups of four
+    // slots, both contiguous from the tile's first slot; 16-byte pieces
+    uint8_t *base = p.codes[side] + ((size_t)ub * p.n_kv_heads + h) * (size_t)(side == 0 ? p.cap64 : p.cap4) * ROWB +
+                    (size_t)slot0 * ROWB;
+    for (int o = tid * 16; o < TILE_ROWS * ROWB; o += 256 * 16) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(tb + o);
+        if (side == 0) {
+            const int t = t0 + (o & 1023) / 16;    // a key piece is one slot's slice
+            if (t >= lo && t < hi) *reinterpret_cast<uint4 *>(base + o) = v;
+        } else {
+            const int s4 = t0 + 4 * (o / (4 * ROWB));   // a value piece: 4 byte positions of one group
+            if (s4 >= lo && s4 + 4 <= hi) {
+                *reinterpret_cast<uint4 *>(base + o) = v;
+            } else {
+                // a group cut by the call's first or last row: its rows only
+                const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int m = 0; m < 4; m++)
+                    if (s4 + m >= lo && s4 + m < hi)
+#pragma unroll
+                        for (int e = 0; e < 4; e++) base[o + 4 * e + m] = (uint8_t)(wd[e] >> (8 * m));
+            }
+        }
+    }
+}
+
+template <int HD, int KB, int VB>
+__global__ __launch_bounds__(256) void append_tile_kernel(AppendParams p)
+{
+    if (blockIdx.z == 0) append_tile<HD, KB>(p, blockIdx.x, blockIdx.y, 0);
+    else append_tile<HD, VB>(p, blockIdx.x, blockIdx.y, 1);
 }
 
 } // namespace kvq

@@ -169,6 +169,95 @@ def test_append_skips_out_of_range(oq):
     assert np.all(kc[1, 0, 8:] == 127) and np.all(kc[1, 0, :8] == 0x5A)
 
 
+@pytest.mark.parametrize("kb,vb", [(4, 4), (8, 4), (8, 8), (4, 8)])
+@pytest.mark.parametrize("HD,group", [(128, 0), (128, 32), (64, 0), (64, 32)])
+def test_bulk_append_matches_rows(oq, kb, vb, HD, group):
+    """A bulk append (the 64-slot tile kernel) stores bit for bit what one
+    append per row (the row kernel) stores, for tiles cut by unaligned and
+    negative starts and by the capacity, contiguous and paged."""
+    kvq = need_gpu()
+    import torch
+    from gpu_util import assert_same_storage, paged_table
+    from workloads.device import positions, to_device
+    B, H, cap, n = 4, 2, 512, 300
+    gs = group or HD
+    starts = [37, 0, -5, cap - 200]                  # the last runs 100 rows past the capacity
+    rng = np.random.default_rng(kb * 7 + vb + HD + gs)
+    K = (rng.standard_normal((B, H, n, HD)) * rng.uniform(0.1, 4.0, (B, H, n, 1))).astype(np.float32)
+    V = rng.standard_normal((B, H, n, HD)).astype(np.float32)
+    bulk = kvq.alloc_cache(B, H, HD, cap, kb, vb, gs)
+    rows = kvq.alloc_cache(B, H, HD, cap, kb, vb, gs)
+    P, pps = 64, cap // 64
+    table = paged_table(B, pps, B * pps + 2, kb + vb)
+    paged = kvq.alloc_cache(B, H, HD, cap, kb, vb, gs, page_size=P, n_pages=B * pps + 2,
+                            block_table=to_device(table))
+    kd, vd = to_device(K), to_device(V)
+    for c in (bulk, paged):
+        kvq.kvq_append(c, kd, vd, n, positions(starts))
+    for i in range(n):
+        kvq.kvq_append(rows, kd[:, :, i:i + 1].contiguous(), vd[:, :, i:i + 1].contiguous(), 1,
+                       positions([s0 + i for s0 in starts]))
+    torch.cuda.synchronize()
+    for name in ("k_codes", "v_codes", "k_scales", "v_scales"):
+        assert torch.equal(getattr(bulk, name), getattr(rows, name)), name
+    assert_same_storage(paged, table, rows)
+    # and the stored rows are the oracle's codes
+    for b, s0 in enumerate(starts):
+        slots = {s0 + i: s0 + i for i in range(n) if 0 <= s0 + i < cap}
+        Kp = np.zeros((1, H, cap, HD), np.float32)
+        Vp = np.zeros((1, H, cap, HD), np.float32)
+        for sl in slots:
+            Kp[0, :, sl], Vp[0, :, sl] = K[b, :, sl - s0], V[b, :, sl - s0]
+        check_codes(oq, bulk.sequence(b), Kp, Vp, slots)
+
+
+@pytest.mark.parametrize("kb,vb", [(4, 4), (8, 8)])
+def test_codes_near_half_integers(oq, kb, vb):
+    """Values whose quotient by the scale lies within a few ulps of k + 1/2
+    (the rounding boundary), for normal and subnormal fp16 scales and a
+    scale rounded down from 1.45 * 2^-24: both append kernels store the
+    oracle's codes, decided by the IEEE quotient."""
+    kvq = need_gpu()
+    import torch
+    from workloads.device import positions, to_device
+    B, H, HD, n, g = 2, 2, 128, 128, 32
+    qmax = 127 if kb == 8 else 7
+    rng = np.random.default_rng(91 + kb)
+    f16 = lambda v: np.float32(np.float16(v))
+    scales = [f16(1.0), f16(0.0371), f16(3.3e-3), f16(7.1e-5), np.float32(3 * 2.0 ** -24),
+              np.float32(2.0 ** -24), f16(250.0)]
+    X = np.zeros((B, H, n, HD), np.float32)
+    for idx in np.ndindex(B, H, n, HD // g):
+        S = scales[rng.integers(len(scales))]
+        grp = np.empty(g, np.float32)
+        grp[0] = np.float32(qmax) * S                   # amax / qmax = S exactly
+        if S == np.float32(2.0 ** -24) and rng.random() < 0.5:
+            grp[0] = np.float32(1.45 * 2.0 ** -24) * np.float32(qmax)   # scale rounds down to 2^-24
+        k = rng.integers(-qmax, qmax, g - 1)
+        # half of them just outside the window where the exact divide decides
+        off = np.where(rng.random(g - 1) < 0.5, 0.0, rng.uniform(0.8e-4, 3e-4, g - 1) * rng.choice([-1, 1], g - 1))
+        x = ((k + 0.5 + off) * np.float64(S)).astype(np.float32)
+        for _ in range(3):                              # nudge by -3 .. 3 ulps
+            step = rng.integers(-1, 2, g - 1)
+            x = np.where(step > 0, np.nextafter(x, np.float32(np.inf)),
+                         np.where(step < 0, np.nextafter(x, np.float32(-np.inf)), x)).astype(np.float32)
+        grp[1:] = np.clip(x, -grp[0], grp[0])
+        rng.shuffle(grp)
+        b, h, t, j = idx
+        X[b, h, t, j * g:(j + 1) * g] = grp
+    bulk = kvq.alloc_cache(B, H, HD, n, kb, vb, g)
+    rows = kvq.alloc_cache(B, H, HD, n, kb, vb, g)
+    xd = to_device(X)
+    kvq.kvq_append(bulk, xd, xd, n, positions([0, 0]))
+    for p0 in range(0, n, 16):
+        part = to_device(X[:, :, p0:p0 + 16])
+        kvq.kvq_append(rows, part, part, 16, positions([p0, p0]))
+    torch.cuda.synchronize()
+    slots = {t: t for t in range(n)}
+    check_codes(oq, bulk, X, X, slots)
+    check_codes(oq, rows, X, X, slots)
+
+
 def test_guard_bands_untouched(oq):
     """Buffers placed between guard bytes: append and decode write only
     their own ranges."""
