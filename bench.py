@@ -68,9 +68,11 @@ def step_bytes(w, mode) -> float:
 
 
 def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = False, log=print,
-             settle_ms: float = 100.0, page_size: int = 0) -> dict:
+             settle_ms: float = 100.0, page_size: int = 0, layer_modes=None) -> dict:
     """One bench line.  page_size > 0 stores the cache in a pool of pages of
-    that many slots, assigned to the sequences in a seeded random order."""
+    that many slots, assigned to the sequences in a seeded random order.
+    layer_modes: one mode per layer (bit widths chosen per layer; `mode`
+    then only names the line and picks the split-alone figure's layer 0)."""
     import torch
 
     import decode_attention_quantized_kvq_amd as kvq
@@ -86,8 +88,9 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
             order = torch.randperm(n_pages, generator=torch.Generator().manual_seed(w.seed + layer))
             paging = dict(page_size=page_size, n_pages=n_pages,
                           block_table=order.to(torch.int32).view(w.batch, pps).to("cuda"))
-        cache = kvq.alloc_cache(w.batch, w.n_kv_heads, w.head_dim, w.capacity, mode.k_bits, mode.v_bits,
-                                _group(mode, w), w.n_anchor, w.window, **paging)
+        lm = layer_modes[layer] if layer_modes else mode
+        cache = kvq.alloc_cache(w.batch, w.n_kv_heads, w.head_dim, w.capacity, lm.k_bits, lm.v_bits,
+                                _group(lm, w), w.n_anchor, w.window, **paging)
         k_last, v_last = fill([cache], w, layer, w.n_pos)
         q = queries(w, layer)
         layers.append((cache, k_last, v_last, q))
@@ -157,7 +160,8 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
         torch.cuda.synchronize()
         return ea.elapsed_time(eb)
 
-    if mode.k_bits < 16:
+    mode0 = layer_modes[0] if layer_modes else mode
+    if mode0.k_bits < 16:
         # the split kernel alone: one query preparation, then split launches on it
         kvq.kvq_prepare_query(cache0, q0, w.n_q_heads, max_len, 0.0, ch, ws, ws_bytes, stream)
         split = lambda: kvq.kvq_decode_partials_prepared(cache0, w.n_q_heads, lens, max_len, ch, ws, ws_bytes, stream)
@@ -204,7 +208,7 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
         del g1, gk
     ms_step_wall = wall_eager / steps * 1e3
     ms_step_gpu = (t_app + t_split + t_comb) * w.n_layers
-    sbytes = step_bytes(w, mode) * w.n_layers
+    sbytes = sum(step_bytes(w, m) for m in layer_modes) if layer_modes else step_bytes(w, mode) * w.n_layers
     # with the MALL scrub inside the loop, wall time includes it: rate from kernel events then
     ms_step = ms_step_gpu if flush else ms_step_graph
     res = {
@@ -219,7 +223,7 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
         "step_GBps": sbytes / (ms_step * 1e-3) / 1e9,
         "tokens_per_s": w.batch / (ms_step * 1e-3),
         "us_append": t_app * 1e3, "us_split": t_split * 1e3, "us_combine": t_comb * 1e3,
-        "split_bytes": split_bytes(w, mode), "split_GBps": split_bytes(w, mode) / (t_split_loop * 1e-3) / 1e9,
+        "split_bytes": split_bytes(w, mode0), "split_GBps": split_bytes(w, mode0) / (t_split_loop * 1e-3) / 1e9,
     }
     res["split_pct_of_peak"] = 100.0 * res["split_GBps"] / PEAK_HBM_GBS
     log(f"[bench] {name} {mode.name}: step {ms_step * 1e3:.1f} us ({res['step_GBps']:.0f} GB/s, "
@@ -227,6 +231,49 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
         f"{ms_step_eager * 1e3:.1f} us); split {t_split_loop * 1e3:.1f} us = {res['split_GBps']:.0f} GB/s "
         f"({res['split_pct_of_peak']:.1f}% of peak); append {t_app * 1e3:.1f} us, combine {t_comb * 1e3:.1f} us")
     del layers, ws, out, scrub
+    torch.cuda.empty_cache()
+    return res
+
+
+def prefill(w, mode, rows_per_call: int = 4096, reps: int = 3, log=print) -> dict:
+    """Bulk quantization of a whole context (a prompt) into the cache:
+    kvq_append in calls of `rows_per_call` rows per sequence over the
+    workload's context, timed with HIP events after one untimed pass.
+    Algorithmic bytes: the float32 K and V rows read, the codes and scales
+    written."""
+    import torch
+
+    import decode_attention_quantized_kvq_amd as kvq
+    from workloads.device import positions
+    cache = kvq.alloc_cache(w.batch, w.n_kv_heads, w.head_dim, w.capacity, mode.k_bits, mode.v_bits,
+                            _group(mode, w))
+    n = min(rows_per_call, w.capacity)
+    g = torch.Generator(device="cuda").manual_seed(w.seed)
+    K = torch.randn((w.batch, w.n_kv_heads, n, w.head_dim), device="cuda", generator=g)
+    V = torch.randn((w.batch, w.n_kv_heads, n, w.head_dim), device="cuda", generator=g)
+    starts = [positions([p0] * w.batch) for p0 in range(0, w.capacity - n + 1, n)]
+    stream = torch.cuda.current_stream()
+
+    def run():
+        for sp in starts:
+            kvq.kvq_append(cache, K, V, n, sp, stream)
+
+    run()
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ea.record(stream)
+    for _ in range(reps):
+        run()
+    eb.record(stream)
+    torch.cuda.synchronize()
+    ms = ea.elapsed_time(eb) / reps
+    rows = w.batch * w.n_kv_heads * n * len(starts)
+    nbytes = rows * w.head_dim * 4 * 2 + rows * bpt_head(mode, w)
+    res = {"workload": w.name, "mode": mode.name, "rows_per_call": n, "calls": len(starts), "ms": ms,
+           "bytes": nbytes, "GBps": nbytes / (ms * 1e-3) / 1e9}
+    res["pct_of_peak"] = 100.0 * res["GBps"] / PEAK_HBM_GBS
+    log(f"[bench] prefill {w.name} {mode.name}: {len(starts)} calls of {n} rows, {ms:.3f} ms = "
+        f"{res['GBps']:.0f} GB/s ({res['pct_of_peak']:.1f}% of peak)")
+    del cache, K, V
     torch.cuda.empty_cache()
     return res
 
@@ -424,7 +471,7 @@ def main() -> int:
     ap.add_argument("--chunk", type=int, default=0, help="split-K chunk (0 = the library's choice)")
     ap.add_argument("--modes", choices=["headline", "targets", "paged", "all"], default="targets",
                     help="headline: the K4V4 32K line only; targets: + K8V4 at 32K; paged: + both 32K "
-                         "workloads in 256-slot pages; all: every workload")
+                         "workloads in 256-slot pages and bulk prefill; all: every workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe-traffic", action="store_true",
                     help="copy 1 GiB then launch the headline split kernel 3 times (for counter runs)")
@@ -472,8 +519,17 @@ def main() -> int:
             extra.append(run_mode(wl.K8V4_8K, m, args.steps, args.warmup, args.chunk, flush=True, log=log))
         for m in wl.TINYLOOP.modes:
             extra.append(run_mode(wl.TINYLOOP, m, max(3, args.steps // 4), 2, args.chunk, log=log))
+        # bit widths per layer: int8 in the first and last two layers, int4 between
+        n_l = wl.TINYLOOP.n_layers
+        per_layer = [wl.K8V8 if li < 2 or li >= n_l - 2 else wl.K4V4 for li in range(n_l)]
+        extra.append(run_mode(wl.TINYLOOP, wl.Mode("k8v8-ends-k4v4", 4, 4), max(3, args.steps // 4), 2, args.chunk,
+                              log=log, layer_modes=per_layer))
         for m in wl.TINY.modes:
             extra.append(run_mode(wl.TINY, m, args.steps, args.warmup, args.chunk, log=log))
+    prefills = []
+    if args.modes in ("paged", "all"):
+        prefills = [prefill(wl.K4V4_32K, wl.K4V4, log=log), prefill(wl.K8V4_32K, wl.K8V4, log=log),
+                    prefill(wl.K4V4_32K, wl.FP16, log=log)]
 
     probe = read_probe(log=log)
     cpu = None if args.no_cpu_baseline else cpu_baseline(head_w, head_m, log=log)
@@ -515,6 +571,8 @@ def main() -> int:
         "cpu_baseline": cpu,
         "modes": {f"{r['workload']}/{r['mode']}": {k: (round(v, 4) if isinstance(v, float) else v)
                                                    for k, v in r.items()} for r in [head] + extra},
+        "prefill": {f"{r['workload']}/{r['mode']}": {k: (round(v, 4) if isinstance(v, float) else v)
+                                                     for k, v in r.items()} for r in prefills},
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -452,6 +452,59 @@ def test_graph_replay_matches_eager(oq, fused):
         assert torch.equal(out, want), f"replay {r}"
 
 
+def test_layers_of_mixed_widths_in_one_graph(oq):
+    """Bit widths chosen per layer (KVSplit's per-layer roadmap): four layers
+    with K8V8, K4V4 in 32-value groups, K8V4 and FP16 caches, one decode step
+    each, captured together in one HIP graph sharing one workspace; every
+    replay gives each layer's eager output bit for bit, and each matches the
+    oracle."""
+    kvq = need_gpu()
+    import torch
+    from workloads.device import positions, to_device
+    B, H, G, HD, n = 2, 2, 4, 128, 600
+    modes = [(8, 8, HD), (4, 4, 32), (8, 4, HD), (16, 16, HD)]
+    layers = []
+    for li, (kb, vb, gs) in enumerate(modes):
+        K, V, q = _data(B, H, n, HD, H * G, 40 + li)
+        cache = kvq.alloc_cache(B, H, HD, n, kb, vb, gs)
+        kvq.kvq_append(cache, to_device(K[:, :, : n - 1]), to_device(V[:, :, : n - 1]), n - 1, positions([0, 0]))
+        out = torch.zeros((B, H * G, HD), dtype=torch.float32, device="cuda")
+        layers.append((cache, to_device(K[:, :, n - 1:]), to_device(V[:, :, n - 1:]), to_device(q), out, K, V, q))
+    pos, lens = positions([n - 1] * B), positions([n] * B)
+    ws_bytes = max(kvq.kvq_workspace_bytes(c, H * G, n, 0) for c, *_ in layers)
+    ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")
+
+    def step(st):
+        for cache, k1, v1, qd, out, *_ in layers:
+            kvq.kvq_decode_step(cache, k1, v1, 1, pos, qd, H * G, lens, n, 0.0, 0, out, ws, ws_bytes, st)
+
+    step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    want = [l[4].clone() for l in layers]
+    for (kb, vb, gs), (_, _, _, _, _, K, V, q), w in zip(modes, layers, want):
+        got = w.cpu().numpy()
+        for b in range(B):
+            ref = oq.decode_step(kb, vb, gs, 0, 0, K[b], V[b], q[b], softmax_default(HD))
+            assert_close(got[b], ref, f"layer kb={kb} vb={vb} g={gs} b={b}")
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        step(cs)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cs):
+        step(cs)
+    for r in range(3):
+        for l in layers:
+            l[4].zero_()
+        ws.fill_(float(r + 1))                       # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for li, l in enumerate(layers):
+            assert torch.equal(l[4], want[li]), f"replay {r} layer {li}"
+
+
 def test_read_probe_runs():
     """The read-bandwidth probe reads every block it is given (an all-zero
     buffer folds to zero in every workgroup) and rejects bad sizes."""
