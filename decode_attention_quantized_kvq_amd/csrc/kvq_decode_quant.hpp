@@ -53,10 +53,15 @@ namespace kvq {
 
 constexpr int QD_THREADS = 256;
 constexpr int QD_WAVES = QD_THREADS / 64;
-// positions per wave sub-chunk: 512, or 256 / 128 when many heads and scale
-// groups make the per-position LDS large.  (A sub-chunk's value sums stay
-// exact in uint32: at most 512 * 32767 * 255 < 2^32.)
-__host__ __device__ constexpr int qd_sub(int G, int vg) { return G * vg >= 16 ? 128 : G * vg >= 8 ? 256 : 512; }
+// Positions per wave sub-chunk: 512 while G x vg < 8, else 256 (the maxima,
+// merge and prologue then run half as often as at 128, and the compiler keeps
+// the G = 4, vg = 4 loop in 156 VGPRs instead of 245); G = 8 with 2 or 4
+// scale groups takes 128, as 256 would not fit the LDS.  (A sub-chunk's value
+// sums stay exact in uint32: at most 512 * 32767 * 255 < 2^32.)
+__host__ __device__ constexpr int qd_sub(int G, int vg)
+{
+    return G == 8 && vg >= 2 ? 128 : G * vg >= 8 ? 256 : 512;
+}
 constexpr int Q_RANGE = 30000;
 constexpr int QD_PF = 16;       // value group loads in flight per lane
 constexpr int W_RANGE = 32767;
