@@ -150,15 +150,23 @@ int auto_chunk(const kvq_cache *c, int n_q_heads, int max_seq_len)
     const long long units = (long long)c->batch * c->n_kv_heads;
     const int L = max_len_of(c, max_seq_len);
     // The largest chunk of at most 2048 slots that fits the LDS budget and
-    // still gives >= 8 workgroups per CU over 256 CUs; when no chunk does,
-    // the smallest one (most workgroups): 64 slots, or 256 for integer
-    // caches, whose waves take 64 positions per step.  (Measured at 32K
-    // contexts: 4096-slot chunks leave a longer ragged last round, 1024-slot
-    // ones pay each workgroup's start and final merge twice as often.)
-    const int smallest = quant_modes(c) ? 256 : 64;
+    // still gives enough workgroups; when no chunk does, the smallest one.
+    // Float caches: >= 8 workgroups per CU over 256 CUs, at least 64 slots.
+    // Integer caches: >= one round of 4 workgroups per CU (1024), at least
+    // 512 slots: their workgroups carry a fixed start (query digits, first
+    // tile) and final merge, so fewer, longer ones win once the chip holds
+    // them all.  (Measured: at 32K contexts 4096-slot chunks leave a longer
+    // ragged last round and 1024-slot ones pay the start and merge twice as
+    // often; a 1600-slot window over 256 units steps in 44 us at 512 against
+    // 53 us at 256; a 34-layer 1K-context step in 547 us at 512 against 629
+    // at 256 and 634 at 1024.)
+    const bool q = quant_modes(c);
+    const int smallest = q ? 512 : 64;
+    const long long want = q ? 1024 : 2048;
     for (int ch = 2048; ch >= smallest; ch >>= 1) {
-        if (lds_bytes(c, G, ch) > kAutoLds) continue;
-        if (units * ((L + ch - 1) / ch) >= 2048) return ch;
+        // (an integer cache's LDS does not depend on the chunk)
+        if (!q && lds_bytes(c, G, ch) > kAutoLds) continue;
+        if (units * ((L + ch - 1) / ch) >= want) return ch;
     }
     return smallest;
 }
@@ -420,6 +428,7 @@ AppendTileFn pick_append_tile_hd(int kb, int vb)
 AppendTileFn pick_append_tile(const kvq_cache *c, int n_new)
 {
     if (n_new < APPEND_TILE_MIN_ROWS || !quantized(c->k_bits) || c->window != 0 || per_row(c)) return nullptr;
+    if ((long long)c->batch * c->n_kv_heads > 65535) return nullptr;   // grid y: the row kernel takes these
     return c->head_dim == 64 ? pick_append_tile_hd<64>(c->k_bits, c->v_bits)
                              : pick_append_tile_hd<128>(c->k_bits, c->v_bits);
 }
@@ -437,8 +446,6 @@ int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n
     if (AppendTileFn tile = pick_append_tile(c, n_new)) {
         // tiles of 64 slots from start & ~63 (start is read on the device)
         const unsigned tiles = (unsigned)((n_new + 2 * TILE_ROWS - 2) / TILE_ROWS);
-        if ((unsigned long long)c->batch * c->n_kv_heads > 65535u)
-            return fail(KVQ_ERR_SHAPE, "batch * n_kv_heads too large for a bulk append");
         hipLaunchKernelGGL(tile, dim3(tiles, (unsigned)(c->batch * c->n_kv_heads), 2), dim3(256), 0, s, p);
         return hip_status("append_tile_kernel launch");
     }

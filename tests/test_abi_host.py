@@ -307,18 +307,28 @@ def test_workspace_and_chunks(kvq):
     assert kvq.kvq_workspace_bytes(f, 8, 1000, 0) == ((16 * nc * 8 + 255) // 256) * 256 + 16 * nc * 128 * 4
     # max_seq_len beyond capacity sizes by capacity
     assert kvq.kvq_workspace_bytes(d, 32, 10 ** 9, 1024) == kvq.kvq_workspace_bytes(d, 32, 32768, 1024)
-    # short contexts use the smallest chunk: 256 slots for integer caches, 64 for float ones
+    # short contexts use the smallest chunk: 512 slots for integer caches, 64 for float ones
     small = _desc(kvq, batch=1, n_kv_heads=4, head_dim=64, capacity=257, group_size=64)
-    assert kvq.kvq_chunk_tokens(small, 4, 257) == 256
+    assert kvq.kvq_chunk_tokens(small, 4, 257) == 512
     small_f = _desc(kvq, batch=1, n_kv_heads=4, head_dim=64, capacity=257, k_bits=16, v_bits=16)
     assert kvq.kvq_chunk_tokens(small_f, 4, 257) == 64
-    # integer caches: the chunk is not bounded by LDS; 2048 at 32K for 256 and
-    # for 128 units, 1024 for 64 units
+    # integer caches: the chunk is not bounded by LDS; the largest that gives
+    # >= 1024 workgroups: 2048 at 32K for 256, 128 and 64 units, 1024 at 8K for
+    # 128 units, 512 for a 1600-slot window over 256 units (and for 1K contexts)
     assert kvq.kvq_chunk_tokens(d, 32, 32768) == 2048
     d8 = _desc(kvq, batch=16, n_kv_heads=8, capacity=32768, k_bits=8, v_bits=4)
     assert kvq.kvq_chunk_tokens(d8, 32, 32768) == 2048
     d4 = _desc(kvq, batch=8, n_kv_heads=8, capacity=32768, k_bits=8, v_bits=4)
-    assert kvq.kvq_chunk_tokens(d4, 32, 32768) == 1024
+    assert kvq.kvq_chunk_tokens(d4, 32, 32768) == 2048
+    d8k = _desc(kvq, batch=16, n_kv_heads=8, capacity=8192, k_bits=8, v_bits=4)
+    assert kvq.kvq_chunk_tokens(d8k, 32, 8192) == 1024
+    win = _desc(kvq, batch=32, n_kv_heads=8, capacity=1600, k_bits=4, v_bits=4, n_anchor=64, window=1536)
+    assert kvq.kvq_chunk_tokens(win, 32, 32768) == 512
+    tl = _desc(kvq, batch=8, n_kv_heads=16, capacity=1024)
+    assert kvq.kvq_chunk_tokens(tl, 16, 1024) == 512
+    # 32-value scale groups at G = 4 (57 KB of LDS): the same choice
+    g32 = _desc(kvq, batch=32, n_kv_heads=8, capacity=32768, k_bits=4, v_bits=4, group_size=32)
+    assert kvq.kvq_chunk_tokens(g32, 32, 32768) == 2048
 
 
 def test_binding_has_no_fallback(kvq, monkeypatch, tmp_path):
