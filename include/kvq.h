@@ -178,7 +178,10 @@ int kvq_cache_sizes(const kvq_cache *c, size_t *k_codes_bytes, size_t *v_codes_b
  * positions older than the call's last row) is not stored, so one call with
  * n_new rows leaves the cache exactly as n_new single-row calls would.
  * n_new == 0 is a no-op.  Rows written by one call must not be read by
- * kernels running concurrently on another stream.
+ * kernels running concurrently on another stream.  One launch: a row-wise
+ * kernel, or, for n_new >= 64 rows into an 8/4-bit cache without a window
+ * and with per-head or group scales (a prompt's prefill), a kernel over
+ * 64-slot tiles that stores the same bytes.
  */
 int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n_new,
                const int32_t *start_pos, void *stream);
@@ -217,8 +220,17 @@ int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n
  *                and C chunks: float ml[P][C][2] = (m, l) at offset 0, then
  *                float acc[P][C][head_dim] at offset round_up(8*P*C, 256);
  *                with 8/4-bit keys, scratch for the query's fixed-point form
- *                follows.  An empty chunk has m = -inf, l = 0, acc = 0.
- * Results are deterministic: no atomics, fixed chunk partition and order.
+ *                and one int32 ticket counter per (sequence, KV head) for
+ *                kvq_decode_step follow.  An empty chunk has m = -inf, l = 0,
+ *                acc = 0.
+ * Results are deterministic: the chunk partition and the merge order are
+ * fixed (kvq_decode_step's in-kernel merge takes an atomic ticket only to
+ * decide which workgroup merges, not in what order).
+ *
+ * kvq_chunk_tokens() returns the library's chunk: the largest power of two
+ * <= 2048 slots that still gives >= 1024 workgroups (sequences x KV heads x
+ * chunks), at least 512, for 8/4-bit caches; >= 2048 workgroups, at least
+ * 64 slots and within the LDS budget, for 16/32-bit caches.
  */
 int kvq_chunk_tokens(const kvq_cache *c, int n_q_heads, int max_seq_len);
 
