@@ -284,6 +284,29 @@ __global__ __launch_bounds__(APPEND_THREADS) void append_kernel(AppendParams p)
 // ------------------------------------------------------------------------
 constexpr int TILE_ROWS = 64;
 
+// Maximum over aligned groups of `lanes` (8, 16 or 32) lanes of values >= 0,
+// in every lane of the group.  Non-negative floats order like their bit
+// patterns, so an integer max is exact; inside a 16-lane row DPP steps
+// (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror)
+// leave each lane with its 2-, 4-, 8- and 16-lane maximum.  For 32 lanes,
+// v_permlane16_swap with v as both operands returns (v with its odd rows
+// replaced by the even rows below them, v with its even rows replaced by
+// the odd rows above them): their max is max(v[i], v[i ^ 16]) in every lane.
+// All 64 lanes must be active.
+__device__ __forceinline__ float group_max_abs(float a, int lanes)
+{
+    int v = __float_as_int(a);
+    v = max(v, dpp_i<0xB1, 0xF, true>(0, v));
+    v = max(v, dpp_i<0x4E, 0xF, true>(0, v));
+    v = max(v, dpp_i<0x141, 0xF, true>(0, v));
+    if (lanes >= 16) v = max(v, dpp_i<0x140, 0xF, true>(0, v));
+    if (lanes >= 32) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        v = max((int)r[0], (int)r[1]);
+    }
+    return __int_as_float(v);
+}
+
 template <int HD, int BITS>
 __device__ __forceinline__ void append_tile(const AppendParams &p, int tile, int bh, int side)
 {
@@ -324,8 +347,8 @@ __device__ __forceinline__ void append_tile(const AppendParams &p, int tile, int
         const int e = k * 256 + tid, r = e / LPR, c = 4 * (e % LPR);
         const float x[4] = {__uint_as_float(raw[k].x), __uint_as_float(raw[k].y), __uint_as_float(raw[k].z),
                             __uint_as_float(raw[k].w)};
-        float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
-        for (int m = 1; m < g / 4; m <<= 1) amax = fmaxf(amax, shfl_xor(amax, m));   // the group's lanes
+        const float amax = group_max_abs(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))),
+                                         g / 4);
         const uint16_t sh = scale_bits_from_amax(amax, qmax);
         const float sc = f16_bits_to_f32(sh), rs = code_rcp(sc);
         const int t = t0 + r;
