@@ -172,10 +172,15 @@ __device__ __forceinline__ void qprep_block(const float *__restrict__ q, int32_t
     // unit = b * Hkv + kvh
     const float *qh = q + (size_t)unit * G * HD;         // query heads unit*G .. unit*G+G-1
     __shared__ float amax[G];
+    __shared__ float qv[G * HD];                         // q, read from memory once
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int h = wave; h < G; h += 4) {
         float a = 0.0f;
-        for (int c = lane; c < HD; c += 64) a = fmaxf(a, fabsf(qh[h * HD + c]));
+        for (int c = lane; c < HD; c += 64) {
+            const float v = qh[h * HD + c];
+            qv[h * HD + c] = v;
+            a = fmaxf(a, fabsf(v));
+        }
         a = wave_max(a);
         if (lane == 0) amax[h] = a;
     }
@@ -189,7 +194,7 @@ __device__ __forceinline__ void qprep_block(const float *__restrict__ q, int32_t
         for (int j = 0; j < ND; j++) d[j] = 0;
 #pragma unroll
         for (int e = 0; e < CPC; e++) {
-            int qi = (int)fminf(fmaxf(rintf(qh[h * HD + col * CPC + e] * inv), -(float)Q_RANGE), (float)Q_RANGE);
+            int qi = (int)fminf(fmaxf(rintf(qv[h * HD + col * CPC + e] * inv), -(float)Q_RANGE), (float)Q_RANGE);
 #pragma unroll
             for (int j = 0; j < ND; j++) {
                 const int half = 1 << (BITS - 1), mask = (1 << BITS) - 1;
