@@ -105,7 +105,12 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
     out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     pos = positions([w.n_pos - 1] * w.batch)
     lens = positions([w.n_pos] * w.batch)
-    scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if flush else None   # 1 GiB > 256 MB MALL
+    # MALL scrub: a 1 GiB read (> the 256 MB MALL) before each step evicts the
+    # cache's lines with clean ones, so the step reads cold data and pays for
+    # no write-back of the scrub itself (a 1 GiB write would leave the MALL
+    # full of dirty lines to be written back inside the timed step)
+    scrub = torch.ones(1 << 28, dtype=torch.float32, device="cuda") if flush else None
+    scrub_out = torch.empty((), dtype=torch.float32, device="cuda") if flush else None
     stream = torch.cuda.current_stream()
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps * w.n_layers)]
@@ -114,7 +119,7 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
         # the whole hot path of a decode step: one call per layer
         for cache, k_last, v_last, q in layers:
             if scrub is not None:
-                scrub.zero_()
+                torch.sum(scrub, dim=0, out=scrub_out)
             kvq.kvq_decode_step(cache, k_last, v_last, 1, pos, q, w.n_q_heads, lens, max_len, 0.0, ch, out, ws,
                                 ws_bytes, st)
 
@@ -123,7 +128,7 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
         for li, (cache, k_last, v_last, q) in enumerate(layers):
             e = ev[record * w.n_layers + li]
             if scrub is not None:
-                scrub.zero_()
+                torch.sum(scrub, dim=0, out=scrub_out)
             e[0].record(st)
             kvq.kvq_append(cache, k_last, v_last, 1, pos, st)
             e[1].record(st)
@@ -230,7 +235,7 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
         f"{res['tokens_per_s']:.0f} tok/s; 1-step graph {(ms_step_graph1 or 0) * 1e3:.1f} us, eager "
         f"{ms_step_eager * 1e3:.1f} us); split {t_split_loop * 1e3:.1f} us = {res['split_GBps']:.0f} GB/s "
         f"({res['split_pct_of_peak']:.1f}% of peak); append {t_app * 1e3:.1f} us, combine {t_comb * 1e3:.1f} us")
-    del layers, ws, out, scrub
+    del layers, ws, out, scrub, scrub_out
     torch.cuda.empty_cache()
     return res
 
