@@ -149,9 +149,13 @@ int auto_chunk(const kvq_cache *c, int n_q_heads, int max_seq_len)
     const int G = n_q_heads / c->n_kv_heads;
     const long long units = (long long)c->batch * c->n_kv_heads;
     const int L = max_len_of(c, max_seq_len);
-    // The largest chunk of at most 2048 slots that fits the LDS budget and
-    // still gives enough workgroups; when no chunk does, the smallest one.
-    // Float caches: >= 8 workgroups per CU over 256 CUs, at least 64 slots.
+    // The largest chunk of at most 2048 slots (1024 for float caches) that
+    // fits the LDS budget and still gives enough workgroups; when no chunk
+    // does, the smallest one.
+    // Float caches: >= 8 workgroups per CU over 256 CUs, at least 64 slots;
+    // at most 1024, where a chunk's scores take 16 KB of LDS at G = 4 and 6
+    // workgroups fit a CU (2048: 4; FP16 at 32K ran 701 us at 1024 against
+    // 777 us at 2048).
     // Integer caches: >= one round of 4 workgroups per CU (1024), at least
     // 512 slots: their workgroups carry a fixed start (query digits, first
     // tile) and final merge, so fewer, longer ones win once the chip holds
@@ -163,7 +167,7 @@ int auto_chunk(const kvq_cache *c, int n_q_heads, int max_seq_len)
     const bool q = quant_modes(c);
     const int smallest = q ? 512 : 64;
     const long long want = q ? 1024 : 2048;
-    for (int ch = 2048; ch >= smallest; ch >>= 1) {
+    for (int ch = q ? 2048 : 1024; ch >= smallest; ch >>= 1) {
         // (an integer cache's LDS does not depend on the chunk)
         if (!q && lds_bytes(c, G, ch) > kAutoLds) continue;
         if (units * ((L + ch - 1) / ch) >= want) return ch;

@@ -229,8 +229,9 @@ int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n
  *
  * kvq_chunk_tokens() returns the library's chunk: the largest power of two
  * <= 2048 slots that still gives >= 1024 workgroups (sequences x KV heads x
- * chunks), at least 512, for 8/4-bit caches; >= 2048 workgroups, at least
- * 64 slots and within the LDS budget, for 16/32-bit caches.
+ * chunks), at least 512, for 8/4-bit caches; at most 1024, >= 2048
+ * workgroups, at least 64 slots and within the LDS budget, for 16/32-bit
+ * caches.
  */
 int kvq_chunk_tokens(const kvq_cache *c, int n_q_heads, int max_seq_len);
 

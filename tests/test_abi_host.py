@@ -329,6 +329,11 @@ def test_workspace_and_chunks(kvq):
     # 32-value scale groups at G = 4 (57 KB of LDS): the same choice
     g32 = _desc(kvq, batch=32, n_kv_heads=8, capacity=32768, k_bits=4, v_bits=4, group_size=32)
     assert kvq.kvq_chunk_tokens(g32, 32, 32768) == 2048
+    # float caches: at most 1024 slots (32K, 256 units), >= 2048 workgroups (8K, 128 units: 512)
+    f32k = _desc(kvq, batch=32, n_kv_heads=8, capacity=32768, k_bits=16, v_bits=16)
+    assert kvq.kvq_chunk_tokens(f32k, 32, 32768) == 1024
+    f8k = _desc(kvq, batch=16, n_kv_heads=8, capacity=8192, k_bits=16, v_bits=16)
+    assert kvq.kvq_chunk_tokens(f8k, 32, 8192) == 512
 
 
 def test_binding_has_no_fallback(kvq, monkeypatch, tmp_path):
