@@ -139,6 +139,32 @@ def test_32k_paged(oq, w, mode):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("kb,vb", [(4, 4), (8, 8), (16, 16)])
+def test_maximum_units(oq, kb, vb):
+    """The largest grid the library launches: 8191 sequences x 8 KV heads =
+    65528 (sequence, KV head) units (the limit is 65535), a 64-slot context
+    appended in one bulk call and decoded; sampled sequences against the
+    oracle, codes bit for bit."""
+    kvq = need_gpu()
+    import torch
+    from workloads.device import decode, positions
+    B, H, G, HD, n = 8191, 8, 1, 64, 64
+    gen = torch.Generator(device="cuda").manual_seed(77 + kb)
+    K = torch.randn((B, H, n, HD), device="cuda", generator=gen)
+    V = torch.randn((B, H, n, HD), device="cuda", generator=gen)
+    q = torch.randn((B, H * G, HD), device="cuda", generator=gen)
+    cache = kvq.alloc_cache(B, H, HD, n, kb, vb, HD)
+    kvq.kvq_append(cache, K, V, n, positions([0] * B))
+    out = decode(cache, q, H * G, positions([n] * B), n).cpu().numpy()
+    for b in (0, 4095, B - 1):
+        Kb, Vb, qb = K[b].cpu().numpy(), V[b].cpu().numpy(), q[b].cpu().numpy()
+        check_codes(oq, cache.sequence(b), Kb[None], Vb[None], linear_slots(n, n))
+        want = oq.decode_step(kb, vb, HD, 0, 0, Kb, Vb, qb, 1.0 / np.sqrt(HD))
+        assert_close(out[b], want, f"max units kb={kb} vb={vb} b={b}")
+    del cache, K, V
+    torch.cuda.empty_cache()
+
+
 def test_k4v4_window(oq):
     w = wl.K4V4_WINDOW
     _run(oq, w, w.modes, sample_b=(0, 13, 31))
