@@ -165,6 +165,33 @@ def test_maximum_units(oq, kb, vb):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("kb,vb", [(4, 4), (8, 4), (16, 16)])
+def test_million_position_context(oq, kb, vb):
+    """One sequence and KV head with 2^20 positions (4 query heads): a bulk
+    append of the whole context, then 1024 chunks of 1024 slots (2048 of 512
+    for fp16) merged by the combine; the output against the oracle, codes
+    bit for bit on 2000 sampled slots."""
+    kvq = need_gpu()
+    import torch
+    from workloads.device import decode, positions, to_device
+    B, H, G, HD, n = 1, 1, 4, 128, 1 << 20
+    rng = np.random.default_rng(99 + kb)
+    K = rng.standard_normal((B, H, n, HD), dtype=np.float32)
+    V = rng.standard_normal((B, H, n, HD), dtype=np.float32)
+    q = rng.standard_normal((B, H * G, HD), dtype=np.float32)
+    cache = kvq.alloc_cache(B, H, HD, n, kb, vb, HD)
+    kvq.kvq_append(cache, to_device(K), to_device(V), n, positions([0]))
+    # >= 1024 workgroups for integer caches, >= 2048 for float ones
+    assert kvq.kvq_chunk_tokens(cache, H * G, n) == (1024 if kb < 16 else 512)
+    out = decode(cache, to_device(q), H * G, positions([n]), n).cpu().numpy()
+    sample = {int(t): int(t) for t in np.unique(np.concatenate([rng.integers(0, n, 1990), np.arange(5), n - 5 + np.arange(5)]))}
+    check_codes(oq, cache, K, V, sample)
+    want = oq.decode_step(kb, vb, HD, 0, 0, K[0], V[0], q[0], 1.0 / np.sqrt(HD))
+    assert_close(out[0], want, f"1M positions kb={kb} vb={vb}")
+    del cache
+    torch.cuda.empty_cache()
+
+
 def test_k4v4_window(oq):
     w = wl.K4V4_WINDOW
     _run(oq, w, w.modes, sample_b=(0, 13, 31))
