@@ -283,6 +283,80 @@ def prefill(w, mode, rows_per_call: int = 4096, reps: int = 3, log=print) -> dic
     return res
 
 
+def generation_loop(w, mode, reps: int = 5, log=print) -> dict:
+    """A generation loop on one sequence (the mni-ml-like workload): the
+    prompt appended in one call, then one kvq_decode_step per generated
+    token (append its row, attend with its query), all rows and queries
+    already in device memory.  Timed as eager calls and as one HIP graph of
+    the whole loop; tokens/s = generated tokens / loop time."""
+    import torch
+
+    import decode_attention_quantized_kvq_amd as kvq
+    from workloads.device import positions, to_device
+    cache = kvq.alloc_cache(w.batch, w.n_kv_heads, w.head_dim, w.capacity, mode.k_bits, mode.v_bits,
+                            _group(mode, w))
+    k_rows, v_rows = wl_rows(w, 0)
+    kd, vd = to_device(k_rows[None]), to_device(v_rows[None])      # [1][Hkv][n_pos][HD]
+    kvq.kvq_append(cache, kd[:, :, :w.prompt].contiguous(), vd[:, :, :w.prompt].contiguous(), w.prompt,
+                   positions([0]))
+    n_gen = w.n_pos - w.prompt
+    rows = [(kd[:, :, p:p + 1].contiguous(), vd[:, :, p:p + 1].contiguous()) for p in range(w.prompt, w.n_pos)]
+    qs = [to_device(wl_query(w, s)[None]) for s in range(n_gen)]
+    pos = [positions([w.prompt + s]) for s in range(n_gen)]
+    lens = [positions([w.prompt + s + 1]) for s in range(n_gen)]
+    ws_bytes = kvq.kvq_workspace_bytes(cache, w.n_q_heads, w.capacity, 0)
+    ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")
+    out = torch.empty((1, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+
+    def loop(st):
+        for s_ in range(n_gen):
+            kvq.kvq_decode_step(cache, rows[s_][0], rows[s_][1], 1, pos[s_], qs[s_], w.n_q_heads, lens[s_],
+                                w.capacity, 0.0, 0, out, ws, ws_bytes, st)
+
+    stream = torch.cuda.current_stream()
+    loop(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        loop(stream)
+    torch.cuda.synchronize()
+    eager_s = (time.perf_counter() - t0) / reps
+    cs = torch.cuda.Stream()
+    cs.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cs):
+        loop(cs)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    graph_s = (time.perf_counter() - t0) / reps
+    res = {"workload": w.name, "mode": mode.name, "prompt": w.prompt, "generated": n_gen,
+           "cache_bytes_per_token": kvq.kvq_bytes_per_token(mode.k_bits, mode.v_bits, w.n_kv_heads, w.head_dim,
+                                                            _group(mode, w)),
+           "us_per_token_eager": eager_s / n_gen * 1e6, "us_per_token_graph": graph_s / n_gen * 1e6,
+           "tokens_per_s_eager": n_gen / eager_s, "tokens_per_s_graph": n_gen / graph_s}
+    log(f"[bench] generation {w.name} {mode.name}: {n_gen} tokens after a {w.prompt}-token prompt, "
+        f"{res['tokens_per_s_graph']:.0f} tok/s in one graph ({res['us_per_token_graph']:.1f} us/token), "
+        f"{res['tokens_per_s_eager']:.0f} tok/s eager; cache {res['cache_bytes_per_token']} B/token")
+    del g, cache, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def wl_rows(w, layer: int):
+    """K and V rows of sequence 0 of `layer`: ([Hkv][n_pos][HD], [Hkv][n_pos][HD])."""
+    import workloads as wl
+    return wl.rows(w, wl.K_STREAM, layer, 0, w.n_pos), wl.rows(w, wl.V_STREAM, layer, 0, w.n_pos)
+
+
+def wl_query(w, step: int):
+    import workloads as wl
+    return wl.query(w, 0, 0, step)
+
+
 def read_probe(log=print, gib: int = 2, launches: int = 50) -> dict:
     """The bandwidth a plain read stream reaches on this device
     (kvq_read_probe over `gib` GiB, larger than the 256 MB MALL), after a
@@ -531,6 +605,7 @@ def main() -> int:
                               log=log, layer_modes=per_layer))
         for m in wl.TINY.modes:
             extra.append(run_mode(wl.TINY, m, args.steps, args.warmup, args.chunk, log=log))
+    gens = [generation_loop(wl.MNIML, m, log=log) for m in wl.MNIML.modes] if args.modes == "all" else []
     prefills = []
     if args.modes in ("paged", "all"):
         prefills = [prefill(wl.K4V4_32K, wl.K4V4, log=log), prefill(wl.K8V4_32K, wl.K8V4, log=log),
@@ -578,6 +653,8 @@ def main() -> int:
                                                    for k, v in r.items()} for r in [head] + extra},
         "prefill": {f"{r['workload']}/{r['mode']}": {k: (round(v, 4) if isinstance(v, float) else v)
                                                      for k, v in r.items()} for r in prefills},
+        "generation": {f"{r['workload']}/{r['mode']}": {k: (round(v, 4) if isinstance(v, float) else v)
+                                                        for k, v in r.items()} for r in gens},
     }
     print(json.dumps(line), flush=True)
     return 0
