@@ -149,6 +149,29 @@ __device__ __forceinline__ void store_codes(uint8_t *codes, size_t unit, int cap
     }
 }
 
+// Maximum over aligned groups of `lanes` (1, 2, 4, ..., 32) lanes of values >= 0,
+// in every lane of the group.  Non-negative floats order like their bit
+// patterns, so an integer max is exact; inside a 16-lane row DPP steps
+// (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror)
+// leave each lane with its 2-, 4-, 8- and 16-lane maximum.  For 32 lanes,
+// v_permlane16_swap with v as both operands returns (v with its odd rows
+// replaced by the even rows below them, v with its even rows replaced by
+// the odd rows above them): their max is max(v[i], v[i ^ 16]) in every lane.
+// All 64 lanes must be active.
+__device__ __forceinline__ float group_max_abs(float a, int lanes)
+{
+    int v = __float_as_int(a);
+    if (lanes >= 2) v = max(v, dpp_i<0xB1, 0xF, true>(0, v));
+    if (lanes >= 4) v = max(v, dpp_i<0x4E, 0xF, true>(0, v));
+    if (lanes >= 8) v = max(v, dpp_i<0x141, 0xF, true>(0, v));
+    if (lanes >= 16) v = max(v, dpp_i<0x140, 0xF, true>(0, v));
+    if (lanes >= 32) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        v = max((int)r[0], (int)r[1]);
+    }
+    return __int_as_float(v);
+}
+
 // One block of the append grid: x = batch * n_new rows, y = passes over the
 // row (groups inside a head) or 1 (per-row scale), z = side (0 = K, 1 = V).
 // 256 threads; block-uniform early exits only.
@@ -251,9 +274,7 @@ __device__ __forceinline__ void append_block(const AppendParams &p, int bx, int 
 #pragma unroll
     for (int j = 0; j < 8; j++)
         amax = fmaxf(amax, fabsf(x[j]));
-    const int lanes = p.group / APPEND_ELEMS;
-    for (int m = 1; m < lanes; m <<= 1)
-        amax = fmaxf(amax, shfl_xor(amax, m));
+    amax = group_max_abs(amax, p.group / APPEND_ELEMS);
     const uint16_t sh = scale_bits_from_amax(amax, qmax);
     const float s = f16_bits_to_f32(sh);
     uint32_t w0, w1;
@@ -283,29 +304,6 @@ __global__ __launch_bounds__(APPEND_THREADS) void append_kernel(AppendParams p)
 // z = side.
 // ------------------------------------------------------------------------
 constexpr int TILE_ROWS = 64;
-
-// Maximum over aligned groups of `lanes` (8, 16 or 32) lanes of values >= 0,
-// in every lane of the group.  Non-negative floats order like their bit
-// patterns, so an integer max is exact; inside a 16-lane row DPP steps
-// (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror)
-// leave each lane with its 2-, 4-, 8- and 16-lane maximum.  For 32 lanes,
-// v_permlane16_swap with v as both operands returns (v with its odd rows
-// replaced by the even rows below them, v with its even rows replaced by
-// the odd rows above them): their max is max(v[i], v[i ^ 16]) in every lane.
-// All 64 lanes must be active.
-__device__ __forceinline__ float group_max_abs(float a, int lanes)
-{
-    int v = __float_as_int(a);
-    v = max(v, dpp_i<0xB1, 0xF, true>(0, v));
-    v = max(v, dpp_i<0x4E, 0xF, true>(0, v));
-    v = max(v, dpp_i<0x141, 0xF, true>(0, v));
-    if (lanes >= 16) v = max(v, dpp_i<0x140, 0xF, true>(0, v));
-    if (lanes >= 32) {
-        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-        v = max((int)r[0], (int)r[1]);
-    }
-    return __int_as_float(v);
-}
 
 template <int HD, int BITS>
 __device__ __forceinline__ void append_tile(const AppendParams &p, int tile, int bh, int side)
