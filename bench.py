@@ -231,8 +231,9 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
         "split_bytes": split_bytes(w, mode0), "split_GBps": split_bytes(w, mode0) / (t_split_loop * 1e-3) / 1e9,
     }
     res["split_pct_of_peak"] = 100.0 * res["split_GBps"] / PEAK_HBM_GBS
+    g1s = f"{ms_step_graph1 * 1e3:.1f} us" if ms_step_graph1 is not None else "not timed (MALL scrubbed)"
     log(f"[bench] {name} {mode.name}: step {ms_step * 1e3:.1f} us ({res['step_GBps']:.0f} GB/s, "
-        f"{res['tokens_per_s']:.0f} tok/s; 1-step graph {(ms_step_graph1 or 0) * 1e3:.1f} us, eager "
+        f"{res['tokens_per_s']:.0f} tok/s; 1-step graph {g1s}, eager "
         f"{ms_step_eager * 1e3:.1f} us); split {t_split_loop * 1e3:.1f} us = {res['split_GBps']:.0f} GB/s "
         f"({res['split_pct_of_peak']:.1f}% of peak); append {t_app * 1e3:.1f} us, combine {t_comb * 1e3:.1f} us")
     del layers, ws, out, scrub, scrub_out
