@@ -441,9 +441,10 @@ def cpu_baseline(w, mode, log=print, budget_s: float = 12.0) -> dict:
     }
 
 
-def traffic_record(w, mode):
-    """HBM bytes per launch of the split kernel from the committed counter
-    summary, if it was taken on the kernel sources as they are now."""
+def traffic_record(key: str):
+    """HBM bytes per launch of the split kernel of workload/mode `key` from
+    the committed counter summary, if it was taken on the kernel sources as
+    they are now."""
     import hashlib
     path = ROOT / "profiles" / "traffic.json"
     if not path.exists():
@@ -452,7 +453,7 @@ def traffic_record(w, mode):
     h = hashlib.sha256()
     for f in rec.get("sources", []):
         h.update((ROOT / f).read_bytes())
-    entry = rec.get("workloads", {}).get(f"{w.name}/{mode.name}")
+    entry = rec.get("workloads", {}).get(key)
     if entry is None or h.hexdigest() != rec.get("sha256"):
         return None
     return entry
@@ -463,12 +464,20 @@ TRAFFIC_SOURCES = ["decode_attention_quantized_kvq_amd/csrc/kvq_decode_quant.hpp
                    "decode_attention_quantized_kvq_amd/csrc/kvq.hip"]
 
 
-def record_traffic(fetch_csv: str, write_csv: str, log=print) -> int:
-    """Turn the two counter runs of --probe-traffic into profiles/traffic.json:
-    each counter scaled by what it reads for the 1 GiB copy of the same run,
-    averaged over the three split launches."""
+PROBE_WORKLOADS = {"k4v4-32k": ("K4V4_32K", "K4V4", "decode_quant_kernel<4,4,128,4,1,false>"),
+                   "k8v4-32k": ("K8V4_32K", "K8V4", "decode_quant_kernel<8,4,128,4,1,false>")}
+
+
+def record_traffic(fetch_csv: str, write_csv: str, workload: str = "k4v4-32k", log=print) -> int:
+    """Turn the two counter runs of --probe-traffic into the workload's entry
+    of profiles/traffic.json: each counter scaled by what it reads for the
+    1 GiB copy of the same run, averaged over the three split launches.
+    Entries of other workloads are kept while the kernel sources are those
+    they were taken on."""
     import csv
     import hashlib
+
+    import workloads as wl
 
     def per_kernel(path, counter):
         vals = {}
@@ -478,51 +487,58 @@ def record_traffic(fetch_csv: str, write_csv: str, log=print) -> int:
             vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)  # KiB -> bytes
         return vals
 
-    w, mode = __import__("workloads").K4V4_32K, __import__("workloads").K4V4
-    out = {}
+    wname, mname, kernel = PROBE_WORKLOADS[workload]
+    w, mode = getattr(wl, wname), getattr(wl, mname)
+    counters = {}
     for name, path, counter, truth in (("fetch", fetch_csv, "FETCH_SIZE", 1 << 30), ("write", write_csv, "WRITE_SIZE", 1 << 30)):
         vals = per_kernel(path, counter)
         copy = max(v for k, v_ in vals.items() if "copyBuffer" in k or "copy" in k.lower() for v in v_)
         factor = truth / copy
         dec = [v for k, v_ in vals.items() if "decode_quant_kernel" in k for v in v_]
         prep = [v for k, v_ in vals.items() if "qprep_kernel" in k for v in v_]
-        out[name] = {"counter": counter, "copy_reads": copy, "factor": factor,
-                     "decode_raw": sum(dec) / len(dec), "prep_raw": sum(prep) / len(prep) if prep else 0.0}
+        counters[name] = {"counter": counter, "copy_reads": copy, "factor": factor,
+                          "decode_raw": sum(dec) / len(dec), "prep_raw": sum(prep) / len(prep) if prep else 0.0}
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES:
         h.update((ROOT / f).read_bytes())
-    dec_bytes = out["fetch"]["decode_raw"] * out["fetch"]["factor"] + out["write"]["decode_raw"] * out["write"]["factor"]
-    rec = {
+    path = ROOT / "profiles" / "traffic.json"
+    rec = json.loads(path.read_text()) if path.exists() else {}
+    if rec.get("sha256") != h.hexdigest():
+        rec = {}
+    rec.update({
         "sources": TRAFFIC_SOURCES, "sha256": h.hexdigest(),
-        "method": "rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, of `python bench.py --probe-traffic`; "
-                  "each counter scaled by its reading for a 1 GiB device copy in the same run",
-        "counters": out,
-        "workloads": {f"{w.name}/{mode.name}": {
-            "kernel": "decode_quant_kernel<4,4,128,4,1,false>",
-            "bytes_per_launch": round(dec_bytes),
-            "fetch_bytes": round(out["fetch"]["decode_raw"] * out["fetch"]["factor"]),
-            "write_bytes": round(out["write"]["decode_raw"] * out["write"]["factor"]),
-            "algorithmic_bytes": split_bytes(w, mode),
-            "ratio_to_algorithmic": dec_bytes / split_bytes(w, mode),
-        }},
+        "method": "rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, of `python bench.py --probe-traffic "
+                  "--probe-workload <workload>`; each counter scaled by its reading for a 1 GiB device copy in "
+                  "the same run",
+    })
+    fetch = counters["fetch"]["decode_raw"] * counters["fetch"]["factor"]
+    write = counters["write"]["decode_raw"] * counters["write"]["factor"]
+    rec.setdefault("workloads", {})[f"{w.name}/{mode.name}"] = {
+        "kernel": kernel,
+        "bytes_per_launch": round(fetch + write),
+        "fetch_bytes": round(fetch),
+        "write_bytes": round(write),
+        "algorithmic_bytes": split_bytes(w, mode),
+        "ratio_to_algorithmic": (fetch + write) / split_bytes(w, mode),
+        "counters": counters,
     }
     (ROOT / "profiles").mkdir(exist_ok=True)
-    (ROOT / "profiles" / "traffic.json").write_text(json.dumps(rec, indent=1) + "\n")
+    path.write_text(json.dumps(rec, indent=1) + "\n")
     log(json.dumps(rec["workloads"], indent=1))
     return 0
 
 
-def probe_traffic(chunk: int, log=print) -> int:
+def probe_traffic(chunk: int, workload: str = "k4v4-32k", log=print) -> int:
     """For a counter run (rocprofv3 --pmc FETCH_SIZE or WRITE_SIZE): a plain
     device copy of 1 GiB (the calibration), then three split-kernel launches
-    of the headline workload."""
+    of one 32K workload (the headline K4V4 one by default, or K8V4)."""
     import torch
 
     import decode_attention_quantized_kvq_amd as kvq
     import workloads as wl
     from workloads.device import fill, positions, queries
 
-    w, mode = wl.K4V4_32K, wl.K4V4
+    w, mode = {"k4v4-32k": (wl.K4V4_32K, wl.K4V4), "k8v4-32k": (wl.K8V4_32K, wl.K8V4)}[workload]
     cache = kvq.alloc_cache(w.batch, w.n_kv_heads, w.head_dim, w.capacity, mode.k_bits, mode.v_bits,
                             _group(mode, w), w.n_anchor, w.window)
     fill([cache], w, 0, w.n_pos)
@@ -554,14 +570,16 @@ def main() -> int:
                          "workloads in 256-slot pages and bulk prefill; all: every workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe-traffic", action="store_true",
-                    help="copy 1 GiB then launch the headline split kernel 3 times (for counter runs)")
+                    help="copy 1 GiB then launch the split kernel of --probe-workload 3 times (for counter runs)")
+    ap.add_argument("--probe-workload", choices=["k4v4-32k", "k8v4-32k"], default="k4v4-32k",
+                    help="the workload --probe-traffic launches and --record-traffic records")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from the two counter runs (CPU only)")
     ap.add_argument("--quiet", action="store_true")
     args = ap.parse_args()
 
     if args.record_traffic:
-        return record_traffic(*args.record_traffic)
+        return record_traffic(*args.record_traffic, args.probe_workload)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -580,7 +598,7 @@ def main() -> int:
     dev = torch.cuda.get_device_properties(0)
     log(f"[bench] device: {dev.name} ({dev.multi_processor_count} CUs)")
     if args.probe_traffic:
-        return probe_traffic(args.chunk, log=log)
+        return probe_traffic(args.chunk, args.probe_workload, log=log)
 
     head_w, head_m = wl.K4V4_32K, wl.K4V4
     head = run_mode(head_w, head_m, args.steps, args.warmup, args.chunk, log=log)
@@ -614,8 +632,12 @@ def main() -> int:
 
     probe = read_probe(log=log)
     cpu = None if args.no_cpu_baseline else cpu_baseline(head_w, head_m, log=log)
-    tr = traffic_record(head_w, head_m)
+    tr = traffic_record(f"{head_w.name}/{head_m.name}")
     traffic = None if tr is None else tr["bytes_per_launch"]
+    for r in [head] + extra:
+        # counted HBM bytes of the split kernel, where a counter run covers it
+        t = traffic_record(f"{r['workload']}/{r['mode']}") if r["page_size"] == 0 else None
+        r["split_traffic_bytes"] = None if t is None else t["bytes_per_launch"]
 
     line = {
         "metric": METRIC,
