@@ -4,6 +4,8 @@ lengths, appends in pieces and the fused decode step, drawn together so that
 combinations the targeted tests do not spell out are run too.  Each draw is
 checked against the oracle (outputs within tolerance; stored codes bit for
 bit where the cache is contiguous)."""
+import os
+
 import numpy as np
 import pytest
 
@@ -46,7 +48,8 @@ def draw(seed):
                 n_pieces=n_pieces, fused=bool(rng.random() < 0.5), rng=rng)
 
 
-@pytest.mark.parametrize("seed", range(160))
+# KVQ_RANDOM_SEEDS sets the number of draws (1200 run in about 20 s)
+@pytest.mark.parametrize("seed", range(int(os.environ.get("KVQ_RANDOM_SEEDS", "1200"))))
 def test_random_configuration(oq, seed):
     kvq = need_gpu()
     import torch
