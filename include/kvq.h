@@ -280,12 +280,13 @@ int kvq_decode_attn(const kvq_cache *c, const float *q, int n_q_heads, const int
  * kvq_decode_attn(c, q, ..., stream), with the same arguments, rules and
  * results, bit for bit.  On an 8/4-bit cache the append and the query's
  * fixed-point preparation share the first launch, then the split kernel,
- * then the combine; when a sequence's context spans at most 4 chunks the
- * split kernel's last workgroup per (sequence, KV head) merges the partials
- * itself (same arithmetic, one launch fewer for short contexts, where the
- * launches dominate).  On a 16/32-bit cache: append, split, combine.  The
- * workspace holds the merge's ticket counters, which the first launch
- * zeroes each step (no memset, so the step can be captured in a graph).
+ * then the combine; when max_seq_len (capped at the capacity) spans at
+ * most 4 chunks, the split kernel's last workgroup per (sequence, KV head)
+ * merges the partials itself (same arithmetic, one launch fewer for short
+ * contexts, where the launches dominate).  On a 16/32-bit cache: append,
+ * split, combine.  The workspace holds the merge's ticket counters, which
+ * the first launch zeroes each step (no memset, so the step can be captured
+ * in a graph).
  * Every argument is checked before anything is enqueued; on an error
  * nothing is.
  */
