@@ -177,7 +177,7 @@ int auto_chunk(const kvq_cache *c, int n_q_heads, int max_seq_len)
 
 using FloatFn = void (*)(FloatParams);
 using QuantFn = void (*)(QuantParams);
-using PrepFn = void (*)(const float *, int32_t *, float *, float, int *);
+using PrepFn = void (*)(const float *, int32_t *, float *, int32_t *, float, int *);
 
 template <int B, int HD, bool PG>
 FloatFn pick_float_g(int G)
@@ -263,7 +263,7 @@ PrepFn pick_prep(int kb, int hd, int G)
     return hd == 64 ? pick_prep_g<8, 64>(G) : pick_prep_g<8, 128>(G);
 }
 
-using StepPrepFn = void (*)(AppendParams, int, int, const float *, int32_t *, float *, float, int *);
+using StepPrepFn = void (*)(AppendParams, int, int, const float *, int32_t *, float *, int32_t *, float, int *);
 
 template <int KB, int HD>
 StepPrepFn pick_step_g(int G)
@@ -286,9 +286,10 @@ StepPrepFn pick_step(int kb, int hd, int G)
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace: ml [P][C][2] | acc [P][C][HD] | (quantized keys) query digits
-// [B*Hkv][K_COLS][ND][G] int32 | query scales [P] float.
+// [B*Hkv][ND+1][K_COLS][G] int32 | query scales [P] float | extra-digit
+// flags [B*Hkv] int32 | ticket counters [B*Hkv] int32.
 struct WsLayout {
-    size_t ml, acc, qdig, qsc, cnt, total;
+    size_t ml, acc, qdig, qsc, qflag, cnt, total;
 };
 
 WsLayout ws_layout(int batch, int n_q_heads, int head_dim, int n_chunks, int n_kv_heads, int k_bits)
@@ -298,16 +299,19 @@ WsLayout ws_layout(int batch, int n_q_heads, int head_dim, int n_chunks, int n_k
     w.ml = 0;
     w.acc = align256(P * n_chunks * 2 * sizeof(float));
     size_t off = w.acc + P * n_chunks * head_dim * sizeof(float);
-    w.qdig = w.qsc = w.cnt = 0;
+    w.qdig = w.qsc = w.qflag = w.cnt = 0;
     if (quantized(k_bits)) {
+        const size_t units = (size_t)batch * n_kv_heads;
         const size_t cols = (size_t)head_dim * k_bits / 32;
-        const size_t nd = k_bits == 4 ? 4 : 2;
+        const size_t nd = (k_bits == 4 ? 4 : 2) + 1;   // Horner digits and the extra low one
         w.qdig = align256(off);
-        off = w.qdig + (size_t)batch * n_kv_heads * cols * nd * (n_q_heads / n_kv_heads) * 4;
+        off = w.qdig + units * cols * nd * (n_q_heads / n_kv_heads) * 4;
         w.qsc = align256(off);
         off = w.qsc + P * sizeof(float);
+        w.qflag = align256(off);
+        off = w.qflag + units * sizeof(int32_t);
         w.cnt = align256(off);                       // the fused step's ticket counters
-        off = w.cnt + (size_t)batch * n_kv_heads * sizeof(int);
+        off = w.cnt + units * sizeof(int);
     }
     w.total = off;
     return w;
@@ -578,6 +582,7 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
     if (!fn || !prep || !sprep) return fail(KVQ_ERR_BITS, "no kernel for k_bits=%d v_bits=%d", c->k_bits, c->v_bits);
     int32_t *qdig = reinterpret_cast<int32_t *>(ws + wl.qdig);
     float *qsc = reinterpret_cast<float *>(ws + wl.qsc);
+    int32_t *qflag = reinterpret_cast<int32_t *>(ws + wl.qflag);
     if (out && phases != (PHASE_PREP | PHASE_SPLIT)) return fail(KVQ_ERR_ARG, "a fused combine needs both phases");
     int *cnt = out ? reinterpret_cast<int *>(ws + wl.cnt) : nullptr;
     const unsigned units = (unsigned)(c->batch * c->n_kv_heads);
@@ -587,9 +592,9 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
         if (ap && ap_grid.x > 0) {
             const unsigned n_app = ap_grid.x * ap_grid.y * 2;
             hipLaunchKernelGGL(sprep, dim3(n_app + units), dim3(256), 0, st_, *ap, (int)ap_grid.x, (int)ap_grid.y, q,
-                               qdig, qsc, qk_scale, cnt);
+                               qdig, qsc, qflag, qk_scale, cnt);
         } else {
-            hipLaunchKernelGGL(prep, dim3(units), dim3(256), 0, st_, q, qdig, qsc, qk_scale, cnt);
+            hipLaunchKernelGGL(prep, dim3(units), dim3(256), 0, st_, q, qdig, qsc, qflag, qk_scale, cnt);
         }
         const int hs = hip_status("query prep launch");
         if (hs) return hs;
@@ -603,6 +608,7 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
     p.v_scales = static_cast<const uint16_t *>(c->v_scales);
     p.qdig = qdig;
     p.qsc = qsc;
+    p.qflag = qflag;
     p.seq_len = seq_len;
     p.ws_ml = reinterpret_cast<float *>(ws + wl.ml);
     p.ws_acc = reinterpret_cast<float *>(ws + wl.acc);

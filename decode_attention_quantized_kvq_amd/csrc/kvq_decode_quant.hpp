@@ -15,15 +15,22 @@
 //    split into balanced digits (four base-16 digits against int4 keys, two
 //    base-256 digits against int8 keys) so v_dot8_i32_i4 / v_dot4_i32_i8
 //    take the stored code words unchanged (digit-major Horner: one exact
-//    int32 sum per head and position);
-//  * the value weights w = 2^(z - max z) * s_v, per chunk, as
-//    w_int = rint(w * 32767 / max s_v) split into two unsigned bytes, so
-//    v_dot4_u32_u8 runs over four positions at once against value codes
-//    stored four positions interleaved and offset binary (code + 8 or
-//    code + 128, never negative); the offset's share, bias * sum(w), is
-//    subtracted once at the end.
-// Rounding happens only in q_int (|dq| <= s_q / 2) and in w_int
-// (|dw| <= max s_v / 65534); accumulation is exact in int32, then fp32.
+//    int32 sum per head and position).  When some head of a (sequence, KV
+//    head) has a channel beyond 5 times its rms (an outlier channel, which
+//    would leave the others few bits), the query also carries one low digit
+//    d = rint(14 (int4) or 254 (int8) * (q / s_q - q_int)) whose sum joins
+//    the score in float; either way |dq| <= max|q| / 60000 <= |q|_2 / 12000
+//    per channel, at most 8.3e-5 of |q|_2 in norm;
+//  * the value weights w = 2^(z - max z) * s_v of a sub-chunk, per head and
+//    scale group, as w_int = rint(w * 32767 / N), N the sub-chunk's largest
+//    w, split into two unsigned bytes, so v_dot4_u32_u8 runs over four
+//    positions at once against value codes stored four positions
+//    interleaved and offset binary (code + 8 or code + 128, never negative);
+//    the offset's share, bias * sum(w), is subtracted once at the end.
+// Rounding happens only in the query's digits and in w_int
+// (|dw| <= N / 65534, relative to the sub-chunk's own largest weight
+// whatever the spread of the value scales or of the softmax);
+// accumulation is exact in int32, then fp32.
 //
 // Workgroup = 4 waves = one context chunk of one (sequence, KV head); each
 // wave owns a quarter of the chunk and streams it in sub-chunks of 512
@@ -32,9 +39,11 @@
 // sub-chunk:
 //   1. keys, one lane per position: scores -> LDS; the query digits are
 //      wave-uniform and come from SGPRs (prepared per (sequence, KV head) by
-//      qprep_kernel); value scales -> LDS; the sub-chunk's maxima (DPP).
-//   2. weights, one lane per four positions: p = 2^(z - max), w_int packed
-//      four positions per word -> LDS (over the sub-chunk's scores).
+//      qprep_kernel); value scales -> LDS; the sub-chunk's score maxima (DPP).
+//   2. weights, one lane per four positions: p = 2^(z - max) and the
+//      products p * s_v, whose maximum per head and group (DPP) sets the
+//      fixed point; then w_int packed four positions per word -> LDS (over
+//      the sub-chunk's scores).
 //   3. values: a lane owns fixed byte positions (two channels) of every
 //      4-position group and accumulates v_dot4_u32_u8 over the sub-chunk's
 //      groups (int4: the even channel's nibbles and the whole bytes, even +
@@ -63,6 +72,10 @@ __host__ __device__ constexpr int qd_sub(int G, int vg)
     return G == 8 && vg >= 2 ? 128 : G * vg >= 8 ? 256 : 512;
 }
 constexpr int Q_RANGE = 30000;
+// the query's extra low digit: taken when max|q| > Q_OUTLIER * rms(q) for a
+// head of the unit; its base keeps |d| within the key width's signed digit
+constexpr float Q_OUTLIER = 5.0f;
+__host__ __device__ constexpr int qx_base(int KB) { return KB == 4 ? 14 : 254; }
 constexpr int QD_PF = 16;       // value group loads in flight per lane
 constexpr int W_RANGE = 32767;
 
@@ -70,7 +83,8 @@ template <int KB, int VB, int HD, int G> struct QT {
     static constexpr int K_ROW = HD * KB / 8;          // bytes per key row
     static constexpr int K_U4 = K_ROW / 16;            // 16-byte loads per key row
     static constexpr int K_COLS = K_ROW / 4;           // dwords per key row
-    static constexpr int ND = KB == 4 ? 4 : 2;         // query digits
+    static constexpr int ND = KB == 4 ? 4 : 2;         // query digits (Horner)
+    static constexpr int NDX = ND + 1;                 // digits stored: the Horner ones, then the extra low one
     static constexpr int DBASE = KB == 4 ? 16 : 256;   // digit base
     static constexpr int CPC = KB == 4 ? 8 : 4;        // channels per key dword
     static constexpr int V_ROW = HD * VB / 8;          // bytes per value row
@@ -91,8 +105,9 @@ struct QuantParams {
     const uint8_t *v_codes;    // [B][Hkv][cap4/4][V_ROW][4]  (4 positions interleaved per byte)
     const uint16_t *k_scales;
     const uint16_t *v_scales;
-    const int32_t *qdig;       // [B*Hkv][ND][K_COLS][G] packed query digits (digit-major)
+    const int32_t *qdig;       // [B*Hkv][ND + 1][K_COLS][G] packed query digits (digit-major; digit ND the extra low one)
     const float *qsc;          // [B*Hq]: s_q * softmax_scale * log2(e)
+    const int32_t *qflag;      // [B*Hkv]: 1 when the query carries its extra low digit
     const int32_t *seq_len;
     float *ws_ml;
     float *ws_acc;
@@ -159,42 +174,66 @@ __host__ __device__ inline QuantSmem quant_smem(int G, int HD, int vg)
 // into ND balanced digits; digit j of the channels of key dword `col` is
 // packed like the codes (int4: channel 8col+i in nibble i; int8: channel
 // 4col+i in byte i) at qdig[unit][j][col][h] (digit-major, the order the
-// decode kernel reads them in).
+// decode kernel reads them in).  When a head of the unit has
+// max|q| > 5 rms(q), digit ND holds d = rint(base * (q / s_q - q_int)) for
+// every head (base 14 or 254: |d| <= 7 or 127) and qflag[unit] = 1, else
+// digit ND is zero and qflag[unit] = 0.
 // ---------------------------------------------------------------------------
 template <int KB, int HD, int G>
 __device__ __forceinline__ void qprep_block(const float *__restrict__ q, int32_t *__restrict__ qdig,
-                                            float *__restrict__ qsc, float qk_scale, int unit, int *cnt)
+                                            float *__restrict__ qsc, int32_t *__restrict__ qflag, float qk_scale,
+                                            int unit, int *cnt)
 {
     constexpr int K_COLS = HD * KB / 32;
     constexpr int ND = KB == 4 ? 4 : 2;
     constexpr int CPC = KB == 4 ? 8 : 4;
     constexpr int BITS = KB == 4 ? 4 : 8;
+    constexpr int XMAX = (1 << (BITS - 1)) - 1;
     // unit = b * Hkv + kvh
     const float *qh = q + (size_t)unit * G * HD;         // query heads unit*G .. unit*G+G-1
     __shared__ float amax[G];
+    __shared__ int xflag;
     __shared__ float qv[G * HD];                         // q, read from memory once
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) xflag = 0;
+    __syncthreads();
     for (int h = wave; h < G; h += 4) {
-        float a = 0.0f;
+        float a = 0.0f, ss = 0.0f;
         for (int c = lane; c < HD; c += 64) {
             const float v = qh[h * HD + c];
             qv[h * HD + c] = v;
             a = fmaxf(a, fabsf(v));
+            ss = fmaf(v, v, ss);
         }
         a = wave_max(a);
-        if (lane == 0) amax[h] = a;
+        ss = wave_sum(ss);
+        if (lane == 0) {
+            amax[h] = a;
+            // max|q| > 5 rms(q): the 16-bit form would leave the other
+            // channels too few bits
+            if (a * a > Q_OUTLIER * Q_OUTLIER * (ss / (float)HD)) atomicOr(&xflag, 1);
+        }
     }
     __syncthreads();
+    const bool xq = xflag != 0;
+    constexpr float XB = (float)qx_base(KB);
     for (int i = tid; i < K_COLS * G; i += 256) {
         const int col = i / G, h = i - col * G;
         const float sq = amax[h] / (float)Q_RANGE;
         const float inv = sq > 0.0f ? 1.0f / sq : 0.0f;
-        uint32_t d[ND];
+        uint32_t d[ND + 1];
 #pragma unroll
-        for (int j = 0; j < ND; j++) d[j] = 0;
+        for (int j = 0; j <= ND; j++) d[j] = 0;
 #pragma unroll
         for (int e = 0; e < CPC; e++) {
-            int qi = (int)fminf(fmaxf(rintf(qv[h * HD + col * CPC + e] * inv), -(float)Q_RANGE), (float)Q_RANGE);
+            const float qq = qv[h * HD + col * CPC + e];
+            int qi = (int)fminf(fmaxf(rintf(qq * inv), -(float)Q_RANGE), (float)Q_RANGE);
+            if (xq) {
+                // the rest of q / s_q beyond q_int (one rounding), in 1/base units
+                const float r = fmaf(qq, inv, -(float)qi);
+                const int dx = (int)fminf(fmaxf(rintf(r * XB), -(float)XMAX), (float)XMAX);
+                d[ND] |= (uint32_t)(dx & ((1 << BITS) - 1)) << (BITS * e);
+            }
 #pragma unroll
             for (int j = 0; j < ND; j++) {
                 const int half = 1 << (BITS - 1), mask = (1 << BITS) - 1;
@@ -204,17 +243,21 @@ __device__ __forceinline__ void qprep_block(const float *__restrict__ q, int32_t
             }
         }
 #pragma unroll
-        for (int j = 0; j < ND; j++) qdig[(((size_t)unit * ND + j) * K_COLS + col) * G + h] = (int32_t)d[j];
+        for (int j = 0; j <= ND; j++) qdig[(((size_t)unit * (ND + 1) + j) * K_COLS + col) * G + h] = (int32_t)d[j];
     }
     if (tid < G) qsc[unit * G + tid] = amax[tid] / (float)Q_RANGE * qk_scale;
-    if (cnt && tid == 0) cnt[unit] = 0;              // the fused step's ticket counter
+    if (tid == 0) {
+        qflag[unit] = xq ? 1 : 0;
+        if (cnt) cnt[unit] = 0;                      // the fused step's ticket counter
+    }
 }
 
 template <int KB, int HD, int G>
 __global__ __launch_bounds__(256) void qprep_kernel(const float *__restrict__ q, int32_t *__restrict__ qdig,
-                                                    float *__restrict__ qsc, float qk_scale, int *cnt)
+                                                    float *__restrict__ qsc, int32_t *__restrict__ qflag,
+                                                    float qk_scale, int *cnt)
 {
-    qprep_block<KB, HD, G>(q, qdig, qsc, qk_scale, blockIdx.x, cnt);
+    qprep_block<KB, HD, G>(q, qdig, qsc, qflag, qk_scale, blockIdx.x, cnt);
 }
 
 template <int KB>
@@ -255,13 +298,13 @@ __device__ __forceinline__ void pack_w(uint32_t w0, uint32_t w1, uint32_t w2, ui
 // KG = scale groups per head row for both keys and values (1: groups of
 // head_dim, or one scale per position shared by all heads; 2 or 4: groups of
 // head_dim / KG channels); key dots are summed per group.
-// waves per SIMD the register allocation must allow: the contiguous int4
-// key and value instances with G x KG <= 4 fit 128 VGPRs (4 waves) by
-// themselves; their paged instances would miss it by a register or two, so
-// they ask for it (the others take what they need)
+// waves per SIMD the register allocation must allow: the int4 key and value
+// instances with G x KG <= 4 fit 128 VGPRs (4 waves) when asked to (left
+// alone the compiler takes a few more and drops to 3); the others take what
+// they need
 __host__ __device__ constexpr int qd_min_waves(int KB, int VB, int G, int KG, bool paged)
 {
-    return paged && KB == 4 && VB == 4 && G * KG <= 4 ? 4 : 1;
+    return KB == 4 && VB == 4 && G * KG <= 4 ? 4 : 1;
 }
 
 template <int KB, int VB, int HD, int G, int KG, bool PAGED>
@@ -360,7 +403,10 @@ void decode_quant_kernel(QuantParams p)
         if constexpr (PAGED) return (w0 + tw) & ((1 << p.page_shift) - 1);
         else return w0 + tw;
     };
-    const KVQ_CONST int32_t *qd = (const KVQ_CONST int32_t *)(p.qdig + (size_t)bh * T::ND * T::K_COLS * G);
+    const KVQ_CONST int32_t *qd = (const KVQ_CONST int32_t *)(p.qdig + (size_t)bh * T::NDX * T::K_COLS * G);
+    // the query's extra low digit (wave-uniform: one flag per (sequence, KV head))
+    const bool xq = ((const KVQ_CONST int32_t *)p.qflag)[bh] != 0;
+    constexpr float XINV = 1.0f / (float)qx_base(KB);
     const uint32_t ko = lane * 16;
     const uint32_t kso = lane * p.k_sc_t * 2, vso = lane * p.v_sc_t * 2;
     struct Tile {
@@ -390,9 +436,7 @@ void decode_quant_kernel(QuantParams p)
             d.vs[g] = bld_u16(vsrs, vso + 2 * g);
         }
     };
-    float mloc[G];                                   // per-lane maxima of the current sub-chunk:
-    uint32_t vmloc[KG];                              // scores; value scales as fp16 bits (>= 0, so
-                                                     // the largest bits are the largest value)
+    float mloc[G];                                   // per-lane score maxima of the current sub-chunk
     // scores of one tile (tb: first position of the tile within the wave;
     // sc0: first position of the sub-chunk)
     auto compute = [&](int tb, int sc0, const Tile &c) {
@@ -402,7 +446,6 @@ void decode_quant_kernel(QuantParams p)
         for (int g = 0; g < KG; g++) {
             // (zero past the wave's range: the load returned zero)
             if (valid) vsl[(t - sc0) * KG + g] = (uint16_t)c.vs[g];
-            vmloc[g] = max(vmloc[g], c.vs[g]);
         }
         // an opaque zero offset, redefined every tile, keeps the digit loads
         // inside the loop (hoisted, they would need hundreds of SGPRs)
@@ -457,6 +500,21 @@ void decode_quant_kernel(QuantParams p)
             const float sk = f16_bits_to_f32((uint16_t)c.ks[blk]);
 #pragma unroll
             for (int h = 0; h < G; h++) z[h] = blk == 0 ? (float)acc[h] * sk : fmaf((float)acc[h], sk, z[h]);
+            if (xq) {
+                // the extra low digit: its exact int32 sum, 1/base of a unit
+                const KVQ_CONST int32_t *qx = qdl + T::ND * T::K_COLS * G;
+#pragma unroll
+                for (int cc = 0; cc < CPB; cc++) {
+                    const int col = blk * CPB + cc;
+                    const int kw = (int)kword(c.k[col / 4], col);
+#pragma unroll
+                    for (int h = 0; h < G; h++)
+                        acc[h] = cc == 0 ? kdot0<KB>(qx[col * G + h], kw) : kdot<KB>(qx[col * G + h], kw, acc[h]);
+                }
+                const float skx = sk * XINV;
+#pragma unroll
+                for (int h = 0; h < G; h++) z[h] = fmaf((float)acc[h], skx, z[h]);
+            }
         }
         if (valid) {
 #pragma unroll
@@ -574,8 +632,6 @@ void decode_quant_kernel(QuantParams p)
         // ---------------- pass 1: scores of the sub-chunk ----------------------
 #pragma unroll
         for (int h = 0; h < G; h++) mloc[h] = -INFINITY;
-#pragma unroll
-        for (int g = 0; g < KG; g++) vmloc[g] = 0u;
         // (tiles run in pairs, both halves unconditionally: a half past the
         // end sees only invalid lanes and zero rows, and the code stays free
         // of a merge point that would send the two register sets through
@@ -597,86 +653,125 @@ void decode_quant_kernel(QuantParams p)
             for (int f = 0; f < PF; f++) vload(f, rs);
         }
         compute(tb + 64, sc0, tb_);
-        float ms[G], vms[KG];                        // sub-chunk maxima, wave-uniform
+        float ms[G];                                 // sub-chunk score maxima, wave-uniform
 #pragma unroll
         for (int h = 0; h < G; h++) ms[h] = wave_max_u(mloc[h]);
-#pragma unroll
-        for (int g = 0; g < KG; g++) vms[g] = f16_bits_to_f32((uint16_t)wave_max_ui((int)vmloc[g]));
 
         // ---------------- pass 2: weights, one lane per 4 positions ---------------
-        // p = 2^(qs * (z - ms)) <= 1; w_int = rint(p * s_v * 32767 / vms),
-        // rounded by one fma onto 1.5 * 2^23 (the integer lands in the low
-        // mantissa bits); bytes packed four positions per word.
+        // (a) p = 2^(qs * (z - ms)) <= 1, written over its score, and the
+        // largest product p * s_v per head and scale group, N (DPP; the
+        // products are >= 0, so their bits compare as integers); (b) w_int =
+        // rint(p * s_v * 32767 / N), rounded by one fma onto 1.5 * 2^23 (the
+        // integer lands in the low mantissa bits), bytes packed four positions
+        // per word.  One lane per group of 4 positions and turn; a lane only
+        // rewrites the scores it has read, and the weight words go over
+        // positions whose p every lane has already read.
         float lloc[G];
         int wsl[KG][G];
+        float nrm[KG][G];                            // N per scale group and head, wave-uniform
         {
             constexpr float MAGIC = 12582912.0f;     // 1.5 * 2^23
+            constexpr int TURNS = (S / 4 + 63) / 64;
+            auto rd = [&](const float *src, float (&zz)[G]) {
+                if constexpr (G % 4 == 0) {
+#pragma unroll
+                    for (int h = 0; h < G; h += 4) {
+                        const float4 v = *reinterpret_cast<const float4 *>(src + h);
+                        zz[h] = v.x; zz[h + 1] = v.y; zz[h + 2] = v.z; zz[h + 3] = v.w;
+                    }
+                } else if constexpr (G == 2) {
+                    const float2 v = *reinterpret_cast<const float2 *>(src);
+                    zz[0] = v.x; zz[1] = v.y;
+                } else {
+                    zz[0] = src[0];
+                }
+            };
+            auto wr = [&](float *dst, const float (&zz)[G]) {
+                if constexpr (G % 4 == 0) {
+#pragma unroll
+                    for (int h = 0; h < G; h += 4)
+                        *reinterpret_cast<float4 *>(dst + h) = make_float4(zz[h], zz[h + 1], zz[h + 2], zz[h + 3]);
+                } else if constexpr (G == 2) {
+                    *reinterpret_cast<float2 *>(dst) = make_float2(zz[0], zz[1]);
+                } else {
+                    dst[0] = zz[0];
+                }
+            };
             float nqm[G];
+            int pmx[KG][G];
 #pragma unroll
             for (int h = 0; h < G; h++) {
                 nqm[h] = -ms[h] * qs[h];
                 lloc[h] = 0.0f;
+#pragma unroll
+                for (int g = 0; g < KG; g++) {
+                    wsl[g][h] = 0;
+                    pmx[g][h] = 0;
+                }
             }
+#pragma unroll
+            for (int t = 0; t < TURNS; t++) {
+                const int tq = 4 * (t * 64 + lane);  // first position of the group (within the sub-chunk)
+                if (tq < ns) {
+#pragma unroll
+                    for (int k = 0; k < 4; k++) {
+                        const bool valid = tq + k < ns;
+                        float *src = zs + (size_t)(tq + k) * G;
+                        float pr[G];
+                        rd(src, pr);
+#pragma unroll
+                        for (int h = 0; h < G; h++) {
+                            pr[h] = valid ? __builtin_amdgcn_exp2f(fmaf(pr[h], qs[h], nqm[h])) : 0.0f;
+                            lloc[h] += pr[h];
+                        }
+                        wr(src, pr);
+#pragma unroll
+                        for (int g = 0; g < KG; g++) {
+                            const float sv = valid ? f16_bits_to_f32(vsl[(tq + k) * KG + g]) : 0.0f;
+#pragma unroll
+                            for (int h = 0; h < G; h++)
+                                pmx[g][h] = max(pmx[g][h], __builtin_bit_cast(int, pr[h] * sv));
+                        }
+                    }
+                }
+            }
+            float fsc[KG][G];
 #pragma unroll
             for (int g = 0; g < KG; g++)
 #pragma unroll
-                for (int h = 0; h < G; h++) wsl[g][h] = 0;
-            float fsc[KG];
+                for (int h = 0; h < G; h++) {
+                    nrm[g][h] = __builtin_bit_cast(float, wave_max_ui(pmx[g][h]));
+                    fsc[g][h] = nrm[g][h] > 0.0f ? (float)W_RANGE * __builtin_amdgcn_rcpf(nrm[g][h]) : 0.0f;
+                }
 #pragma unroll
-            for (int g = 0; g < KG; g++) fsc[g] = vms[g] > 0.0f ? (float)W_RANGE * __builtin_amdgcn_rcpf(vms[g]) : 0.0f;
-            // S / 4 groups of 4 positions, one per lane and turn (the weight
-            // words go over the scores: a turn writes only rows it or an
-            // earlier turn has read)
+            for (int t = 0; t < TURNS; t++) {
+                const int grp = t * 64 + lane;
+                const int tq = 4 * grp;
+                if (tq < ns) {
+                    float pr[4][G];
 #pragma unroll
-            for (int gq = 0; gq < S / 4; gq += 64) {
-            const int grp = gq + lane;
-            const int tq = 4 * grp;                  // first position of the group (within the sub-chunk)
-            if (tq < ns) {
-                float pr[4][G];
+                    for (int k = 0; k < 4; k++) rd(zs + (size_t)(tq + k) * G, pr[k]);   // (0 past the sub-chunk)
 #pragma unroll
-                for (int k = 0; k < 4; k++) {
-                    const bool valid = tq + k < ns;
-                    const float *src = zs + (size_t)(tq + k) * G;
-                    float zz[G];
-                    if constexpr (G % 4 == 0) {
+                    for (int g = 0; g < KG; g++) {
+                        float sv[4];
 #pragma unroll
-                        for (int h = 0; h < G; h += 4) {
-                            const float4 v = *reinterpret_cast<const float4 *>(src + h);
-                            zz[h] = v.x; zz[h + 1] = v.y; zz[h + 2] = v.z; zz[h + 3] = v.w;
+                        for (int k = 0; k < 4; k++) sv[k] = tq + k < ns ? f16_bits_to_f32(vsl[(tq + k) * KG + g]) : 0.0f;
+                        uint32_t *dst = wdw + ((size_t)g * (S / 4) + grp) * G * 2;
+#pragma unroll
+                        for (int h = 0; h < G; h++) {
+                            uint32_t wb[4];
+#pragma unroll
+                            for (int k = 0; k < 4; k++)
+                                wb[k] = __builtin_bit_cast(uint32_t, fmaf(pr[k][h] * fsc[g][h], sv[k], MAGIC));
+                            uint32_t lo, hi;
+                            pack_w(wb[0], wb[1], wb[2], wb[3], lo, hi);
+                            wsl[g][h] += (int)__builtin_amdgcn_udot4(lo, 0x01010101u, 0u, false)
+                                       + 256 * (int)__builtin_amdgcn_udot4(hi, 0x01010101u, 0u, false);
+                            dst[2 * h] = lo;
+                            dst[2 * h + 1] = hi;
                         }
-                    } else if constexpr (G == 2) {
-                        const float2 v = *reinterpret_cast<const float2 *>(src);
-                        zz[0] = v.x; zz[1] = v.y;
-                    } else {
-                        zz[0] = src[0];
-                    }
-#pragma unroll
-                    for (int h = 0; h < G; h++) {
-                        pr[k][h] = valid ? __builtin_amdgcn_exp2f(fmaf(zz[h], qs[h], nqm[h])) : 0.0f;
-                        lloc[h] += pr[k][h];
                     }
                 }
-#pragma unroll
-                for (int g = 0; g < KG; g++) {
-                    float sv[4];
-#pragma unroll
-                    for (int k = 0; k < 4; k++)
-                        sv[k] = tq + k < ns ? f16_bits_to_f32(vsl[(tq + k) * KG + g]) * fsc[g] : 0.0f;
-                    uint32_t *dst = wdw + ((size_t)g * (S / 4) + grp) * G * 2;
-#pragma unroll
-                    for (int h = 0; h < G; h++) {
-                        uint32_t wb[4];
-#pragma unroll
-                        for (int k = 0; k < 4; k++) wb[k] = __builtin_bit_cast(uint32_t, fmaf(pr[k][h], sv[k], MAGIC));
-                        uint32_t lo, hi;
-                        pack_w(wb[0], wb[1], wb[2], wb[3], lo, hi);
-                        wsl[g][h] += (int)__builtin_amdgcn_udot4(lo, 0x01010101u, 0u, false)
-                                   + 256 * (int)__builtin_amdgcn_udot4(hi, 0x01010101u, 0u, false);
-                        dst[2 * h] = lo;
-                        dst[2 * h + 1] = hi;
-                    }
-                }
-            }
             }
         }
 
@@ -726,10 +821,10 @@ void decode_quant_kernel(QuantParams p)
                 const float fn = __builtin_amdgcn_exp2f(qs[h] * (ms[h] - Mn));
                 M[h] = Mn;
                 lsum[h] = fmaf(lsum[h], fo, lloc[h] * fn);
-                float cg[KG];                        // c = fn * vms / 32767 per scale group
+                float cg[KG];                        // c = fn * N / 32767 per scale group
 #pragma unroll
                 for (int g = 0; g < KG; g++) {
-                    cg[g] = fn * vms[g] * (1.0f / (float)W_RANGE);
+                    cg[g] = fn * nrm[g][h] * (1.0f / (float)W_RANGE);
                     bsum[g][h] = fmaf(bsum[g][h], fo, (float)wsl[g][h] * cg[g]);
                 }
                 // 256 * hi + lo is exact in uint32 (hi bytes <= 127, at most

@@ -15,7 +15,8 @@ namespace kvq {
 // when cnt is not null.  256 threads.
 template <int KB, int HD, int G>
 __global__ __launch_bounds__(256) void step_prep_kernel(AppendParams ap, int app_x, int app_y, const float *q,
-                                                        int32_t *qdig, float *qsc, float qk_scale, int *cnt)
+                                                        int32_t *qdig, float *qsc, int32_t *qflag, float qk_scale,
+                                                        int *cnt)
 {
     const int n_app = app_x * app_y * 2;
     const int bid = blockIdx.x;
@@ -26,7 +27,7 @@ __global__ __launch_bounds__(256) void step_prep_kernel(AppendParams ap, int app
         append_block(ap, r % app_x, r / app_x, side);
         return;
     }
-    qprep_block<KB, HD, G>(q, qdig, qsc, qk_scale, bid - n_app, cnt);
+    qprep_block<KB, HD, G>(q, qdig, qsc, qflag, qk_scale, bid - n_app, cnt);
 }
 
 } // namespace kvq

@@ -289,12 +289,13 @@ def test_workspace_and_chunks(kvq):
     assert 32 * 8 * n_chunks >= 2048                     # 8 workgroups per CU over 256 CUs
     P = 32 * 32
     partials = ((P * n_chunks * 8 + 255) // 256) * 256 + P * n_chunks * 128 * 4
-    # int4 keys: the query's fixed-point digits (4 per value) and scales follow the
-    # partials, then one ticket counter per (sequence, KV head) for the fused step
-    digits = 32 * 8 * 16 * 4 * 4 * 4 + P * 4
-    counters = 32 * 8 * 4
+    # int4 keys: the query's fixed-point digits (4 Horner digits and the extra low
+    # one, per value) and scales follow the partials, then one extra-digit flag and
+    # one ticket counter per (sequence, KV head) for the fused step
+    digits = 32 * 8 * 16 * 5 * 4 * 4 + P * 4
+    counters = 2 * 32 * 8 * 4
     ws = kvq.kvq_workspace_bytes(d, 32, 32768, 0)
-    assert partials + digits + counters <= ws <= partials + digits + counters + 768
+    assert partials + digits + counters <= ws <= partials + digits + counters + 1024
     ws256 = kvq.kvq_workspace_bytes(d, 32, 32768, 256)
     assert ws256 >= ((P * 128 * 8 + 255) // 256) * 256 + P * 128 * 512
     # 8/4-bit caches take chunks in multiples of 256 slots

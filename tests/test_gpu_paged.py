@@ -105,8 +105,10 @@ def test_paged_group_scales(oq, kb, vb):
     run_paged(oq, kb, vb, 32, B=2, H=2, G=4, HD=128, P=64, n_pos=515, seed=40 + kb)
 
 
-def test_paged_per_row_scale(oq):
-    run_paged(oq, 8, 8, -1, B=2, H=4, G=1, HD=64, P=64, n_pos=300, seed=41)
+@pytest.mark.parametrize("kb,vb", [(8, 8), (8, 4), (4, 4), (4, 8)])
+def test_paged_per_row_scale(oq, kb, vb):
+    run_paged(oq, kb, vb, -1, B=2, H=4, G=1, HD=64, P=64, n_pos=300, seed=41 + kb + vb)
+    run_paged(oq, kb, vb, -1, B=2, H=2, G=4, HD=128, P=128, n_pos=600, seed=43 + kb + vb)
 
 
 @pytest.mark.parametrize("kb,vb", [(4, 4), (16, 16)])

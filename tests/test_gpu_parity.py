@@ -74,9 +74,12 @@ def test_group_scales(oq, kb, vb, group):
     run_case(oq, kb, vb, group, B=2, H=2, G=4, HD=128, n_pos=515, seed=7 + group, outliers=True)
 
 
-def test_per_row_scale(oq):
-    """One scale per position over all KV heads (mni-ml's per-tensor INT8)."""
-    run_case(oq, 8, 8, -1, B=2, H=4, G=1, HD=64, n_pos=300, seed=3)
+@pytest.mark.parametrize("kb,vb", [(8, 8), (8, 4), (4, 4), (4, 8)])
+@pytest.mark.parametrize("H,G,HD", [(4, 1, 64), (2, 4, 128), (2, 8, 64)])
+def test_per_row_scale(oq, kb, vb, H, G, HD):
+    """One scale per position over all KV heads (mni-ml's per-tensor INT8),
+    at every integer width pair the descriptor accepts it for."""
+    run_case(oq, kb, vb, -1, B=2, H=H, G=G, HD=HD, n_pos=300, seed=3 + kb * 10 + vb + G)
 
 
 @pytest.mark.parametrize("chunk", [256, 512, 1024, 2048])

@@ -27,7 +27,7 @@ def draw(seed):
     gs = HD
     if quant:
         gs = int(rng.choice([g for g in (32, 64, HD) if HD % g == 0]))
-        if kb == 8 and vb == 8 and H > 1 and rng.random() < 0.2:
+        if H > 1 and rng.random() < 0.2:
             gs = H * HD                              # one scale per position over all heads
     P = int(rng.choice([0, 64, 128, 256]))
     window = rng.random() < 0.3
