@@ -34,8 +34,9 @@ KVQ_ERR_ARG = -9
 EXPORTED = (
     "kvq_bytes_per_token", "kvq_cache_sizes", "kvq_append", "kvq_chunk_tokens", "kvq_workspace_bytes",
     "kvq_decode_partials", "kvq_prepare_query", "kvq_decode_partials_prepared", "kvq_combine", "kvq_decode_attn",
-    "kvq_decode_step", "kvq_read_probe", "kvq_status_str", "kvq_last_error",
+    "kvq_decode_step", "kvq_decode_step_static", "kvq_read_probe", "kvq_status_str", "kvq_last_error",
 )
+KVQ_STATIC_SCRATCH_BYTES = 32 << 20
 
 
 class KvqError(RuntimeError):
@@ -102,6 +103,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_decode_attn.restype = I
         L.kvq_decode_step.argtypes = [C, P, P, I, P, P, I, P, I, ctypes.c_float, I, P, P, S, P]
         L.kvq_decode_step.restype = I
+        L.kvq_decode_step_static.argtypes = [C, P, P, I, P, P, I, P, I, ctypes.c_float, I, P, P]
+        L.kvq_decode_step_static.restype = I
         L.kvq_read_probe.argtypes = [P, S, P, S, P]
         L.kvq_read_probe.restype = I
         L.kvq_status_str.argtypes = [I]
@@ -206,6 +209,13 @@ def kvq_decode_step(cache, k_new, v_new, n_new: int, start_pos, q, n_q_heads: in
     _check(lib().kvq_decode_step(ctypes.byref(_desc(cache)), _ptr(k_new), _ptr(v_new), int(n_new), _ptr(start_pos),
                                  _ptr(q), n_q_heads, _ptr(seq_len), max_seq_len, float(softmax_scale), chunk_tokens,
                                  _ptr(out), _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def kvq_decode_step_static(cache, k_new, v_new, n_new: int, start_pos, q, n_q_heads: int, seq_len,
+                           max_seq_len: int, softmax_scale: float, chunk_tokens: int, out, stream=None) -> None:
+    _check(lib().kvq_decode_step_static(ctypes.byref(_desc(cache)), _ptr(k_new), _ptr(v_new), int(n_new),
+                                        _ptr(start_pos), _ptr(q), n_q_heads, _ptr(seq_len), max_seq_len,
+                                        float(softmax_scale), chunk_tokens, _ptr(out), _stream(stream)))
 
 
 def kvq_read_probe(buf, nbytes: int, sink, sink_bytes: int, stream=None) -> None:

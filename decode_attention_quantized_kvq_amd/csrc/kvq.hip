@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/kvq.h"
 #include "kvq_append.hpp"
@@ -726,6 +727,64 @@ int kvq_decode_step(const kvq_cache *c, const float *k_new, const float *v_new, 
                           &ap, ag);
     if (st) return st;
     return kvq_combine(c->batch, n_q_heads, c->head_dim, nc, workspace, workspace_bytes, out, stream);
+}
+
+} // extern "C"
+
+// ---------------------------------------------------------------------------
+// The library's own workspace for kvq_decode_step_static: one array per
+// device, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: kernels get the address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[KVQ_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device), or an error status.
+int static_scratch(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_ERR_HIP, "device %d beyond the %d the library tracks", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(KVQ_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return KVQ_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int kvq_decode_step_static(const kvq_cache *c, const float *k_new, const float *v_new, int n_new,
+                           const int32_t *start_pos, const float *q, int n_q_heads, const int32_t *seq_len,
+                           int max_seq_len, float softmax_scale, int chunk_tokens, float *out, void *stream)
+{
+    int ch, nc;
+    int st = resolve_chunk(c, n_q_heads, max_seq_len, chunk_tokens, &ch, &nc);
+    if (st) return st;
+    const size_t need = cache_ws_bytes(c, n_q_heads, nc);
+    if (need > (size_t)KVQ_STATIC_SCRATCH_BYTES)
+        return fail(KVQ_ERR_WORKSPACE, "this step needs %zu bytes of workspace, beyond the %zu of the static scratch",
+                    need, (size_t)KVQ_STATIC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if ((st = static_scratch(&ws))) return st;
+    return kvq_decode_step(c, k_new, v_new, n_new, start_pos, q, n_q_heads, seq_len, max_seq_len, softmax_scale, ch,
+                           out, ws, (size_t)KVQ_STATIC_SCRATCH_BYTES, stream);
 }
 
 int kvq_read_probe(const void *buf, size_t bytes, void *sink, size_t sink_bytes, void *stream)

@@ -26,7 +26,9 @@
  *   - All buffer pointers are DEVICE pointers owned by the caller.  The
  *     library never allocates, frees or synchronizes; every call only
  *     enqueues kernels on `stream` (a hipStream_t passed as void*, NULL for
- *     the default stream) and returns.
+ *     the default stream) and returns.  Its only device memory of its own is
+ *     the static workspace of kvq_decode_step_static(), part of the loaded
+ *     code object.
  *   - Return value: KVQ_OK when the work was enqueued; a negative KVQ_ERR_*
  *     when a host-side check failed (then nothing was launched), or
  *     KVQ_ERR_HIP when HIP refused the launch.  kvq_last_error() describes
@@ -294,6 +296,30 @@ int kvq_decode_step(const kvq_cache *c, const float *k_new, const float *v_new, 
                     const int32_t *start_pos, const float *q, int n_q_heads, const int32_t *seq_len,
                     int max_seq_len, float softmax_scale, int chunk_tokens, float *out,
                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---- a decode step that allocates nothing ----------------------------- */
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * kvq_decode_step() with the same arguments, rules and results (bit for bit
+ * the same output and cache), minus workspace and workspace_bytes, using a
+ * workspace of KVQ_STATIC_SCRATCH_BYTES that the library keeps in a static
+ * device array, one per device, held until the process ends.  The first
+ * call on a device looks that array's address up (no allocation); no call
+ * allocates or frees memory.  The step needs kvq_workspace_bytes(c,
+ * n_q_heads, max_seq_len, chunk_tokens) bytes of it; a step needing more is
+ * rejected with KVQ_ERR_WORKSPACE before anything is enqueued.  Every call
+ * on one device shares that device's array, and each call leaves its
+ * contents there: two calls that may run at the same time on one device
+ * (different streams, or host threads) race on it and must be ordered by
+ * the caller.  Nothing in it must be cleared between calls (each step
+ * writes everything it reads, its ticket counters included).
+ */
+#define KVQ_STATIC_SCRATCH_BYTES (32u << 20)
+
+int kvq_decode_step_static(const kvq_cache *c, const float *k_new, const float *v_new, int n_new,
+                           const int32_t *start_pos, const float *q, int n_q_heads, const int32_t *seq_len,
+                           int max_seq_len, float softmax_scale, int chunk_tokens, float *out, void *stream);
 
 /* ---- diagnostics ------------------------------------------------------- */
 /*

@@ -354,3 +354,16 @@ def test_product_does_not_touch_oracle():
         text = f.read_text()
         assert "oracle" not in text.lower() or f.name == "__init__.py" and "import oracle" not in text, f
         assert "kvq_oracle" not in text and "import oracle" not in text and "from oracle" not in text, f
+
+
+def test_static_step_rejects_oversize(kvq):
+    """kvq_decode_step_static refuses a step whose workspace exceeds its static
+    array, on the host, before any device call (the descriptor's buffers are
+    never read)."""
+    d = _desc(kvq, batch=64, n_kv_heads=8, capacity=131072, k_bits=16, v_bits=16)
+    need = kvq.kvq_workspace_bytes(d, 32, 131072, 64)
+    assert need > kvq.KVQ_STATIC_SCRATCH_BYTES
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_decode_step_static(d, None, None, 1, None, None, 32, None, 131072, 0.0, 64, None, stream=0)
+    assert e.value.status == kvq.KVQ_ERR_WORKSPACE
+    assert "static scratch" in kvq.kvq_last_error()
