@@ -17,6 +17,14 @@ GB/s of algorithmic bytes (the bytes the method must move: the cache it
 streams, q in, out, and the appended rows); `roofline` prices the split-K
 kernel alone against MI355X's 8 TB/s HBM peak.
 
+By default (--modes all) the line also carries every mode of the other
+workloads, each with its split kernel's rate, % of peak, step time and
+tokens/s (`summary` lists them): K8V4 at 32K, the FP16 / K4V8 / 32-value
+group modes of the 32K shape, the same 32K workloads paged, the 8K K8V4
+workload in K8V4 / FP16 / K8V8 / K4V4 and the 64 + 1536 window (both cold:
+they fit in the 256 MB MALL), TinyLoop-like in K8V8 / FP16 / per-layer
+widths, Tiny, the mni-ml-like generation loop, and bulk prefill.
+
     python bench.py [--steps K] [--warmup W] [--modes headline|targets|paged|all]
 
 Prints one JSON line.
@@ -198,7 +206,7 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
     # (4) the step as HIP graphs: one step per replay, and `steps` steps in
     # one graph (as the layers of a model's decode step run: no host launch
     # between them); the latter is the timed number
-    ms_step_graph1 = ms_step_graph = None
+    ms_step_graph1 = ms_step_graph = ms_step_graph_avg = None
     if scrub is None:
         cs = torch.cuda.Stream()
         cs.wait_stream(stream)
@@ -220,12 +228,26 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
             g1.replay()
         torch.cuda.synchronize()
         ms_step_graph1 = (time.perf_counter() - t0) / steps * 1e3
-        gk.replay()                                  # untimed: the graph's first launch
-        torch.cuda.synchronize()
+        # the K-step graph: untimed replays for >= settle_ms (the clock
+        # transient after the graph's first launch), then exactly K steps (one
+        # replay) timed, and the average over >= settle_ms of replays as a
+        # cross-check
+        t0 = time.perf_counter()
+        while True:
+            gk.replay()
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= settle_ms:
+                break
         t0 = time.perf_counter()
         gk.replay()
         torch.cuda.synchronize()
         ms_step_graph = (time.perf_counter() - t0) / steps * 1e3
+        n_rep = max(1, int(settle_ms / (ms_step_graph * steps)) + 1)
+        t0 = time.perf_counter()
+        for _ in range(n_rep):
+            gk.replay()
+        torch.cuda.synchronize()
+        ms_step_graph_avg = (time.perf_counter() - t0) / (n_rep * steps) * 1e3
         del g1, gk
     ms_step_wall = wall_eager / steps * 1e3
     ms_step_gpu = (t_app + t_split + t_comb) * w.n_layers
@@ -238,7 +260,8 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
         "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "context": attended(w), "n_layers": w.n_layers,
         "capacity": w.capacity, "n_anchor": w.n_anchor, "window": w.window, "group_size": _group(mode, w),
         "chunk_tokens": ch, "n_chunks": n_chunks, "mall_scrub": flush,
-        "ms_per_step": ms_step, "ms_per_step_graph": ms_step_graph, "ms_per_step_graph_1step": ms_step_graph1,
+        "ms_per_step": ms_step, "ms_per_step_graph": ms_step_graph, "ms_per_step_graph_avg": ms_step_graph_avg,
+        "ms_per_step_graph_1step": ms_step_graph1,
         "ms_per_step_eager": ms_step_eager, "ms_per_step_eager_parts_with_events": ms_step_wall,
         "ms_per_step_kernels": ms_step_gpu, "ms_per_step_cold": ms_step_cold,
         "us_split_back_to_back": t_split_loop * 1e3,
@@ -408,18 +431,41 @@ def read_probe(log=print, gib: int = 2, launches: int = 50) -> dict:
             "us_per_launch": round(us, 2), "kernel": "read_probe_kernel (8 x 16-byte nontemporal loads per thread)"}
 
 
-def cpu_baseline(w, mode, log=print, budget_s: float = 12.0) -> dict:
+def _cpu_facts() -> dict:
+    """The host CPU as the process sees it."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = os.cpu_count() or 1
+    return {"nproc": os.cpu_count(), "affinity": affinity, "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "model": model}
+
+
+def cpu_baseline(w, mode, log=print, budget_s: float = 15.0, runs: int = 3) -> dict:
     """The CPU oracle's decode step, untuned, on a bounded sample of the
     workload: whole sequences (every KV and query head, the full context),
-    one per thread, repeated over the batch until about `budget_s` seconds of
-    wall time have been spent (at least one round)."""
+    one per thread, on the CPU share this process may use (its affinity mask,
+    capped by OMP_NUM_THREADS and at 16, the share one GPU's host has).
+    `runs` timed runs of about budget_s / runs seconds each (whole rounds of
+    one sequence per thread, after one untimed round); the median run is
+    reported.  Then one thread alone, median of 3 runs of one sequence."""
     import numpy as np
 
     import oracle
     import workloads as wl
 
     oracle.lib()
-    cores = max(1, min(16, os.cpu_count() or 1, w.batch))
+    facts = _cpu_facts()
+    omp = facts["omp_num_threads"]
+    cores = max(1, min(facts["affinity"], int(omp) if omp and omp.isdigit() else 16, 16, w.batch))
     g = _group(mode, w)
     scale = 1.0 / np.sqrt(w.head_dim)
     seqs = list(range(cores))
@@ -430,36 +476,46 @@ def cpu_baseline(w, mode, log=print, budget_s: float = 12.0) -> dict:
         K, V, q = data[s_]
         oracle.decode_step(mode.k_bits, mode.v_bits, g, w.n_anchor, w.window, K, V, q, scale)
 
-    done = 0
-    t_work = 0.0
-    while done == 0 or t_work < budget_s:
+    def round_():
         threads = [threading.Thread(target=work, args=(s_,)) for s_ in seqs]
         t0 = time.perf_counter()
         for t in threads:
             t.start()
         for t in threads:
             t.join()
-        t_work += time.perf_counter() - t0
-        done += len(seqs)
-    sample_bytes = step_bytes(w, mode) * done / w.batch
-    log(f"[bench] cpu oracle: {done} sequence-steps on {cores} thread(s) in {t_work:.2f} s")
-    # the same oracle on one core: one sequence, at least 2 s
-    one, t_one = 0, 0.0
-    while one == 0 or t_one < 2.0:
+        return time.perf_counter() - t0
+
+    round_()                                         # untimed: first touch of the inputs
+    rates, total = [], 0
+    for _ in range(runs):
+        done, t_run = 0, 0.0
+        while done == 0 or t_run < budget_s / runs:
+            t_run += round_()
+            done += len(seqs)
+        rates.append(done / t_run)                   # sequence-steps per second
+        total += done
+    rate = sorted(rates)[len(rates) // 2]
+    log(f"[bench] cpu oracle: {total} sequence-steps on {cores} thread(s), runs at "
+        f"{', '.join(f'{r:.2f}' for r in rates)} seq-steps/s ({facts['model']}, nproc {facts['nproc']})")
+    one = []
+    for _ in range(3):
         t0 = time.perf_counter()
         work(0)
-        t_one += time.perf_counter() - t0
-        one += 1
-    log(f"[bench] cpu oracle, one core: {one} sequence-steps in {t_one:.2f} s")
+        one.append(time.perf_counter() - t0)
+    t_one = sorted(one)[1]
+    log(f"[bench] cpu oracle, one thread: {t_one:.2f} s per sequence-step (median of 3)")
+    per_seq = step_bytes(w, mode) / w.batch
     return {
-        "value": sample_bytes / t_work / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "value": per_seq * rate / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
         "sample": f"sequences 0-{cores - 1} of {w.name} ({mode.name}; {w.batch} per step), every head, full "
-                  f"{attended(w)}-position context, one sequence per thread, repeated to {done} sequence-steps; "
-                  f"float64 oracle (encode every row, then softmax attention); {t_work:.1f} s of oracle time "
-                  f"(input generation excluded)",
-        "tokens_per_s": done / t_work,
-        "one_core": {"value": step_bytes(w, mode) * one / w.batch / t_one / 1e9, "unit": "GB/s",
-                     "tokens_per_s": one / t_one, "sample": f"sequence 0, {one} sequence-steps, {t_one:.1f} s"},
+                  f"{attended(w)}-position context, one sequence per thread; median of {runs} runs of about "
+                  f"{budget_s / runs:.0f} s ({total} sequence-steps in all); float64 oracle (encode every row, then "
+                  f"softmax attention); input generation excluded",
+        "tokens_per_s": rate,
+        "runs_tokens_per_s": rates,
+        "host": facts,
+        "one_core": {"value": per_seq / t_one / 1e9, "unit": "GB/s", "tokens_per_s": 1.0 / t_one,
+                     "sample": "sequence 0, median of 3 sequence-steps on one thread"},
     }
 
 
@@ -587,7 +643,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--chunk", type=int, default=0, help="split-K chunk (0 = the library's choice)")
-    ap.add_argument("--modes", choices=["headline", "targets", "paged", "all"], default="targets",
+    ap.add_argument("--modes", choices=["headline", "targets", "paged", "all"], default="all",
                     help="headline: the K4V4 32K line only; targets: + K8V4 at 32K; paged: + both 32K "
                          "workloads in 256-slot pages and bulk prefill; all: every workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -701,6 +757,16 @@ def main() -> int:
         "generation": {f"{r['workload']}/{r['mode']}": {k: (round(v, 4) if isinstance(v, float) else v)
                                                         for k, v in r.items()} for r in gens},
     }
+    # one row per mode: split kernel rate, step time and tokens/s
+    line["summary"] = [
+        {"line": f"{r['workload']}/{r['mode']}", "split_GBps": round(r["split_GBps"], 1),
+         "split_pct_of_peak": round(r["split_pct_of_peak"], 2), "step_us": round(r["ms_per_step"] * 1e3, 2),
+         "step_GBps": round(r["step_GBps"], 1), "tokens_per_s": round(r["tokens_per_s"], 1),
+         "cold": r["mall_scrub"]} for r in [head] + extra
+    ] + [
+        {"line": f"generation {r['workload']}/{r['mode']}", "us_per_token": round(r["us_per_token_graph"], 2),
+         "tokens_per_s": round(r["tokens_per_s_graph"], 1)} for r in gens
+    ]
     print(json.dumps(line), flush=True)
     return 0
 

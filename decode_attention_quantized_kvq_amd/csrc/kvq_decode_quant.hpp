@@ -366,9 +366,11 @@ void decode_quant_kernel(QuantParams p)
     const int s0 = wave * sub;
     const int nw = max(min(sub, n_tok - s0), 0);     // positions of this wave
 
+    // (floored so that a zero query keeps -inf scores at -inf: 0 * -inf
+    // would be NaN)
     float qs[G];
 #pragma unroll
-    for (int h = 0; h < G; h++) qs[h] = p.qsc[row0 + h];
+    for (int h = 0; h < G; h++) qs[h] = fmaxf(p.qsc[row0 + h], 1e-30f);
 
     // ---- key stream: tiles of 64 positions, one lane per position, loaded
     // one tile ahead into the other of two register sets; the descriptors
@@ -444,8 +446,9 @@ void decode_quant_kernel(QuantParams p)
         const bool valid = t < nw;
 #pragma unroll
         for (int g = 0; g < KG; g++) {
-            // (zero past the wave's range: the load returned zero)
-            if (valid) vsl[(t - sc0) * KG + g] = (uint16_t)c.vs[g];
+            // (zero past the wave's range: the load returned zero; every
+            // tile of the sub-chunk lies inside its S rows of LDS)
+            vsl[(t - sc0) * KG + g] = (uint16_t)c.vs[g];
         }
         // an opaque zero offset, redefined every tile, keeps the digit loads
         // inside the loop (hoisted, they would need hundreds of SGPRs)
@@ -516,9 +519,13 @@ void decode_quant_kernel(QuantParams p)
                 for (int h = 0; h < G; h++) z[h] = fmaf((float)acc[h], skx, z[h]);
             }
         }
-        if (valid) {
+        {
+            // positions past the wave's range score -inf (their p is then 0)
 #pragma unroll
-            for (int h = 0; h < G; h++) mloc[h] = fmax_nc(mloc[h], z[h]);
+            for (int h = 0; h < G; h++) {
+                z[h] = valid ? z[h] : -INFINITY;
+                mloc[h] = fmax_nc(mloc[h], z[h]);
+            }
             float *dst = zs + (size_t)(t - sc0) * G;
             if constexpr (G % 4 == 0) {
 #pragma unroll
@@ -715,23 +722,29 @@ void decode_quant_kernel(QuantParams p)
                 if (tq < ns) {
 #pragma unroll
                     for (int k = 0; k < 4; k++) {
-                        const bool valid = tq + k < ns;
+                        // (positions past the range hold score -inf, scale 0)
                         float *src = zs + (size_t)(tq + k) * G;
                         float pr[G];
                         rd(src, pr);
 #pragma unroll
                         for (int h = 0; h < G; h++) {
-                            pr[h] = valid ? __builtin_amdgcn_exp2f(fmaf(pr[h], qs[h], nqm[h])) : 0.0f;
+                            pr[h] = __builtin_amdgcn_exp2f(fmaf(pr[h], qs[h], nqm[h]));
                             lloc[h] += pr[h];
                         }
-                        wr(src, pr);
+                        float prod[KG][G];
 #pragma unroll
                         for (int g = 0; g < KG; g++) {
-                            const float sv = valid ? f16_bits_to_f32(vsl[(tq + k) * KG + g]) : 0.0f;
+                            const float sv = f16_bits_to_f32(vsl[(tq + k) * KG + g]);
 #pragma unroll
-                            for (int h = 0; h < G; h++)
-                                pmx[g][h] = max(pmx[g][h], __builtin_bit_cast(int, pr[h] * sv));
+                            for (int h = 0; h < G; h++) {
+                                prod[g][h] = pr[h] * sv;
+                                pmx[g][h] = max(pmx[g][h], __builtin_bit_cast(int, prod[g][h]));
+                            }
                         }
+                        // one scale group: p * s_v goes back, the weight needs
+                        // one fma; more: p goes back
+                        if constexpr (KG == 1) wr(src, prod[0]);
+                        else wr(src, pr);
                     }
                 }
             }
@@ -748,21 +761,24 @@ void decode_quant_kernel(QuantParams p)
                 const int grp = t * 64 + lane;
                 const int tq = 4 * grp;
                 if (tq < ns) {
-                    float pr[4][G];
+                    float pr[4][G];                  // p * s_v (one group) or p
 #pragma unroll
-                    for (int k = 0; k < 4; k++) rd(zs + (size_t)(tq + k) * G, pr[k]);   // (0 past the sub-chunk)
+                    for (int k = 0; k < 4; k++) rd(zs + (size_t)(tq + k) * G, pr[k]);
 #pragma unroll
                     for (int g = 0; g < KG; g++) {
                         float sv[4];
+                        if constexpr (KG > 1) {
 #pragma unroll
-                        for (int k = 0; k < 4; k++) sv[k] = tq + k < ns ? f16_bits_to_f32(vsl[(tq + k) * KG + g]) : 0.0f;
+                            for (int k = 0; k < 4; k++) sv[k] = f16_bits_to_f32(vsl[(tq + k) * KG + g]);
+                        }
                         uint32_t *dst = wdw + ((size_t)g * (S / 4) + grp) * G * 2;
 #pragma unroll
                         for (int h = 0; h < G; h++) {
                             uint32_t wb[4];
 #pragma unroll
                             for (int k = 0; k < 4; k++)
-                                wb[k] = __builtin_bit_cast(uint32_t, fmaf(pr[k][h] * fsc[g][h], sv[k], MAGIC));
+                                wb[k] = __builtin_bit_cast(uint32_t, KG == 1 ? fmaf(pr[k][h], fsc[g][h], MAGIC)
+                                                                             : fmaf(pr[k][h] * fsc[g][h], sv[k], MAGIC));
                             uint32_t lo, hi;
                             pack_w(wb[0], wb[1], wb[2], wb[3], lo, hi);
                             wsl[g][h] += (int)__builtin_amdgcn_udot4(lo, 0x01010101u, 0u, false)
