@@ -653,8 +653,11 @@ def main() -> int:
                     help="the workload --probe-traffic launches and --record-traffic records")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from the two counter runs (CPU only)")
+    ap.add_argument("--only", default="",
+                    help="comma-separated workload names: time only these lines of --modes all (plus the headline)")
     ap.add_argument("--quiet", action="store_true")
     args = ap.parse_args()
+    only = set(x for x in args.only.split(",") if x)
 
     if args.record_traffic:
         return record_traffic(*args.record_traffic, args.probe_workload)
@@ -678,33 +681,42 @@ def main() -> int:
     if args.probe_traffic:
         return probe_traffic(args.chunk, args.probe_workload, log=log)
 
+    def want(name):
+        return not only or name in only
+
     head_w, head_m = wl.K4V4_32K, wl.K4V4
     head = run_mode(head_w, head_m, args.steps, args.warmup, args.chunk, log=log)
     extra = []
-    if args.modes in ("targets", "all"):
+    if args.modes in ("targets", "all") and want("k8v4-32k"):
         extra.append(run_mode(wl.K8V4_32K, wl.K8V4, args.steps, args.warmup, args.chunk, log=log))
-    if args.modes in ("paged", "all"):
+    if args.modes in ("paged", "all") and want("paged"):
         extra.append(run_mode(wl.K4V4_32K, wl.K4V4, args.steps, args.warmup, args.chunk, log=log, page_size=256))
         extra.append(run_mode(wl.K8V4_32K, wl.K8V4, args.steps, args.warmup, args.chunk, log=log, page_size=256))
     if args.modes == "all":
-        extra.append(run_mode(wl.K4V4_32K, wl.FP16, args.steps, args.warmup, args.chunk, log=log))
-        extra.append(run_mode(wl.K4V4_32K, wl.K4V4_G32, args.steps, args.warmup, args.chunk, log=log))
-        extra.append(run_mode(wl.K4V4_32K, wl.K4V8, args.steps, args.warmup, args.chunk, log=log))
-        extra.append(run_mode(wl.K4V4_WINDOW, wl.K4V4, args.steps, args.warmup, args.chunk, flush=True, log=log))
-        for m in wl.K8V4_8K.modes:
-            extra.append(run_mode(wl.K8V4_8K, m, args.steps, args.warmup, args.chunk, flush=True, log=log))
-        for m in wl.TINYLOOP.modes:
-            extra.append(run_mode(wl.TINYLOOP, m, max(3, args.steps // 4), 2, args.chunk, log=log))
-        # bit widths per layer: int8 in the first and last two layers, int4 between
-        n_l = wl.TINYLOOP.n_layers
-        per_layer = [wl.K8V8 if li < 2 or li >= n_l - 2 else wl.K4V4 for li in range(n_l)]
-        extra.append(run_mode(wl.TINYLOOP, wl.Mode("k8v8-ends-k4v4", 4, 4), max(3, args.steps // 4), 2, args.chunk,
-                              log=log, layer_modes=per_layer))
-        for m in wl.TINY.modes:
-            extra.append(run_mode(wl.TINY, m, args.steps, args.warmup, args.chunk, log=log))
-    gens = [generation_loop(wl.MNIML, m, log=log) for m in wl.MNIML.modes] if args.modes == "all" else []
+        if want("k4v4-32k-modes"):
+            extra.append(run_mode(wl.K4V4_32K, wl.FP16, args.steps, args.warmup, args.chunk, log=log))
+            extra.append(run_mode(wl.K4V4_32K, wl.K4V4_G32, args.steps, args.warmup, args.chunk, log=log))
+            extra.append(run_mode(wl.K4V4_32K, wl.K4V8, args.steps, args.warmup, args.chunk, log=log))
+        if want("k4v4-window"):
+            extra.append(run_mode(wl.K4V4_WINDOW, wl.K4V4, args.steps, args.warmup, args.chunk, flush=True, log=log))
+        if want("k8v4-8k"):
+            for m in wl.K8V4_8K.modes:
+                extra.append(run_mode(wl.K8V4_8K, m, args.steps, args.warmup, args.chunk, flush=True, log=log))
+        if want("tinyloop"):
+            for m in wl.TINYLOOP.modes:
+                extra.append(run_mode(wl.TINYLOOP, m, max(3, args.steps // 4), 2, args.chunk, log=log))
+            # bit widths per layer: int8 in the first and last two layers, int4 between
+            n_l = wl.TINYLOOP.n_layers
+            per_layer = [wl.K8V8 if li < 2 or li >= n_l - 2 else wl.K4V4 for li in range(n_l)]
+            extra.append(run_mode(wl.TINYLOOP, wl.Mode("k8v8-ends-k4v4", 4, 4), max(3, args.steps // 4), 2,
+                                  args.chunk, log=log, layer_modes=per_layer))
+        if want("tiny"):
+            for m in wl.TINY.modes:
+                extra.append(run_mode(wl.TINY, m, args.steps, args.warmup, args.chunk, log=log))
+    gens = [generation_loop(wl.MNIML, m, log=log) for m in wl.MNIML.modes] \
+        if args.modes == "all" and want("mniml") else []
     prefills = []
-    if args.modes in ("paged", "all"):
+    if args.modes in ("paged", "all") and want("prefill"):
         prefills = [prefill(wl.K4V4_32K, wl.K4V4, log=log), prefill(wl.K8V4_32K, wl.K8V4, log=log),
                     prefill(wl.K4V4_32K, wl.FP16, log=log)]
 

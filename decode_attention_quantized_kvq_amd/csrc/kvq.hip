@@ -168,6 +168,12 @@ int auto_chunk(const kvq_cache *c, int n_q_heads, int max_seq_len)
     const bool q = quant_modes(c);
     const int smallest = q ? 512 : 64;
     const long long want = q ? 1024 : 2048;
+    // Integer caches with short contexts that cannot fill the chip anyway
+    // (at most one round of 512-slot chunks, <= 1024 slots): one chunk per
+    // (sequence, KV head), so that a decode step is one launch.  (Measured: a
+    // 34-layer 1K-context step 528 against 541 us with two 512-slot chunks
+    // and the merge inside the split kernel.)
+    if (q && L <= 1024 && units * ((L + 511) / 512) <= want) return L <= 512 ? 512 : 1024;
     for (int ch = q ? 2048 : 1024; ch >= smallest; ch >>= 1) {
         // (an integer cache's LDS does not depend on the chunk)
         if (!q && lds_bytes(c, G, ch) > kAutoLds) continue;
@@ -287,8 +293,9 @@ StepPrepFn pick_step(int kb, int hd, int G)
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace: ml [P][C][2] | acc [P][C][HD] | (quantized keys) query digits
-// [B*Hkv][ND+1][K_COLS][G] int32 | query scales [P] float | extra-digit
-// flags [B*Hkv] int32 | ticket counters [B*Hkv] int32.
+// [B*Hkv][qd_stride] int32 (each unit's [ND+1][K_COLS][G] padded to 256
+// bytes) | query scales [P] float | extra-digit flags [B*Hkv] int32 |
+// ticket counters [B*Hkv] int32.
 struct WsLayout {
     size_t ml, acc, qdig, qsc, qflag, cnt, total;
 };
@@ -303,10 +310,8 @@ WsLayout ws_layout(int batch, int n_q_heads, int head_dim, int n_chunks, int n_k
     w.qdig = w.qsc = w.qflag = w.cnt = 0;
     if (quantized(k_bits)) {
         const size_t units = (size_t)batch * n_kv_heads;
-        const size_t cols = (size_t)head_dim * k_bits / 32;
-        const size_t nd = (k_bits == 4 ? 4 : 2) + 1;   // Horner digits and the extra low one
         w.qdig = align256(off);
-        off = w.qdig + units * cols * nd * (n_q_heads / n_kv_heads) * 4;
+        off = w.qdig + units * (size_t)qd_stride(k_bits, head_dim, n_q_heads / n_kv_heads) * 4;
         w.qsc = align256(off);
         off = w.qsc + P * sizeof(float);
         w.qflag = align256(off);
@@ -512,7 +517,7 @@ size_t kvq_workspace_bytes(const kvq_cache *c, int n_q_heads, int max_seq_len, i
 // `ap` (a decode step), the step's append runs first: in the same launch as
 // the query prep on an integer cache, as its own launch otherwise.  Every
 // check runs before anything is enqueued.
-enum { PHASE_PREP = 1, PHASE_SPLIT = 2 };
+enum { PHASE_PREP = 1, PHASE_SPLIT = 2, PHASE_STEP = 4 };
 
 // kvq_decode_step merges inside the split kernel up to this many chunks
 constexpr int FUSED_MERGE_MAX_CHUNKS = 4;
@@ -530,10 +535,14 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
     if ((st = check_pointers(c))) return st;
     if (phases != (PHASE_PREP | PHASE_SPLIT) && !quant_modes(c))
         return fail(KVQ_ERR_BITS, "only 8/4-bit caches have a separate query preparation");
-    if (((phases & PHASE_PREP) && !q) || ((phases & PHASE_SPLIT) && !seq_len) || !workspace)
+    if ((phases & PHASE_STEP) && (nc != 1 || !out || !ap))
+        return fail(KVQ_ERR_ARG, "a one-launch step needs one chunk, the output and the step's rows");
+    const bool uses_q = (phases & (PHASE_PREP | PHASE_STEP)) != 0;
+    const bool uses_len = (phases & (PHASE_SPLIT | PHASE_STEP)) != 0;
+    if ((uses_q && !q) || (uses_len && !seq_len) || !workspace)
         return fail(KVQ_ERR_NULL, "q / seq_len / workspace is NULL");
-    if ((phases & PHASE_PREP) && !aligned(q, 16)) return fail(KVQ_ERR_ALIGN, "q must be 16-byte aligned");
-    if ((phases & PHASE_SPLIT) && !aligned(seq_len, 4)) return fail(KVQ_ERR_ALIGN, "seq_len must be 4-byte aligned");
+    if (uses_q && !aligned(q, 16)) return fail(KVQ_ERR_ALIGN, "q must be 16-byte aligned");
+    if (uses_len && !aligned(seq_len, 4)) return fail(KVQ_ERR_ALIGN, "seq_len must be 4-byte aligned");
     if (!aligned(workspace, 256)) return fail(KVQ_ERR_ALIGN, "workspace must be 256-byte aligned");
     const size_t need = cache_ws_bytes(c, n_q_heads, nc);
     if (workspace_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
@@ -584,12 +593,14 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
     int32_t *qdig = reinterpret_cast<int32_t *>(ws + wl.qdig);
     float *qsc = reinterpret_cast<float *>(ws + wl.qsc);
     int32_t *qflag = reinterpret_cast<int32_t *>(ws + wl.qflag);
-    if (out && phases != (PHASE_PREP | PHASE_SPLIT)) return fail(KVQ_ERR_ARG, "a fused combine needs both phases");
-    int *cnt = out ? reinterpret_cast<int *>(ws + wl.cnt) : nullptr;
+    const bool one_launch = (phases & PHASE_STEP) != 0;
+    if (out && !one_launch && phases != (PHASE_PREP | PHASE_SPLIT))
+        return fail(KVQ_ERR_ARG, "a fused combine needs both phases");
+    int *cnt = out && !one_launch ? reinterpret_cast<int *>(ws + wl.cnt) : nullptr;
     const unsigned units = (unsigned)(c->batch * c->n_kv_heads);
     if (ap && ap_grid.x > 0 && (unsigned long long)ap_grid.x * ap_grid.y * 2 + units > 0x7FFFFFFFull)
         return fail(KVQ_ERR_SHAPE, "batch * n_new too large for a fused step");
-    if (phases & PHASE_PREP) {
+    if ((phases & PHASE_PREP) && !one_launch) {
         if (ap && ap_grid.x > 0) {
             const unsigned n_app = ap_grid.x * ap_grid.y * 2;
             hipLaunchKernelGGL(sprep, dim3(n_app + units), dim3(256), 0, st_, *ap, (int)ap_grid.x, (int)ap_grid.y, q,
@@ -600,7 +611,7 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
         const int hs = hip_status("query prep launch");
         if (hs) return hs;
     }
-    if (!(phases & PHASE_SPLIT)) return KVQ_OK;
+    if (!(phases & (PHASE_SPLIT | PHASE_STEP))) return KVQ_OK;
 
     QuantParams p;
     p.k_codes = static_cast<const uint8_t *>(c->k_codes);
@@ -626,6 +637,20 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
     p.n_chunks = nc;
     p.cnt = cnt;
     p.out = out;
+    p.step = one_launch ? 1 : 0;
+    if (one_launch) {
+        if (ap_grid.x > 0) {
+            p.ap = *ap;
+        } else {
+            std::memset(&p.ap, 0, sizeof(p.ap));     // no rows to store (n_new == 0)
+        }
+        p.q = q;
+        p.qk_scale = qk_scale;
+    } else {
+        std::memset(&p.ap, 0, sizeof(p.ap));
+        p.q = nullptr;
+        p.qk_scale = 0.0f;
+    }
     const bool pr = per_row(c);
     const int gph = groups_per_head(c);
     if (pr) {                                        // strides per storage unit (sequence or page)
@@ -715,11 +740,16 @@ int kvq_decode_step(const kvq_cache *c, const float *k_new, const float *v_new, 
     AppendParams ap;
     dim3 ag;
     if ((st = prepare_append(c, k_new, v_new, n_new, start_pos, &ap, &ag))) return st;
-    // Few chunks per (sequence, KV head): two launches, the split kernel's
-    // last workgroup of each merging the partials (a short split kernel, where
-    // a third launch costs more than that merge).  More chunks: the merge as a
-    // launch of its own (the in-kernel merge adds a store wait to every
-    // workgroup and a serial merge at the end).
+    // One chunk per (sequence, KV head): one launch, each workgroup storing
+    // its head's rows, preparing its query and writing out.  Few chunks: two
+    // launches, the split kernel's last workgroup of each (sequence, KV head)
+    // merging the partials (a short split kernel, where a third launch costs
+    // more than that merge).  More chunks: the merge as a launch of its own
+    // (the in-kernel merge adds a store wait to every workgroup and a serial
+    // merge at the end).
+    if (quant_modes(c) && nc == 1)
+        return enqueue_partials(c, q, n_q_heads, seq_len, max_seq_len, softmax_scale, ch, workspace, workspace_bytes,
+                                stream, &ap, ag, PHASE_STEP, out);
     if (quant_modes(c) && nc <= FUSED_MERGE_MAX_CHUNKS)
         return enqueue_partials(c, q, n_q_heads, seq_len, max_seq_len, softmax_scale, ch, workspace, workspace_bytes,
                                 stream, &ap, ag, PHASE_PREP | PHASE_SPLIT, out);

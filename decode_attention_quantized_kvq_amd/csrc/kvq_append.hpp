@@ -292,6 +292,73 @@ __global__ __launch_bounds__(APPEND_THREADS) void append_kernel(AppendParams p)
     append_block(p, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
+// The call's rows of sequence b for KV head kvh, both sides of an 8/4-bit
+// cache, stored by the one workgroup that then attends over (b, kvh): wave 0
+// the keys, wave 1 the values, lane l the values 8l .. 8l+7 of the row
+// (waves 2 and 3 store nothing).  The encoding, slots and layout are
+// append_block's, value for value; with one scale per position over all
+// heads each of the n_kv_heads workgroups of sequence b computes that scale
+// from the whole row and stores the same bits.
+template <int HD>
+__device__ __forceinline__ void append_head_rows(const AppendParams &p, int b, int kvh)
+{
+    constexpr int LPH = HD / APPEND_ELEMS;             // lanes holding the head's row
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (wave >= 2 || p.n_new <= 0) return;             // wave-uniform
+    const int side = wave;
+    const int bits = p.bits[side];
+    const float qmax = bits == 8 ? 127.0f : 7.0f;
+    const int start = p.start_pos[b];
+    const float *src = p.src[side];
+    const int R = p.n_kv_heads * HD;
+    const bool act = lane < LPH;
+    const int c0 = act ? lane * APPEND_ELEMS : 0;
+    for (int i = 0; i < p.n_new; i++) {
+        const int lslot = append_slot(p, start, start + i);
+        if (lslot < 0) continue;                       // wave-uniform
+        int ub = b, slot = lslot;
+        if (p.page_shift > 0) {
+            ub = p.block_table[(size_t)b * p.pages_per_seq + (lslot >> p.page_shift)];
+            if (ub < 0 || ub >= p.n_pages) continue;   // no page: not stored
+            slot = lslot & ((1 << p.page_shift) - 1);
+        }
+        float x[8];
+        if (act)
+            load8(src + (((size_t)(b * p.n_kv_heads + kvh) * p.n_new + i) * HD + c0), x);
+        else
+#pragma unroll
+            for (int j = 0; j < 8; j++) x[j] = 0.0f;
+        float amax = 0.0f;
+        if (p.per_row) {
+            // one scale over the row of all heads
+            for (int e0 = lane * APPEND_ELEMS; e0 < R; e0 += 64 * APPEND_ELEMS) {
+                const int h = e0 / HD, c = e0 - h * HD;
+                float y[8];
+                load8(src + (((size_t)(b * p.n_kv_heads + h) * p.n_new + i) * HD + c), y);
+#pragma unroll
+                for (int j = 0; j < 8; j++) amax = fmaxf(amax, fabsf(y[j]));
+            }
+            amax = wave_max(amax);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; j++) amax = fmaxf(amax, fabsf(x[j]));
+            amax = group_max_abs(amax, p.group / APPEND_ELEMS);
+        }
+        const uint16_t sh = scale_bits_from_amax(amax, qmax);
+        const float sc = f16_bits_to_f32(sh);
+        uint32_t w0, w1;
+        encode8(x, sc, qmax, bits, w0, w1);
+        if (!act) continue;
+        const size_t unit = (size_t)ub * p.n_kv_heads + kvh;
+        store_codes(p.codes[side], unit, p.cap4, p.cap64, slot, HD * bits / 8, c0, bits, side == 1, w0, w1);
+        if (p.per_row) {
+            if (lane == 0) p.scales[side][(size_t)ub * p.cap_u + slot] = sh;
+        } else if (c0 % p.group == 0) {
+            p.scales[side][(unit * p.cap_u + slot) * (size_t)(HD / p.group) + c0 / p.group] = sh;
+        }
+    }
+}
+
 // ------------------------------------------------------------------------
 // Bulk appends (a prompt's rows in one call) into 8/4-bit caches without a
 // window and with scales per head or per group: one workgroup per 64-slot

@@ -55,6 +55,7 @@
 // (m, l, acc) written.  LDS use does not depend on the chunk length.
 #pragma once
 
+#include "kvq_append.hpp"
 #include "kvq_combine.hpp"
 #include "kvq_device.hpp"
 
@@ -76,6 +77,12 @@ constexpr int Q_RANGE = 30000;
 // head of the unit; its base keeps |d| within the key width's signed digit
 constexpr float Q_OUTLIER = 5.0f;
 __host__ __device__ constexpr int qx_base(int KB) { return KB == 4 ? 14 : 254; }
+// int32 words between two units' query digit blocks ([ND + 1][K_COLS][G]),
+// padded to 256 bytes so that no two units share a cache line
+__host__ __device__ constexpr int qd_stride(int KB, int HD, int G)
+{
+    return (((KB == 4 ? 4 : 2) + 1) * (HD * KB / 32) * G + 63) / 64 * 64;
+}
 constexpr int QD_PF = 16;       // value group loads in flight per lane
 constexpr int W_RANGE = 32767;
 
@@ -105,7 +112,7 @@ struct QuantParams {
     const uint8_t *v_codes;    // [B][Hkv][cap4/4][V_ROW][4]  (4 positions interleaved per byte)
     const uint16_t *k_scales;
     const uint16_t *v_scales;
-    const int32_t *qdig;       // [B*Hkv][ND + 1][K_COLS][G] packed query digits (digit-major; digit ND the extra low one)
+    const int32_t *qdig;       // [B*Hkv][qd_stride] packed query digits: [ND + 1][K_COLS][G] (digit-major; digit ND the extra low one)
     const float *qsc;          // [B*Hq]: s_q * softmax_scale * log2(e)
     const int32_t *qflag;      // [B*Hkv]: 1 when the query carries its extra low digit
     const int32_t *seq_len;
@@ -124,6 +131,14 @@ struct QuantParams {
     // its (sequence, KV head) into out.  cnt == nullptr: partials only.
     int *cnt;
     float *out;
+    // one-launch decode step (step != 0; one chunk per (sequence, KV head)):
+    // each workgroup first stores the step's rows of its head (ap) and
+    // prepares its query (q, qk_scale: digits into its own slot of qdig,
+    // scales and flag kept in registers), and writes out instead of partials
+    int step;
+    AppendParams ap;
+    const float *q;
+    float qk_scale;
     long long k_sc_b, k_sc_h;
     int k_sc_t;
     long long v_sc_b, v_sc_h;
@@ -180,53 +195,50 @@ __host__ __device__ inline QuantSmem quant_smem(int G, int HD, int vg)
 // digit ND is zero and qflag[unit] = 0.
 // ---------------------------------------------------------------------------
 template <int KB, int HD, int G>
-__device__ __forceinline__ void qprep_block(const float *__restrict__ q, int32_t *__restrict__ qdig,
-                                            float *__restrict__ qsc, int32_t *__restrict__ qflag, float qk_scale,
-                                            int unit, int *cnt)
+__device__ __forceinline__ void qprep_core(const float *__restrict__ qh, int32_t *__restrict__ qd, float *s_amax,
+                                           int *s_xflag, float *s_qv)
 {
+    // qh: the unit's G query heads [G][HD]; qd: its digits [ND + 1][K_COLS][G];
+    // s_amax [G], s_xflag, s_qv [G][HD]: LDS.  On return (after a barrier)
+    // s_amax holds max|q| per head and s_xflag whether the extra digit is on.
     constexpr int K_COLS = HD * KB / 32;
     constexpr int ND = KB == 4 ? 4 : 2;
     constexpr int CPC = KB == 4 ? 8 : 4;
     constexpr int BITS = KB == 4 ? 4 : 8;
     constexpr int XMAX = (1 << (BITS - 1)) - 1;
-    // unit = b * Hkv + kvh
-    const float *qh = q + (size_t)unit * G * HD;         // query heads unit*G .. unit*G+G-1
-    __shared__ float amax[G];
-    __shared__ int xflag;
-    __shared__ float qv[G * HD];                         // q, read from memory once
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid == 0) xflag = 0;
+    if (tid == 0) *s_xflag = 0;
     __syncthreads();
     for (int h = wave; h < G; h += 4) {
         float a = 0.0f, ss = 0.0f;
         for (int c = lane; c < HD; c += 64) {
             const float v = qh[h * HD + c];
-            qv[h * HD + c] = v;
+            s_qv[h * HD + c] = v;
             a = fmaxf(a, fabsf(v));
             ss = fmaf(v, v, ss);
         }
         a = wave_max(a);
         ss = wave_sum(ss);
         if (lane == 0) {
-            amax[h] = a;
+            s_amax[h] = a;
             // max|q| > 5 rms(q): the 16-bit form would leave the other
             // channels too few bits
-            if (a * a > Q_OUTLIER * Q_OUTLIER * (ss / (float)HD)) atomicOr(&xflag, 1);
+            if (a * a > Q_OUTLIER * Q_OUTLIER * (ss / (float)HD)) atomicOr(s_xflag, 1);
         }
     }
     __syncthreads();
-    const bool xq = xflag != 0;
+    const bool xq = *s_xflag != 0;
     constexpr float XB = (float)qx_base(KB);
     for (int i = tid; i < K_COLS * G; i += 256) {
         const int col = i / G, h = i - col * G;
-        const float sq = amax[h] / (float)Q_RANGE;
+        const float sq = s_amax[h] / (float)Q_RANGE;
         const float inv = sq > 0.0f ? 1.0f / sq : 0.0f;
         uint32_t d[ND + 1];
 #pragma unroll
         for (int j = 0; j <= ND; j++) d[j] = 0;
 #pragma unroll
         for (int e = 0; e < CPC; e++) {
-            const float qq = qv[h * HD + col * CPC + e];
+            const float qq = s_qv[h * HD + col * CPC + e];
             int qi = (int)fminf(fmaxf(rintf(qq * inv), -(float)Q_RANGE), (float)Q_RANGE);
             if (xq) {
                 // the rest of q / s_q beyond q_int (one rounding), in 1/base units
@@ -243,11 +255,25 @@ __device__ __forceinline__ void qprep_block(const float *__restrict__ q, int32_t
             }
         }
 #pragma unroll
-        for (int j = 0; j <= ND; j++) qdig[(((size_t)unit * (ND + 1) + j) * K_COLS + col) * G + h] = (int32_t)d[j];
+        for (int j = 0; j <= ND; j++) qd[((size_t)j * K_COLS + col) * G + h] = (int32_t)d[j];
     }
+    __syncthreads();
+}
+
+template <int KB, int HD, int G>
+__device__ __forceinline__ void qprep_block(const float *__restrict__ q, int32_t *__restrict__ qdig,
+                                            float *__restrict__ qsc, int32_t *__restrict__ qflag, float qk_scale,
+                                            int unit, int *cnt)
+{
+    // unit = b * Hkv + kvh
+    __shared__ float amax[G];
+    __shared__ int xflag;
+    __shared__ float qv[G * HD];                         // q, read from memory once
+    qprep_core<KB, HD, G>(q + (size_t)unit * G * HD, qdig + (size_t)unit * qd_stride(KB, HD, G), amax, &xflag, qv);
+    const int tid = threadIdx.x;
     if (tid < G) qsc[unit * G + tid] = amax[tid] / (float)Q_RANGE * qk_scale;
     if (tid == 0) {
-        qflag[unit] = xq ? 1 : 0;
+        qflag[unit] = xflag;
         if (cnt) cnt[unit] = 0;                      // the fused step's ticket counter
     }
 }
@@ -337,6 +363,32 @@ void decode_quant_kernel(QuantParams p)
     const size_t ml_hs = (size_t)p.n_chunks * 2;
     const size_t acc_hs = (size_t)p.n_chunks * HD;
 
+    // Query scales (log2 units; floored so that a zero query keeps -inf
+    // scores at -inf: 0 * -inf would be NaN) and the extra-digit flag.
+    float qs[G];
+    bool xq;
+    if (p.step) {
+        // (block-uniform) this is the only workgroup of its (sequence, KV
+        // head): the step's rows of its head, then its query's digits; every
+        // store is complete before a wave reads the cache or the digits
+        append_head_rows<HD>(p.ap, b, kvh);
+        float *s_qv = reinterpret_cast<float *>(smem);
+        float *s_amax = s_qv + G * HD;
+        int *s_xflag = reinterpret_cast<int *>(s_amax + G);
+        qprep_core<KB, HD, G>(p.q + row0 * HD, const_cast<int32_t *>(p.qdig) + (size_t)bh * qd_stride(KB, HD, G),
+                              s_amax, s_xflag, s_qv);
+        __builtin_amdgcn_s_waitcnt(WAIT_VMEM_ALL);
+        __syncthreads();
+#pragma unroll
+        for (int h = 0; h < G; h++) qs[h] = fmaxf(s_amax[h] / (float)Q_RANGE * p.qk_scale, 1e-30f);
+        xq = *s_xflag != 0;
+        __syncthreads();                             // the LDS is reused below
+    } else {
+#pragma unroll
+        for (int h = 0; h < G; h++) qs[h] = fmaxf(p.qsc[row0 + h], 1e-30f);
+        xq = ((const KVQ_CONST int32_t *)p.qflag)[bh] != 0;
+    }
+
     // (block-uniform; the ticket needs one int of LDS, free by then)
     auto finish = [&]() {
         if (p.cnt)
@@ -345,6 +397,10 @@ void decode_quant_kernel(QuantParams p)
     };
 
     if (n_tok <= 0) {
+        if (p.step) {                                // nothing attended: out = 0
+            for (int i = tid; i < G * HD; i += QD_THREADS) p.out[row0 * HD + i] = 0.0f;
+            return;
+        }
         for (int i = tid; i < G * HD; i += QD_THREADS) store_partial(&acc0[(i / HD) * acc_hs + (i % HD)], 0.0f);
         if (tid < G) {
             store_partial(&ml0[tid * ml_hs], -INFINITY);
@@ -366,11 +422,6 @@ void decode_quant_kernel(QuantParams p)
     const int s0 = wave * sub;
     const int nw = max(min(sub, n_tok - s0), 0);     // positions of this wave
 
-    // (floored so that a zero query keeps -inf scores at -inf: 0 * -inf
-    // would be NaN)
-    float qs[G];
-#pragma unroll
-    for (int h = 0; h < G; h++) qs[h] = fmaxf(p.qsc[row0 + h], 1e-30f);
 
     // ---- key stream: tiles of 64 positions, one lane per position, loaded
     // one tile ahead into the other of two register sets; the descriptors
@@ -405,9 +456,7 @@ void decode_quant_kernel(QuantParams p)
         if constexpr (PAGED) return (w0 + tw) & ((1 << p.page_shift) - 1);
         else return w0 + tw;
     };
-    const KVQ_CONST int32_t *qd = (const KVQ_CONST int32_t *)(p.qdig + (size_t)bh * T::NDX * T::K_COLS * G);
-    // the query's extra low digit (wave-uniform: one flag per (sequence, KV head))
-    const bool xq = ((const KVQ_CONST int32_t *)p.qflag)[bh] != 0;
+    const KVQ_CONST int32_t *qd = (const KVQ_CONST int32_t *)(p.qdig + (size_t)bh * qd_stride(KB, HD, G));
     constexpr float XINV = 1.0f / (float)qx_base(KB);
     const uint32_t ko = lane * 16;
     const uint32_t kso = lane * p.k_sc_t * 2, vso = lane * p.v_sc_t * 2;
@@ -917,8 +966,21 @@ void decode_quant_kernel(QuantParams p)
             const float mv = pm[w * G + h];
             if (mv != -INFINITY) s = fmaf(__builtin_amdgcn_exp2f(mv - m), red[(w * G + h) * HD + c], s);
         }
-        store_partial(&acc0[h * acc_hs + c], s);
+        if (p.step) {
+            // the only chunk: out = acc / l (the merge of one chunk, whose
+            // factor 2^(m - m) is 1)
+            float l = 0.0f;
+#pragma unroll
+            for (int w = 0; w < QD_WAVES; w++) {
+                const float mv = pm[w * G + h];
+                if (mv != -INFINITY) l = fmaf(__builtin_amdgcn_exp2f(mv - m), pl[w * G + h], l);
+            }
+            p.out[(row0 + h) * HD + c] = m != -INFINITY && l > 0.0f ? s / l : 0.0f;
+        } else {
+            store_partial(&acc0[h * acc_hs + c], s);
+        }
     }
+    if (p.step) return;
     if (tid < G) {
         float m = pm[tid];
 #pragma unroll

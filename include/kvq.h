@@ -229,11 +229,13 @@ int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n
  * fixed (kvq_decode_step's in-kernel merge takes an atomic ticket only to
  * decide which workgroup merges, not in what order).
  *
- * kvq_chunk_tokens() returns the library's chunk: the largest power of two
- * <= 2048 slots that still gives >= 1024 workgroups (sequences x KV heads x
- * chunks), at least 512, for 8/4-bit caches; at most 1024, >= 2048
- * workgroups, at least 64 slots and within the LDS budget, for 16/32-bit
- * caches.
+ * kvq_chunk_tokens() returns the library's chunk: for 8/4-bit caches, one
+ * chunk per (sequence, KV head) (512 or 1024 slots) when the context is at
+ * most 1024 slots and 512-slot chunks would give at most 1024 workgroups,
+ * else the largest power of two <= 2048 slots that still gives >= 1024
+ * workgroups (sequences x KV heads x chunks), at least 512; for 16/32-bit
+ * caches at most 1024, >= 2048 workgroups, at least 64 slots and within the
+ * LDS budget.
  */
 int kvq_chunk_tokens(const kvq_cache *c, int n_q_heads, int max_seq_len);
 
@@ -280,15 +282,17 @@ int kvq_decode_attn(const kvq_cache *c, const float *q, int n_q_heads, const int
  * adds only the new token's K and V to the cache, then attends over it):
  * exactly kvq_append(c, k_new, v_new, n_new, start_pos, stream) followed by
  * kvq_decode_attn(c, q, ..., stream), with the same arguments, rules and
- * results, bit for bit.  On an 8/4-bit cache the append and the query's
- * fixed-point preparation share the first launch, then the split kernel,
- * then the combine; when max_seq_len (capped at the capacity) spans at
- * most 4 chunks, the split kernel's last workgroup per (sequence, KV head)
- * merges the partials itself (same arithmetic, one launch fewer for short
- * contexts, where the launches dominate).  On a 16/32-bit cache: append,
- * split, combine.  The workspace holds the merge's ticket counters, which
- * the first launch zeroes each step (no memset, so the step can be captured
- * in a graph).
+ * results, bit for bit.  On an 8/4-bit cache whose max_seq_len (capped at
+ * the capacity) fits one chunk: one launch, each workgroup storing the
+ * step's rows of its (sequence, KV head), preparing its query and writing
+ * out.  With more chunks the append and the query's fixed-point preparation
+ * share the first launch, then the split kernel, then the combine; when
+ * max_seq_len spans at most 4 chunks, the split kernel's last workgroup per
+ * (sequence, KV head) merges the partials itself (same arithmetic, one
+ * launch fewer for short contexts, where the launches dominate).  On a
+ * 16/32-bit cache: append, split, combine.  The workspace holds the merge's
+ * ticket counters, which the first launch zeroes each step (no memset, so
+ * the step can be captured in a graph).
  * Every argument is checked before anything is enqueued; on an error
  * nothing is.
  */

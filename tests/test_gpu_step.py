@@ -1,0 +1,160 @@
+"""The one-launch decode step: when a step's context fits one chunk per
+(sequence, KV head) on an 8/4-bit cache, kvq_decode_step runs as a single
+kernel whose workgroups store their head's new rows, prepare their query and
+write the output.  It must leave the cache and the output bit for bit as
+kvq_append followed by kvq_decode_attn with the same chunk does (a split
+launch of one chunk and the combine), and match the oracle."""
+import numpy as np
+import pytest
+
+from gpu_util import assert_close, check_codes, linear_slots, need_gpu, paged_table, softmax_default, window_slots
+
+pytestmark = pytest.mark.gpu
+
+PAIRS = [(8, 8), (8, 4), (4, 4), (4, 8)]
+
+
+def _data(B, H, n, HD, Hq, seed):
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((B, H, n, HD)).astype(np.float32)
+    V = rng.standard_normal((B, H, n, HD)).astype(np.float32)
+    q = rng.standard_normal((B, Hq, HD)).astype(np.float32)
+    return K, V, q
+
+
+def _pair(oq, kb, vb, gs, B, H, G, HD, n, n_new, chunk, seed, n_anchor=0, window=0, lens=None, page=0,
+          scale=0.0):
+    """One step through kvq_decode_step on one cache and through kvq_append +
+    kvq_decode_attn on another; the two must agree bit for bit."""
+    kvq = need_gpu()
+    import torch
+    from workloads.device import positions, to_device
+    Hq = H * G
+    K, V, q = _data(B, H, n, HD, Hq, seed)
+    cap = n_anchor + window if window else n
+    if page:
+        cap = (cap + page - 1) // page * page
+        pps = cap // page
+        table = paged_table(B, pps, B * pps + 2, seed)   # the same pages for both caches
+        tables = [table, table.copy()]
+        caches = [kvq.alloc_cache(B, H, HD, cap, kb, vb, gs, n_anchor, window, page_size=page,
+                                  n_pages=B * pps + 2, block_table=to_device(t)) for t in tables]
+    else:
+        caches = [kvq.alloc_cache(B, H, HD, cap, kb, vb, gs, n_anchor, window) for _ in range(2)]
+    n0 = n - n_new
+    for c in caches:
+        if n0:
+            kvq.kvq_append(c, to_device(K[:, :, :n0]), to_device(V[:, :, :n0]), n0, positions([0] * B))
+    kn, vn, qd = to_device(K[:, :, n0:]), to_device(V[:, :, n0:]), to_device(q)
+    lens = lens or [n] * B
+    pos, sl = positions([n0] * B), positions(lens)
+    max_len = max(max(lens), 1)
+    ws_bytes = kvq.kvq_workspace_bytes(caches[0], Hq, max_len, chunk)
+    L = min(max_len, cap)
+    ch = chunk or kvq.kvq_chunk_tokens(caches[0], Hq, max_len)
+    assert L <= ch                                   # one chunk: the one-launch path
+    outs = [torch.full((B, Hq, HD), 7.0, dtype=torch.float32, device="cuda") for _ in range(2)]
+    wss = [torch.full((ws_bytes // 4 + 64,), 3.0, dtype=torch.float32, device="cuda") for _ in range(2)]
+    kvq.kvq_decode_step(caches[0], kn, vn, n_new, pos, qd, Hq, sl, max_len, scale, chunk, outs[0], wss[0], ws_bytes)
+    kvq.kvq_append(caches[1], kn, vn, n_new, pos)
+    kvq.kvq_decode_attn(caches[1], qd, Hq, sl, max_len, scale, chunk, outs[1], wss[1], ws_bytes)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]), "one-launch step differs from append + decode_attn"
+    for name in ("k_codes", "v_codes", "k_scales", "v_scales"):
+        a, b_ = getattr(caches[0], name), getattr(caches[1], name)
+        if a is not None:
+            assert torch.equal(a, b_), name
+    got = outs[0].cpu().numpy()
+    if not page:
+        slots = window_slots(oq, n, n_anchor, window) if window else linear_slots(n, cap)
+        check_codes(oq, caches[0], K, V, slots)
+    sigma = scale or softmax_default(HD)
+    for b in range(B):
+        Lb = n if window else min(lens[b], cap)
+        if Lb == 0:
+            assert np.all(got[b] == 0)
+            continue
+        want = oq.decode_step(kb, vb, gs, n_anchor, window, K[b][:, :Lb], V[b][:, :Lb], q[b], sigma)
+        assert_close(got[b], want, f"one-launch step kb={kb} vb={vb} g={gs} b={b}")
+    return caches[0], outs[0]
+
+
+@pytest.mark.parametrize("kb,vb", PAIRS)
+@pytest.mark.parametrize("group", [0, 32, -1])
+@pytest.mark.parametrize("G", [1, 4, 8])
+@pytest.mark.parametrize("n_new", [0, 1, 3])
+def test_one_launch_step(oq, kb, vb, group, G, n_new):
+    HD = 64 if G == 8 else 128
+    H = 2
+    gs = HD if group == 0 else (H * HD if group == -1 else group)
+    _pair(oq, kb, vb, gs, B=2, H=H, G=G, HD=HD, n=700, n_new=n_new, chunk=1024, seed=kb * 13 + vb + G + n_new)
+
+
+@pytest.mark.parametrize("kb,vb", [(8, 8), (4, 4)])
+def test_one_launch_step_library_chunk(oq, kb, vb):
+    """Short contexts (Tiny: 257 positions; the mni-ml-like loop's 256) take
+    the one-launch path with the library's own chunk."""
+    _pair(oq, kb, vb, 64, B=1, H=4, G=1, HD=64, n=257, n_new=1, chunk=0, seed=3)
+    _pair(oq, kb, vb, 8 * 64, B=1, H=8, G=1, HD=64, n=256, n_new=1, chunk=0, seed=4)
+
+
+@pytest.mark.parametrize("kb,vb", [(8, 4), (4, 4)])
+def test_one_launch_step_window(oq, kb, vb):
+    """Anchors + ring (64 + 512 slots) after 1500 positions, three rows per step."""
+    _pair(oq, kb, vb, 128, B=2, H=2, G=4, HD=128, n=1500, n_new=3, chunk=1024, seed=11, n_anchor=64, window=512)
+
+
+@pytest.mark.parametrize("kb,vb", [(8, 8), (4, 4)])
+def test_one_launch_step_paged(oq, kb, vb):
+    _pair(oq, kb, vb, 128, B=3, H=2, G=4, HD=128, n=640, n_new=1, chunk=1024, seed=12, page=128)
+
+
+def test_one_launch_step_ragged(oq):
+    """A sequence that attends nothing (its rows are still stored), one that
+    attends a prefix, and an explicit softmax scale."""
+    _pair(oq, 8, 4, 128, B=3, H=2, G=4, HD=128, n=600, n_new=1, chunk=1024, seed=13, lens=[600, 0, 300])
+    _pair(oq, 4, 4, 32, B=2, H=2, G=4, HD=128, n=600, n_new=1, chunk=1024, seed=14, scale=0.5)
+
+
+def test_one_launch_step_graph(oq):
+    """The one-launch step captured in a HIP graph gives the eager output bit
+    for bit on every replay, with eager work between replays."""
+    kvq = need_gpu()
+    import torch
+    from workloads.device import positions, to_device
+    B, H, G, HD, n = 2, 2, 4, 128, 400
+    cache = kvq.alloc_cache(B, H, HD, n, 4, 4, HD)
+    K, V, q = _data(B, H, n, HD, H * G, 21)
+    kvq.kvq_append(cache, to_device(K[:, :, : n - 1]), to_device(V[:, :, : n - 1]), n - 1, positions([0, 0]))
+    k1, v1, qd = to_device(K[:, :, n - 1:]), to_device(V[:, :, n - 1:]), to_device(q)
+    pos, lens = positions([n - 1] * B), positions([n] * B)
+    assert kvq.kvq_chunk_tokens(cache, H * G, n) >= n          # one chunk: the one-launch path
+    ws_bytes = kvq.kvq_workspace_bytes(cache, H * G, n, 0)
+    ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")
+    out = torch.zeros((B, H * G, HD), dtype=torch.float32, device="cuda")
+
+    def step(st):
+        kvq.kvq_decode_step(cache, k1, v1, 1, pos, qd, H * G, lens, n, 0.0, 0, out, ws, ws_bytes, st)
+
+    step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    want = out.clone()
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        step(cs)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cs):
+        step(cs)
+    for r in range(3):
+        out.zero_()
+        ws.fill_(float(r + 1))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), f"replay {r}"
+    got = want.cpu().numpy()
+    for b in range(B):
+        ref = oq.decode_step(4, 4, HD, 0, 0, K[b], V[b], q[b], softmax_default(HD))
+        assert_close(got[b], ref, f"graph one-launch b={b}")
