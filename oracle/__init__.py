@@ -15,7 +15,12 @@ Functions (each cites the page passage its C counterpart follows):
 * ``encode_row`` / ``decode_row``: symmetric per-group quantization with one
   fp16 scale per group and nibble packing (TinyLoop five-modes table, INT8 KV
   and INT4-h rows; KVSplit key/value bit widths).
-* ``bytes_per_token``: TinyLoop memory-formula table.
+* ``quantize_group_asym`` / ``encode_rows_asym`` / ``decode_row_asym``: the
+  asymmetric codec, one fp16 scale and one integer zero point per group (the
+  mni-ml page names scale/zero-point metadata; the min/max affine form with
+  the range widened to contain zero is the reading taken).
+* ``bytes_per_token``: TinyLoop memory-formula table; ``bytes_per_token_zp``
+  the same with the asymmetric codec's metadata as this library stores it.
 * ``slot_of`` / ``attended_positions``: on-device page, sliding-window
   eviction (64 anchors + 1536 recent).
 * ``attend``: softmax attention of one query over the cached rows (mni-ml
@@ -90,6 +95,19 @@ def lib() -> ctypes.CDLL:
         L.oq_decode_step.argtypes = [c_i, c_i, c_i, c_i, c_i, c_i, c_i, P, P, c_l, P, c_i, c_i, c_i,
                                      ctypes.c_double, P]
         L.oq_decode_step.restype = c_i
+        L.oq_levels.argtypes = [c_i]
+        L.oq_levels.restype = c_i
+        L.oq_quantize_group_asym.argtypes = [P, c_i, c_i, P, P, P]
+        L.oq_quantize_group_asym.restype = None
+        L.oq_encode_row_asym.argtypes = [P, c_i, c_i, c_i, P, P, P]
+        L.oq_encode_row_asym.restype = c_i
+        L.oq_decode_row_asym.argtypes = [P, P, P, c_i, c_i, c_i, P]
+        L.oq_decode_row_asym.restype = c_i
+        L.oq_bytes_per_token_zp.argtypes = [c_i, c_i, c_i, c_i, c_i, c_i]
+        L.oq_bytes_per_token_zp.restype = ctypes.c_size_t
+        L.oq_decode_step_zp.argtypes = [c_i, c_i, c_i, c_i, c_i, c_i, c_i, c_i, P, P, c_l, P, c_i, c_i, c_i,
+                                        ctypes.c_double, P]
+        L.oq_decode_step_zp.restype = c_i
         L.oq_f16_from_f32_n.argtypes = [P, ctypes.c_size_t, P]
         L.oq_f16_from_f32_n.restype = None
         L.oq_f16_to_f64_n.argtypes = [P, ctypes.c_size_t, P]
@@ -193,9 +211,54 @@ def decode_row(payload, scales, n: int, g: int, bits: int) -> np.ndarray:
     return out
 
 
+def levels(bits: int) -> int:
+    return int(lib().oq_levels(bits))
+
+
+def quantize_group_asym(x, L: int) -> tuple[np.ndarray, int, int]:
+    """(codes uint8[g] in [0, L], scale bit pattern, zero point) of one group."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    codes = np.zeros(x.size, dtype=np.uint8)
+    sb = np.zeros(1, dtype=np.uint16)
+    zp = np.zeros(1, dtype=np.uint8)
+    lib().oq_quantize_group_asym(_ptr(x), x.size, L, _ptr(codes), _ptr(sb), _ptr(zp))
+    return codes, int(sb[0]), int(zp[0])
+
+
+def encode_rows_asym(x, g: int, bits: int) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """The asymmetric codec over the last axis of x (any leading shape):
+    (payload uint8[..., n*bits/8], scales uint16[..., n/g], zeros uint8[..., n/g])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    lead, n = x.shape[:-1], x.shape[-1]
+    flat = x.reshape(-1, n)
+    P = np.zeros((flat.shape[0], n * bits // 8), dtype=np.uint8)
+    S = np.zeros((flat.shape[0], n // g), dtype=np.uint16)
+    Z = np.zeros((flat.shape[0], n // g), dtype=np.uint8)
+    f = lib().oq_encode_row_asym
+    for i in range(flat.shape[0]):
+        if f(_ptr(flat[i]), n, g, bits, P[i].ctypes.data, S[i].ctypes.data, Z[i].ctypes.data) != 0:
+            raise ValueError("encode_rows_asym: bad arguments")
+    return P.reshape(*lead, -1), S.reshape(*lead, -1), Z.reshape(*lead, -1)
+
+
+def decode_row_asym(payload, scales, zeros, n: int, g: int, bits: int) -> np.ndarray:
+    p = np.ascontiguousarray(payload, dtype=np.uint8)
+    s = np.ascontiguousarray(scales, dtype=np.uint16)
+    z = np.ascontiguousarray(zeros, dtype=np.uint8)
+    out = np.zeros(n, dtype=np.float64)
+    if lib().oq_decode_row_asym(_ptr(p), _ptr(s), _ptr(z), n, g, bits, _ptr(out)) != 0:
+        raise ValueError("decode_row_asym: bad arguments")
+    return out
+
+
 # ---------------------------------------------------------------- accounting / window
 def bytes_per_token(k_bits: int, v_bits: int, n_kv_heads: int, head_dim: int, group_size: int) -> int:
     return int(lib().oq_bytes_per_token(k_bits, v_bits, n_kv_heads, head_dim, group_size))
+
+
+def bytes_per_token_zp(k_bits: int, v_bits: int, n_kv_heads: int, head_dim: int, group_size: int,
+                       asym: int) -> int:
+    return int(lib().oq_bytes_per_token_zp(k_bits, v_bits, n_kv_heads, head_dim, group_size, asym))
 
 
 def slot_of(pos: int, n_anchor: int, window: int) -> int:
@@ -220,10 +283,12 @@ def attend(q, K, V, scale: float) -> np.ndarray:
 
 
 def decode_step(k_bits: int, v_bits: int, group_size: int, n_anchor: int, window: int,
-                k_src, v_src, q, softmax_scale: float, hq_begin: int = 0, hq_end: int | None = None) -> np.ndarray:
+                k_src, v_src, q, softmax_scale: float, hq_begin: int = 0, hq_end: int | None = None,
+                asym: bool = False) -> np.ndarray:
     """One decode step of one sequence.
 
     k_src, v_src: float32 [n_kv_heads][n_pos][head_dim]; q: float32 [n_q_heads][head_dim].
+    asym: the 8/4-bit sides use the asymmetric (zero-point) codec.
     Returns float64 [hq_end-hq_begin][head_dim].
     """
     k_src = np.ascontiguousarray(k_src, dtype=np.float32)
@@ -234,9 +299,9 @@ def decode_step(k_bits: int, v_bits: int, group_size: int, n_anchor: int, window
     if hq_end is None:
         hq_end = hq
     out = np.zeros((hq_end - hq_begin, hd), dtype=np.float64)
-    rc = lib().oq_decode_step(k_bits, v_bits, group_size, hkv, hd, n_anchor, window,
-                              _ptr(k_src), _ptr(v_src), n_pos, _ptr(q), hq, hq_begin, hq_end,
-                              float(softmax_scale), _ptr(out))
+    rc = lib().oq_decode_step_zp(k_bits, v_bits, group_size, 1 if asym else 0, hkv, hd, n_anchor, window,
+                                 _ptr(k_src), _ptr(v_src), n_pos, _ptr(q), hq, hq_begin, hq_end,
+                                 float(softmax_scale), _ptr(out))
     if rc != 0:
         raise ValueError("decode_step: bad arguments")
     return out

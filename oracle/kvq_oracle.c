@@ -35,6 +35,12 @@
  *   - attention is softmax(scale * q.K^T) V over the attended positions, the
  *     newest position included; default scale 1/sqrt(head_dim).
  *   - query head hq reads KV head hq / (n_q_heads / n_kv_heads).
+ *   - the asymmetric (zero-point) codec [MNI: scale/zero-point metadata]:
+ *     per group, the range [lo, hi] = [min(0, min x), max(0, max x)] (zero
+ *     always representable), scale = fp16(RN((hi - lo) / L)) with L = 255 or
+ *     15 levels, zero point z = clamp(rint(-lo / scale), 0, L), code =
+ *     clamp(rint(x / scale) + z, 0, L), all quotients IEEE fp32; value =
+ *     (code - z) * scale.
  */
 #include <math.h>
 #include <stdint.h>
@@ -246,6 +252,94 @@ int oq_decode_row(const uint8_t *payload, const uint16_t *scales, int n, int g, 
 }
 
 /* ------------------------------------------------------------------ */
+/* Asymmetric (zero-point) quantization of one group [MNI].            */
+/* ------------------------------------------------------------------ */
+
+/* Code levels: 255 for 8 bits, 15 for 4 bits (codes 0 .. L). */
+int oq_levels(int bits)
+{
+    if (bits == 8) return 255;
+    if (bits == 4) return 15;
+    return 0;
+}
+
+/*
+ * One group of g float32 values -> g codes in [0, L], one fp16 scale (bit
+ * pattern) and one integer zero point in [0, L].  Dequantized value =
+ * (code - zero) * scale.  The range is widened to contain 0, so that 0 maps
+ * to the zero point exactly.  A zero scale (an all-zero group, or a range
+ * below the fp16 grid) gives codes 0 and zero point 0.
+ */
+void oq_quantize_group_asym(const float *x, int g, int levels, uint8_t *codes, uint16_t *scale_bits, uint8_t *zero)
+{
+    float lo = 0.0f, hi = 0.0f;
+    for (int i = 0; i < g; i++) {
+        if (x[i] < lo) lo = x[i];
+        if (x[i] > hi) hi = x[i];
+    }
+    float span = hi - lo;                                /* IEEE fp32 */
+    float s32 = span / (float)levels;                    /* IEEE fp32 divide */
+    uint16_t sh = oq_f16_scale_from_f32(s32);
+    float s = (float)oq_f16_to_f64(sh);                  /* the stored scale */
+    *scale_bits = sh;
+    if (s == 0.0f) {
+        *zero = 0;
+        for (int i = 0; i < g; i++) codes[i] = 0;
+        return;
+    }
+    float zf = rintf(-lo / s);                           /* IEEE fp32 divide, ties to even */
+    if (zf > (float)levels) zf = (float)levels;
+    if (zf < 0.0f) zf = 0.0f;
+    *zero = (uint8_t)zf;
+    for (int i = 0; i < g; i++) {
+        float c = rintf(x[i] / s) + zf;                  /* IEEE fp32 divide, ties to even */
+        if (c > (float)levels) c = (float)levels;
+        if (c < 0.0f) c = 0.0f;
+        codes[i] = (uint8_t)c;
+    }
+}
+
+/*
+ * Encode one stored row of n values (n a multiple of g) with the asymmetric
+ * codec: `payload` receives n*bits/8 bytes of codes (8 bits: one unsigned
+ * byte per element; 4 bits: element 2j in the low nibble of byte j),
+ * `scales` n/g fp16 patterns and `zeros` n/g zero points.  Returns 0, or -1
+ * on a bad argument.
+ */
+int oq_encode_row_asym(const float *x, int n, int g, int bits, uint8_t *payload, uint16_t *scales, uint8_t *zeros)
+{
+    int L = oq_levels(bits);
+    if (L == 0 || g <= 0 || n % g != 0 || (bits == 4 && g % 2 != 0))
+        return -1;
+    uint8_t *codes = (uint8_t *)malloc((size_t)g);
+    for (int grp = 0; grp < n / g; grp++) {
+        oq_quantize_group_asym(x + (size_t)grp * g, g, L, codes, &scales[grp], &zeros[grp]);
+        if (bits == 8) {
+            memcpy(payload + (size_t)grp * g, codes, (size_t)g);
+        } else {
+            uint8_t *dst = payload + (size_t)grp * g / 2;
+            for (int j = 0; j < g / 2; j++)
+                dst[j] = (uint8_t)((codes[2 * j] & 0x0Fu) | ((codes[2 * j + 1] & 0x0Fu) << 4));
+        }
+    }
+    free(codes);
+    return 0;
+}
+
+/* Inverse of oq_encode_row_asym: (code - zero) * scale, exactly in float64. */
+int oq_decode_row_asym(const uint8_t *payload, const uint16_t *scales, const uint8_t *zeros, int n, int g, int bits,
+                       double *out)
+{
+    if (oq_levels(bits) == 0 || g <= 0 || n % g != 0)
+        return -1;
+    for (int i = 0; i < n; i++) {
+        int code = bits == 8 ? payload[i] : ((payload[i / 2] >> (4 * (i & 1))) & 0x0F);
+        out[i] = (double)(code - (int)zeros[i / g]) * oq_f16_to_f64(scales[i / g]);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* Cache accounting [TL memory-formula table].                         */
 /* ------------------------------------------------------------------ */
 
@@ -278,6 +372,24 @@ size_t oq_bytes_per_token(int k_bits, int v_bits, int n_kv_heads, int head_dim, 
         }
     }
     return total;
+}
+
+/*
+ * The same with the asymmetric codec's metadata as this library stores it:
+ * each quantized side keeps, per group, a 32-bit word (the fp16 scale and a
+ * 16-bit field holding the zero point), so 4 bytes per group instead of 2.
+ * asym == 0 is oq_bytes_per_token.
+ */
+size_t oq_bytes_per_token_zp(int k_bits, int v_bits, int n_kv_heads, int head_dim, int group_size, int asym)
+{
+    size_t sym = oq_bytes_per_token(k_bits, v_bits, n_kv_heads, head_dim, group_size);
+    if (sym == 0 || !asym)
+        return sym;
+    size_t D = (size_t)n_kv_heads * (size_t)head_dim;
+    size_t extra = 0;
+    if (k_bits < 16) extra += 2 * (D / (size_t)group_size);
+    if (v_bits < 16) extra += 2 * (D / (size_t)group_size);
+    return sym + extra;
 }
 
 /* ------------------------------------------------------------------ */
@@ -368,11 +480,42 @@ void oq_attend(const double *q, const double *K, const double *V, long n, int hd
  * decoded back exactly, and query heads [hq_begin, hq_end) attend over it.
  * out: float64 [hq_end-hq_begin][head_dim].  Returns 0, or -1 on bad input.
  */
+/* One row of n values through the codec of one side and back (float64):
+ * the symmetric codec, or the asymmetric one (asym != 0) on 8/4-bit sides. */
+static int encode_decode(const float *x, int n, int g, int bits, int asym, uint8_t *payload, uint16_t *scales,
+                         uint8_t *zeros, double *out)
+{
+    if (asym && bits < 16) {
+        int rc = oq_encode_row_asym(x, n, g, bits, payload, scales, zeros);
+        return rc | oq_decode_row_asym(payload, scales, zeros, n, g, bits, out);
+    }
+    int rc = oq_encode_row(x, n, g, bits, payload, scales);
+    return rc | oq_decode_row(payload, scales, n, g, bits, out);
+}
+
+int oq_decode_step_zp(int k_bits, int v_bits, int group_size, int asym, int n_kv_heads, int head_dim,
+                      int n_anchor, int window,
+                      const float *k_src, const float *v_src, long n_pos,
+                      const float *q, int n_q_heads, int hq_begin, int hq_end,
+                      double softmax_scale, double *out);
+
 int oq_decode_step(int k_bits, int v_bits, int group_size, int n_kv_heads, int head_dim,
                    int n_anchor, int window,
                    const float *k_src, const float *v_src, long n_pos,
                    const float *q, int n_q_heads, int hq_begin, int hq_end,
                    double softmax_scale, double *out)
+{
+    return oq_decode_step_zp(k_bits, v_bits, group_size, 0, n_kv_heads, head_dim, n_anchor, window, k_src, v_src,
+                             n_pos, q, n_q_heads, hq_begin, hq_end, softmax_scale, out);
+}
+
+/* oq_decode_step with the codec chosen: asym != 0 encodes the 8/4-bit sides
+ * with the asymmetric (zero-point) codec. */
+int oq_decode_step_zp(int k_bits, int v_bits, int group_size, int asym, int n_kv_heads, int head_dim,
+                      int n_anchor, int window,
+                      const float *k_src, const float *v_src, long n_pos,
+                      const float *q, int n_q_heads, int hq_begin, int hq_end,
+                      double softmax_scale, double *out)
 {
     if (n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0 || hq_begin < 0 || hq_end > n_q_heads)
         return -1;
@@ -390,6 +533,7 @@ int oq_decode_step(int k_bits, int v_bits, int group_size, int n_kv_heads, int h
     float *row = (float *)malloc((size_t)D * sizeof(float));
     uint8_t *payload = (uint8_t *)malloc((size_t)D * 4);
     uint16_t *scales = (uint16_t *)malloc((size_t)D * sizeof(uint16_t));
+    uint8_t *zeros = (uint8_t *)malloc((size_t)D);
     double *dec = (double *)malloc((size_t)D * sizeof(double));
     double *K = (double *)malloc((size_t)(n_att > 0 ? n_att : 1) * head_dim * sizeof(double));
     double *V = (double *)malloc((size_t)(n_att > 0 ? n_att : 1) * head_dim * sizeof(double));
@@ -412,15 +556,14 @@ int oq_decode_step(int k_bits, int v_bits, int group_size, int n_kv_heads, int h
                         for (int h = 0; h < n_kv_heads; h++)
                             memcpy(row + (size_t)h * head_dim,
                                    src + ((size_t)h * n_pos + p) * head_dim, (size_t)head_dim * 4);
-                        rc |= oq_encode_row(row, D, D, bits, payload, scales);
-                        rc |= oq_decode_row(payload, scales, D, D, bits, dec);
+                        rc |= encode_decode(row, D, D, bits, asym, payload, scales, zeros, dec);
                         memcpy(dst + (size_t)i * head_dim, dec + (size_t)kv * head_dim,
                                (size_t)head_dim * sizeof(double));
                     } else {
                         int g = bits < 16 ? group_size : head_dim;
                         const float *r = src + ((size_t)kv * n_pos + p) * head_dim;
-                        rc |= oq_encode_row(r, head_dim, g, bits, payload, scales);
-                        rc |= oq_decode_row(payload, scales, head_dim, g, bits, dst + (size_t)i * head_dim);
+                        rc |= encode_decode(r, head_dim, g, bits, asym, payload, scales, zeros,
+                                            dst + (size_t)i * head_dim);
                     }
                 }
             }
@@ -431,7 +574,7 @@ int oq_decode_step(int k_bits, int v_bits, int group_size, int n_kv_heads, int h
         oq_attend(qd, K, V, n_att, head_dim, softmax_scale, out + (size_t)(hq - hq_begin) * head_dim);
     }
 
-    free(pos); free(row); free(payload); free(scales); free(dec); free(K); free(V); free(qd);
+    free(pos); free(row); free(payload); free(scales); free(zeros); free(dec); free(K); free(V); free(qd);
     return rc ? -1 : 0;
 }
 
