@@ -64,6 +64,7 @@ class kvq_cache(ctypes.Structure):
         ("page_size", ctypes.c_int32),
         ("n_pages", ctypes.c_int32),
         ("block_table", ctypes.c_void_p),
+        ("zero_point", ctypes.c_int32),
     ]
 
 
@@ -263,16 +264,17 @@ class Cache:
 
 def alloc_cache(batch: int, n_kv_heads: int, head_dim: int, capacity: int, k_bits: int, v_bits: int,
                 group_size: int = 0, n_anchor: int = 0, window: int = 0, device="cuda",
-                page_size: int = 0, n_pages: int = 0, block_table=None) -> Cache:
+                page_size: int = 0, n_pages: int = 0, block_table=None, zero_point: int = 0) -> Cache:
     """Allocate the four cache buffers with torch (zero-filled) and describe them.
 
     group_size 0 means one scale per head (group_size = head_dim).  page_size > 0
     allocates pools of n_pages pages of page_size slots instead of one region per
     sequence; block_table is then an int32 device tensor of batch x
-    (capacity / page_size) page indices, kept alive by the returned Cache."""
+    (capacity / page_size) page indices, kept alive by the returned Cache.
+    zero_point 1 selects the zero-point codec (scale buffers of 32-bit words)."""
     import torch
     d = kvq_cache(batch, n_kv_heads, head_dim, capacity, k_bits, v_bits, group_size or head_dim, n_anchor, window,
-                  None, None, None, None, page_size, n_pages, None)
+                  None, None, None, None, page_size, n_pages, None, zero_point)
     keep = []
     if page_size:
         if block_table is None:

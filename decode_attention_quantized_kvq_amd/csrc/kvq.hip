@@ -17,6 +17,18 @@
 
 using namespace kvq;
 
+// The split kernel's instances are compiled in their own translation units
+// (kvq_inst.hip, one per family), in parallel.
+namespace kvq {
+KVQ_QUANT_ALL(KVQ_QUANT_DECLARE)
+
+// the row append: grid (batch * n_new rows, passes over the row, side)
+__global__ __launch_bounds__(APPEND_THREADS) void append_kernel(AppendParams p)
+{
+    append_block(p, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+}
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -72,6 +84,12 @@ int check_geometry(const kvq_cache *c)
             return fail(KVQ_ERR_GROUP, "group_size %d must divide head_dim %d (multiple of 32) or equal n_kv_heads*head_dim",
                         g, c->head_dim);
     }
+    if (c->zero_point != 0 && c->zero_point != 1)
+        return fail(KVQ_ERR_ARG, "zero_point %d must be 0 or 1", c->zero_point);
+    if (c->zero_point && !quantized(c->k_bits))
+        return fail(KVQ_ERR_BITS, "the zero-point codec needs 8/4-bit sides (k_bits=%d)", c->k_bits);
+    if (c->zero_point && c->page_size != 0)
+        return fail(KVQ_ERR_ARG, "the zero-point codec is not available with paged storage");
     if (c->n_anchor < 0 || c->window < 0)
         return fail(KVQ_ERR_WINDOW, "n_anchor (%d) and window (%d) must be >= 0", c->n_anchor, c->window);
     if (c->window == 0 && c->n_anchor != 0)
@@ -138,7 +156,7 @@ size_t lds_bytes(const kvq_cache *c, int G, int chunk)
 {
     if (quant_modes(c)) {
         const int vg = groups_per_head(c);
-        return (size_t)quant_smem(G, c->head_dim, vg).total;
+        return (size_t)quant_smem(G, c->head_dim, vg, c->zero_point != 0).total;
     }
     return (size_t)float_smem(G, c->head_dim, chunk).total;
 }
@@ -184,7 +202,7 @@ int auto_chunk(const kvq_cache *c, int n_q_heads, int max_seq_len)
 
 using FloatFn = void (*)(FloatParams);
 using QuantFn = void (*)(QuantParams);
-using PrepFn = void (*)(const float *, int32_t *, float *, int32_t *, float, int *);
+using PrepFn = void (*)(const float *, int32_t *, float *, int32_t *, float, int *, int);
 
 template <int B, int HD, bool PG>
 FloatFn pick_float_g(int G)
@@ -210,46 +228,48 @@ FloatFn pick_float(int bits, int hd, int G, bool pg)
     return pg ? pick_float_p<true>(bits, hd, G) : pick_float_p<false>(bits, hd, G);
 }
 
-template <int KB, int VB, int HD, int KG, bool PG>
+template <int KB, int VB, int HD, int KG, bool PG, bool ZP>
 QuantFn pick_quant_g(int G)
 {
     switch (G) {
-    case 1: return decode_quant_kernel<KB, VB, HD, 1, KG, PG>;
-    case 2: return decode_quant_kernel<KB, VB, HD, 2, KG, PG>;
-    case 4: return decode_quant_kernel<KB, VB, HD, 4, KG, PG>;
-    case 8: return decode_quant_kernel<KB, VB, HD, 8, KG, PG>;
+    case 1: return decode_quant_kernel<KB, VB, HD, 1, KG, PG, ZP>;
+    case 2: return decode_quant_kernel<KB, VB, HD, 2, KG, PG, ZP>;
+    case 4: return decode_quant_kernel<KB, VB, HD, 4, KG, PG, ZP>;
+    case 8: return decode_quant_kernel<KB, VB, HD, 8, KG, PG, ZP>;
     }
     return nullptr;
 }
 
-template <int KB, int VB, bool PG>
+template <int KB, int VB, bool PG, bool ZP>
 QuantFn pick_quant_hd(int hd, int G, int kg)
 {
     if (hd == 64)
-        return kg == 2 ? pick_quant_g<KB, VB, 64, 2, PG>(G) : kg == 1 ? pick_quant_g<KB, VB, 64, 1, PG>(G) : nullptr;
+        return kg == 2 ? pick_quant_g<KB, VB, 64, 2, PG, ZP>(G) : kg == 1 ? pick_quant_g<KB, VB, 64, 1, PG, ZP>(G) : nullptr;
     switch (kg) {
-    case 1: return pick_quant_g<KB, VB, 128, 1, PG>(G);
-    case 2: return pick_quant_g<KB, VB, 128, 2, PG>(G);
-    case 4: return pick_quant_g<KB, VB, 128, 4, PG>(G);
+    case 1: return pick_quant_g<KB, VB, 128, 1, PG, ZP>(G);
+    case 2: return pick_quant_g<KB, VB, 128, 2, PG, ZP>(G);
+    case 4: return pick_quant_g<KB, VB, 128, 4, PG, ZP>(G);
     }
     return nullptr;
 }
 
-template <bool PG>
+template <bool PG, bool ZP>
 QuantFn pick_quant_p(int kb, int vb, int hd, int G, int kg)
 {
-    if (kb == 8 && vb == 8) return pick_quant_hd<8, 8, PG>(hd, G, kg);
-    if (kb == 8 && vb == 4) return pick_quant_hd<8, 4, PG>(hd, G, kg);
-    if (kb == 4 && vb == 4) return pick_quant_hd<4, 4, PG>(hd, G, kg);
-    if (kb == 4 && vb == 8) return pick_quant_hd<4, 8, PG>(hd, G, kg);
+    if (kb == 8 && vb == 8) return pick_quant_hd<8, 8, PG, ZP>(hd, G, kg);
+    if (kb == 8 && vb == 4) return pick_quant_hd<8, 4, PG, ZP>(hd, G, kg);
+    if (kb == 4 && vb == 4) return pick_quant_hd<4, 4, PG, ZP>(hd, G, kg);
+    if (kb == 4 && vb == 8) return pick_quant_hd<4, 8, PG, ZP>(hd, G, kg);
     return nullptr;
 }
 
 // kg: scale groups per head row (head_dim / group_size; 1 for one scale per
-// position shared by all heads); pg: paged storage
-QuantFn pick_quant(int kb, int vb, int hd, int G, int kg, bool pg)
+// position shared by all heads); pg: paged storage; zp: the zero-point codec
+// (contiguous storage only)
+QuantFn pick_quant(int kb, int vb, int hd, int G, int kg, bool pg, bool zp)
 {
-    return pg ? pick_quant_p<true>(kb, vb, hd, G, kg) : pick_quant_p<false>(kb, vb, hd, G, kg);
+    if (zp) return pg ? nullptr : pick_quant_p<false, true>(kb, vb, hd, G, kg);
+    return pg ? pick_quant_p<true, false>(kb, vb, hd, G, kg) : pick_quant_p<false, false>(kb, vb, hd, G, kg);
 }
 
 template <int KB, int HD>
@@ -270,7 +290,7 @@ PrepFn pick_prep(int kb, int hd, int G)
     return hd == 64 ? pick_prep_g<8, 64>(G) : pick_prep_g<8, 128>(G);
 }
 
-using StepPrepFn = void (*)(AppendParams, int, int, const float *, int32_t *, float *, int32_t *, float, int *);
+using StepPrepFn = void (*)(AppendParams, int, int, const float *, int32_t *, float *, int32_t *, float, int *, int);
 
 template <int KB, int HD>
 StepPrepFn pick_step_g(int G)
@@ -372,8 +392,9 @@ int kvq_cache_sizes(const kvq_cache *c, size_t *kc, size_t *vc, size_t *ksb, siz
         const size_t vrows = quantized(c->v_bits) ? U * c->n_kv_heads * cap4_of(c) : rows;
         *vc = vrows * c->head_dim * c->v_bits / 8;
     }
-    if (ksb) *ksb = quantized(c->k_bits) ? sc * 2 : 0;
-    if (vsb) *vsb = quantized(c->v_bits) ? sc * 2 : 0;
+    const size_t scb = c->zero_point ? 4 : 2;       // fp16 scale, or scale | zero point word
+    if (ksb) *ksb = quantized(c->k_bits) ? sc * scb : 0;
+    if (vsb) *vsb = quantized(c->v_bits) ? sc * scb : 0;
     return ok();
 }
 
@@ -419,6 +440,7 @@ static int prepare_append(const kvq_cache *c, const float *k_new, const float *v
     p->n_anchor = c->n_anchor;
     p->window = c->window;
     p->per_row = per_row(c) && quantized(c->k_bits) ? 1 : 0;
+    p->zp = c->zero_point && quantized(c->k_bits) ? 1 : 0;
     p->group = p->per_row ? c->n_kv_heads * c->head_dim : (quantized(c->k_bits) ? c->group_size : c->head_dim);
     const int R = c->n_kv_heads * c->head_dim;
     const int passes = p->per_row ? 1 : (R + APPEND_SPAN - 1) / APPEND_SPAN;
@@ -441,7 +463,8 @@ AppendTileFn pick_append_tile_hd(int kb, int vb)
 
 AppendTileFn pick_append_tile(const kvq_cache *c, int n_new)
 {
-    if (n_new < APPEND_TILE_MIN_ROWS || !quantized(c->k_bits) || c->window != 0 || per_row(c)) return nullptr;
+    if (n_new < APPEND_TILE_MIN_ROWS || !quantized(c->k_bits) || c->window != 0 || per_row(c) || c->zero_point)
+        return nullptr;
     if ((long long)c->batch * c->n_kv_heads > 65535) return nullptr;   // grid y: the row kernel takes these
     return c->head_dim == 64 ? pick_append_tile_hd<64>(c->k_bits, c->v_bits)
                              : pick_append_tile_hd<128>(c->k_bits, c->v_bits);
@@ -586,7 +609,8 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
         return hip_status("decode_float_kernel launch");
     }
 
-    QuantFn fn = pick_quant(c->k_bits, c->v_bits, c->head_dim, G, groups_per_head(c), paged(c));
+    QuantFn fn = pick_quant(c->k_bits, c->v_bits, c->head_dim, G, groups_per_head(c), paged(c), c->zero_point != 0);
+    const int kg = c->zero_point ? groups_per_head(c) : 0;   // per-group query sums for the zero-point codec
     PrepFn prep = pick_prep(c->k_bits, c->head_dim, G);
     StepPrepFn sprep = pick_step(c->k_bits, c->head_dim, G);
     if (!fn || !prep || !sprep) return fail(KVQ_ERR_BITS, "no kernel for k_bits=%d v_bits=%d", c->k_bits, c->v_bits);
@@ -604,9 +628,9 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
         if (ap && ap_grid.x > 0) {
             const unsigned n_app = ap_grid.x * ap_grid.y * 2;
             hipLaunchKernelGGL(sprep, dim3(n_app + units), dim3(256), 0, st_, *ap, (int)ap_grid.x, (int)ap_grid.y, q,
-                               qdig, qsc, qflag, qk_scale, cnt);
+                               qdig, qsc, qflag, qk_scale, cnt, kg);
         } else {
-            hipLaunchKernelGGL(prep, dim3(units), dim3(256), 0, st_, q, qdig, qsc, qflag, qk_scale, cnt);
+            hipLaunchKernelGGL(prep, dim3(units), dim3(256), 0, st_, q, qdig, qsc, qflag, qk_scale, cnt, kg);
         }
         const int hs = hip_status("query prep launch");
         if (hs) return hs;

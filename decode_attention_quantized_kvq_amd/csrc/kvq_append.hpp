@@ -7,6 +7,11 @@
 //   IEEE fp32, stored scale = fp16 nearest-even of s32 (65504 when it would
 //   overflow), code = clamp(rint_even(x / stored scale), -qmax, qmax), with
 //   the divide correctly rounded (HIP's default fp32 division).
+//   8/4-bit side with a zero point (the scale/zero-point metadata the
+//   mni-ml page names): per group, lo = min(0, min x), hi = max(0, max x),
+//   stored scale = fp16(RN((hi - lo) / L)), L = 255 or 15 levels, zero =
+//   clamp(rint(-lo / scale), 0, L), code = clamp(rint(x / scale) + zero,
+//   0, L); the scale and the zero point share one 32-bit word.
 // Slots follow the on-device page's window with anchors (ring storage).
 #pragma once
 
@@ -33,6 +38,7 @@ struct AppendParams {
     const int32_t *block_table;
     int group;                // elements per scale
     int per_row;              // 1: one scale per position over all heads
+    int zp;                   // 1: zero-point codec (scales are 32-bit words: fp16 scale | zero << 16)
 };
 
 // Slot of `pos` for a call whose rows run start .. start+n_new-1, or -1
@@ -82,6 +88,64 @@ __device__ __forceinline__ int code_of(float x, float s, float rs, float qmax)
 
 // the reciprocal code_of takes (1 for a zero scale, whose codes are 0)
 __device__ __forceinline__ float code_rcp(float s) { return __builtin_amdgcn_rcpf(s > 0.0f ? s : 1.0f); }
+
+// rint(RN(x / s)) for s > 0, decided as code_of decides it: valid while
+// |x / s| < 256 (then q is within 9.2e-5 of RN(x / s), inside the 1e-4 tie
+// margin); beyond, only the side of the result matters to the callers,
+// which clamp to [0, L] with L <= 255.
+__device__ __forceinline__ float rint_quot(float x, float s, float rs)
+{
+    const float q = x * rs;
+    float r = rintf(q);
+    if (fabsf(q - r) > 0.5f - 1.0e-4f) r = rintf(x / s);
+    return r;
+}
+
+// The zero-point codec of one group, given hi = max(0, max x) and m2 =
+// max(0, -min x) = -lo over the group: the 32-bit scale word (fp16 scale |
+// zero << 16), the scale and the zero point.
+__device__ __forceinline__ uint32_t zp_word(float hi, float m2, float L, float &sc, float &zf)
+{
+    const float s32 = (hi + m2) / L;               // RN(hi - lo) / L, IEEE fp32
+    uint16_t sh = f32_to_f16_bits(s32);
+    if ((sh & 0x7FFFu) == 0x7C00u) sh = 0x7BFFu;   // would overflow: saturate
+    sc = f16_bits_to_f32(sh);
+    zf = 0.0f;
+    if (sc > 0.0f) zf = fminf(fmaxf(rint_quot(m2, sc, code_rcp(sc)), 0.0f), L);
+    return (uint32_t)sh | ((uint32_t)zf << 16);
+}
+
+// One zero-point code, less 2^(bits-1) (so it packs like a signed code: the
+// keys' stored field is its two's complement, the values' its offset binary,
+// which is the code itself).
+__device__ __forceinline__ int zp_code(float x, float sc, float rs, float zf, float L, int half)
+{
+    if (!(sc > 0.0f)) return -half;
+    return (int)fminf(fmaxf(rint_quot(x, sc, rs) + zf, 0.0f), L) - half;
+}
+
+// 8 values -> 8 zero-point codes (less 2^(bits-1)), packed like encode8.
+__device__ __forceinline__ void encode8_zp(const float (&x)[8], float sc, float zf, int bits, uint32_t &w0, uint32_t &w1)
+{
+    const float L = bits == 8 ? 255.0f : 15.0f;
+    const int half = bits == 8 ? 128 : 8;
+    const float rs = code_rcp(sc);
+    int c[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) c[j] = zp_code(x[j], sc, rs, zf, L, half);
+    if (bits == 8) {
+        w0 = (uint32_t)(c[0] & 0xFF) | ((uint32_t)(c[1] & 0xFF) << 8) | ((uint32_t)(c[2] & 0xFF) << 16) |
+             ((uint32_t)(c[3] & 0xFF) << 24);
+        w1 = (uint32_t)(c[4] & 0xFF) | ((uint32_t)(c[5] & 0xFF) << 8) | ((uint32_t)(c[6] & 0xFF) << 16) |
+             ((uint32_t)(c[7] & 0xFF) << 24);
+    } else {
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) w |= (uint32_t)(c[j] & 0xF) << (4 * j);
+        w0 = w;
+        w1 = 0;
+    }
+}
 
 // 8 values -> 8 codes against stored scale s (s > 0), packed for `bits`.
 __device__ __forceinline__ void encode8(const float (&x)[8], float s, float qmax, int bits, uint32_t &w0, uint32_t &w1)
@@ -203,35 +267,50 @@ __device__ __forceinline__ void append_block(const AppendParams &p, int bx, int 
     const int tid = threadIdx.x;
 
     if (p.per_row && bits < 16) {
-        // one scale over the whole row of all heads: block-wide amax first
-        __shared__ float red[APPEND_THREADS / 64];
-        float amax = 0.0f;
+        // one scale over the whole row of all heads: block-wide maxima first
+        // (amax; or, with a zero point, max(0, max x) and max(0, -min x))
+        __shared__ float red[2][APPEND_THREADS / 64];
+        float amax = 0.0f, m2 = 0.0f;
         for (int e0 = tid * APPEND_ELEMS; e0 < R; e0 += APPEND_SPAN) {
             const int h = e0 / HD, c0 = e0 - h * HD;
             float x[8];
             load8(src + (((size_t)(b * p.n_kv_heads + h) * p.n_new + i) * HD + c0), x);
 #pragma unroll
-            for (int j = 0; j < 8; j++)
-                amax = fmaxf(amax, fabsf(x[j]));
+            for (int j = 0; j < 8; j++) {
+                amax = fmaxf(amax, p.zp ? x[j] : fabsf(x[j]));
+                m2 = fmaxf(m2, -x[j]);
+            }
         }
         amax = wave_max(amax);
-        if ((tid & 63) == 0)
-            red[tid >> 6] = amax;
+        m2 = wave_max(m2);
+        if ((tid & 63) == 0) {
+            red[0][tid >> 6] = amax;
+            red[1][tid >> 6] = m2;
+        }
         __syncthreads();
-        amax = red[0];
+        amax = red[0][0];
+        m2 = red[1][0];
 #pragma unroll
-        for (int w = 1; w < APPEND_THREADS / 64; w++)
-            amax = fmaxf(amax, red[w]);
-        const uint16_t sh = scale_bits_from_amax(amax, qmax);
-        const float s = f16_bits_to_f32(sh);
-        if (tid == 0)
-            scales[(size_t)ub * p.cap_u + slot] = sh;
+        for (int w = 1; w < APPEND_THREADS / 64; w++) {
+            amax = fmaxf(amax, red[0][w]);
+            m2 = fmaxf(m2, red[1][w]);
+        }
+        float s, zf = 0.0f;
+        if (p.zp) {
+            const uint32_t word = zp_word(amax, m2, bits == 8 ? 255.0f : 15.0f, s, zf);
+            if (tid == 0) reinterpret_cast<uint32_t *>(scales)[(size_t)ub * p.cap_u + slot] = word;
+        } else {
+            const uint16_t sh = scale_bits_from_amax(amax, qmax);
+            s = f16_bits_to_f32(sh);
+            if (tid == 0) scales[(size_t)ub * p.cap_u + slot] = sh;
+        }
         for (int e0 = tid * APPEND_ELEMS; e0 < R; e0 += APPEND_SPAN) {
             const int h = e0 / HD, c0 = e0 - h * HD;
             float x[8];
             load8(src + (((size_t)(b * p.n_kv_heads + h) * p.n_new + i) * HD + c0), x);
             uint32_t w0, w1;
-            encode8(x, s, qmax, bits, w0, w1);
+            if (p.zp) encode8_zp(x, s, zf, bits, w0, w1);
+            else encode8(x, s, qmax, bits, w0, w1);
             store_codes(codes, (size_t)ub * p.n_kv_heads + h, p.cap4, p.cap64, slot, HD * bits / 8, c0, bits,
                         side == 1, w0, w1);
         }
@@ -270,26 +349,39 @@ __device__ __forceinline__ void append_block(const AppendParams &p, int bx, int 
     }
 
     // groups of p.group values inside a head: p.group / 8 consecutive lanes
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; j++)
-        amax = fmaxf(amax, fabsf(x[j]));
-    amax = group_max_abs(amax, p.group / APPEND_ELEMS);
-    const uint16_t sh = scale_bits_from_amax(amax, qmax);
-    const float s = f16_bits_to_f32(sh);
     uint32_t w0, w1;
-    encode8(x, s, qmax, bits, w0, w1);
+    uint32_t word;
+    if (p.zp) {
+        float hi = 0.0f, m2 = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            hi = fmaxf(hi, x[j]);
+            m2 = fmaxf(m2, -x[j]);
+        }
+        hi = group_max_abs(hi, p.group / APPEND_ELEMS);
+        m2 = group_max_abs(m2, p.group / APPEND_ELEMS);
+        float s, zf;
+        word = zp_word(hi, m2, bits == 8 ? 255.0f : 15.0f, s, zf);
+        encode8_zp(x, s, zf, bits, w0, w1);
+    } else {
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            amax = fmaxf(amax, fabsf(x[j]));
+        amax = group_max_abs(amax, p.group / APPEND_ELEMS);
+        const uint16_t sh = scale_bits_from_amax(amax, qmax);
+        word = sh;
+        encode8(x, f16_bits_to_f32(sh), qmax, bits, w0, w1);
+    }
     if (!active)
         return;
     store_codes(codes, (size_t)ub * p.n_kv_heads + h, p.cap4, p.cap64, slot, HD * bits / 8, c0, bits, side == 1,
                 w0, w1);
-    if (c0 % p.group == 0)
-        scales[row * (size_t)(HD / p.group) + c0 / p.group] = sh;
-}
-
-__global__ __launch_bounds__(APPEND_THREADS) void append_kernel(AppendParams p)
-{
-    append_block(p, blockIdx.x, blockIdx.y, blockIdx.z);
+    if (c0 % p.group == 0) {
+        const size_t si = row * (size_t)(HD / p.group) + c0 / p.group;
+        if (p.zp) reinterpret_cast<uint32_t *>(scales)[si] = word;
+        else scales[si] = (uint16_t)word;
+    }
 }
 
 // The call's rows of sequence b for KV head kvh, both sides of an 8/4-bit
@@ -328,7 +420,8 @@ __device__ __forceinline__ void append_head_rows(const AppendParams &p, int b, i
         else
 #pragma unroll
             for (int j = 0; j < 8; j++) x[j] = 0.0f;
-        float amax = 0.0f;
+        // amax (symmetric), or max(0, max x) and max(0, -min x) (zero point)
+        float amax = 0.0f, m2 = 0.0f;
         if (p.per_row) {
             // one scale over the row of all heads
             for (int e0 = lane * APPEND_ELEMS; e0 < R; e0 += 64 * APPEND_ELEMS) {
@@ -336,25 +429,44 @@ __device__ __forceinline__ void append_head_rows(const AppendParams &p, int b, i
                 float y[8];
                 load8(src + (((size_t)(b * p.n_kv_heads + h) * p.n_new + i) * HD + c), y);
 #pragma unroll
-                for (int j = 0; j < 8; j++) amax = fmaxf(amax, fabsf(y[j]));
+                for (int j = 0; j < 8; j++) {
+                    amax = fmaxf(amax, p.zp ? y[j] : fabsf(y[j]));
+                    m2 = fmaxf(m2, -y[j]);
+                }
             }
             amax = wave_max(amax);
+            m2 = wave_max(m2);
         } else {
 #pragma unroll
-            for (int j = 0; j < 8; j++) amax = fmaxf(amax, fabsf(x[j]));
+            for (int j = 0; j < 8; j++) {
+                amax = fmaxf(amax, p.zp ? x[j] : fabsf(x[j]));
+                m2 = fmaxf(m2, -x[j]);
+            }
             amax = group_max_abs(amax, p.group / APPEND_ELEMS);
+            m2 = group_max_abs(m2, p.group / APPEND_ELEMS);
         }
-        const uint16_t sh = scale_bits_from_amax(amax, qmax);
-        const float sc = f16_bits_to_f32(sh);
-        uint32_t w0, w1;
-        encode8(x, sc, qmax, bits, w0, w1);
+        uint32_t w0, w1, word;
+        if (p.zp) {
+            float sc, zf;
+            word = zp_word(amax, m2, bits == 8 ? 255.0f : 15.0f, sc, zf);
+            encode8_zp(x, sc, zf, bits, w0, w1);
+        } else {
+            const uint16_t sh = scale_bits_from_amax(amax, qmax);
+            word = sh;
+            encode8(x, f16_bits_to_f32(sh), qmax, bits, w0, w1);
+        }
         if (!act) continue;
         const size_t unit = (size_t)ub * p.n_kv_heads + kvh;
         store_codes(p.codes[side], unit, p.cap4, p.cap64, slot, HD * bits / 8, c0, bits, side == 1, w0, w1);
+        size_t si = SIZE_MAX;
         if (p.per_row) {
-            if (lane == 0) p.scales[side][(size_t)ub * p.cap_u + slot] = sh;
+            if (lane == 0) si = (size_t)ub * p.cap_u + slot;
         } else if (c0 % p.group == 0) {
-            p.scales[side][(unit * p.cap_u + slot) * (size_t)(HD / p.group) + c0 / p.group] = sh;
+            si = (unit * p.cap_u + slot) * (size_t)(HD / p.group) + c0 / p.group;
+        }
+        if (si != SIZE_MAX) {
+            if (p.zp) reinterpret_cast<uint32_t *>(p.scales[side])[si] = word;
+            else p.scales[side][si] = (uint16_t)word;
         }
     }
 }

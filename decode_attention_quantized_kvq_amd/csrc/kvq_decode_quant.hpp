@@ -55,6 +55,8 @@
 // (m, l, acc) written.  LDS use does not depend on the chunk length.
 #pragma once
 
+#include <type_traits>
+
 #include "kvq_append.hpp"
 #include "kvq_combine.hpp"
 #include "kvq_device.hpp"
@@ -66,22 +68,28 @@ constexpr int QD_WAVES = QD_THREADS / 64;
 // Positions per wave sub-chunk: 512 while G x vg < 8, else 256 (the maxima,
 // merge and prologue then run half as often as at 128, and the compiler keeps
 // the G = 4, vg = 4 loop in 156 VGPRs instead of 245); G = 8 with 2 or 4
-// scale groups takes 128, as 256 would not fit the LDS.  (A sub-chunk's value
-// sums stay exact in uint32: at most 512 * 32767 * 255 < 2^32.)
-__host__ __device__ constexpr int qd_sub(int G, int vg)
+// scale groups, and the zero-point codec's G x vg >= 16 (whose scale words
+// take twice the LDS), take 128, as 256 would not fit the 64 KiB of LDS.
+// (A sub-chunk's value sums stay exact in uint32: at most
+// 512 * 32767 * 255 < 2^32.)
+__host__ __device__ constexpr int qd_sub(int G, int vg, bool zp = false)
 {
-    return G == 8 && vg >= 2 ? 128 : G * vg >= 8 ? 256 : 512;
+    return (G == 8 && vg >= 2) || (zp && G * vg >= 16) ? 128 : G * vg >= 8 ? 256 : 512;
 }
 constexpr int Q_RANGE = 30000;
 // the query's extra low digit: taken when max|q| > Q_OUTLIER * rms(q) for a
 // head of the unit; its base keeps |d| within the key width's signed digit
 constexpr float Q_OUTLIER = 5.0f;
 __host__ __device__ constexpr int qx_base(int KB) { return KB == 4 ? 14 : 254; }
-// int32 words between two units' query digit blocks ([ND + 1][K_COLS][G]),
-// padded to 256 bytes so that no two units share a cache line
+// int32 words between two units' query digit blocks, padded to 256 bytes
+// so that no two units share a cache line: the digits [ND + 1][K_COLS][G],
+// then (for the zero-point codec) the query's integer sums per scale group,
+// [QS_GROUPS][G] for q_int and [QS_GROUPS][G] for the extra low digit
+constexpr int QS_GROUPS = 4;
+__host__ __device__ constexpr int qd_digits(int KB, int HD, int G) { return ((KB == 4 ? 4 : 2) + 1) * (HD * KB / 32) * G; }
 __host__ __device__ constexpr int qd_stride(int KB, int HD, int G)
 {
-    return (((KB == 4 ? 4 : 2) + 1) * (HD * KB / 32) * G + 63) / 64 * 64;
+    return (qd_digits(KB, HD, G) + 2 * QS_GROUPS * G + 63) / 64 * 64;
 }
 constexpr int QD_PF = 16;       // value group loads in flight per lane
 constexpr int W_RANGE = 32767;
@@ -154,15 +162,15 @@ struct QuantSmem {
 // [vg][S/4][G][lo, hi] (over the scores when vg == 1); then the
 // cross-wave merge area (over the scores when it fits) and the wave maxima
 // and sums.
-__host__ __device__ inline QuantSmem quant_smem(int G, int HD, int vg)
+__host__ __device__ inline QuantSmem quant_smem(int G, int HD, int vg, bool zp = false)
 {
     QuantSmem s;
-    const int S = qd_sub(G, vg);
+    const int S = qd_sub(G, vg, zp);
     int off = 0;
     s.zs = off;
     off += QD_WAVES * S * G * 4;
     s.vs = off;
-    off += QD_WAVES * S * vg * 2;
+    off += QD_WAVES * S * vg * (zp ? 4 : 2);            // value scale (and zero point) words
     s.wd_alias = vg == 1;
     if (s.wd_alias) {
         s.wd = s.zs;
@@ -196,7 +204,7 @@ __host__ __device__ inline QuantSmem quant_smem(int G, int HD, int vg)
 // ---------------------------------------------------------------------------
 template <int KB, int HD, int G>
 __device__ __forceinline__ void qprep_core(const float *__restrict__ qh, int32_t *__restrict__ qd, float *s_amax,
-                                           int *s_xflag, float *s_qv)
+                                           int *s_xflag, float *s_qv, int kg)
 {
     // qh: the unit's G query heads [G][HD]; qd: its digits [ND + 1][K_COLS][G];
     // s_amax [G], s_xflag, s_qv [G][HD]: LDS.  On return (after a barrier)
@@ -257,19 +265,36 @@ __device__ __forceinline__ void qprep_core(const float *__restrict__ qh, int32_t
 #pragma unroll
         for (int j = 0; j <= ND; j++) qd[((size_t)j * K_COLS + col) * G + h] = (int32_t)d[j];
     }
+    // The query's integer sums over each of the kg scale groups of a head
+    // (q_int, and the extra low digit): what the zero-point codec's keys
+    // subtract, zero point times sum, from a group's score.
+    for (int i = tid; i < kg * G; i += 256) {
+        const int g = i / G, h = i - g * G;
+        const float sq = s_amax[h] / (float)Q_RANGE;
+        const float inv = sq > 0.0f ? 1.0f / sq : 0.0f;
+        int sum = 0, sumx = 0;
+        for (int c = g * (HD / kg); c < (g + 1) * (HD / kg); c++) {
+            const float qq = s_qv[h * HD + c];
+            const int qi = (int)fminf(fmaxf(rintf(qq * inv), -(float)Q_RANGE), (float)Q_RANGE);
+            sum += qi;
+            if (xq) sumx += (int)fminf(fmaxf(rintf(fmaf(qq, inv, -(float)qi) * XB), -(float)XMAX), (float)XMAX);
+        }
+        qd[qd_digits(KB, HD, G) + g * G + h] = sum;
+        qd[qd_digits(KB, HD, G) + (QS_GROUPS + g) * G + h] = sumx;
+    }
     __syncthreads();
 }
 
 template <int KB, int HD, int G>
 __device__ __forceinline__ void qprep_block(const float *__restrict__ q, int32_t *__restrict__ qdig,
                                             float *__restrict__ qsc, int32_t *__restrict__ qflag, float qk_scale,
-                                            int unit, int *cnt)
+                                            int unit, int *cnt, int kg)
 {
     // unit = b * Hkv + kvh
     __shared__ float amax[G];
     __shared__ int xflag;
     __shared__ float qv[G * HD];                         // q, read from memory once
-    qprep_core<KB, HD, G>(q + (size_t)unit * G * HD, qdig + (size_t)unit * qd_stride(KB, HD, G), amax, &xflag, qv);
+    qprep_core<KB, HD, G>(q + (size_t)unit * G * HD, qdig + (size_t)unit * qd_stride(KB, HD, G), amax, &xflag, qv, kg);
     const int tid = threadIdx.x;
     if (tid < G) qsc[unit * G + tid] = amax[tid] / (float)Q_RANGE * qk_scale;
     if (tid == 0) {
@@ -281,9 +306,9 @@ __device__ __forceinline__ void qprep_block(const float *__restrict__ q, int32_t
 template <int KB, int HD, int G>
 __global__ __launch_bounds__(256) void qprep_kernel(const float *__restrict__ q, int32_t *__restrict__ qdig,
                                                     float *__restrict__ qsc, int32_t *__restrict__ qflag,
-                                                    float qk_scale, int *cnt)
+                                                    float qk_scale, int *cnt, int kg)
 {
-    qprep_block<KB, HD, G>(q, qdig, qsc, qflag, qk_scale, blockIdx.x, cnt);
+    qprep_block<KB, HD, G>(q, qdig, qsc, qflag, qk_scale, blockIdx.x, cnt, kg);
 }
 
 template <int KB>
@@ -326,19 +351,21 @@ __device__ __forceinline__ void pack_w(uint32_t w0, uint32_t w1, uint32_t w2, ui
 // head_dim / KG channels); key dots are summed per group.
 // waves per SIMD the register allocation must allow: the int4 key and value
 // instances with G x KG <= 4 fit 128 VGPRs (4 waves) when asked to (left
-// alone the compiler takes a few more and drops to 3); the others take what
-// they need
-__host__ __device__ constexpr int qd_min_waves(int KB, int VB, int G, int KG, bool paged)
+// alone the compiler takes a few more and drops to 3); the others, and the
+// zero-point instances (which would spill at 128), take what they need
+__host__ __device__ constexpr int qd_min_waves(int KB, int VB, int G, int KG, bool paged, bool zp)
 {
-    return KB == 4 && VB == 4 && G * KG <= 4 ? 4 : 1;
+    return KB == 4 && VB == 4 && G * KG <= 4 && !zp ? 4 : 1;
 }
 
-template <int KB, int VB, int HD, int G, int KG, bool PAGED>
-__global__ __launch_bounds__(QD_THREADS) __attribute__((amdgpu_waves_per_eu(qd_min_waves(KB, VB, G, KG, PAGED))))
+// ZP: the zero-point codec (32-bit scale words: fp16 scale | zero << 16;
+// keys stored as code - 2^(KB-1), values as the code).
+template <int KB, int VB, int HD, int G, int KG, bool PAGED, bool ZP = false>
+__global__ __launch_bounds__(QD_THREADS) __attribute__((amdgpu_waves_per_eu(qd_min_waves(KB, VB, G, KG, PAGED, ZP))))
 void decode_quant_kernel(QuantParams p)
 {
     using T = QT<KB, VB, HD, G>;
-    constexpr int S = qd_sub(G, KG);
+    constexpr int S = qd_sub(G, KG, ZP);
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -376,7 +403,7 @@ void decode_quant_kernel(QuantParams p)
         float *s_amax = s_qv + G * HD;
         int *s_xflag = reinterpret_cast<int *>(s_amax + G);
         qprep_core<KB, HD, G>(p.q + row0 * HD, const_cast<int32_t *>(p.qdig) + (size_t)bh * qd_stride(KB, HD, G),
-                              s_amax, s_xflag, s_qv);
+                              s_amax, s_xflag, s_qv, ZP ? KG : 0);
         __builtin_amdgcn_s_waitcnt(WAIT_VMEM_ALL);
         __syncthreads();
 #pragma unroll
@@ -410,9 +437,11 @@ void decode_quant_kernel(QuantParams p)
         return;
     }
 
-    const QuantSmem lay = quant_smem(G, HD, KG);
+    const QuantSmem lay = quant_smem(G, HD, KG, ZP);
+    constexpr int SCB = ZP ? 4 : 2;                  // bytes per scale entry
     float *zs = reinterpret_cast<float *>(smem + lay.zs) + wave * S * G;       // this wave's scores
-    uint16_t *vsl = reinterpret_cast<uint16_t *>(smem + lay.vs) + wave * S * KG;   // and value scales
+    using VsT = typename std::conditional<ZP, uint32_t, uint16_t>::type;
+    VsT *vsl = reinterpret_cast<VsT *>(smem + lay.vs) + wave * S * KG;   // and value scale words
     uint32_t *wdw = lay.wd_alias ? reinterpret_cast<uint32_t *>(zs)
                                  : reinterpret_cast<uint32_t *>(smem + lay.wd) + wave * KG * (S / 4) * G * 2;
     float *red = reinterpret_cast<float *>(smem + lay.red);
@@ -459,7 +488,7 @@ void decode_quant_kernel(QuantParams p)
     const KVQ_CONST int32_t *qd = (const KVQ_CONST int32_t *)(p.qdig + (size_t)bh * qd_stride(KB, HD, G));
     constexpr float XINV = 1.0f / (float)qx_base(KB);
     const uint32_t ko = lane * 16;
-    const uint32_t kso = lane * p.k_sc_t * 2, vso = lane * p.v_sc_t * 2;
+    const uint32_t kso = lane * p.k_sc_t * SCB, vso = lane * p.v_sc_t * SCB;
     struct Tile {
         uint4 k[T::K_U4];
         uint32_t ks[KG], vs[KG];
@@ -472,10 +501,12 @@ void decode_quant_kernel(QuantParams p)
         const int uu = u < 0 ? 0 : u;
         const uint8_t *kb = p.k_codes + (((size_t)uu * p.n_kv_heads + kvh) * p.cap64 + sl) * T::K_ROW;
         const rsrc_t krs = make_rsrc(kb, kbytes);
-        const rsrc_t ksrs = make_rsrc(p.k_scales + uu * p.k_sc_b + kvh * p.k_sc_h + (size_t)sl * p.k_sc_t,
-                                      rem * p.k_sc_t * 2);
-        const rsrc_t vsrs = make_rsrc(p.v_scales + uu * p.v_sc_b + kvh * p.v_sc_h + (size_t)sl * p.v_sc_t,
-                                      rem * p.v_sc_t * 2);
+        const rsrc_t ksrs = make_rsrc(reinterpret_cast<const char *>(p.k_scales) +
+                                          (uu * p.k_sc_b + kvh * p.k_sc_h + (size_t)sl * p.k_sc_t) * SCB,
+                                      rem * p.k_sc_t * SCB);
+        const rsrc_t vsrs = make_rsrc(reinterpret_cast<const char *>(p.v_scales) +
+                                          (uu * p.v_sc_b + kvh * p.v_sc_h + (size_t)sl * p.v_sc_t) * SCB,
+                                      rem * p.v_sc_t * SCB);
         // (immediate offsets reach 4 KiB: int8 rows use a second descriptor
         // for slices 4..7)
         const rsrc_t krs2 = make_rsrc(kb + 4096, kbytes > 4096 ? kbytes - 4096 : 0);
@@ -483,8 +514,13 @@ void decode_quant_kernel(QuantParams p)
         for (int u4 = 0; u4 < T::K_U4; u4++) d.k[u4] = bld_u4<CP_NT>(u4 < 4 ? krs : krs2, ko + (u4 % 4) * 1024);
 #pragma unroll
         for (int g = 0; g < KG; g++) {
-            d.ks[g] = bld_u16(ksrs, kso + 2 * g);
-            d.vs[g] = bld_u16(vsrs, vso + 2 * g);
+            if constexpr (ZP) {
+                d.ks[g] = bld_u32<0>(ksrs, kso + 4 * g);
+                d.vs[g] = bld_u32<0>(vsrs, vso + 4 * g);
+            } else {
+                d.ks[g] = bld_u16(ksrs, kso + 2 * g);
+                d.vs[g] = bld_u16(vsrs, vso + 2 * g);
+            }
         }
     };
     float mloc[G];                                   // per-lane score maxima of the current sub-chunk
@@ -497,7 +533,7 @@ void decode_quant_kernel(QuantParams p)
         for (int g = 0; g < KG; g++) {
             // (zero past the wave's range: the load returned zero; every
             // tile of the sub-chunk lies inside its S rows of LDS)
-            vsl[(t - sc0) * KG + g] = (uint16_t)c.vs[g];
+            vsl[(t - sc0) * KG + g] = (VsT)c.vs[g];
         }
         // an opaque zero offset, redefined every tile, keeps the digit loads
         // inside the loop (hoisted, they would need hundreds of SGPRs)
@@ -550,6 +586,15 @@ void decode_quant_kernel(QuantParams p)
                 }
             }
             const float sk = f16_bits_to_f32((uint16_t)c.ks[blk]);
+            // zero-point codec: the stored code is code - 2^(KB-1), so the
+            // group's score is sk * (acc - (zero - 2^(KB-1)) * sum q_int)
+            int zk = 0;
+            if constexpr (ZP) {
+                zk = (int)(c.ks[blk] >> 16) - (1 << (KB - 1));
+                const KVQ_CONST int32_t *qsum = qdl + qd_digits(KB, HD, G) + blk * G;
+#pragma unroll
+                for (int h = 0; h < G; h++) acc[h] -= __mul24(zk, qsum[h]);
+            }
 #pragma unroll
             for (int h = 0; h < G; h++) z[h] = blk == 0 ? (float)acc[h] * sk : fmaf((float)acc[h], sk, z[h]);
             if (xq) {
@@ -562,6 +607,11 @@ void decode_quant_kernel(QuantParams p)
 #pragma unroll
                     for (int h = 0; h < G; h++)
                         acc[h] = cc == 0 ? kdot0<KB>(qx[col * G + h], kw) : kdot<KB>(qx[col * G + h], kw, acc[h]);
+                }
+                if constexpr (ZP) {
+                    const KVQ_CONST int32_t *qsx = qdl + qd_digits(KB, HD, G) + (QS_GROUPS + blk) * G;
+#pragma unroll
+                    for (int h = 0; h < G; h++) acc[h] -= __mul24(zk, qsx[h]);
                 }
                 const float skx = sk * XINV;
 #pragma unroll
@@ -723,7 +773,8 @@ void decode_quant_kernel(QuantParams p)
         // rewrites the scores it has read, and the weight words go over
         // positions whose p every lane has already read.
         float lloc[G];
-        int wsl[KG][G];
+        int wsl[KG][G];                              // sum of w_int (symmetric: the offset binary's share)
+        uint32_t wzl[KG][G], wzh[KG][G];             // zero point: sum of w_int * zero, low / high weight bytes
         float nrm[KG][G];                            // N per scale group and head, wave-uniform
         {
             constexpr float MAGIC = 12582912.0f;     // 1.5 * 2^23
@@ -762,6 +813,7 @@ void decode_quant_kernel(QuantParams p)
 #pragma unroll
                 for (int g = 0; g < KG; g++) {
                     wsl[g][h] = 0;
+                    wzl[g][h] = wzh[g][h] = 0u;
                     pmx[g][h] = 0;
                 }
             }
@@ -783,7 +835,7 @@ void decode_quant_kernel(QuantParams p)
                         float prod[KG][G];
 #pragma unroll
                         for (int g = 0; g < KG; g++) {
-                            const float sv = f16_bits_to_f32(vsl[(tq + k) * KG + g]);
+                            const float sv = f16_bits_to_f32((uint16_t)vsl[(tq + k) * KG + g]);
 #pragma unroll
                             for (int h = 0; h < G; h++) {
                                 prod[g][h] = pr[h] * sv;
@@ -818,7 +870,16 @@ void decode_quant_kernel(QuantParams p)
                         float sv[4];
                         if constexpr (KG > 1) {
 #pragma unroll
-                            for (int k = 0; k < 4; k++) sv[k] = f16_bits_to_f32(vsl[(tq + k) * KG + g]);
+                            for (int k = 0; k < 4; k++) sv[k] = f16_bits_to_f32((uint16_t)vsl[(tq + k) * KG + g]);
+                        }
+                        // zero point: the four positions' zero points, one byte each
+                        uint32_t zb = 0;
+                        if constexpr (ZP) {
+                            const uint32_t a0 = vsl[(tq + 0) * KG + g], a1 = vsl[(tq + 1) * KG + g];
+                            const uint32_t a2 = vsl[(tq + 2) * KG + g], a3 = vsl[(tq + 3) * KG + g];
+                            const uint32_t z01 = __builtin_amdgcn_perm(a1, a0, 0x0c0c0602u);   // a0.b2 a1.b2
+                            const uint32_t z23 = __builtin_amdgcn_perm(a3, a2, 0x0c0c0602u);
+                            zb = __builtin_amdgcn_perm(z23, z01, 0x05040100u);
                         }
                         uint32_t *dst = wdw + ((size_t)g * (S / 4) + grp) * G * 2;
 #pragma unroll
@@ -830,8 +891,13 @@ void decode_quant_kernel(QuantParams p)
                                                                              : fmaf(pr[k][h] * fsc[g][h], sv[k], MAGIC));
                             uint32_t lo, hi;
                             pack_w(wb[0], wb[1], wb[2], wb[3], lo, hi);
-                            wsl[g][h] += (int)__builtin_amdgcn_udot4(lo, 0x01010101u, 0u, false)
-                                       + 256 * (int)__builtin_amdgcn_udot4(hi, 0x01010101u, 0u, false);
+                            if constexpr (ZP) {
+                                wzl[g][h] = __builtin_amdgcn_udot4(lo, zb, wzl[g][h], false);
+                                wzh[g][h] = __builtin_amdgcn_udot4(hi, zb, wzh[g][h], false);
+                            } else {
+                                wsl[g][h] += (int)__builtin_amdgcn_udot4(lo, 0x01010101u, 0u, false)
+                                           + 256 * (int)__builtin_amdgcn_udot4(hi, 0x01010101u, 0u, false);
+                            }
                             dst[2 * h] = lo;
                             dst[2 * h + 1] = hi;
                         }
@@ -890,7 +956,11 @@ void decode_quant_kernel(QuantParams p)
 #pragma unroll
                 for (int g = 0; g < KG; g++) {
                     cg[g] = fn * nrm[g][h] * (1.0f / (float)W_RANGE);
-                    bsum[g][h] = fmaf(bsum[g][h], fo, (float)wsl[g][h] * cg[g]);
+                    // the stored values' offset, in w_int units: bias * sum w
+                    // (offset binary), or sum w * zero (zero point)
+                    const float woff = ZP ? fmaf(256.0f, (float)wzh[g][h], (float)wzl[g][h])
+                                          : (float)wsl[g][h] * (VB == 4 ? 8.0f : 128.0f);
+                    bsum[g][h] = fmaf(bsum[g][h], fo, woff * cg[g]);
                 }
                 // 256 * hi + lo is exact in uint32 (hi bytes <= 127, at most
                 // 128 groups a sub-chunk: <= 512 * 32767 * 255 < 2^32)
@@ -925,14 +995,14 @@ void decode_quant_kernel(QuantParams p)
                 for (int c = 0; c < T::V_ACC; c++) af[h][c] += __shfl_xor(af[h][c], m, 64);
     }
     {
-        // the offset binary: code = stored - bias, so subtract bias * sum(w)
-        // (in the same fixed-point units) from every channel
-        const float bias = VB == 4 ? 8.0f : 128.0f;
+        // the stored value is code + bias (offset binary) or code + zero (zero
+        // point): subtract the offset's share, bias * sum w or sum w * zero,
+        // which bsum holds in the accumulators' units, from every channel
 #pragma unroll
         for (int g = 0; g < KG; g++)
 #pragma unroll
             for (int h = 0; h < G; h++) {
-                const float ob = bias * wave_sum_u(bsum[g][h]);
+                const float ob = wave_sum_u(bsum[g][h]);
 #pragma unroll
                 for (int c = 0; c < T::V_ACC; c++)
                     if ((qsl * T::V_ACC + c) / (HD / KG) == g) af[h][c] -= ob;
@@ -996,5 +1066,33 @@ void decode_quant_kernel(QuantParams p)
     }
     finish();
 }
+
+// Every (head_dim, query heads per KV head, scale groups per head)
+// instance of one (key width, value width, paged, zero point) family of the
+// split kernel: head_dim 64 with 1 or 2 scale groups, head_dim 128 with 1, 2
+// or 4; G in {1, 2, 4, 8}.  X(KB, VB, HD, G, KG, PG, ZP) is applied to each.
+#define KVQ_QUANT_FAMILY(X, KB, VB, PG, ZP)                                                     \
+    X(KB, VB, 64, 1, 1, PG, ZP) X(KB, VB, 64, 2, 1, PG, ZP) X(KB, VB, 64, 4, 1, PG, ZP)          \
+    X(KB, VB, 64, 8, 1, PG, ZP) X(KB, VB, 64, 1, 2, PG, ZP) X(KB, VB, 64, 2, 2, PG, ZP)          \
+    X(KB, VB, 64, 4, 2, PG, ZP) X(KB, VB, 64, 8, 2, PG, ZP) X(KB, VB, 128, 1, 1, PG, ZP)         \
+    X(KB, VB, 128, 2, 1, PG, ZP) X(KB, VB, 128, 4, 1, PG, ZP) X(KB, VB, 128, 8, 1, PG, ZP)       \
+    X(KB, VB, 128, 1, 2, PG, ZP) X(KB, VB, 128, 2, 2, PG, ZP) X(KB, VB, 128, 4, 2, PG, ZP)       \
+    X(KB, VB, 128, 8, 2, PG, ZP) X(KB, VB, 128, 1, 4, PG, ZP) X(KB, VB, 128, 2, 4, PG, ZP)       \
+    X(KB, VB, 128, 4, 4, PG, ZP) X(KB, VB, 128, 8, 4, PG, ZP)
+
+// all families the library dispatches to: four width pairs, contiguous and
+// paged, and the zero-point codec on contiguous storage
+#define KVQ_QUANT_ALL(X)                                                                        \
+    KVQ_QUANT_FAMILY(X, 8, 8, false, false) KVQ_QUANT_FAMILY(X, 8, 4, false, false)              \
+    KVQ_QUANT_FAMILY(X, 4, 4, false, false) KVQ_QUANT_FAMILY(X, 4, 8, false, false)              \
+    KVQ_QUANT_FAMILY(X, 8, 8, true, false) KVQ_QUANT_FAMILY(X, 8, 4, true, false)                \
+    KVQ_QUANT_FAMILY(X, 4, 4, true, false) KVQ_QUANT_FAMILY(X, 4, 8, true, false)                \
+    KVQ_QUANT_FAMILY(X, 8, 8, false, true) KVQ_QUANT_FAMILY(X, 8, 4, false, true)                \
+    KVQ_QUANT_FAMILY(X, 4, 4, false, true) KVQ_QUANT_FAMILY(X, 4, 8, false, true)
+
+#define KVQ_QUANT_DECLARE(KB, VB, HD, G, KG, PG, ZP) \
+    extern template __global__ void decode_quant_kernel<KB, VB, HD, G, KG, PG, ZP>(QuantParams);
+#define KVQ_QUANT_DEFINE(KB, VB, HD, G, KG, PG, ZP) \
+    template __global__ void decode_quant_kernel<KB, VB, HD, G, KG, PG, ZP>(QuantParams);
 
 } // namespace kvq

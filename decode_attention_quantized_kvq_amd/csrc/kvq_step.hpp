@@ -16,7 +16,7 @@ namespace kvq {
 template <int KB, int HD, int G>
 __global__ __launch_bounds__(256) void step_prep_kernel(AppendParams ap, int app_x, int app_y, const float *q,
                                                         int32_t *qdig, float *qsc, int32_t *qflag, float qk_scale,
-                                                        int *cnt)
+                                                        int *cnt, int kg)
 {
     const int n_app = app_x * app_y * 2;
     const int bid = blockIdx.x;
@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void step_prep_kernel(AppendParams ap, int app
         append_block(ap, r % app_x, r / app_x, side);
         return;
     }
-    qprep_block<KB, HD, G>(q, qdig, qsc, qflag, qk_scale, bid - n_app, cnt);
+    qprep_block<KB, HD, G>(q, qdig, qsc, qflag, qk_scale, bid - n_app, cnt, kg);
 }
 
 } // namespace kvq

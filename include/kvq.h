@@ -137,6 +137,7 @@ typedef struct kvq_cache {
     int32_t page_size;    /* 0 = contiguous */
     int32_t n_pages;
     const int32_t *block_table;
+    int32_t zero_point;   /* 0 = symmetric codes; 1 = zero-point codec (8/4-bit, contiguous) */
 } kvq_cache;
 
 /* ---- accounting ------------------------------------------------------ */

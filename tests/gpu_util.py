@@ -172,3 +172,58 @@ def assert_same_storage(paged, table, contig):
         if spare:
             u = unit_view(paged, name)
             assert not torch.any(u[torch.as_tensor(spare, device=u.device)]), f"{name}: a spare page was written"
+
+
+# ---------------------------------------------------------------- zero-point codec
+def zp_arrays(cache):
+    """(k_codes, v_codes, k_scales, k_zeros, v_scales, v_zeros) of a zero-point
+    cache as the oracle's unsigned codes: keys are stored as code - 2^(bits-1)
+    (two's complement, so code XOR 0x80 per byte or 0x8 per nibble), values as
+    the code; scale words hold the fp16 scale in the low and the zero point in
+    the high half."""
+    d = cache.desc
+    B, H, HD, cap = d.batch, d.n_kv_heads, d.head_dim, d.capacity
+    KR = HD * d.k_bits // 8
+    cap64 = (cap + 63) // 64 * 64
+    kraw = cache.k_codes.cpu().numpy()
+    kc = (kraw[:B * H * cap64 * KR].reshape(B, H, cap64 // 64, KR // 16, 64, 16).transpose(0, 1, 2, 4, 3, 5)
+          .reshape(B, H, cap64, KR)[:, :, :cap]) ^ np.uint8(0x80 if d.k_bits == 8 else 0x88)
+    VR = HD * d.v_bits // 8
+    cap4 = (cap + 3) // 4 * 4
+    vraw = cache.v_codes.cpu().numpy()
+    vc = vraw[:B * H * cap4 * VR].reshape(B, H, cap4 // 4, VR, 4).transpose(0, 1, 2, 4, 3).reshape(B, H, cap4, VR)[:, :, :cap]
+    per_row = d.group_size == H * HD and H > 1
+    out = [kc, vc]
+    for t in (cache.k_scales, cache.v_scales):
+        w = t.cpu().numpy().view(np.uint32)
+        w = w.reshape(B, cap) if per_row else w.reshape(B, H, cap, HD // d.group_size)
+        out += [(w & 0xFFFF).astype(np.uint16), (w >> 16).astype(np.uint8)]
+    return out
+
+
+def check_codes_zp(oq, cache, K, V, positions_of_slot):
+    """Bit-exact check of every stored row of a zero-point cache against the
+    oracle's asymmetric codec: codes, fp16 scales and zero points."""
+    d = cache.desc
+    B, H, HD = d.batch, d.n_kv_heads, d.head_dim
+    kc, vc, ks, kz, vs, vz = zp_arrays(cache)
+    slots = np.array(sorted(positions_of_slot), dtype=np.int64)
+    pos = np.array([positions_of_slot[s] for s in slots], dtype=np.int64)
+    per_row = d.group_size == H * HD and H > 1
+    for name, src, codes, scales, zeros, bits in (("K", K, kc, ks, kz, d.k_bits), ("V", V, vc, vs, vz, d.v_bits)):
+        if per_row:
+            for b in range(B):
+                rows_ = src[b][:, pos, :].transpose(1, 0, 2).reshape(len(pos), H * HD)
+                p, s, z = oq.encode_rows_asym(rows_, H * HD, bits)
+                got = codes[b][:, slots, :].transpose(1, 0, 2).reshape(len(pos), -1)
+                assert np.array_equal(got, p), f"{name} codes differ (b={b}, per-row)"
+                assert np.array_equal(scales[b][slots], s[:, 0]), f"{name} scales differ (b={b})"
+                assert np.array_equal(zeros[b][slots], z[:, 0]), f"{name} zero points differ (b={b})"
+        else:
+            p, s, z = oq.encode_rows_asym(src[:, :, pos, :], d.group_size, bits)
+            got = codes[:, :, slots, :]
+            if not np.array_equal(got, p):
+                bad = np.argwhere(got != p)[:5]
+                raise AssertionError(f"{name} codes differ at {bad.tolist()} (bits={bits})")
+            assert np.array_equal(scales[:, :, slots, :], s), f"{name} scales differ"
+            assert np.array_equal(zeros[:, :, slots, :], z), f"{name} zero points differ"

@@ -290,9 +290,12 @@ def test_workspace_and_chunks(kvq):
     P = 32 * 32
     partials = ((P * n_chunks * 8 + 255) // 256) * 256 + P * n_chunks * 128 * 4
     # int4 keys: the query's fixed-point digits (4 Horner digits and the extra low
-    # one, per value) and scales follow the partials, then one extra-digit flag and
-    # one ticket counter per (sequence, KV head) for the fused step
-    digits = 32 * 8 * 16 * 5 * 4 * 4 + P * 4
+    # one, per value; then two sums per scale group and head for the zero-point
+    # codec; each unit's block padded to 256 bytes) and scales follow the partials,
+    # then one extra-digit flag and one ticket counter per (sequence, KV head) for
+    # the fused step
+    words = -(-(16 * 5 * 4 + 2 * 4 * 4) // 64) * 64
+    digits = 32 * 8 * words * 4 + P * 4
     counters = 2 * 32 * 8 * 4
     ws = kvq.kvq_workspace_bytes(d, 32, 32768, 0)
     assert partials + digits + counters <= ws <= partials + digits + counters + 1024
@@ -373,3 +376,27 @@ def test_static_step_rejects_oversize(kvq):
         kvq.kvq_decode_step_static(d, None, None, 1, None, None, 32, None, 131072, 0.0, 64, None, stream=0)
     assert e.value.status == kvq.KVQ_ERR_WORKSPACE
     assert "static scratch" in kvq.kvq_last_error()
+
+
+def test_zero_point_rules(kvq):
+    """The zero-point codec: 8/4-bit contiguous caches only; its scale buffers
+    hold 32-bit words (fp16 scale | zero point), twice the symmetric size."""
+    d = _desc(kvq, batch=2, n_kv_heads=2, capacity=100, k_bits=4, v_bits=8, group_size=32)
+    sym = kvq.kvq_cache_sizes(d)
+    d.zero_point = 1
+    zp = kvq.kvq_cache_sizes(d)
+    assert zp[:2] == sym[:2] and zp[2] == 2 * sym[2] and zp[3] == 2 * sym[3]
+    d.zero_point = 2
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_cache_sizes(d)
+    assert e.value.status == kvq.KVQ_ERR_ARG
+    f = _desc(kvq, k_bits=16, v_bits=16)
+    f.zero_point = 1
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_cache_sizes(f)
+    assert e.value.status == kvq.KVQ_ERR_BITS
+    pg = _desc(kvq, capacity=128, k_bits=8, v_bits=8)
+    pg.page_size, pg.n_pages, pg.block_table, pg.zero_point = 64, 4, 0x30000, 1
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_cache_sizes(pg)
+    assert e.value.status == kvq.KVQ_ERR_ARG

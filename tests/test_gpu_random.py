@@ -9,7 +9,8 @@ import os
 import numpy as np
 import pytest
 
-from gpu_util import assert_close, check_codes, linear_slots, need_gpu, paged_table, softmax_default, window_slots
+from gpu_util import (assert_close, check_codes, check_codes_zp, linear_slots, need_gpu, paged_table, softmax_default,
+                      window_slots)
 
 pytestmark = pytest.mark.gpu
 
@@ -40,12 +41,13 @@ def draw(seed):
         A = W = 0
         n_pos = int(rng.integers(1, 1600))
         cap = ((n_pos + (P or 1) - 1) // (P or 1)) * (P or 1) + int(rng.choice([0, P or 7]))
+    zp = bool(quant and not P and rng.random() < 0.25)   # the zero-point codec (contiguous storage)
     chunk = int(rng.choice([0, 256, 512, 1024]))
     if not quant and chunk:
         chunk = int(rng.choice([64, 128, 256]))
     n_pieces = int(rng.integers(1, 4))
     return dict(kb=kb, vb=vb, HD=HD, G=G, H=H, B=B, gs=gs, P=P, A=A, W=W, cap=cap, n_pos=n_pos, chunk=chunk,
-                n_pieces=n_pieces, fused=bool(rng.random() < 0.5), rng=rng)
+                n_pieces=n_pieces, fused=bool(rng.random() < 0.5), zp=zp, rng=rng)
 
 
 # KVQ_RANDOM_SEEDS sets the number of draws (1200 run in about 20 s)
@@ -71,7 +73,7 @@ def test_random_configuration(oq, seed):
         cache = kvq.alloc_cache(B, H, HD, cap, kb, vb, gs, A, W, page_size=P, n_pages=B * pps + 3,
                                 block_table=to_device(table))
     else:
-        cache = kvq.alloc_cache(B, H, HD, cap, kb, vb, gs, A, W)
+        cache = kvq.alloc_cache(B, H, HD, cap, kb, vb, gs, A, W, zero_point=int(c["zp"]))
     # the context before the step's row, appended in pieces
     n0 = n_pos - 1
     cuts = sorted(set([0, n0] + [int(x) for x in rng.integers(0, n0 + 1, c["n_pieces"] - 1)]))
@@ -96,11 +98,11 @@ def test_random_configuration(oq, seed):
     got = out.cpu().numpy()
     if not P:
         slots = window_slots(oq, n_pos, A, W) if W else linear_slots(n_pos, cap)
-        check_codes(oq, cache, K, V, slots)
+        (check_codes_zp if c["zp"] else check_codes)(oq, cache, K, V, slots)
     for b in range(B):
         L = n_pos if W else min(lens[b], cap)
         if L == 0:
             assert np.all(got[b] == 0), desc
             continue
-        want = oq.decode_step(kb, vb, gs, A, W, K[b][:, :L], V[b][:, :L], q[b], softmax_default(HD))
+        want = oq.decode_step(kb, vb, gs, A, W, K[b][:, :L], V[b][:, :L], q[b], softmax_default(HD), asym=c["zp"])
         assert_close(got[b], want, f"{desc} b={b} L={L}")
