@@ -156,12 +156,18 @@ struct QuantParams {
 struct QuantSmem {
     int zs, vs, wd, red, misc, total;
     bool wd_alias;             // weight words overwrite each wave's own scores
+    bool vs_in_wd;             // value scales sit in the tail of each 4-position block of weight words
 };
 
-// Per wave: scores [S][G] fp32, value scales [S][vg] fp16 bits, weight words
-// [vg][S/4][G][lo, hi] (over the scores when vg == 1); then the
-// cross-wave merge area (over the scores when it fits) and the wave maxima
-// and sums.
+// Per wave: scores [S][G] fp32, value scales [S][vg] fp16 bits (or 32-bit
+// scale | zero words), weight words [S/4][vg][G][lo, hi] (over the scores
+// when vg == 1); then the cross-wave merge area (over the scores when it
+// fits) and the wave maxima and sums.  With several scale groups and the
+// symmetric codec the value scales of 4 positions ([4][vg] fp16) occupy the
+// last 2 vg words of those positions' block of weight words, which only the
+// lane that reads them later overwrites; this keeps the G = 4, vg = 4
+// layout at 48 KiB, three workgroups a CU, where its own area (56 KiB) would
+// allow two.
 __host__ __device__ inline QuantSmem quant_smem(int G, int HD, int vg, bool zp = false)
 {
     QuantSmem s;
@@ -169,8 +175,9 @@ __host__ __device__ inline QuantSmem quant_smem(int G, int HD, int vg, bool zp =
     int off = 0;
     s.zs = off;
     off += QD_WAVES * S * G * 4;
+    s.vs_in_wd = vg > 1 && !zp;
     s.vs = off;
-    off += QD_WAVES * S * vg * (zp ? 4 : 2);            // value scale (and zero point) words
+    if (!s.vs_in_wd) off += QD_WAVES * S * vg * (zp ? 4 : 2);   // value scale (and zero point) words
     s.wd_alias = vg == 1;
     if (s.wd_alias) {
         s.wd = s.zs;
@@ -407,8 +414,10 @@ void decode_quant_kernel(QuantParams p)
         __builtin_amdgcn_s_waitcnt(WAIT_VMEM_ALL);
         __syncthreads();
 #pragma unroll
-        for (int h = 0; h < G; h++) qs[h] = fmaxf(s_amax[h] / (float)Q_RANGE * p.qk_scale, 1e-30f);
-        xq = *s_xflag != 0;
+        for (int h = 0; h < G; h++)                  // (LDS values: made wave-uniform for the compiler)
+            qs[h] = __int_as_float(__builtin_amdgcn_readfirstlane(
+                __float_as_int(fmaxf(s_amax[h] / (float)Q_RANGE * p.qk_scale, 1e-30f))));
+        xq = __builtin_amdgcn_readfirstlane(*s_xflag) != 0;
         __syncthreads();                             // the LDS is reused below
     } else {
 #pragma unroll
@@ -439,11 +448,51 @@ void decode_quant_kernel(QuantParams p)
 
     const QuantSmem lay = quant_smem(G, HD, KG, ZP);
     constexpr int SCB = ZP ? 4 : 2;                  // bytes per scale entry
+    constexpr int SW = (KG * SCB + 3) / 4;           // 32-bit words of one position's scales (one tensor)
+    constexpr bool VS_IN_WD = KG > 1 && !ZP;         // value scales inside the weight words' area
+    constexpr int WBLK = KG * G * 2;                 // weight words of one 4-position group
     float *zs = reinterpret_cast<float *>(smem + lay.zs) + wave * S * G;       // this wave's scores
-    using VsT = typename std::conditional<ZP, uint32_t, uint16_t>::type;
-    VsT *vsl = reinterpret_cast<VsT *>(smem + lay.vs) + wave * S * KG;   // and value scale words
     uint32_t *wdw = lay.wd_alias ? reinterpret_cast<uint32_t *>(zs)
                                  : reinterpret_cast<uint32_t *>(smem + lay.wd) + wave * KG * (S / 4) * G * 2;
+    // value scale words of position pos (within the sub-chunk): one fp16 (one
+    // scale group), 2 fp16 a word (several groups: the last 2 KG words of the
+    // position's 4-group block of weight words), or 32-bit scale | zero words
+    uint16_t *vs16 = reinterpret_cast<uint16_t *>(smem + lay.vs) + wave * S;
+    uint32_t *vsw = VS_IN_WD ? wdw : reinterpret_cast<uint32_t *>(smem + lay.vs) + wave * S * KG;
+    auto vs_word = [&](int pos) -> int {
+        if constexpr (VS_IN_WD) return (pos >> 2) * WBLK + (WBLK - 2 * KG) + (pos & 3) * (KG / 2);
+        else return pos * KG;
+    };
+    auto vs_rd = [&](int pos, uint32_t (&w)[SW]) {
+        if constexpr (!ZP && KG == 1) {
+            w[0] = vs16[pos];
+        } else if constexpr (SW == 1) {
+            w[0] = vsw[vs_word(pos)];
+        } else if constexpr (SW == 2) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(vsw + vs_word(pos));
+            w[0] = v.x; w[1] = v.y;
+        } else {
+            const uint4 v = *reinterpret_cast<const uint4 *>(vsw + vs_word(pos));
+            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        }
+    };
+    auto vs_wr = [&](int pos, const uint32_t (&w)[SW]) {
+        if constexpr (!ZP && KG == 1) {
+            vs16[pos] = (uint16_t)w[0];
+        } else if constexpr (SW == 1) {
+            vsw[vs_word(pos)] = w[0];
+        } else if constexpr (SW == 2) {
+            *reinterpret_cast<uint2 *>(vsw + vs_word(pos)) = make_uint2(w[0], w[1]);
+        } else {
+            *reinterpret_cast<uint4 *>(vsw + vs_word(pos)) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    };
+    // scale word of group g (fp16 bits, or fp16 | zero << 16)
+    auto sc_of = [](const uint32_t (&w)[SW], int g) -> uint32_t {
+        if constexpr (ZP) return w[g];
+        else if constexpr (KG == 1) return w[0];
+        else return (w[g >> 1] >> (16 * (g & 1))) & 0xFFFFu;
+    };
     float *red = reinterpret_cast<float *>(smem + lay.red);
     float *misc = reinterpret_cast<float *>(smem + lay.misc);
 
@@ -491,7 +540,7 @@ void decode_quant_kernel(QuantParams p)
     const uint32_t kso = lane * p.k_sc_t * SCB, vso = lane * p.v_sc_t * SCB;
     struct Tile {
         uint4 k[T::K_U4];
-        uint32_t ks[KG], vs[KG];
+        uint32_t ks[SW], vs[SW];                     // the position's scale words (sc_of)
     };
     auto load = [&](int tb, Tile &d) {
         const int u = unit_of(tb);
@@ -512,15 +561,21 @@ void decode_quant_kernel(QuantParams p)
         const rsrc_t krs2 = make_rsrc(kb + 4096, kbytes > 4096 ? kbytes - 4096 : 0);
 #pragma unroll
         for (int u4 = 0; u4 < T::K_U4; u4++) d.k[u4] = bld_u4<CP_NT>(u4 < 4 ? krs : krs2, ko + (u4 % 4) * 1024);
-#pragma unroll
-        for (int g = 0; g < KG; g++) {
-            if constexpr (ZP) {
-                d.ks[g] = bld_u32<0>(ksrs, kso + 4 * g);
-                d.vs[g] = bld_u32<0>(vsrs, vso + 4 * g);
-            } else {
-                d.ks[g] = bld_u16(ksrs, kso + 2 * g);
-                d.vs[g] = bld_u16(vsrs, vso + 2 * g);
-            }
+        // (a position's scale words are contiguous: one load each)
+        if constexpr (SW == 1 && SCB * KG == 2) {
+            d.ks[0] = bld_u16(ksrs, kso);
+            d.vs[0] = bld_u16(vsrs, vso);
+        } else if constexpr (SW == 1) {
+            d.ks[0] = bld_u32<0>(ksrs, kso);
+            d.vs[0] = bld_u32<0>(vsrs, vso);
+        } else if constexpr (SW == 2) {
+            const uint2 a = bld_u2(ksrs, kso), v = bld_u2(vsrs, vso);
+            d.ks[0] = a.x; d.ks[1] = a.y;
+            d.vs[0] = v.x; d.vs[1] = v.y;
+        } else {
+            const uint4 a = bld_u4<0>(ksrs, kso), v = bld_u4<0>(vsrs, vso);
+            d.ks[0] = a.x; d.ks[1] = a.y; d.ks[2] = a.z; d.ks[3] = a.w;
+            d.vs[0] = v.x; d.vs[1] = v.y; d.vs[2] = v.z; d.vs[3] = v.w;
         }
     };
     float mloc[G];                                   // per-lane score maxima of the current sub-chunk
@@ -529,12 +584,9 @@ void decode_quant_kernel(QuantParams p)
     auto compute = [&](int tb, int sc0, const Tile &c) {
         const int t = tb + lane;
         const bool valid = t < nw;
-#pragma unroll
-        for (int g = 0; g < KG; g++) {
-            // (zero past the wave's range: the load returned zero; every
-            // tile of the sub-chunk lies inside its S rows of LDS)
-            vsl[(t - sc0) * KG + g] = (VsT)c.vs[g];
-        }
+        // (zero past the wave's range: the load returned zero; every tile of
+        // the sub-chunk lies inside its S rows of LDS)
+        vs_wr(t - sc0, c.vs);
         // an opaque zero offset, redefined every tile, keeps the digit loads
         // inside the loop (hoisted, they would need hundreds of SGPRs)
         int qz;
@@ -585,12 +637,12 @@ void decode_quant_kernel(QuantParams p)
                     }
                 }
             }
-            const float sk = f16_bits_to_f32((uint16_t)c.ks[blk]);
+            const float sk = f16_bits_to_f32((uint16_t)sc_of(c.ks, blk));
             // zero-point codec: the stored code is code - 2^(KB-1), so the
             // group's score is sk * (acc - (zero - 2^(KB-1)) * sum q_int)
             int zk = 0;
             if constexpr (ZP) {
-                zk = (int)(c.ks[blk] >> 16) - (1 << (KB - 1));
+                zk = (int)(sc_of(c.ks, blk) >> 16) - (1 << (KB - 1));
                 const KVQ_CONST int32_t *qsum = qdl + qd_digits(KB, HD, G) + blk * G;
 #pragma unroll
                 for (int h = 0; h < G; h++) acc[h] -= __mul24(zk, qsum[h]);
@@ -681,13 +733,13 @@ void decode_quant_kernel(QuantParams p)
         for (int d = 0; d < T::V_DPL; d++) buf[f][d] = bld_u32<T::V_CP>(rs.r[f / NPF], vo + (f % NPF) * GSTEP + d * 4);
     };
     const int vgrp = (qsl * T::V_DPL * T::V_CPD) / (HD / KG);   // value scale group of the lane
-    const uint32_t *wdg = wdw + (size_t)vgrp * (S / 4) * G * 2;
+    const uint32_t *wdg = wdw + (size_t)vgrp * G * 2;
     uint32_t accl[G][T::V_ACC], acch[G][T::V_ACC];
     // one 4-position group: weight words of local group rg (LDS broadcast)
     // times the value codes this lane holds for it
     auto group = [&](int rg, const uint32_t (&x)[T::V_DPL]) {
         uint32_t wl[G], wh[G];
-        const uint32_t *src = wdg + (size_t)rg * G * 2;
+        const uint32_t *src = wdg + (size_t)rg * WBLK;
 #pragma unroll
         for (int h = 0; h < G; h++) {
             wl[h] = src[2 * h];
@@ -833,9 +885,11 @@ void decode_quant_kernel(QuantParams p)
                             lloc[h] += pr[h];
                         }
                         float prod[KG][G];
+                        uint32_t vw[SW];
+                        vs_rd(tq + k, vw);
 #pragma unroll
                         for (int g = 0; g < KG; g++) {
-                            const float sv = f16_bits_to_f32((uint16_t)vsl[(tq + k) * KG + g]);
+                            const float sv = f16_bits_to_f32((uint16_t)sc_of(vw, g));
 #pragma unroll
                             for (int h = 0; h < G; h++) {
                                 prod[g][h] = pr[h] * sv;
@@ -865,23 +919,30 @@ void decode_quant_kernel(QuantParams p)
                     float pr[4][G];                  // p * s_v (one group) or p
 #pragma unroll
                     for (int k = 0; k < 4; k++) rd(zs + (size_t)(tq + k) * G, pr[k]);
+                    // the 4 positions' value scale words, all read before the
+                    // first weight word goes out (they may share its block)
+                    uint32_t vw[4][SW];
+                    if constexpr (KG > 1 || ZP) {
+#pragma unroll
+                        for (int k = 0; k < 4; k++) vs_rd(tq + k, vw[k]);
+                    }
 #pragma unroll
                     for (int g = 0; g < KG; g++) {
                         float sv[4];
                         if constexpr (KG > 1) {
 #pragma unroll
-                            for (int k = 0; k < 4; k++) sv[k] = f16_bits_to_f32((uint16_t)vsl[(tq + k) * KG + g]);
+                            for (int k = 0; k < 4; k++) sv[k] = f16_bits_to_f32((uint16_t)sc_of(vw[k], g));
                         }
                         // zero point: the four positions' zero points, one byte each
                         uint32_t zb = 0;
                         if constexpr (ZP) {
-                            const uint32_t a0 = vsl[(tq + 0) * KG + g], a1 = vsl[(tq + 1) * KG + g];
-                            const uint32_t a2 = vsl[(tq + 2) * KG + g], a3 = vsl[(tq + 3) * KG + g];
+                            const uint32_t a0 = sc_of(vw[0], g), a1 = sc_of(vw[1], g);
+                            const uint32_t a2 = sc_of(vw[2], g), a3 = sc_of(vw[3], g);
                             const uint32_t z01 = __builtin_amdgcn_perm(a1, a0, 0x0c0c0602u);   // a0.b2 a1.b2
                             const uint32_t z23 = __builtin_amdgcn_perm(a3, a2, 0x0c0c0602u);
                             zb = __builtin_amdgcn_perm(z23, z01, 0x05040100u);
                         }
-                        uint32_t *dst = wdw + ((size_t)g * (S / 4) + grp) * G * 2;
+                        uint32_t *dst = wdw + ((size_t)grp * KG + g) * G * 2;
 #pragma unroll
                         for (int h = 0; h < G; h++) {
                             uint32_t wb[4];

@@ -55,6 +55,7 @@ __device__ __forceinline__ float wave_sum(float v)
 #define KVQ_CONST __attribute__((address_space(4)))
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 ld_u4(const void *p)
 {
     const u32x4_t v = *(const KVQ_GLOBAL u32x4_t *)p;
@@ -102,6 +103,11 @@ __device__ __forceinline__ uint4 bld_u4(rsrc_t r, uint32_t off)
 {
     const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CP);
     return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 bld_u2(rsrc_t r, uint32_t off)
+{
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    return make_uint2(v.x, v.y);
 }
 template <int CP = 0>
 __device__ __forceinline__ uint32_t bld_u32(rsrc_t r, uint32_t off)
