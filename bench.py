@@ -107,8 +107,8 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
 
     max_len = w.n_pos
     ch = kvq.kvq_chunk_tokens(layers[0][0], w.n_q_heads, max_len) if chunk == 0 else chunk
-    n_chunks = -(-min(max_len, w.capacity) // ch)
-    ws_bytes = kvq.kvq_workspace_bytes(layers[0][0], w.n_q_heads, max_len, ch)
+    n_chunks = kvq.kvq_chunk_count(layers[0][0], w.n_q_heads, max_len, chunk)
+    ws_bytes = kvq.kvq_workspace_bytes(layers[0][0], w.n_q_heads, max_len, chunk)
     ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")
     out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     pos = positions([w.n_pos - 1] * w.batch)
@@ -128,7 +128,7 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
         for cache, k_last, v_last, q in layers:
             if scrub is not None:
                 torch.sum(scrub, dim=0, out=scrub_out)
-            kvq.kvq_decode_step(cache, k_last, v_last, 1, pos, q, w.n_q_heads, lens, max_len, 0.0, ch, out, ws,
+            kvq.kvq_decode_step(cache, k_last, v_last, 1, pos, q, w.n_q_heads, lens, max_len, 0.0, chunk, out, ws,
                                 ws_bytes, st)
 
     def parts_step(record, st):
@@ -140,7 +140,7 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
             e[0].record(st)
             kvq.kvq_append(cache, k_last, v_last, 1, pos, st)
             e[1].record(st)
-            kvq.kvq_decode_partials(cache, q, w.n_q_heads, lens, max_len, 0.0, ch, ws, ws_bytes, st)
+            kvq.kvq_decode_partials(cache, q, w.n_q_heads, lens, max_len, 0.0, chunk, ws, ws_bytes, st)
             e[2].record(st)
             kvq.kvq_combine(w.batch, w.n_q_heads, w.head_dim, n_chunks, ws, ws_bytes, out, st)
             e[3].record(st)
@@ -168,7 +168,7 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
                 e = ev_step[s_ * w.n_layers + li]
                 torch.sum(scrub, dim=0, out=scrub_out)
                 e[0].record(stream)
-                kvq.kvq_decode_step(cache, k_last, v_last, 1, pos, q, w.n_q_heads, lens, max_len, 0.0, ch, out,
+                kvq.kvq_decode_step(cache, k_last, v_last, 1, pos, q, w.n_q_heads, lens, max_len, 0.0, chunk, out,
                                     ws, ws_bytes, stream)
                 e[1].record(stream)
         torch.cuda.synchronize()
@@ -192,10 +192,10 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
     mode0 = layer_modes[0] if layer_modes else mode
     if mode0.k_bits < 16:
         # the split kernel alone: one query preparation, then split launches on it
-        kvq.kvq_prepare_query(cache0, q0, w.n_q_heads, max_len, 0.0, ch, ws, ws_bytes, stream)
-        split = lambda: kvq.kvq_decode_partials_prepared(cache0, w.n_q_heads, lens, max_len, ch, ws, ws_bytes, stream)
+        kvq.kvq_prepare_query(cache0, q0, w.n_q_heads, max_len, 0.0, chunk, ws, ws_bytes, stream)
+        split = lambda: kvq.kvq_decode_partials_prepared(cache0, w.n_q_heads, lens, max_len, chunk, ws, ws_bytes, stream)
     else:
-        split = lambda: kvq.kvq_decode_partials(cache0, q0, w.n_q_heads, lens, max_len, 0.0, ch, ws, ws_bytes, stream)
+        split = lambda: kvq.kvq_decode_partials(cache0, q0, w.n_q_heads, lens, max_len, 0.0, chunk, ws, ws_bytes, stream)
     settled = 0.0
     while settled < settle_ms:
         settled += timed(split, 50)
@@ -622,7 +622,7 @@ def probe_traffic(chunk: int, workload: str = "k4v4-32k", log=print) -> int:
     fill([cache], w, 0, w.n_pos)
     q = queries(w, 0)
     ch = kvq.kvq_chunk_tokens(cache, w.n_q_heads, w.n_pos) if chunk == 0 else chunk
-    ws_bytes = kvq.kvq_workspace_bytes(cache, w.n_q_heads, w.n_pos, ch)
+    ws_bytes = kvq.kvq_workspace_bytes(cache, w.n_q_heads, w.n_pos, chunk)
     ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")
     lens = positions([w.n_pos] * w.batch)
     src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
@@ -631,7 +631,7 @@ def probe_traffic(chunk: int, workload: str = "k4v4-32k", log=print) -> int:
     dst.copy_(src)                                   # 1 GiB read, 1 GiB written
     torch.cuda.synchronize()
     for _ in range(3):
-        kvq.kvq_decode_partials(cache, q, w.n_q_heads, lens, w.n_pos, 0.0, ch, ws, ws_bytes)
+        kvq.kvq_decode_partials(cache, q, w.n_q_heads, lens, w.n_pos, 0.0, chunk, ws, ws_bytes)
     torch.cuda.synchronize()
     log(f"[bench] traffic probe: copy 1 GiB, 3 launches of {w.name}/{mode.name} (chunk {ch})")
     return 0

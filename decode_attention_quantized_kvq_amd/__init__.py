@@ -32,7 +32,8 @@ KVQ_ERR_HIP = -8
 KVQ_ERR_ARG = -9
 
 EXPORTED = (
-    "kvq_bytes_per_token", "kvq_cache_sizes", "kvq_append", "kvq_chunk_tokens", "kvq_workspace_bytes",
+    "kvq_bytes_per_token", "kvq_cache_sizes", "kvq_append", "kvq_chunk_tokens", "kvq_chunk_count",
+    "kvq_workspace_bytes",
     "kvq_decode_partials", "kvq_prepare_query", "kvq_decode_partials_prepared", "kvq_combine", "kvq_decode_attn",
     "kvq_decode_step", "kvq_decode_step_static", "kvq_read_probe", "kvq_status_str", "kvq_last_error",
 )
@@ -90,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_append.restype = I
         L.kvq_chunk_tokens.argtypes = [C, I, I]
         L.kvq_chunk_tokens.restype = I
+        L.kvq_chunk_count.argtypes = [C, I, I, I]
+        L.kvq_chunk_count.restype = I
         L.kvq_workspace_bytes.argtypes = [C, I, I, I]
         L.kvq_workspace_bytes.restype = S
         L.kvq_decode_partials.argtypes = [C, P, I, P, I, ctypes.c_float, I, P, S, P]
@@ -163,6 +166,10 @@ def kvq_append(cache, k_new, v_new, n_new: int, start_pos, stream=None) -> None:
 
 def kvq_chunk_tokens(cache, n_q_heads: int, max_seq_len: int) -> int:
     return _check(lib().kvq_chunk_tokens(ctypes.byref(_desc(cache)), n_q_heads, max_seq_len))
+
+
+def kvq_chunk_count(cache, n_q_heads: int, max_seq_len: int, chunk_tokens: int = 0) -> int:
+    return _check(lib().kvq_chunk_count(ctypes.byref(_desc(cache)), n_q_heads, max_seq_len, chunk_tokens))
 
 
 def kvq_workspace_bytes(cache, n_q_heads: int, max_seq_len: int, chunk_tokens: int = 0) -> int:

@@ -526,6 +526,15 @@ static size_t cache_ws_bytes(const kvq_cache *c, int n_q_heads, int n_chunks)
     return ws_layout(c->batch, n_q_heads, c->head_dim, n_chunks, c->n_kv_heads, c->k_bits).total;
 }
 
+int kvq_chunk_count(const kvq_cache *c, int n_q_heads, int max_seq_len, int chunk_tokens)
+{
+    int ch, nc;
+    const int st = resolve_chunk(c, n_q_heads, max_seq_len, chunk_tokens, &ch, &nc);
+    if (st) return st;
+    ok();
+    return nc;
+}
+
 size_t kvq_workspace_bytes(const kvq_cache *c, int n_q_heads, int max_seq_len, int chunk_tokens)
 {
     int ch, nc;

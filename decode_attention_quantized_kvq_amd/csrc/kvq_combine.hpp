@@ -40,8 +40,11 @@ struct PlainLoad {
     __device__ __forceinline__ float operator()(const float *p) const { return *p; }
 };
 
-// partials written by other workgroups of the same launch, after an acquire
-// fence: loads that read the coherent copy (never the scalar cache)
+// partials written by other workgroups of the same launch: relaxed
+// device-scope loads, which read the device-coherent copy (never the scalar
+// cache, never a stale line of this XCD's L2).  No acquire fence precedes
+// them: the ordering they rely on is the hardware's, stated at
+// combine_if_last.
 struct AgentLoad {
     __device__ __forceinline__ float operator()(const float *p) const
     {
@@ -82,6 +85,15 @@ constexpr int WAIT_VMEM_ALL = 0x0F70;
 // loads.  Each counter is zeroed before the launch (by the query preparation
 // that precedes it), so every launch starts from zero; no workgroup waits
 // for another.  flag: one int of LDS.
+// Memory ordering: there is no release/acquire pair (a __threadfence()
+// before the ticket made the fused step several times slower).  The merge
+// relies on this gfx9-family behaviour: a device-scope store has reached
+// the device-coherent level shared by all XCDs once the storing thread's
+// vmcnt is 0; the ticket is a device-scope atomic performed there after
+// every thread of the workgroup has passed that wait (the barrier); the
+// merging workgroup's device-scope loads are issued after it draws the
+// last ticket and read that level.  So every partial is visible to the
+// merge, by hardware behaviour rather than by the HIP memory model.
 template <int HD, int G, int THREADS>
 __device__ __forceinline__ void combine_if_last(const float *ml, const float *acc, float *out, int *cnt,
                                                 int n_chunks, size_t row0, int *flag)

@@ -202,11 +202,12 @@ int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n
  *   most recent positions, so slot order differs from position order, which
  *   softmax does not see.  L == 0 gives out = 0.
  *
- * The work is split along the context into chunks of `chunk_tokens` slots:
- * kvq_decode_partials() writes per-chunk partial results (running max m in
- * log2 units, sum l, and unnormalized accumulator) into the workspace;
- * kvq_combine() merges them; kvq_decode_attn() does both.  Splitting the two
- * lets the partials of several devices be merged by one kvq_combine().
+ * The work is split along the context into chunks of `chunk_tokens` slots
+ * (C = kvq_chunk_count() of them): kvq_decode_partials() writes per-chunk
+ * partial results (running max m in log2 units, sum l, and unnormalized
+ * accumulator) into the workspace; kvq_combine() merges them;
+ * kvq_decode_attn() does both.  Splitting the two lets the partials of
+ * several devices be merged by one kvq_combine().
  *
  * q, out       : float32 [batch][n_q_heads][head_dim], 16-byte aligned.
  *                n_q_heads must be n_kv_heads * G with G in {1, 2, 4, 8}.
@@ -220,7 +221,7 @@ int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n
  *                whose working set fits the device's LDS (else KVQ_ERR_ARG).
  * workspace    : device memory of at least kvq_workspace_bytes(...) bytes,
  *                256-byte aligned.  Layout, for P = batch * n_q_heads rows
- *                and C chunks: float ml[P][C][2] = (m, l) at offset 0, then
+ *                and C = kvq_chunk_count(...) chunks: float ml[P][C][2] = (m, l) at offset 0, then
  *                float acc[P][C][head_dim] at offset round_up(8*P*C, 256);
  *                with 8/4-bit keys, scratch for the query's fixed-point form
  *                and one int32 ticket counter per (sequence, KV head) for
@@ -237,8 +238,15 @@ int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n
  * workgroups (sequences x KV heads x chunks), at least 512; for 16/32-bit
  * caches at most 1024, >= 2048 workgroups, at least 64 slots and within the
  * LDS budget.
+ *
+ * kvq_chunk_count() returns C, the chunks per (sequence, KV head) for these
+ * arguments: ceil(L / chunk) for L = min(max_seq_len, capacity) and the
+ * chunk of chunk_tokens (or of kvq_chunk_tokens() when it is 0), or a
+ * negative status.  kvq_combine() takes it as n_chunks.
  */
 int kvq_chunk_tokens(const kvq_cache *c, int n_q_heads, int max_seq_len);
+
+int kvq_chunk_count(const kvq_cache *c, int n_q_heads, int max_seq_len, int chunk_tokens);
 
 size_t kvq_workspace_bytes(const kvq_cache *c, int n_q_heads, int max_seq_len, int chunk_tokens);
 

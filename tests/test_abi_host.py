@@ -285,7 +285,8 @@ def test_workspace_and_chunks(kvq):
     d = _desc(kvq, batch=32, n_kv_heads=8, capacity=32768, k_bits=4, v_bits=4)
     ch = kvq.kvq_chunk_tokens(d, 32, 32768)
     assert ch % 64 == 0 and 64 <= ch <= 4096
-    n_chunks = -(-32768 // ch)
+    n_chunks = kvq.kvq_chunk_count(d, 32, 32768, 0)
+    assert n_chunks == -(-32768 // ch)
     assert 32 * 8 * n_chunks >= 2048                     # 8 workgroups per CU over 256 CUs
     P = 32 * 32
     partials = ((P * n_chunks * 8 + 255) // 256) * 256 + P * n_chunks * 128 * 4
@@ -344,6 +345,25 @@ def test_workspace_and_chunks(kvq):
     assert kvq.kvq_chunk_tokens(f32k, 32, 32768) == 1024
     f8k = _desc(kvq, batch=16, n_kv_heads=8, capacity=8192, k_bits=16, v_bits=16)
     assert kvq.kvq_chunk_tokens(f8k, 32, 8192) == 512
+
+
+def test_chunk_count(kvq):
+    d = _desc(kvq, batch=32, n_kv_heads=8, capacity=32768, k_bits=4, v_bits=4)
+    assert kvq.kvq_chunk_count(d, 32, 32768) == 16
+    assert kvq.kvq_chunk_count(d, 32, 32768, 1024) == 32
+    assert kvq.kvq_chunk_count(d, 32, 30001, 1024) == 30
+    assert kvq.kvq_chunk_count(d, 32, 10 ** 9, 4096) == 8          # L is capped by the capacity
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        B, H = int(rng.integers(1, 65)), int(rng.choice([1, 2, 4, 8]))
+        L = int(rng.integers(1, 65536))
+        dd = _desc(kvq, batch=B, n_kv_heads=H, capacity=L, k_bits=int(rng.choice([4, 8, 16])), v_bits=4)
+        if dd.k_bits == 16:
+            dd.v_bits = 16
+        ch = kvq.kvq_chunk_tokens(dd, H * 4, L)
+        assert kvq.kvq_chunk_count(dd, H * 4, L) == -(-L // ch), (B, H, L, ch)
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_chunk_count(d, 32, 0)
 
 
 def test_binding_has_no_fallback(kvq, monkeypatch, tmp_path):
