@@ -542,8 +542,9 @@ TRAFFIC_SOURCES = ["decode_attention_quantized_kvq_amd/csrc/kvq_decode_quant.hpp
                    "decode_attention_quantized_kvq_amd/csrc/kvq.hip"]
 
 
-PROBE_WORKLOADS = {"k4v4-32k": ("K4V4_32K", "K4V4", "decode_quant_kernel<4,4,128,4,1,false>"),
-                   "k8v4-32k": ("K8V4_32K", "K8V4", "decode_quant_kernel<8,4,128,4,1,false>")}
+PROBE_WORKLOADS = {"k4v4-32k": ("K4V4_32K", "K4V4", "decode_quant_kernel<4,4,128,4,1,false,false>"),
+                   "k8v4-32k": ("K8V4_32K", "K8V4", "decode_quant_kernel<8,4,128,4,1,false,false>"),
+                   "k4v4-g32-32k": ("K4V4_32K", "K4V4_G32", "decode_quant_kernel<4,4,128,4,4,false,false>")}
 
 
 def record_traffic(fetch_csv: str, write_csv: str, workload: str = "k4v4-32k", log=print) -> int:
@@ -616,7 +617,8 @@ def probe_traffic(chunk: int, workload: str = "k4v4-32k", log=print) -> int:
     import workloads as wl
     from workloads.device import fill, positions, queries
 
-    w, mode = {"k4v4-32k": (wl.K4V4_32K, wl.K4V4), "k8v4-32k": (wl.K8V4_32K, wl.K8V4)}[workload]
+    wname, mname, _ = PROBE_WORKLOADS[workload]
+    w, mode = getattr(wl, wname), getattr(wl, mname)
     cache = kvq.alloc_cache(w.batch, w.n_kv_heads, w.head_dim, w.capacity, mode.k_bits, mode.v_bits,
                             _group(mode, w), w.n_anchor, w.window)
     fill([cache], w, 0, w.n_pos)
@@ -649,7 +651,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe-traffic", action="store_true",
                     help="copy 1 GiB then launch the split kernel of --probe-workload 3 times (for counter runs)")
-    ap.add_argument("--probe-workload", choices=["k4v4-32k", "k8v4-32k"], default="k4v4-32k",
+    ap.add_argument("--probe-workload", choices=sorted(PROBE_WORKLOADS), default="k4v4-32k",
                     help="the workload --probe-traffic launches and --record-traffic records")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from the two counter runs (CPU only)")
@@ -750,7 +752,7 @@ def main() -> int:
         "pct_of_peak": round(100.0 * head["step_GBps"] / PEAK_HBM_GBS, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_quant_kernel<4,4,128,4,1,false>",
+            "kernel": PROBE_WORKLOADS["k4v4-32k"][2],
             "achieved": round(head["split_GBps"], 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

@@ -57,7 +57,7 @@ def test_traffic_record_round_trip(bench, tmp_path, monkeypatch):
         shutil.copy(ROOT / f, tmp_path / f)
     monkeypatch.setattr(bench, "ROOT", tmp_path)
     copy = "__amd_rocclr_copyBuffer"
-    dec = "void kvq::decode_quant_kernel<4, 4, 128, 4, 1, false>(kvq::QuantParams)"
+    dec = "void kvq::decode_quant_kernel<4, 4, 128, 4, 1, false, false>(kvq::QuantParams)"
     # FETCH_SIZE reads half of the copy's 1 GiB (factor 2); WRITE_SIZE all of it
     _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", [(copy, 524288), (dec, 1000), (dec, 1002), (dec, 1004)])
     _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", [(copy, 1048576), (dec, 10), (dec, 10), (dec, 10)])
