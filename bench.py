@@ -48,10 +48,14 @@ METRIC = "decode-attention achieved HBM GB/s (% of MI355X peak) and tokens/s per
 
 
 def bpt_head(mode, w) -> float:
-    """Cache bytes per position per KV head (fp16 scales included)."""
+    """Cache bytes per position per KV head (fp16 scales included; the
+    zero-point codec stores a 32-bit word, scale and zero, per group)."""
     import decode_attention_quantized_kvq_amd as kvq
     g = _group(mode, w)
-    return kvq.kvq_bytes_per_token(mode.k_bits, mode.v_bits, w.n_kv_heads, w.head_dim, g) / w.n_kv_heads
+    b = kvq.kvq_bytes_per_token(mode.k_bits, mode.v_bits, w.n_kv_heads, w.head_dim, g) / w.n_kv_heads
+    if getattr(mode, "zero_point", False):
+        b += 2 * (w.head_dim / g) * ((mode.k_bits < 16) + (mode.v_bits < 16))
+    return b
 
 
 def _group(mode, w) -> int:
@@ -98,7 +102,7 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
                           block_table=order.to(torch.int32).view(w.batch, pps).to("cuda"))
         lm = layer_modes[layer] if layer_modes else mode
         cache = kvq.alloc_cache(w.batch, w.n_kv_heads, w.head_dim, w.capacity, lm.k_bits, lm.v_bits,
-                                _group(lm, w), w.n_anchor, w.window, **paging)
+                                _group(lm, w), w.n_anchor, w.window, zero_point=int(lm.zero_point), **paging)
         k_last, v_last = fill([cache], w, layer, w.n_pos)
         q = queries(w, layer)
         layers.append((cache, k_last, v_last, q))
@@ -699,6 +703,7 @@ def main() -> int:
             extra.append(run_mode(wl.K4V4_32K, wl.FP16, args.steps, args.warmup, args.chunk, log=log))
             extra.append(run_mode(wl.K4V4_32K, wl.K4V4_G32, args.steps, args.warmup, args.chunk, log=log))
             extra.append(run_mode(wl.K4V4_32K, wl.K4V8, args.steps, args.warmup, args.chunk, log=log))
+            extra.append(run_mode(wl.K4V4_32K, wl.K4V4_ZP, args.steps, args.warmup, args.chunk, log=log))
         if want("k4v4-window"):
             extra.append(run_mode(wl.K4V4_WINDOW, wl.K4V4, args.steps, args.warmup, args.chunk, flush=True, log=log))
         if want("k8v4-8k"):

@@ -29,14 +29,16 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stdout + r.stderr
 
 
-@pytest.mark.parametrize("wname,mname,expect", [("K4V4_32K", "K4V4", 1_107_820_544), ("K8V4_32K", "K8V4", 822_345_728)])
+@pytest.mark.parametrize("wname,mname,expect", [("K4V4_32K", "K4V4", 1_107_820_544), ("K8V4_32K", "K8V4", 822_345_728),
+                                               ("K4V4_32K", "K4V4_ZP", 1_107_820_544 + 32 * 8 * 32768 * 4)])
 def test_split_bytes(bench, oq, wname, mname, expect):
     """Cache bytes of every attended position of every (sequence, KV head),
-    plus the fp32 queries: by the oracle's formula and by hand."""
+    plus the fp32 queries: by the oracle's formula and by hand (the
+    zero-point codec: 4 bytes per group and side instead of 2)."""
     import workloads as wl
     w, m = getattr(wl, wname), getattr(wl, mname)
     g = m.group_size(w.n_kv_heads, w.head_dim)
-    per_pos = oq.bytes_per_token(m.k_bits, m.v_bits, w.n_kv_heads, w.head_dim, g)
+    per_pos = oq.bytes_per_token_zp(m.k_bits, m.v_bits, w.n_kv_heads, w.head_dim, g, int(m.zero_point))
     want = w.batch * min(w.n_pos, w.capacity) * per_pos + w.batch * w.n_q_heads * w.head_dim * 4
     assert bench.split_bytes(w, m) == want == expect
 

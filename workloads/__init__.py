@@ -31,12 +31,14 @@ class Mode:
     bits 32 = float32 rows, 16 = fp16 rows, 8 / 4 = symmetric codes with one
     fp16 scale per ``group`` elements (ignored for 16/32-bit sides).
     ``group = 0`` means one scale per head (group = head_dim); ``group = -1``
-    means one scale per position row across all KV heads.
+    means one scale per position row across all KV heads.  ``zero_point``:
+    the asymmetric codec (an fp16 scale and an integer zero point per group).
     """
     name: str
     k_bits: int
     v_bits: int
     group: int = 0
+    zero_point: bool = False
 
     def group_size(self, n_kv_heads: int, head_dim: int) -> int:
         if self.group == 0:
@@ -54,6 +56,7 @@ K4V4 = Mode("k4v4", 4, 4)
 K4V8 = Mode("k4v8", 4, 8)
 K8V8_ROW = Mode("k8v8-row", 8, 8, -1)
 K4V4_G32 = Mode("k4v4-g32", 4, 4, 32)      # one scale per 32 codes (KVSplit's footprint ratios)
+K4V4_ZP = Mode("k4v4-zp", 4, 4, 0, True)   # per-head scale and zero point
 
 
 @dataclass(frozen=True)
