@@ -4,7 +4,8 @@
 One step = the whole hot path for one batch, one kvq_decode_step call per
 layer: quantize-append the step's new K/V row of every sequence and KV head
 into the cache, split-K decode attention over the cache and the merge of the
-chunk partials (three launches).  Inputs are resident in HBM before timing.
+chunk partials (three launches at 32K; one when a context is one chunk per
+sequence and KV head).  Inputs are resident in HBM before timing.
 The K timed steps run as one HIP graph of K steps (the way a model's layers
 follow each other inside one decode step); the line also reports a graph of
 one step replayed K times, eager steps, and the separate calls timed with
@@ -20,7 +21,7 @@ kernel alone against MI355X's 8 TB/s HBM peak.
 By default (--modes all) the line also carries every mode of the other
 workloads, each with its split kernel's rate, % of peak, step time and
 tokens/s (`summary` lists them): K8V4 at 32K, the FP16 / K4V8 / 32-value
-group modes of the 32K shape, the same 32K workloads paged, the 8K K8V4
+group / zero-point modes of the 32K shape, the same 32K workloads paged, the 8K K8V4
 workload in K8V4 / FP16 / K8V8 / K4V4 and the 64 + 1536 window (both cold:
 they fit in the 256 MB MALL), TinyLoop-like in K8V8 / FP16 / per-layer
 widths, Tiny, the mni-ml-like generation loop, and bulk prefill.
