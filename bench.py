@@ -114,7 +114,7 @@ def run_mode(w, mode, steps: int, warmup: int, chunk: int = 0, flush: bool = Fal
     ch = kvq.kvq_chunk_tokens(layers[0][0], w.n_q_heads, max_len) if chunk == 0 else chunk
     n_chunks = kvq.kvq_chunk_count(layers[0][0], w.n_q_heads, max_len, chunk)
     ws_bytes = kvq.kvq_workspace_bytes(layers[0][0], w.n_q_heads, max_len, chunk)
-    ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")   # zero-filled: the step's ticket counters
     out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     pos = positions([w.n_pos - 1] * w.batch)
     lens = positions([w.n_pos] * w.batch)
@@ -356,7 +356,7 @@ def generation_loop(w, mode, reps: int = 5, log=print) -> dict:
     pos = [positions([w.prompt + s]) for s in range(n_gen)]
     lens = [positions([w.prompt + s + 1]) for s in range(n_gen)]
     ws_bytes = kvq.kvq_workspace_bytes(cache, w.n_q_heads, w.capacity, 0)
-    ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")   # zero-filled: the step's ticket counters
     out = torch.empty((1, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
 
     def loop(st):

@@ -163,6 +163,13 @@ size_t lds_bytes(const kvq_cache *c, int G, int chunk)
 
 int max_len_of(const kvq_cache *c, int max_seq_len) { return max_seq_len < c->capacity ? max_seq_len : c->capacity; }
 
+// kvq_decode_step runs as one launch up to kStepMaxChunks chunks per
+// (sequence, KV head), the last workgroup of each merging, and as two
+// launches (append with query preparation, then the split kernel whose last
+// workgroups merge) up to kFusedMaxChunks
+constexpr int kStepMaxChunks = 2;
+constexpr int kFusedMaxChunks = 4;
+
 int auto_chunk(const kvq_cache *c, int n_q_heads, int max_seq_len)
 {
     const int G = n_q_heads / c->n_kv_heads;
@@ -180,24 +187,27 @@ int auto_chunk(const kvq_cache *c, int n_q_heads, int max_seq_len)
     // tile) and final merge, so fewer, longer ones win once the chip holds
     // them all.  (Measured: at 32K contexts 4096-slot chunks leave a longer
     // ragged last round and 1024-slot ones pay the start and merge twice as
-    // often; a 1600-slot window over 256 units steps in 44 us at 512 against
-    // 53 us at 256; a 34-layer 1K-context step in 547 us at 512 against 629
-    // at 256 and 634 at 1024.)
+    // often.)
     const bool q = quant_modes(c);
     const int smallest = q ? 512 : 64;
     const long long want = q ? 1024 : 2048;
-    // Integer caches with short contexts that cannot fill the chip anyway
-    // (at most one round of 512-slot chunks, <= 1024 slots): one chunk per
-    // (sequence, KV head), so that a decode step is one launch.  (Measured: a
-    // 34-layer 1K-context step 528 against 541 us with two 512-slot chunks
-    // and the merge inside the split kernel.)
-    if (q && L <= 1024 && units * ((L + 511) / 512) <= want) return L <= 512 ? 512 : 1024;
+    int pick = smallest;
     for (int ch = q ? 2048 : 1024; ch >= smallest; ch >>= 1) {
         // (an integer cache's LDS does not depend on the chunk)
         if (!q && lds_bytes(c, G, ch) > kAutoLds) continue;
-        if (units * ((L + ch - 1) / ch) >= want) return ch;
+        if (units * ((L + ch - 1) / ch) >= want) {
+            pick = ch;
+            break;
+        }
     }
-    return smallest;
+    // Integer caches with short contexts (<= 2048 slots) that this rule would
+    // split in more than two chunks: two chunks at most, so that a decode step
+    // is one launch (measured: the 1600-slot window over 256 units, cold,
+    // 36.3 us a step in two 1024-slot chunks against 38.4 in four 512-slot
+    // ones in one launch and ≈ 36.5 in two launches; a 34-layer 1K-context
+    // step 503 us in two 512-slot chunks against 548 in one of 1024).
+    if (q && L <= 2048 && (L + pick - 1) / pick > kStepMaxChunks) pick = L > 1024 ? 1024 : 512;
+    return pick;
 }
 
 using FloatFn = void (*)(FloatParams);
@@ -313,9 +323,11 @@ StepPrepFn pick_step(int kb, int hd, int G)
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace: ml [P][C][2] | acc [P][C][HD] | (quantized keys) query digits
-// [B*Hkv][qd_stride] int32 (each unit's [ND+1][K_COLS][G] padded to 256
-// bytes) | query scales [P] float | extra-digit flags [B*Hkv] int32 |
-// ticket counters [B*Hkv] int32.
+// [B*Hkv][S][qd_stride] int32 (each slot's [ND+1][K_COLS][G] padded to 256
+// bytes; S = C slots, one per chunk for the one-launch step, when
+// C <= kStepMaxChunks, else 1) | query scales [P] float | extra-digit flags
+// [B*Hkv] int32 | ticket counters [B*Hkv] int32 (zero between calls; in the
+// last bytes of the caller's extent, see cnt_offset).
 struct WsLayout {
     size_t ml, acc, qdig, qsc, qflag, cnt, total;
 };
@@ -330,17 +342,30 @@ WsLayout ws_layout(int batch, int n_q_heads, int head_dim, int n_chunks, int n_k
     w.qdig = w.qsc = w.qflag = w.cnt = 0;
     if (quantized(k_bits)) {
         const size_t units = (size_t)batch * n_kv_heads;
+        const size_t slots = n_chunks <= kStepMaxChunks ? (size_t)n_chunks : 1;
         w.qdig = align256(off);
-        off = w.qdig + units * (size_t)qd_stride(k_bits, head_dim, n_q_heads / n_kv_heads) * 4;
+        off = w.qdig + units * slots * (size_t)qd_stride(k_bits, head_dim, n_q_heads / n_kv_heads) * 4;
         w.qsc = align256(off);
         off = w.qsc + P * sizeof(float);
         w.qflag = align256(off);
         off = w.qflag + units * sizeof(int32_t);
-        w.cnt = align256(off);                       // the fused step's ticket counters
-        off = w.cnt + units * sizeof(int);
+        // the step's ticket counters: the last round_up(4 units, 256) bytes
+        // (cnt_offset places them by the caller's workspace_bytes)
+        w.cnt = align256(off);
+        off = w.cnt + align256(units * sizeof(int));
     }
     w.total = off;
     return w;
+}
+
+// Offset of the ticket counters in a workspace of `bytes` bytes: the last
+// round_up(4 units, 256) bytes, aligned down to 256.  It depends only on the
+// extent the caller hands over and on the number of (sequence, KV head)
+// pairs, so calls of other geometries sharing that workspace (and passing the
+// same extent) never write over them: their own data ends before.
+size_t cnt_offset(size_t bytes, size_t units)
+{
+    return (bytes - align256(units * sizeof(int))) & ~(size_t)255;
 }
 
 size_t ws_bytes(int batch, int n_q_heads, int head_dim, int n_chunks)
@@ -551,11 +576,10 @@ size_t kvq_workspace_bytes(const kvq_cache *c, int n_q_heads, int max_seq_len, i
 // check runs before anything is enqueued.
 enum { PHASE_PREP = 1, PHASE_SPLIT = 2, PHASE_STEP = 4 };
 
-// kvq_decode_step merges inside the split kernel up to this many chunks
-constexpr int FUSED_MERGE_MAX_CHUNKS = 4;
-
-// out != nullptr (integer caches, both phases): the split kernel's last
-// workgroup per (sequence, KV head) also merges the partials into out
+// PHASE_STEP (integer caches, at most kStepMaxChunks chunks): the one-launch
+// decode step, writing out.  out with both other phases (integer caches, at
+// most kFusedMaxChunks chunks): the split kernel's last workgroup per
+// (sequence, KV head) also merges the partials into out.
 static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, const int32_t *seq_len,
                             int max_seq_len, float softmax_scale, int chunk_tokens, void *workspace,
                             size_t workspace_bytes, void *stream, const AppendParams *ap, dim3 ap_grid,
@@ -567,8 +591,9 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
     if ((st = check_pointers(c))) return st;
     if (phases != (PHASE_PREP | PHASE_SPLIT) && !quant_modes(c))
         return fail(KVQ_ERR_BITS, "only 8/4-bit caches have a separate query preparation");
-    if ((phases & PHASE_STEP) && (nc != 1 || !out || !ap))
-        return fail(KVQ_ERR_ARG, "a one-launch step needs one chunk, the output and the step's rows");
+    if ((phases & PHASE_STEP) && (nc > kStepMaxChunks || !out || !ap))
+        return fail(KVQ_ERR_ARG, "a one-launch step needs at most %d chunks, the output and the step's rows",
+                    kStepMaxChunks);
     const bool uses_q = (phases & (PHASE_PREP | PHASE_STEP)) != 0;
     const bool uses_len = (phases & (PHASE_SPLIT | PHASE_STEP)) != 0;
     if ((uses_q && !q) || (uses_len && !seq_len) || !workspace)
@@ -628,8 +653,13 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
     int32_t *qflag = reinterpret_cast<int32_t *>(ws + wl.qflag);
     const bool one_launch = (phases & PHASE_STEP) != 0;
     if (out && !one_launch && phases != (PHASE_PREP | PHASE_SPLIT))
-        return fail(KVQ_ERR_ARG, "a fused combine needs both phases");
-    int *cnt = out && !one_launch ? reinterpret_cast<int *>(ws + wl.cnt) : nullptr;
+        return fail(KVQ_ERR_ARG, "a merge inside the split kernel needs both phases");
+    // the split kernel's last workgroups merge through the ticket counters:
+    // in the one-launch step with several chunks, and in the two-launch one
+    // (whose query preparation also zeroes them)
+    int *cnt = (one_launch && nc > 1) || (out && !one_launch)
+                   ? reinterpret_cast<int *>(ws + cnt_offset(workspace_bytes, (size_t)c->batch * c->n_kv_heads))
+                   : nullptr;
     const unsigned units = (unsigned)(c->batch * c->n_kv_heads);
     if (ap && ap_grid.x > 0 && (unsigned long long)ap_grid.x * ap_grid.y * 2 + units > 0x7FFFFFFFull)
         return fail(KVQ_ERR_SHAPE, "batch * n_new too large for a fused step");
@@ -773,17 +803,19 @@ int kvq_decode_step(const kvq_cache *c, const float *k_new, const float *v_new, 
     AppendParams ap;
     dim3 ag;
     if ((st = prepare_append(c, k_new, v_new, n_new, start_pos, &ap, &ag))) return st;
-    // One chunk per (sequence, KV head): one launch, each workgroup storing
-    // its head's rows, preparing its query and writing out.  Few chunks: two
-    // launches, the split kernel's last workgroup of each (sequence, KV head)
-    // merging the partials (a short split kernel, where a third launch costs
-    // more than that merge).  More chunks: the merge as a launch of its own
-    // (the in-kernel merge adds a store wait to every workgroup and a serial
-    // merge at the end).
-    if (quant_modes(c) && nc == 1)
+    // One or two chunks per (sequence, KV head) on an integer cache: one
+    // launch, each workgroup storing the step's rows of its chunk, preparing
+    // its query and, with one chunk, writing out; with two the last
+    // workgroup of each (sequence, KV head) merges the partials and sets its
+    // ticket counter back to zero.  Three or four: the append with the query
+    // preparation, then the split kernel merging in its last workgroups (each
+    // workgroup preparing its own query costs more there than the launch).
+    // More chunks: the merge as a launch of its own (the in-kernel merge adds
+    // a store wait to every workgroup and a serial merge at the end).
+    if (quant_modes(c) && nc <= kStepMaxChunks)
         return enqueue_partials(c, q, n_q_heads, seq_len, max_seq_len, softmax_scale, ch, workspace, workspace_bytes,
                                 stream, &ap, ag, PHASE_STEP, out);
-    if (quant_modes(c) && nc <= FUSED_MERGE_MAX_CHUNKS)
+    if (quant_modes(c) && nc <= kFusedMaxChunks)
         return enqueue_partials(c, q, n_q_heads, seq_len, max_seq_len, softmax_scale, ch, workspace, workspace_bytes,
                                 stream, &ap, ag, PHASE_PREP | PHASE_SPLIT, out);
     st = enqueue_partials(c, q, n_q_heads, seq_len, max_seq_len, softmax_scale, ch, workspace, workspace_bytes, stream,

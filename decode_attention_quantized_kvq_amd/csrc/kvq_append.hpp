@@ -384,15 +384,16 @@ __device__ __forceinline__ void append_block(const AppendParams &p, int bx, int 
     }
 }
 
-// The call's rows of sequence b for KV head kvh, both sides of an 8/4-bit
-// cache, stored by the one workgroup that then attends over (b, kvh): wave 0
-// the keys, wave 1 the values, lane l the values 8l .. 8l+7 of the row
-// (waves 2 and 3 store nothing).  The encoding, slots and layout are
-// append_block's, value for value; with one scale per position over all
-// heads each of the n_kv_heads workgroups of sequence b computes that scale
-// from the whole row and stores the same bits.
+// The call's rows of sequence b for KV head kvh whose slots lie in
+// [lo, hi), both sides of an 8/4-bit cache, stored by the workgroup that then
+// attends over those slots of (b, kvh): wave 0 the keys, wave 1 the values,
+// lane l the values 8l .. 8l+7 of the row (waves 2 and 3 store nothing).
+// The encoding, slots and layout are append_block's, value for value; with
+// one scale per position over all heads each of the n_kv_heads workgroups
+// that store a row of sequence b computes that scale from the whole row and
+// stores the same bits.
 template <int HD>
-__device__ __forceinline__ void append_head_rows(const AppendParams &p, int b, int kvh)
+__device__ __forceinline__ void append_head_rows(const AppendParams &p, int b, int kvh, int lo, int hi)
 {
     constexpr int LPH = HD / APPEND_ELEMS;             // lanes holding the head's row
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -407,7 +408,7 @@ __device__ __forceinline__ void append_head_rows(const AppendParams &p, int b, i
     const int c0 = act ? lane * APPEND_ELEMS : 0;
     for (int i = 0; i < p.n_new; i++) {
         const int lslot = append_slot(p, start, start + i);
-        if (lslot < 0) continue;                       // wave-uniform
+        if (lslot < 0 || lslot < lo || lslot >= hi) continue;   // wave-uniform
         int ub = b, slot = lslot;
         if (p.page_shift > 0) {
             ub = p.block_table[(size_t)b * p.pages_per_seq + (lslot >> p.page_shift)];

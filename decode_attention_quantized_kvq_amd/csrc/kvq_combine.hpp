@@ -82,9 +82,11 @@ constexpr int WAIT_VMEM_ALL = 0x0F70;
 // for its own stores, then one ticket per workgroup on the counter of its
 // (sequence, KV head); the workgroup that draws the last ticket merges the G
 // rows row0 .. row0 + G - 1 into out, reading the partials with device-scope
-// loads.  Each counter is zeroed before the launch (by the query preparation
-// that precedes it), so every launch starts from zero; no workgroup waits
-// for another.  flag: one int of LDS.
+// loads, and sets the counter back to zero: every other workgroup of the
+// (sequence, KV head) has taken its ticket by then, so the counter is zero
+// for the next launch (the first launch on a workspace needs it zero: the
+// workspace is handed over zero-filled).  No workgroup waits for another.
+// flag: one int of LDS.
 // Memory ordering: there is no release/acquire pair (a __threadfence()
 // before the ticket made the fused step several times slower).  The merge
 // relies on this gfx9-family behaviour: a device-scope store has reached
@@ -108,6 +110,7 @@ __device__ __forceinline__ void combine_if_last(const float *ml, const float *ac
         const int h = i / HD, c = i - h * HD;
         out[(row0 + h) * HD + c] = combine_one<HD>(ml, acc, n_chunks, row0 + h, c, AgentLoad{});
     }
+    if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 } // namespace kvq

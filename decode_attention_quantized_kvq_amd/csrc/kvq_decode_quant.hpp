@@ -139,10 +139,13 @@ struct QuantParams {
     // its (sequence, KV head) into out.  cnt == nullptr: partials only.
     int *cnt;
     float *out;
-    // one-launch decode step (step != 0; one chunk per (sequence, KV head)):
-    // each workgroup first stores the step's rows of its head (ap) and
-    // prepares its query (q, qk_scale: digits into its own slot of qdig,
-    // scales and flag kept in registers), and writes out instead of partials
+    // one-launch decode step (step != 0; at most 4 chunks per (sequence, KV
+    // head)): each workgroup first stores the step's rows of its head whose
+    // slots fall in its chunk (the last chunk also takes those past it) (ap)
+    // and prepares its query (q, qk_scale: digits into its own slot of
+    // qdig, one per (sequence, KV head) and chunk; scales and flag kept in
+    // registers); with one chunk it writes out instead of partials, with
+    // more the last workgroup of the (sequence, KV head) merges (cnt)
     int step;
     AppendParams ap;
     const float *q;
@@ -397,6 +400,10 @@ void decode_quant_kernel(QuantParams p)
     const size_t ml_hs = (size_t)p.n_chunks * 2;
     const size_t acc_hs = (size_t)p.n_chunks * HD;
 
+    // the query digits' slot: per (sequence, KV head), or per chunk too in
+    // the one-launch step (each workgroup prepares its own)
+    const size_t qslot = p.step ? (size_t)bh * p.n_chunks + chunk_id : (size_t)bh;
+
     // Query scales (log2 units; floored so that a zero query keeps -inf
     // scores at -inf: 0 * -inf would be NaN) and the extra-digit flag.
     float qs[G];
@@ -405,11 +412,11 @@ void decode_quant_kernel(QuantParams p)
         // (block-uniform) this is the only workgroup of its (sequence, KV
         // head): the step's rows of its head, then its query's digits; every
         // store is complete before a wave reads the cache or the digits
-        append_head_rows<HD>(p.ap, b, kvh);
+        append_head_rows<HD>(p.ap, b, kvh, t0, chunk_id == p.n_chunks - 1 ? 0x7FFFFFFF : t0 + CH);
         float *s_qv = reinterpret_cast<float *>(smem);
         float *s_amax = s_qv + G * HD;
         int *s_xflag = reinterpret_cast<int *>(s_amax + G);
-        qprep_core<KB, HD, G>(p.q + row0 * HD, const_cast<int32_t *>(p.qdig) + (size_t)bh * qd_stride(KB, HD, G),
+        qprep_core<KB, HD, G>(p.q + row0 * HD, const_cast<int32_t *>(p.qdig) + qslot * qd_stride(KB, HD, G),
                               s_amax, s_xflag, s_qv, ZP ? KG : 0);
         __builtin_amdgcn_s_waitcnt(WAIT_VMEM_ALL);
         __syncthreads();
@@ -433,7 +440,7 @@ void decode_quant_kernel(QuantParams p)
     };
 
     if (n_tok <= 0) {
-        if (p.step) {                                // nothing attended: out = 0
+        if (p.step && p.n_chunks == 1) {             // nothing attended: out = 0
             for (int i = tid; i < G * HD; i += QD_THREADS) p.out[row0 * HD + i] = 0.0f;
             return;
         }
@@ -534,7 +541,7 @@ void decode_quant_kernel(QuantParams p)
         if constexpr (PAGED) return (w0 + tw) & ((1 << p.page_shift) - 1);
         else return w0 + tw;
     };
-    const KVQ_CONST int32_t *qd = (const KVQ_CONST int32_t *)(p.qdig + (size_t)bh * qd_stride(KB, HD, G));
+    const KVQ_CONST int32_t *qd = (const KVQ_CONST int32_t *)(p.qdig + qslot * qd_stride(KB, HD, G));
     constexpr float XINV = 1.0f / (float)qx_base(KB);
     const uint32_t ko = lane * 16;
     const uint32_t kso = lane * p.k_sc_t * SCB, vso = lane * p.v_sc_t * SCB;
@@ -1097,7 +1104,7 @@ void decode_quant_kernel(QuantParams p)
             const float mv = pm[w * G + h];
             if (mv != -INFINITY) s = fmaf(__builtin_amdgcn_exp2f(mv - m), red[(w * G + h) * HD + c], s);
         }
-        if (p.step) {
+        if (p.step && p.n_chunks == 1) {
             // the only chunk: out = acc / l (the merge of one chunk, whose
             // factor 2^(m - m) is 1)
             float l = 0.0f;
@@ -1111,7 +1118,7 @@ void decode_quant_kernel(QuantParams p)
             store_partial(&acc0[h * acc_hs + c], s);
         }
     }
-    if (p.step) return;
+    if (p.step && p.n_chunks == 1) return;
     if (tid < G) {
         float m = pm[tid];
 #pragma unroll

@@ -226,18 +226,27 @@ int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n
  *                with 8/4-bit keys, scratch for the query's fixed-point form
  *                and one int32 ticket counter per (sequence, KV head) for
  *                kvq_decode_step follow.  An empty chunk has m = -inf, l = 0,
- *                acc = 0.
+ *                acc = 0.  kvq_decode_step's ticket counters (8/4-bit
+ *                caches): one int32 per (sequence, KV head) in the last
+ *                round_up(4 * batch * n_kv_heads, 256) bytes of the
+ *                workspace_bytes given (their start aligned down to 256
+ *                bytes); a step needs them zero when it starts and leaves
+ *                them zero.  Hand a workspace over zero-filled before its
+ *                first kvq_decode_step; calls that share it pass the same
+ *                workspace_bytes (then no other call writes over the
+ *                counters, whatever its geometry); a call with another
+ *                batch * n_kv_heads on it needs them zeroed again.
  * Results are deterministic: the chunk partition and the merge order are
  * fixed (kvq_decode_step's in-kernel merge takes an atomic ticket only to
  * decide which workgroup merges, not in what order).
  *
- * kvq_chunk_tokens() returns the library's chunk: for 8/4-bit caches, one
- * chunk per (sequence, KV head) (512 or 1024 slots) when the context is at
- * most 1024 slots and 512-slot chunks would give at most 1024 workgroups,
- * else the largest power of two <= 2048 slots that still gives >= 1024
- * workgroups (sequences x KV heads x chunks), at least 512; for 16/32-bit
- * caches at most 1024, >= 2048 workgroups, at least 64 slots and within the
- * LDS budget.
+ * kvq_chunk_tokens() returns the library's chunk: for 8/4-bit caches the
+ * largest power of two <= 2048 slots that still gives >= 1024 workgroups
+ * (sequences x KV heads x chunks), at least 512, except that a context of at
+ * most 2048 slots which that would split in more than two chunks takes 512
+ * (<= 1024 slots) or 1024 (so that its decode step is one launch); for
+ * 16/32-bit caches at most 1024, >= 2048 workgroups, at least 64 slots and
+ * within the LDS budget.
  *
  * kvq_chunk_count() returns C, the chunks per (sequence, KV head) for these
  * arguments: ceil(L / chunk) for L = min(max_seq_len, capacity) and the
@@ -292,16 +301,19 @@ int kvq_decode_attn(const kvq_cache *c, const float *q, int n_q_heads, const int
  * exactly kvq_append(c, k_new, v_new, n_new, start_pos, stream) followed by
  * kvq_decode_attn(c, q, ..., stream), with the same arguments, rules and
  * results, bit for bit.  On an 8/4-bit cache whose max_seq_len (capped at
- * the capacity) fits one chunk: one launch, each workgroup storing the
- * step's rows of its (sequence, KV head), preparing its query and writing
- * out.  With more chunks the append and the query's fixed-point preparation
- * share the first launch, then the split kernel, then the combine; when
- * max_seq_len spans at most 4 chunks, the split kernel's last workgroup per
- * (sequence, KV head) merges the partials itself (same arithmetic, one
- * launch fewer for short contexts, where the launches dominate).  On a
- * 16/32-bit cache: append, split, combine.  The workspace holds the merge's
- * ticket counters, which the first launch zeroes each step (no memset, so
- * the step can be captured in a graph).
+ * the capacity) spans one or two chunks: one launch, each workgroup storing
+ * the step's rows whose slots fall in its chunk (the last chunk also those
+ * past it), preparing its query and, with one chunk, writing out; with two,
+ * the last workgroup of each (sequence, KV head) to finish merges the
+ * partials (the combine's arithmetic) and sets the workspace's ticket
+ * counter of that (sequence, KV head) back to zero.  The counters must
+ * therefore be zero when a step starts: a workspace is handed over
+ * zero-filled before its first kvq_decode_step, and every step leaves them
+ * zero (no memset, so the step can be captured in a graph and replayed).
+ * With more chunks the append and the query's fixed-point preparation share
+ * the first launch, then the split kernel, then (beyond 4 chunks) the
+ * combine; up to 4 chunks the split kernel's last workgroups merge.  On a
+ * 16/32-bit cache: append, split, combine.
  * Every argument is checked before anything is enqueued; on an error
  * nothing is.
  */
@@ -325,8 +337,8 @@ int kvq_decode_step(const kvq_cache *c, const float *k_new, const float *v_new, 
  * on one device shares that device's array, and each call leaves its
  * contents there: two calls that may run at the same time on one device
  * (different streams, or host threads) race on it and must be ordered by
- * the caller.  Nothing in it must be cleared between calls (each step
- * writes everything it reads, its ticket counters included).
+ * the caller.  Nothing in it must be cleared (the array starts zero-filled
+ * and each step leaves its ticket counters zero).
  */
 #define KVQ_STATIC_SCRATCH_BYTES (32u << 20)
 

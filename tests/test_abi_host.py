@@ -319,9 +319,9 @@ def test_workspace_and_chunks(kvq):
     assert kvq.kvq_chunk_tokens(small_f, 4, 257) == 64
     # integer caches: the chunk is not bounded by LDS; the largest that gives
     # >= 1024 workgroups: 2048 at 32K for 256, 128 and 64 units, 1024 at 8K for
-    # 128 units, 512 for a 1600-slot window over 256 units; contexts of at most
-    # 1024 slots that one round of 512-slot chunks covers: one chunk (the
-    # one-launch decode step)
+    # 128 units; contexts of at most 2048 slots that this would split in more
+    # than two chunks take two at most (the one-launch decode step): 1024 for
+    # a 1600-slot window over 256 units, 512 for 1K contexts
     assert kvq.kvq_chunk_tokens(d, 32, 32768) == 2048
     d8 = _desc(kvq, batch=16, n_kv_heads=8, capacity=32768, k_bits=8, v_bits=4)
     assert kvq.kvq_chunk_tokens(d8, 32, 32768) == 2048
@@ -330,13 +330,17 @@ def test_workspace_and_chunks(kvq):
     d8k = _desc(kvq, batch=16, n_kv_heads=8, capacity=8192, k_bits=8, v_bits=4)
     assert kvq.kvq_chunk_tokens(d8k, 32, 8192) == 1024
     win = _desc(kvq, batch=32, n_kv_heads=8, capacity=1600, k_bits=4, v_bits=4, n_anchor=64, window=1536)
-    assert kvq.kvq_chunk_tokens(win, 32, 32768) == 512
+    assert kvq.kvq_chunk_tokens(win, 32, 32768) == 1024
+    assert kvq.kvq_chunk_count(win, 32, 32768) == 2
     tl = _desc(kvq, batch=8, n_kv_heads=16, capacity=1024)
-    assert kvq.kvq_chunk_tokens(tl, 16, 1024) == 1024
-    assert kvq.kvq_chunk_tokens(tl, 16, 600) == 1024
+    assert kvq.kvq_chunk_tokens(tl, 16, 1024) == 512
+    assert kvq.kvq_chunk_count(tl, 16, 1024) == 2
+    assert kvq.kvq_chunk_tokens(tl, 16, 600) == 512
     assert kvq.kvq_chunk_tokens(tl, 16, 512) == 512
     mid = _desc(kvq, batch=75, n_kv_heads=8, capacity=1024)     # 1200 workgroups of 512 slots fill the chip
     assert kvq.kvq_chunk_tokens(mid, 8, 1024) == 512
+    big = _desc(kvq, batch=256, n_kv_heads=8, capacity=2048)    # 2048 workgroups of 2048 slots
+    assert kvq.kvq_chunk_tokens(big, 8, 2048) == 2048
     # 32-value scale groups at G = 4 (57 KB of LDS): the same choice
     g32 = _desc(kvq, batch=32, n_kv_heads=8, capacity=32768, k_bits=4, v_bits=4, group_size=32)
     assert kvq.kvq_chunk_tokens(g32, 32, 32768) == 2048

@@ -101,7 +101,8 @@ def _run(oq, kb, vb, group, K, V, q, sigma, n_anchor=0, window=0, chunk=0, fused
     kn, vn, qd = to_device(K[:, :, n0:]), to_device(V[:, :, n0:]), to_device(q)
     pos, lens = positions([n0] * B), positions([n_pos] * B)
     ws_bytes = kvq.kvq_workspace_bytes(cache, Hq, n_pos, chunk)
-    ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")
+    # (kvq_decode_step takes a zero-filled workspace)
+    ws = (torch.zeros if fused else torch.empty)(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")
     out = torch.full((B, Hq, HD), 5.0, dtype=torch.float32, device="cuda")
     if fused:
         kvq.kvq_decode_step(cache, kn, vn, 1, pos, qd, Hq, lens, n_pos, sigma, chunk, out, ws, ws_bytes)

@@ -183,6 +183,7 @@ def test_paged_decode_step(oq, kb, vb, group, n_new):
     ws_bytes = kvq.kvq_workspace_bytes(contig, H * G, n, 0)
     outs = [torch.full((B, H * G, HD), 7.0, dtype=torch.float32, device="cuda") for _ in range(3)]
     wss = [torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda") for _ in range(3)]
+    wss[0].zero_()                                   # kvq_decode_step takes a zero-filled workspace
     kvq.kvq_decode_step(ps[0], kn, vn, n_new, pos, qd, H * G, lens, n, 0.0, 0, outs[0], wss[0], ws_bytes)
     for i in (1, 2):
         kvq.kvq_append(caches[i], kn, vn, n_new, pos)

@@ -362,6 +362,7 @@ def test_decode_step_matches_separate_calls(oq, kb, vb, group, n_new):
     ws_bytes = kvq.kvq_workspace_bytes(caches[0], H * G, n, 0)
     outs = [torch.full((B, H * G, HD), 7.0, dtype=torch.float32, device="cuda") for _ in range(2)]
     wss = [torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda") for _ in range(2)]
+    wss[0].zero_()                                   # kvq_decode_step takes a zero-filled workspace
     kvq.kvq_decode_step(caches[0], kn, vn, n_new, pos, qd, H * G, lens, n, 0.0, 0, outs[0], wss[0], ws_bytes)
     kvq.kvq_append(caches[1], kn, vn, n_new, pos)
     kvq.kvq_decode_attn(caches[1], qd, H * G, lens, n, 0.0, 0, outs[1], wss[1], ws_bytes)
@@ -397,7 +398,8 @@ def test_decode_step_merge_rule(oq, kb, vb, n):
     pos, lens = positions([n0] * B), positions([n, n - 300])
     ws_bytes = kvq.kvq_workspace_bytes(caches[0], H * G, n, ch)
     outs = [torch.full((B, H * G, HD), 7.0, dtype=torch.float32, device="cuda") for _ in range(2)]
-    wss = [torch.full((ws_bytes // 4 + 64,), 3.0, dtype=torch.float32, device="cuda") for _ in range(2)]
+    # the step's workspace zero-filled (its ticket counters), the separate calls' any
+    wss = [torch.full((ws_bytes // 4 + 64,), v, dtype=torch.float32, device="cuda") for v in (0.0, 3.0)]
     for _ in range(2):                                  # the second step reuses the workspace's counters
         kvq.kvq_decode_step(caches[0], kn, vn, 1, pos, qd, H * G, lens, n, 0.0, ch, outs[0], wss[0], ws_bytes)
     kvq.kvq_append(caches[1], kn, vn, 1, pos)
@@ -425,7 +427,7 @@ def test_graph_replay_matches_eager(oq, fused):
     k1, v1, qd = to_device(K[:, :, n - 1:]), to_device(V[:, :, n - 1:]), to_device(q)
     pos, lens = positions([n - 1] * B), positions([n] * B)
     ws_bytes = kvq.kvq_workspace_bytes(cache, H * G, n, 0)
-    ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")   # zero-filled for kvq_decode_step
     out = torch.zeros((B, H * G, HD), dtype=torch.float32, device="cuda")
 
     def step(st):
@@ -448,7 +450,9 @@ def test_graph_replay_matches_eager(oq, fused):
         step(cs)
     for r in range(3):
         out.zero_()
-        ws.fill_(float(r + 1))                       # eager work between replays
+        # eager work between replays (the step's workspace comes back
+        # zero-filled, as kvq_decode_step takes it; the separate calls' any)
+        ws.fill_(0.0 if fused else float(r + 1))
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
@@ -475,7 +479,7 @@ def test_layers_of_mixed_widths_in_one_graph(oq):
         layers.append((cache, to_device(K[:, :, n - 1:]), to_device(V[:, :, n - 1:]), to_device(q), out, K, V, q))
     pos, lens = positions([n - 1] * B), positions([n] * B)
     ws_bytes = max(kvq.kvq_workspace_bytes(c, H * G, n, 0) for c, *_ in layers)
-    ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")   # zero-filled for kvq_decode_step
 
     def step(st):
         for cache, k1, v1, qd, out, *_ in layers:
@@ -500,7 +504,7 @@ def test_layers_of_mixed_widths_in_one_graph(oq):
     for r in range(3):
         for l in layers:
             l[4].zero_()
-        ws.fill_(float(r + 1))                       # eager work between replays
+        ws.zero_()                                   # eager work between replays (the step takes it zero-filled)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()

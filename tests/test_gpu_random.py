@@ -85,7 +85,8 @@ def test_random_configuration(oq, seed):
         lens[-1] = int(rng.integers(0, n_pos + 1))   # a sequence attending a prefix (or nothing)
     max_len = max(max(lens), 1)
     ws_bytes = kvq.kvq_workspace_bytes(cache, Hq, max_len, c["chunk"])
-    ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")
+    # (kvq_decode_step takes a zero-filled workspace)
+    ws = (torch.zeros if c["fused"] else torch.empty)(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")
     out = torch.full((B, Hq, HD), 5.0, dtype=torch.float32, device="cuda")
     kn, vn, qd = to_device(K[:, :, n0:]), to_device(V[:, :, n0:]), to_device(q)
     pos, sl = positions([n0] * B), positions(lens)

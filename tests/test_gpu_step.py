@@ -1,9 +1,12 @@
-"""The one-launch decode step: when a step's context fits one chunk per
+"""The short decode step: when a step's context spans at most 2 chunks per
 (sequence, KV head) on an 8/4-bit cache, kvq_decode_step runs as a single
-kernel whose workgroups store their head's new rows, prepare their query and
-write the output.  It must leave the cache and the output bit for bit as
+kernel whose workgroups store the new rows of their chunk, prepare their
+query and write the output (one chunk) or partials that the last workgroup
+of the (sequence, KV head) merges, setting its ticket counter back to zero;
+at 3 or 4 chunks as two launches, the split kernel merging in its last
+workgroups.  Either must leave the cache and the output bit for bit as
 kvq_append followed by kvq_decode_attn with the same chunk does (a split
-launch of one chunk and the combine), and match the oracle."""
+launch and the combine), and match the oracle."""
 import numpy as np
 import pytest
 
@@ -23,7 +26,7 @@ def _data(B, H, n, HD, Hq, seed):
 
 
 def _pair(oq, kb, vb, gs, B, H, G, HD, n, n_new, chunk, seed, n_anchor=0, window=0, lens=None, page=0,
-          scale=0.0):
+          scale=0.0, reps=1):
     """One step through kvq_decode_step on one cache and through kvq_append +
     kvq_decode_attn on another; the two must agree bit for bit."""
     kvq = need_gpu()
@@ -50,12 +53,13 @@ def _pair(oq, kb, vb, gs, B, H, G, HD, n, n_new, chunk, seed, n_anchor=0, window
     pos, sl = positions([n0] * B), positions(lens)
     max_len = max(max(lens), 1)
     ws_bytes = kvq.kvq_workspace_bytes(caches[0], Hq, max_len, chunk)
-    L = min(max_len, cap)
-    ch = chunk or kvq.kvq_chunk_tokens(caches[0], Hq, max_len)
-    assert L <= ch                                   # one chunk: the one-launch path
+    assert kvq.kvq_chunk_count(caches[0], Hq, max_len, chunk) <= 4     # the one-launch path
     outs = [torch.full((B, Hq, HD), 7.0, dtype=torch.float32, device="cuda") for _ in range(2)]
-    wss = [torch.full((ws_bytes // 4 + 64,), 3.0, dtype=torch.float32, device="cuda") for _ in range(2)]
-    kvq.kvq_decode_step(caches[0], kn, vn, n_new, pos, qd, Hq, sl, max_len, scale, chunk, outs[0], wss[0], ws_bytes)
+    # the step's workspace zero-filled (its ticket counters), the separate calls' any
+    wss = [torch.full((ws_bytes // 4 + 64,), v, dtype=torch.float32, device="cuda") for v in (0.0, 3.0)]
+    for _ in range(reps):                            # later steps find the counters back at zero
+        kvq.kvq_decode_step(caches[0], kn, vn, n_new, pos, qd, Hq, sl, max_len, scale, chunk, outs[0], wss[0],
+                            ws_bytes)
     kvq.kvq_append(caches[1], kn, vn, n_new, pos)
     kvq.kvq_decode_attn(caches[1], qd, Hq, sl, max_len, scale, chunk, outs[1], wss[1], ws_bytes)
     torch.cuda.synchronize()
@@ -158,3 +162,83 @@ def test_one_launch_step_graph(oq):
     for b in range(B):
         ref = oq.decode_step(4, 4, HD, 0, 0, K[b], V[b], q[b], softmax_default(HD))
         assert_close(got[b], ref, f"graph one-launch b={b}")
+
+
+@pytest.mark.parametrize("kb,vb", PAIRS)
+@pytest.mark.parametrize("n,n_new,chunk", [(700, 1, 512), (1024, 3, 512), (513, 1, 512), (600, 0, 512),
+                                           (700, 1, 256), (1024, 3, 256)])
+def test_one_launch_step_chunks(oq, kb, vb, n, n_new, chunk):
+    """Two chunks per (sequence, KV head) in one launch (512-slot chunks):
+    the new rows are stored by the workgroup of their chunk, the last
+    workgroup merges; three or four (256-slot chunks) in two launches.
+    Three steps in a row on one workspace (the counters come back to zero)."""
+    _pair(oq, kb, vb, 128, B=2, H=2, G=4, HD=128, n=n, n_new=n_new, chunk=chunk, seed=kb + vb + n + n_new,
+          reps=3)
+
+
+@pytest.mark.parametrize("kb,vb", [(8, 4), (4, 4)])
+def test_one_launch_step_chunks_window(oq, kb, vb):
+    """Anchors + ring (64 + 512 slots: two 512-slot chunks, one launch, or
+    three 256-slot ones); the step's rows land in the ring wherever the wrap
+    puts them."""
+    for n, seed, ch in ((1500, 51, 512), (1777, 52, 512), (1777, 53, 256)):
+        _pair(oq, kb, vb, 128, B=2, H=2, G=4, HD=128, n=n, n_new=3, chunk=ch, seed=seed + kb, n_anchor=64,
+              window=512, reps=2)
+
+
+def test_one_launch_step_chunks_ragged_paged(oq):
+    """Sequences attending nothing, a prefix, or all of four chunks (the rows
+    are stored all the same); paged storage; group and per-position scales;
+    an explicit softmax scale."""
+    _pair(oq, 8, 4, 128, B=3, H=2, G=4, HD=128, n=1000, n_new=1, chunk=512, seed=61, lens=[1000, 0, 300])
+    _pair(oq, 8, 4, 128, B=3, H=2, G=4, HD=128, n=1000, n_new=1, chunk=256, seed=65, lens=[1000, 0, 300])
+    _pair(oq, 4, 4, 128, B=3, H=2, G=4, HD=128, n=1000, n_new=1, chunk=512, seed=62, page=128, reps=2)
+    _pair(oq, 4, 8, 32, B=2, H=2, G=4, HD=128, n=900, n_new=2, chunk=512, seed=63, scale=0.5)
+    _pair(oq, 8, 8, 2 * 64, B=2, H=2, G=1, HD=64, n=800, n_new=1, chunk=512, seed=64)
+
+
+def test_one_launch_step_chunks_graph(oq):
+    """Two chunks per (sequence, KV head), one launch, captured in a HIP
+    graph: every replay gives the eager output bit for bit (the merge's
+    ticket counters are back at zero after each), with eager work on other
+    memory between replays."""
+    kvq = need_gpu()
+    import torch
+    from workloads.device import positions, to_device
+    B, H, G, HD, n, ch = 2, 2, 4, 128, 700, 512
+    cache = kvq.alloc_cache(B, H, HD, n, 4, 4, HD)
+    K, V, q = _data(B, H, n, HD, H * G, 22)
+    kvq.kvq_append(cache, to_device(K[:, :, : n - 1]), to_device(V[:, :, : n - 1]), n - 1, positions([0, 0]))
+    k1, v1, qd = to_device(K[:, :, n - 1:]), to_device(V[:, :, n - 1:]), to_device(q)
+    pos, lens = positions([n - 1] * B), positions([n] * B)
+    assert kvq.kvq_chunk_count(cache, H * G, n, ch) == 2
+    ws_bytes = kvq.kvq_workspace_bytes(cache, H * G, n, ch)
+    ws = torch.zeros(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")
+    out = torch.zeros((B, H * G, HD), dtype=torch.float32, device="cuda")
+    other = torch.zeros(1 << 20, dtype=torch.float32, device="cuda")
+
+    def step(st):
+        kvq.kvq_decode_step(cache, k1, v1, 1, pos, qd, H * G, lens, n, 0.0, ch, out, ws, ws_bytes, st)
+
+    step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    want = out.clone()
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        step(cs)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cs):
+        step(cs)
+    for r in range(4):
+        out.zero_()
+        other.fill_(float(r + 1))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), f"replay {r}"
+    got = want.cpu().numpy()
+    for b in range(B):
+        ref = oq.decode_step(4, 4, HD, 0, 0, K[b], V[b], q[b], softmax_default(HD))
+        assert_close(got[b], ref, f"graph two-chunk step b={b}")

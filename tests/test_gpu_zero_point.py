@@ -45,7 +45,8 @@ def run_zp(oq, kb, vb, gs, B, H, G, HD, n, seed, n_anchor=0, window=0, chunk=0, 
     pos, sl = positions([n0] * B), positions(lens)
     max_len = max(max(lens), 1)
     ws_bytes = kvq.kvq_workspace_bytes(cache, Hq, max_len, chunk)
-    ws = torch.full((ws_bytes // 4 + 64,), 3.0, dtype=torch.float32, device="cuda")
+    # (kvq_decode_step takes a zero-filled workspace; the separate calls any)
+    ws = torch.full((ws_bytes // 4 + 64,), 0.0 if fused else 3.0, dtype=torch.float32, device="cuda")
     out = torch.full((B, Hq, HD), 5.0, dtype=torch.float32, device="cuda")
     sc = sigma or softmax_default(HD)
     if fused:
@@ -113,7 +114,7 @@ def test_zero_point_decode_step(oq, kb, vb, n):
     pos, sl = positions([n - 1] * B), positions([n, n - 77])
     ws_bytes = kvq.kvq_workspace_bytes(caches[0], H * G, n, 0)
     outs = [torch.full((B, H * G, HD), 7.0, device="cuda") for _ in range(2)]
-    wss = [torch.full((ws_bytes // 4 + 64,), 3.0, device="cuda") for _ in range(2)]
+    wss = [torch.full((ws_bytes // 4 + 64,), v, device="cuda") for v in (0.0, 3.0)]   # the step's zero-filled
     kvq.kvq_decode_step(caches[0], kn, vn, 1, pos, qd, H * G, sl, n, 0.0, 0, outs[0], wss[0], ws_bytes)
     kvq.kvq_append(caches[1], kn, vn, 1, pos)
     kvq.kvq_decode_attn(caches[1], qd, H * G, sl, n, 0.0, 0, outs[1], wss[1], ws_bytes)

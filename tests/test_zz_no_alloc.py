@@ -27,7 +27,7 @@ def _step_pair(oq, kvq, kb, vb, B, H, G, HD, n, seed, chunk=0):
     outs = [torch.full((B, H * G, HD), 7.0, dtype=torch.float32, device="cuda") for _ in range(2)]
     ws_bytes = kvq.kvq_workspace_bytes(caches[0], H * G, n, chunk)
     assert ws_bytes <= kvq.KVQ_STATIC_SCRATCH_BYTES
-    ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(ws_bytes // 4 + 64, dtype=torch.float32, device="cuda")   # zero-filled, as the step takes it
     kvq.kvq_decode_step(caches[0], kn, vn, 1, pos, qd, H * G, lens, n, 0.0, chunk, outs[0], ws, ws_bytes)
     kvq.kvq_decode_step_static(caches[1], kn, vn, 1, pos, qd, H * G, lens, n, 0.0, chunk, outs[1])
     torch.cuda.synchronize()
