@@ -337,8 +337,9 @@ int kvq_decode_step(const kvq_cache *c, const float *k_new, const float *v_new, 
  * on one device shares that device's array, and each call leaves its
  * contents there: two calls that may run at the same time on one device
  * (different streams, or host threads) race on it and must be ordered by
- * the caller.  Nothing in it must be cleared (the array starts zero-filled
- * and each step leaves its ticket counters zero).
+ * the caller.  Nothing in it must be cleared: the array starts zero-filled,
+ * every call passes its whole extent as workspace_bytes (so the ticket
+ * counters sit in its last bytes), and each step leaves them zero.
  */
 #define KVQ_STATIC_SCRATCH_BYTES (32u << 20)
 
