@@ -39,7 +39,8 @@
 // sub-chunk:
 //   1. keys, one lane per position: scores -> LDS; the query digits are
 //      wave-uniform and come from SGPRs (prepared per (sequence, KV head) by
-//      qprep_kernel); value scales -> LDS; the sub-chunk's score maxima (DPP).
+//      qprep_kernel, or by the workgroup itself in the one-launch step);
+//      value scales -> LDS; the sub-chunk's score maxima (DPP).
 //   2. weights, one lane per four positions: p = 2^(z - max) and the
 //      products p * s_v, whose maximum per head and group (DPP) sets the
 //      fixed point; then w_int packed four positions per word -> LDS (over
@@ -120,7 +121,8 @@ struct QuantParams {
     const uint8_t *v_codes;    // [B][Hkv][cap4/4][V_ROW][4]  (4 positions interleaved per byte)
     const uint16_t *k_scales;
     const uint16_t *v_scales;
-    const int32_t *qdig;       // [B*Hkv][qd_stride] packed query digits: [ND + 1][K_COLS][G] (digit-major; digit ND the extra low one)
+    const int32_t *qdig;       // [B*Hkv][qd_stride] packed query digits: [ND + 1][K_COLS][G] (digit-major; digit ND the extra low one);
+                               // the one-launch step: [B*Hkv][n_chunks][qd_stride], one slot per workgroup
     const float *qsc;          // [B*Hq]: s_q * softmax_scale * log2(e)
     const int32_t *qflag;      // [B*Hkv]: 1 when the query carries its extra low digit
     const int32_t *seq_len;
