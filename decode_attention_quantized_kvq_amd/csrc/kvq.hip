@@ -725,7 +725,8 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
         p.k_sc_h = p.v_sc_h = (long long)cap_u(c) * gph;
         p.k_sc_t = p.v_sc_t = gph;
     }
-    hipLaunchKernelGGL(fn, grid, dim3(QD_THREADS), lds, st_, p);
+    hipLaunchKernelGGL(fn, dim3((unsigned)nc, (unsigned)c->n_kv_heads, (unsigned)c->batch), dim3(QD_THREADS), lds,
+                       st_, p);
     return hip_status("decode_quant_kernel launch");
 }
 

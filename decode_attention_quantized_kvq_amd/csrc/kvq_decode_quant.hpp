@@ -167,7 +167,7 @@ struct QuantSmem {
 // Per wave: scores [S][G] fp32, value scales [S][vg] fp16 bits (or 32-bit
 // scale | zero words), weight words [S/4][vg][G][lo, hi] (over the scores
 // when vg == 1); then the cross-wave merge area (over the scores when it
-// fits) and the wave maxima and sums.  With several scale groups and the
+// fits) and the wave maxima, sums and merge factors.  With several scale groups and the
 // symmetric codec the value scales of 4 positions ([4][vg] fp16) occupy the
 // last 2 vg words of those positions' block of weight words, which only the
 // lane that reads them later overwrites; this keeps the G = 4, vg = 4
@@ -198,7 +198,7 @@ __host__ __device__ inline QuantSmem quant_smem(int G, int HD, int vg, bool zp =
         off += red;
     }
     s.misc = off;
-    off += 2 * QD_WAVES * G * 4;                   // wave maxima and sums
+    off += (3 * QD_WAVES + 2) * G * 4;             // wave maxima, sums and merge factors; merged max and sum
     s.total = off;
     return s;
 }
@@ -384,10 +384,10 @@ void decode_quant_kernel(QuantParams p)
     // wave index as a wave-uniform (scalar) value, so that everything derived
     // from it (the wave's range, its buffer descriptors) stays in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int chunk_id = blockIdx.x;
-    const int bh = blockIdx.y;
-    const int b = bh / p.n_kv_heads;
-    const int kvh = bh - b * p.n_kv_heads;
+    const int chunk_id = blockIdx.x;                 // grid: (chunks, KV heads, sequences)
+    const int kvh = blockIdx.y;
+    const int b = blockIdx.z;
+    const int bh = b * p.n_kv_heads + kvh;
     const int Hq = p.n_kv_heads * G;
     const int CH = p.chunk;
 
@@ -1095,32 +1095,9 @@ void decode_quant_kernel(QuantParams p)
         }
     }
     __syncthreads();
-    for (int i = tid; i < G * HD; i += QD_THREADS) {
-        const int h = i / HD, c = i - h * HD;
-        float m = pm[h];
-#pragma unroll
-        for (int w = 1; w < QD_WAVES; w++) m = fmaxf(m, pm[w * G + h]);
-        float s = 0.0f;
-#pragma unroll
-        for (int w = 0; w < QD_WAVES; w++) {
-            const float mv = pm[w * G + h];
-            if (mv != -INFINITY) s = fmaf(__builtin_amdgcn_exp2f(mv - m), red[(w * G + h) * HD + c], s);
-        }
-        if (p.step && p.n_chunks == 1) {
-            // the only chunk: out = acc / l (the merge of one chunk, whose
-            // factor 2^(m - m) is 1)
-            float l = 0.0f;
-#pragma unroll
-            for (int w = 0; w < QD_WAVES; w++) {
-                const float mv = pm[w * G + h];
-                if (mv != -INFINITY) l = fmaf(__builtin_amdgcn_exp2f(mv - m), pl[w * G + h], l);
-            }
-            p.out[(row0 + h) * HD + c] = m != -INFINITY && l > 0.0f ? s / l : 0.0f;
-        } else {
-            store_partial(&acc0[h * acc_hs + c], s);
-        }
-    }
-    if (p.step && p.n_chunks == 1) return;
+    // per head, once: the merged max m, the waves' factors 2^(m_w - m) (0 for
+    // a wave that saw nothing) and the merged sum l
+    float *pf = pl + QD_WAVES * G;                   // [QD_WAVES][G] factors, then [G] m, [G] l
     if (tid < G) {
         float m = pm[tid];
 #pragma unroll
@@ -1129,10 +1106,31 @@ void decode_quant_kernel(QuantParams p)
 #pragma unroll
         for (int w = 0; w < QD_WAVES; w++) {
             const float mv = pm[w * G + tid];
-            if (mv != -INFINITY) l = fmaf(__builtin_amdgcn_exp2f(mv - m), pl[w * G + tid], l);
+            const float f = mv != -INFINITY ? __builtin_amdgcn_exp2f(mv - m) : 0.0f;
+            pf[w * G + tid] = f;
+            l = fmaf(f, pl[w * G + tid], l);
         }
-        store_partial(&ml0[tid * ml_hs], m);
-        store_partial(&ml0[tid * ml_hs + 1], l);
+        pf[QD_WAVES * G + tid] = m;
+        pf[QD_WAVES * G + G + tid] = l;
+    }
+    __syncthreads();
+    const bool write_out = p.step && p.n_chunks == 1;   // the only chunk: out = acc / l
+    for (int i = tid; i < G * HD; i += QD_THREADS) {
+        const int h = i / HD, c = i - h * HD;
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < QD_WAVES; w++) s = fmaf(pf[w * G + h], red[(w * G + h) * HD + c], s);
+        if (write_out) {
+            const float m = pf[QD_WAVES * G + h], l = pf[QD_WAVES * G + G + h];
+            p.out[(row0 + h) * HD + c] = m != -INFINITY && l > 0.0f ? s / l : 0.0f;
+        } else {
+            store_partial(&acc0[h * acc_hs + c], s);
+        }
+    }
+    if (write_out) return;
+    if (tid < G) {
+        store_partial(&ml0[tid * ml_hs], pf[QD_WAVES * G + tid]);
+        store_partial(&ml0[tid * ml_hs + 1], pf[QD_WAVES * G + G + tid]);
     }
     finish();
 }
