@@ -45,7 +45,7 @@ COMMON_FLAGS = [
 DEVICE_FLAGS = ["--cuda-device-only", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 # (key bits, value bits, paged, zero point): the families kvq.hip declares
-FAMILIES = [(kb, vb, pg, zp) for pg, zp in (("false", "false"), ("true", "false"), ("false", "true"))
+FAMILIES = [(kb, vb, pg, zp) for pg, zp in (("false", "false"), ("true", "false"), ("false", "true"), ("true", "true"))
             for kb, vb in ((8, 8), (8, 4), (4, 4), (4, 8))]
 
 

@@ -88,8 +88,6 @@ int check_geometry(const kvq_cache *c)
         return fail(KVQ_ERR_ARG, "zero_point %d must be 0 or 1", c->zero_point);
     if (c->zero_point && !quantized(c->k_bits))
         return fail(KVQ_ERR_BITS, "the zero-point codec needs 8/4-bit sides (k_bits=%d)", c->k_bits);
-    if (c->zero_point && c->page_size != 0)
-        return fail(KVQ_ERR_ARG, "the zero-point codec is not available with paged storage");
     if (c->n_anchor < 0 || c->window < 0)
         return fail(KVQ_ERR_WINDOW, "n_anchor (%d) and window (%d) must be >= 0", c->n_anchor, c->window);
     if (c->window == 0 && c->n_anchor != 0)
@@ -116,8 +114,9 @@ int check_pointers(const kvq_cache *c)
         return fail(KVQ_ERR_ALIGN, "k_codes / v_codes must be 16-byte aligned");
     if (quantized(c->k_bits) && !c->k_scales) return fail(KVQ_ERR_NULL, "k_scales is NULL for a quantized key side");
     if (quantized(c->v_bits) && !c->v_scales) return fail(KVQ_ERR_NULL, "v_scales is NULL for a quantized value side");
-    if ((c->k_scales && !aligned(c->k_scales, 2)) || (c->v_scales && !aligned(c->v_scales, 2)))
-        return fail(KVQ_ERR_ALIGN, "scale buffers must be 2-byte aligned");
+    const int sa = c->zero_point ? 4 : 2;            // fp16 scales, or 32-bit scale | zero point words
+    if ((c->k_scales && !aligned(c->k_scales, sa)) || (c->v_scales && !aligned(c->v_scales, sa)))
+        return fail(KVQ_ERR_ALIGN, "scale buffers must be %d-byte aligned", sa);
     if (c->page_size != 0) {
         if (!c->block_table) return fail(KVQ_ERR_NULL, "block_table is NULL for paged storage");
         if (!aligned(c->block_table, 4)) return fail(KVQ_ERR_ALIGN, "block_table must be 4-byte aligned");
@@ -275,10 +274,9 @@ QuantFn pick_quant_p(int kb, int vb, int hd, int G, int kg)
 
 // kg: scale groups per head row (head_dim / group_size; 1 for one scale per
 // position shared by all heads); pg: paged storage; zp: the zero-point codec
-// (contiguous storage only)
 QuantFn pick_quant(int kb, int vb, int hd, int G, int kg, bool pg, bool zp)
 {
-    if (zp) return pg ? nullptr : pick_quant_p<false, true>(kb, vb, hd, G, kg);
+    if (zp) return pg ? pick_quant_p<true, true>(kb, vb, hd, G, kg) : pick_quant_p<false, true>(kb, vb, hd, G, kg);
     return pg ? pick_quant_p<true, false>(kb, vb, hd, G, kg) : pick_quant_p<false, false>(kb, vb, hd, G, kg);
 }
 

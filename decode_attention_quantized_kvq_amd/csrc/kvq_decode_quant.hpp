@@ -1148,15 +1148,17 @@ void decode_quant_kernel(QuantParams p)
     X(KB, VB, 128, 8, 2, PG, ZP) X(KB, VB, 128, 1, 4, PG, ZP) X(KB, VB, 128, 2, 4, PG, ZP)       \
     X(KB, VB, 128, 4, 4, PG, ZP) X(KB, VB, 128, 8, 4, PG, ZP)
 
-// all families the library dispatches to: four width pairs, contiguous and
-// paged, and the zero-point codec on contiguous storage
+// all families the library dispatches to: four width pairs, each contiguous
+// and paged, with the symmetric and the zero-point codec
 #define KVQ_QUANT_ALL(X)                                                                        \
     KVQ_QUANT_FAMILY(X, 8, 8, false, false) KVQ_QUANT_FAMILY(X, 8, 4, false, false)              \
     KVQ_QUANT_FAMILY(X, 4, 4, false, false) KVQ_QUANT_FAMILY(X, 4, 8, false, false)              \
     KVQ_QUANT_FAMILY(X, 8, 8, true, false) KVQ_QUANT_FAMILY(X, 8, 4, true, false)                \
     KVQ_QUANT_FAMILY(X, 4, 4, true, false) KVQ_QUANT_FAMILY(X, 4, 8, true, false)                \
     KVQ_QUANT_FAMILY(X, 8, 8, false, true) KVQ_QUANT_FAMILY(X, 8, 4, false, true)                \
-    KVQ_QUANT_FAMILY(X, 4, 4, false, true) KVQ_QUANT_FAMILY(X, 4, 8, false, true)
+    KVQ_QUANT_FAMILY(X, 4, 4, false, true) KVQ_QUANT_FAMILY(X, 4, 8, false, true)                \
+    KVQ_QUANT_FAMILY(X, 8, 8, true, true) KVQ_QUANT_FAMILY(X, 8, 4, true, true)                  \
+    KVQ_QUANT_FAMILY(X, 4, 4, true, true) KVQ_QUANT_FAMILY(X, 4, 8, true, true)
 
 #define KVQ_QUANT_DECLARE(KB, VB, HD, G, KG, PG, ZP) \
     extern template __global__ void decode_quant_kernel<KB, VB, HD, G, KG, PG, ZP>(QuantParams);

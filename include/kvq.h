@@ -119,6 +119,19 @@ extern "C" {
  * an entry outside [0, n_pages) is never written (the append skips the row)
  * and its slots read as zero codes.  page_size == 0: contiguous storage,
  * n_pages and block_table ignored.
+ *
+ * Zero-point codec (zero_point = 1; the scale / zero-point metadata of the
+ * mni-ml page, "why INT8 loses no speed"; 8/4-bit pairs only, contiguous or
+ * paged): per group of g values, lo = min(0, min x), hi = max(0, max x),
+ * scale = fp16(RN((hi - lo) / L)) with L = 255 or 15 levels (65504 when it
+ * would overflow), zero = clamp(rint(-lo / scale), 0, L), code =
+ * clamp(rint(x / scale) + zero, 0, L) in [0, L], decoded as
+ * (code - zero) * scale; an all-zero group stores scale 0, zero 0, codes 0.
+ * Codes are stored less 2^(bits-1) in the fields above (keys: the two's
+ * complement of code - 128 or code - 8; values: the offset binary of the
+ * same, which is the code itself).  The scale buffers then hold one 32-bit
+ * word per scale entry, fp16 scale bits in the low half and the zero point
+ * in the high half, 4-byte aligned: twice the symmetric codec's bytes.
  */
 typedef struct kvq_cache {
     int32_t batch;
@@ -137,7 +150,7 @@ typedef struct kvq_cache {
     int32_t page_size;    /* 0 = contiguous */
     int32_t n_pages;
     const int32_t *block_table;
-    int32_t zero_point;   /* 0 = symmetric codes; 1 = zero-point codec (8/4-bit, contiguous) */
+    int32_t zero_point;   /* 0 = symmetric codes; 1 = zero-point codec (8/4-bit sides) */
 } kvq_cache;
 
 /* ---- accounting ------------------------------------------------------ */

@@ -403,8 +403,9 @@ def test_static_step_rejects_oversize(kvq):
 
 
 def test_zero_point_rules(kvq):
-    """The zero-point codec: 8/4-bit contiguous caches only; its scale buffers
-    hold 32-bit words (fp16 scale | zero point), twice the symmetric size."""
+    """The zero-point codec: 8/4-bit caches, contiguous or paged; its scale
+    buffers hold 32-bit words (fp16 scale | zero point), twice the symmetric
+    size, and must be 4-byte aligned."""
     d = _desc(kvq, batch=2, n_kv_heads=2, capacity=100, k_bits=4, v_bits=8, group_size=32)
     sym = kvq.kvq_cache_sizes(d)
     d.zero_point = 1
@@ -419,8 +420,16 @@ def test_zero_point_rules(kvq):
     with pytest.raises(kvq.KvqError) as e:
         kvq.kvq_cache_sizes(f)
     assert e.value.status == kvq.KVQ_ERR_BITS
-    pg = _desc(kvq, capacity=128, k_bits=8, v_bits=8)
-    pg.page_size, pg.n_pages, pg.block_table, pg.zero_point = 64, 4, 0x30000, 1
+    pg = _desc(kvq, capacity=128, k_bits=8, v_bits=4)
+    pg.page_size, pg.n_pages, pg.block_table = 64, 5, 0x30000
+    psym = kvq.kvq_cache_sizes(pg)
+    pg.zero_point = 1
+    pz = kvq.kvq_cache_sizes(pg)
+    assert pz[:2] == psym[:2] and pz[2] == 2 * psym[2] == 5 * 2 * 64 * 4 and pz[3] == 2 * psym[3]
+    ok = 0x30000
+    c = _desc(kvq, k_bits=8, v_bits=8)
+    c.zero_point = 1
+    c.k_codes, c.v_codes, c.k_scales, c.v_scales = ok, ok, ok, ok + 2     # 2-byte aligned scale words
     with pytest.raises(kvq.KvqError) as e:
-        kvq.kvq_cache_sizes(pg)
-    assert e.value.status == kvq.KVQ_ERR_ARG
+        kvq.kvq_append(c, ok, ok, 1, ok, 0)
+    assert e.value.status == kvq.KVQ_ERR_ALIGN and "4-byte aligned" in kvq.kvq_last_error()

@@ -3,7 +3,7 @@ addressed through a block table, holds bit for bit what a contiguous cache
 holds once its pages are gathered in table order, and decodes to the same
 outputs bit for bit (and within tolerance of the oracle), for every kernel
 instantiation, window mode, ragged lengths, appends that cross pages, the
-fused step, and table entries that name no page."""
+fused step, table entries that name no page, and the zero-point codec."""
 import numpy as np
 import pytest
 
@@ -23,11 +23,11 @@ def _data(B, H, n_pos, HD, Hq, seed):
     return K, V, q
 
 
-def _paged(kvq, table, n_pages, B, H, HD, cap, kb, vb, gs, P, n_anchor=0, window=0):
+def _paged(kvq, table, n_pages, B, H, HD, cap, kb, vb, gs, P, n_anchor=0, window=0, zp=0):
     from workloads.device import to_device
     bt = to_device(np.ascontiguousarray(table, np.int32))
     return kvq.alloc_cache(B, H, HD, cap, kb, vb, gs, n_anchor, window, page_size=P, n_pages=n_pages,
-                           block_table=bt)
+                           block_table=bt, zero_point=zp)
 
 
 def _append_pieces(kvq, caches, K, V, pieces):
@@ -44,20 +44,25 @@ def _append_pieces(kvq, caches, K, V, pieces):
 
 
 def run_paged(oq, kb, vb, group, B=3, H=2, G=4, HD=128, P=64, n_pos=700, pieces=(0.3, 0.002, 0.5, 1.0),
-              seq_lens=None, chunk=0, n_anchor=0, window=0, spare=5, seed=0):
+              seq_lens=None, chunk=0, n_anchor=0, window=0, spare=5, seed=0, zp=0):
     kvq = need_gpu()
     import torch
     from workloads.device import decode, positions, to_device
     Hq = H * G
     K, V, q = _data(B, H, n_pos, HD, Hq, seed)
+    if zp:
+        # asymmetric ranges, so that the zero points matter
+        rng = np.random.default_rng(seed + 1)
+        K += np.float32(1.5) * rng.standard_normal((B, H, 1, HD)).astype(np.float32)
+        V += np.float32(-0.8) + np.float32(0.5) * rng.standard_normal((B, H, n_pos, 1)).astype(np.float32)
     cap = n_anchor + window if window else (n_pos + P - 1) // P * P
     assert cap % P == 0
     pps = cap // P
     n_pages = B * pps + spare
     table = paged_table(B, pps, n_pages, seed)
     gs = group_size_of(kb, vb, group, H, HD)
-    contig = kvq.alloc_cache(B, H, HD, cap, kb, vb, gs, n_anchor, window)
-    paged = _paged(kvq, table, n_pages, B, H, HD, cap, kb, vb, gs, P, n_anchor, window)
+    contig = kvq.alloc_cache(B, H, HD, cap, kb, vb, gs, n_anchor, window, zero_point=zp)
+    paged = _paged(kvq, table, n_pages, B, H, HD, cap, kb, vb, gs, P, n_anchor, window, zp)
     _append_pieces(kvq, [contig, paged], K, V, pieces)
     torch.cuda.synchronize()
     assert_same_storage(paged, table, contig)
@@ -74,8 +79,8 @@ def run_paged(oq, kb, vb, group, B=3, H=2, G=4, HD=128, P=64, n_pos=700, pieces=
         if L == 0:
             assert np.all(got[b] == 0)
             continue
-        want = oq.decode_step(kb, vb, gs, n_anchor, window, K[b][:, :L], V[b][:, :L], q[b], sc)
-        assert_close(got[b], want, f"paged P={P} kb={kb} vb={vb} HD={HD} G={G} b={b} L={L}")
+        want = oq.decode_step(kb, vb, gs, n_anchor, window, K[b][:, :L], V[b][:, :L], q[b], sc, asym=bool(zp))
+        assert_close(got[b], want, f"paged P={P} kb={kb} vb={vb} HD={HD} G={G} zp={zp} b={b} L={L}")
 
 
 @pytest.mark.parametrize("kb,vb,group", MODES)
@@ -118,6 +123,31 @@ def test_paged_window(oq, kb, vb):
     run_paged(oq, kb, vb, 0, B=2, H=2, G=4, HD=128, P=64, n_pos=700, n_anchor=64, window=192, seed=50 + kb)
 
 
+ZP_PAIRS = [(8, 8), (8, 4), (4, 4), (4, 8)]
+
+
+@pytest.mark.parametrize("kb,vb", ZP_PAIRS)
+@pytest.mark.parametrize("group", [0, 32, -1])
+@pytest.mark.parametrize("P", [64, 256])
+def test_paged_zero_point(oq, kb, vb, group, P):
+    """The zero-point codec on paged storage: per-head, 32-value group and
+    per-position scale words, pages of 64 and 256 slots, ragged lengths."""
+    H, G = (4, 1) if group == -1 else (2, 4)
+    run_paged(oq, kb, vb, group, H=H, G=G, HD=128, P=P, seq_lens=[700, 333, 1], zp=1,
+              seed=80 + kb * 10 + vb + P + max(group, 0))
+
+
+@pytest.mark.parametrize("kb,vb", [(4, 4), (8, 4)])
+def test_paged_zero_point_shapes(oq, kb, vb):
+    """head_dim 64 with two scale groups, G = 2 and 8, a window over pages,
+    and chunks that start inside pages."""
+    run_paged(oq, kb, vb, 32, B=2, H=2, G=2, HD=64, P=64, n_pos=515, zp=1, seed=90 + kb)
+    run_paged(oq, kb, vb, 0, B=2, H=2, G=8, HD=128, P=128, n_pos=901, zp=1, seed=91 + kb)
+    run_paged(oq, kb, vb, 0, B=2, H=2, G=4, HD=128, P=64, n_pos=700, n_anchor=64, window=192, zp=1, seed=92 + kb)
+    run_paged(oq, kb, vb, 0, B=2, H=2, G=4, HD=128, P=512, n_pos=3001, chunk=256, seq_lens=[3001, 2050], zp=1,
+              seed=93 + kb)
+
+
 @pytest.mark.parametrize("kb,vb,group", [(4, 4, 0), (8, 8, 0), (16, 16, 0), (8, 4, 0)])
 def test_paged_invalid_entries(oq, kb, vb, group):
     """Table entries outside [0, n_pages) are skipped by the append and read
@@ -156,12 +186,12 @@ def test_paged_invalid_entries(oq, kb, vb, group):
     assert torch.all(torch.isfinite(ox))
 
 
-@pytest.mark.parametrize("kb,vb,group", [(4, 4, 0), (8, 4, 0), (16, 16, 0)])
+@pytest.mark.parametrize("kb,vb,group,zp", [(4, 4, 0, 0), (8, 4, 0, 0), (16, 16, 0, 0), (4, 4, 32, 1), (8, 8, 0, 1)])
 @pytest.mark.parametrize("n_new", [1, 3])
-def test_paged_decode_step(oq, kb, vb, group, n_new):
+def test_paged_decode_step(oq, kb, vb, group, zp, n_new):
     """kvq_decode_step on a paged cache, its new rows crossing a page
     boundary, equals the separate calls on the same pages and on a
-    contiguous cache."""
+    contiguous cache (symmetric and zero-point codecs)."""
     kvq = need_gpu()
     import torch
     from workloads.device import positions, to_device
@@ -173,8 +203,8 @@ def test_paged_decode_step(oq, kb, vb, group, n_new):
     table = paged_table(B, pps, n_pages, 70 + n_new)
     gs = group_size_of(kb, vb, group, H, HD)
     K, V, q = _data(B, H, n, HD, H * G, 70 + n_new + kb)
-    ps = [_paged(kvq, table, n_pages, B, H, HD, cap, kb, vb, gs, P) for _ in range(2)]
-    contig = kvq.alloc_cache(B, H, HD, cap, kb, vb, gs)
+    ps = [_paged(kvq, table, n_pages, B, H, HD, cap, kb, vb, gs, P, zp=zp) for _ in range(2)]
+    contig = kvq.alloc_cache(B, H, HD, cap, kb, vb, gs, zero_point=zp)
     caches = ps + [contig]
     for c in caches:
         kvq.kvq_append(c, to_device(K[:, :, :n0]), to_device(V[:, :, :n0]), n0, positions([0] * B))
@@ -196,5 +226,5 @@ def test_paged_decode_step(oq, kb, vb, group, n_new):
     assert_same_storage(ps[0], table, contig)
     got = outs[0].cpu().numpy()
     for b in range(B):
-        want = oq.decode_step(kb, vb, gs, 0, 0, K[b], V[b], q[b], softmax_default(HD))
-        assert_close(got[b], want, f"paged step kb={kb} vb={vb} n_new={n_new} b={b}")
+        want = oq.decode_step(kb, vb, gs, 0, 0, K[b], V[b], q[b], softmax_default(HD), asym=bool(zp))
+        assert_close(got[b], want, f"paged step kb={kb} vb={vb} zp={zp} n_new={n_new} b={b}")

@@ -41,7 +41,7 @@ def draw(seed):
         A = W = 0
         n_pos = int(rng.integers(1, 1600))
         cap = ((n_pos + (P or 1) - 1) // (P or 1)) * (P or 1) + int(rng.choice([0, P or 7]))
-    zp = bool(quant and not P and rng.random() < 0.25)   # the zero-point codec (contiguous storage)
+    zp = bool(quant and rng.random() < 0.25)          # the zero-point codec
     chunk = int(rng.choice([0, 256, 512, 1024]))
     if not quant and chunk:
         chunk = int(rng.choice([64, 128, 256]))
@@ -71,7 +71,7 @@ def test_random_configuration(oq, seed):
         pps = cap // P
         table = paged_table(B, pps, B * pps + 3, seed)
         cache = kvq.alloc_cache(B, H, HD, cap, kb, vb, gs, A, W, page_size=P, n_pages=B * pps + 3,
-                                block_table=to_device(table))
+                                block_table=to_device(table), zero_point=int(c["zp"]))
     else:
         cache = kvq.alloc_cache(B, H, HD, cap, kb, vb, gs, A, W, zero_point=int(c["zp"]))
     # the context before the step's row, appended in pieces
