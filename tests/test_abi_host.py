@@ -433,3 +433,49 @@ def test_zero_point_rules(kvq):
     with pytest.raises(kvq.KvqError) as e:
         kvq.kvq_append(c, ok, ok, 1, ok, 0)
     assert e.value.status == kvq.KVQ_ERR_ALIGN and "4-byte aligned" in kvq.kvq_last_error()
+
+
+def test_header_is_c_and_links_from_c(kvq, tmp_path):
+    """kvq.h compiles as strict C99 and a C program linked against libkvq.so
+    calls the host-only entry points (no GPU work): TinyLoop's 4160 / 8192
+    bytes per token, a cache's buffer sizes, the chunk rule, an error string."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi.c"
+    src.write_text(r"""
+#include <stdio.h>
+#include <string.h>
+#include "kvq.h"
+int main(void)
+{
+    kvq_cache c;
+    size_t kc = 0, vc = 0, ks = 0, vs = 0;
+    memset(&c, 0, sizeof c);
+    c.batch = 2; c.n_kv_heads = 8; c.head_dim = 128; c.capacity = 1000;
+    c.k_bits = 4; c.v_bits = 4; c.group_size = 128;
+    if (kvq_cache_sizes(&c, &kc, &vc, &ks, &vs) != KVQ_OK) return 1;
+    printf("%zu %zu\n", kvq_bytes_per_token(8, 8, 16, 128, 128), kvq_bytes_per_token(16, 16, 16, 128, 128));
+    printf("%zu %zu %zu %zu\n", kc, vc, ks, vs);
+    printf("%d %d\n", kvq_chunk_tokens(&c, 32, 1000), kvq_chunk_count(&c, 32, 1000, 0));
+    c.head_dim = 96;
+    printf("%d %s\n", kvq_cache_sizes(&c, NULL, NULL, NULL, NULL), kvq_status_str(KVQ_ERR_SHAPE));
+    return 0;
+}
+""")
+    exe = tmp_path / "abi"
+    libdir = kvq.LIB_PATH.parent
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", f"-I{ROOT / 'include'}", str(src),
+                    f"-L{libdir}", "-lkvq", f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    assert out[0].split() == ["4160", "8192"]
+    cap64, cap4 = 1024, 1000
+    assert [int(x) for x in out[1].split()] == [2 * 8 * cap64 * 64, 2 * 8 * cap4 * 64, 2 * 8 * 1000 * 2,
+                                               2 * 8 * 1000 * 2]
+    ch, n = (int(x) for x in out[2].split())
+    assert ch == kvq.kvq_chunk_tokens(kvq.kvq_cache(2, 8, 128, 1000, 4, 4, 128, 0, 0), 32, 1000)
+    assert n == (1000 + ch - 1) // ch
+    st, msg = out[3].split(" ", 1)
+    assert int(st) == kvq.KVQ_ERR_SHAPE and msg == kvq.kvq_status_str(kvq.KVQ_ERR_SHAPE)
