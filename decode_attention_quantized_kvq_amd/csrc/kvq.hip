@@ -330,16 +330,22 @@ struct WsLayout {
     size_t ml, acc, qdig, qsc, qflag, cnt, total;
 };
 
-WsLayout ws_layout(int batch, int n_q_heads, int head_dim, int n_chunks, int n_kv_heads, int k_bits)
+// cnt_zone: a cache's workspace (kvq_workspace_bytes) ends with the zone of
+// the step's ticket counters, round_up(4 units, 256) bytes, on 16/32-bit
+// caches too (whose calls leave it untouched), so that the data of no call
+// reaches the counters of an 8/4-bit cache of as many (sequence, KV head)
+// pairs sharing the workspace; kvq_combine's partials alone have none.
+WsLayout ws_layout(int batch, int n_q_heads, int head_dim, int n_chunks, int n_kv_heads, int k_bits,
+                   bool cnt_zone = true)
 {
     const size_t P = (size_t)batch * n_q_heads;
+    const size_t units = (size_t)batch * n_kv_heads;
     WsLayout w;
     w.ml = 0;
     w.acc = align256(P * n_chunks * 2 * sizeof(float));
     size_t off = w.acc + P * n_chunks * head_dim * sizeof(float);
     w.qdig = w.qsc = w.qflag = w.cnt = 0;
     if (quantized(k_bits)) {
-        const size_t units = (size_t)batch * n_kv_heads;
         const size_t slots = n_chunks <= kStepMaxChunks ? (size_t)n_chunks : 1;
         w.qdig = align256(off);
         off = w.qdig + units * slots * (size_t)qd_stride(k_bits, head_dim, n_q_heads / n_kv_heads) * 4;
@@ -347,6 +353,8 @@ WsLayout ws_layout(int batch, int n_q_heads, int head_dim, int n_chunks, int n_k
         off = w.qsc + P * sizeof(float);
         w.qflag = align256(off);
         off = w.qflag + units * sizeof(int32_t);
+    }
+    if (cnt_zone) {
         // the step's ticket counters: the last round_up(4 units, 256) bytes
         // (cnt_offset places them by the caller's workspace_bytes)
         w.cnt = align256(off);
@@ -366,9 +374,10 @@ size_t cnt_offset(size_t bytes, size_t units)
     return (bytes - align256(units * sizeof(int))) & ~(size_t)255;
 }
 
+// kvq_combine's workspace: the partials only
 size_t ws_bytes(int batch, int n_q_heads, int head_dim, int n_chunks)
 {
-    return ws_layout(batch, n_q_heads, head_dim, n_chunks, 1, 32).total;
+    return ws_layout(batch, n_q_heads, head_dim, n_chunks, 1, 32, false).total;
 }
 
 int hip_status(const char *what)
@@ -837,6 +846,9 @@ static __device__ __align__(256) unsigned char scratch[KVQ_STATIC_SCRATCH_BYTES]
 namespace {
 
 constexpr int kMaxDevices = 64;
+// the static scratch's counter zone: room for the 65535 (sequence, KV head)
+// pairs a cache may have
+constexpr size_t kStaticCntZone = 256 * 1024;
 std::mutex g_scratch_mu;
 void *g_scratch_ptr[kMaxDevices] = {};
 
@@ -871,10 +883,18 @@ int kvq_decode_step_static(const kvq_cache *c, const float *k_new, const float *
     int ch, nc;
     int st = resolve_chunk(c, n_q_heads, max_seq_len, chunk_tokens, &ch, &nc);
     if (st) return st;
+    // The last kStaticCntZone bytes of the array hold the ticket counters of
+    // every geometry (each in the last round_up(4 units, 256) bytes); every
+    // step's other data stays below them, so no call writes over the
+    // counters of another, whatever their geometries.
+    const size_t units = (size_t)c->batch * c->n_kv_heads;
+    const size_t cnt = align256(units * sizeof(int));
     const size_t need = cache_ws_bytes(c, n_q_heads, nc);
-    if (need > (size_t)KVQ_STATIC_SCRATCH_BYTES)
-        return fail(KVQ_ERR_WORKSPACE, "this step needs %zu bytes of workspace, beyond the %zu of the static scratch",
-                    need, (size_t)KVQ_STATIC_SCRATCH_BYTES);
+    if (cnt > kStaticCntZone || need - cnt > (size_t)KVQ_STATIC_SCRATCH_BYTES - kStaticCntZone)
+        return fail(KVQ_ERR_WORKSPACE,
+                    "this step needs %zu bytes of workspace and %zu (sequence, KV head) counters, beyond the static "
+                    "scratch's %zu bytes (its last %zu for counters)",
+                    need, units, (size_t)KVQ_STATIC_SCRATCH_BYTES, kStaticCntZone);
     void *ws = nullptr;
     if ((st = static_scratch(&ws))) return st;
     return kvq_decode_step(c, k_new, v_new, n_new, start_pos, q, n_q_heads, seq_len, max_seq_len, softmax_scale, ch,

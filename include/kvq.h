@@ -244,11 +244,14 @@ int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n
  *                round_up(4 * batch * n_kv_heads, 256) bytes of the
  *                workspace_bytes given (their start aligned down to 256
  *                bytes); a step needs them zero when it starts and leaves
- *                them zero.  Hand a workspace over zero-filled before its
+ *                them zero.  kvq_workspace_bytes() of every cache, 16/32-bit
+ *                ones too, ends with that zone, which no call's other data
+ *                reaches.  Hand a workspace over zero-filled before its
  *                first kvq_decode_step; calls that share it pass the same
- *                workspace_bytes (then no other call writes over the
- *                counters, whatever its geometry); a call with another
- *                batch * n_kv_heads on it needs them zeroed again.
+ *                workspace_bytes (then no call of the same batch *
+ *                n_kv_heads writes over the counters, whatever its widths,
+ *                heads or chunks); a call with another batch * n_kv_heads
+ *                on it needs them zeroed again.
  * Results are deterministic: the chunk partition and the merge order are
  * fixed (kvq_decode_step's in-kernel merge takes an atomic ticket only to
  * decide which workgroup merges, not in what order).
@@ -352,7 +355,11 @@ int kvq_decode_step(const kvq_cache *c, const float *k_new, const float *v_new, 
  * (different streams, or host threads) race on it and must be ordered by
  * the caller.  Nothing in it must be cleared: the array starts zero-filled,
  * every call passes its whole extent as workspace_bytes (so the ticket
- * counters sit in its last bytes), and each step leaves them zero.
+ * counters sit in its last bytes), and each step leaves them zero.  The
+ * last 256 KiB of the array are kept for those counters, whatever the
+ * geometry (room for the 65535 (sequence, KV head) pairs a cache may have):
+ * a step whose other workspace data would not fit below them is rejected
+ * with KVQ_ERR_WORKSPACE.
  */
 #define KVQ_STATIC_SCRATCH_BYTES (32u << 20)
 

@@ -306,10 +306,13 @@ def test_workspace_and_chunks(kvq):
     with pytest.raises(kvq.KvqError) as e:
         kvq.kvq_workspace_bytes(d, 32, 32768, 64)
     assert e.value.status == -9
-    # float caches need the partials only
+    # float caches need the partials, then the zone where an 8/4-bit cache of
+    # as many (sequence, KV head) pairs sharing the workspace keeps its ticket
+    # counters (256 bytes for 4 pairs), left untouched
     f = _desc(kvq, batch=2, n_kv_heads=2, capacity=1000, k_bits=16, v_bits=16)
     nc = -(-1000 // kvq.kvq_chunk_tokens(f, 8, 1000))
-    assert kvq.kvq_workspace_bytes(f, 8, 1000, 0) == ((16 * nc * 8 + 255) // 256) * 256 + 16 * nc * 128 * 4
+    fpart = ((16 * nc * 8 + 255) // 256) * 256 + 16 * nc * 128 * 4
+    assert kvq.kvq_workspace_bytes(f, 8, 1000, 0) == (fpart + 255) // 256 * 256 + 256
     # max_seq_len beyond capacity sizes by capacity
     assert kvq.kvq_workspace_bytes(d, 32, 10 ** 9, 1024) == kvq.kvq_workspace_bytes(d, 32, 32768, 1024)
     # short contexts use the smallest chunk: 512 slots for integer caches, 64 for float ones
@@ -400,6 +403,19 @@ def test_static_step_rejects_oversize(kvq):
         kvq.kvq_decode_step_static(d, None, None, 1, None, None, 32, None, 131072, 0.0, 64, None, stream=0)
     assert e.value.status == kvq.KVQ_ERR_WORKSPACE
     assert "static scratch" in kvq.kvq_last_error()
+    # the array's last 256 KiB are the ticket counters' zone: a step whose
+    # other data would reach into it is refused although its whole need fits
+    zone = 256 * 1024
+    f = _desc(kvq, batch=32, n_kv_heads=8, capacity=63 * 64, k_bits=16, v_bits=16)
+    need = kvq.kvq_workspace_bytes(f, 32, 63 * 64, 64)
+    cnt = 32 * 8 * 4
+    assert kvq.KVQ_STATIC_SCRATCH_BYTES - zone < need - cnt and need <= kvq.KVQ_STATIC_SCRATCH_BYTES
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_decode_step_static(f, None, None, 1, None, None, 32, None, 63 * 64, 0.0, 64, None, stream=0)
+    assert e.value.status == kvq.KVQ_ERR_WORKSPACE
+    # (the zone holds the counters of the most (sequence, KV head) pairs a
+    # cache may have: 65535 x 4 bytes)
+    assert 65535 * 4 <= zone
 
 
 def test_zero_point_rules(kvq):

@@ -493,6 +493,17 @@ def test_layers_of_mixed_widths_in_one_graph(oq):
         for b in range(B):
             ref = oq.decode_step(kb, vb, gs, 0, 0, K[b], V[b], q[b], softmax_default(HD))
             assert_close(got[b], ref, f"layer kb={kb} vb={vb} g={gs} b={b}")
+    # more steps on the same workspace, never cleared again: the FP16 layer's
+    # partials (the largest need, so they reach the end of the data) leave
+    # the integer layers' ticket counters alone, and every step leaves them
+    # zero
+    for r in range(2):
+        for l in layers:
+            l[4].zero_()
+        step(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        for li, l in enumerate(layers):
+            assert torch.equal(l[4], want[li]), f"eager step {r + 2} layer {li}"
     g = torch.cuda.CUDAGraph()
     cs = torch.cuda.Stream()
     cs.wait_stream(torch.cuda.current_stream())
@@ -503,8 +514,7 @@ def test_layers_of_mixed_widths_in_one_graph(oq):
         step(cs)
     for r in range(3):
         for l in layers:
-            l[4].zero_()
-        ws.zero_()                                   # eager work between replays (the step takes it zero-filled)
+            l[4].zero_()                             # eager work between replays (the workspace is not cleared)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()

@@ -242,3 +242,56 @@ def test_one_launch_step_chunks_graph(oq):
     for b in range(B):
         ref = oq.decode_step(4, 4, HD, 0, 0, K[b], V[b], q[b], softmax_default(HD))
         assert_close(got[b], ref, f"graph two-chunk step b={b}")
+
+
+def test_shared_workspace_float_and_integer_layers(oq):
+    """Layers of an FP16 cache and of 8/4-bit caches (one-launch steps over
+    two chunks) sharing one workspace, sized by the largest need (the FP16
+    layer's: its partials reach the end of its data), never cleared after
+    the first step: several decode steps in a row, each layer's output bit
+    for bit that of the same layer on a workspace of its own, and the cache
+    contents the same."""
+    kvq = need_gpu()
+    import torch
+    from workloads.device import positions, to_device
+    B, H, G, HD, n0, steps = 4, 4, 1, 128, 900, 3
+    modes = [(16, 16, HD), (8, 8, HD), (4, 4, 32)]
+    Hq = H * G
+    layers = []
+    for li, (kb, vb, gs) in enumerate(modes):
+        K, V, q = _data(B, H, n0 + steps, HD, Hq, 90 + li)
+        pair = [kvq.alloc_cache(B, H, HD, n0 + steps, kb, vb, gs) for _ in range(2)]
+        for c in pair:
+            kvq.kvq_append(c, to_device(K[:, :, :n0]), to_device(V[:, :, :n0]), n0, positions([0] * B))
+        layers.append((pair, K, V, q))
+    n_max = n0 + steps
+    needs = [kvq.kvq_workspace_bytes(p[0], Hq, n_max, 0) for p, *_ in layers]
+    assert needs[0] == max(needs)                    # the FP16 layer's partials fill the shared extent
+    for (p, *_), (kb, _, _) in zip(layers, modes):
+        if kb < 16:
+            assert kvq.kvq_chunk_count(p[0], Hq, n_max, 0) == 2   # one launch, merged by the last workgroup
+    shared_bytes = max(needs)
+    shared = torch.zeros(shared_bytes // 4 + 64, dtype=torch.float32, device="cuda")
+    own = [torch.zeros(nb // 4 + 64, dtype=torch.float32, device="cuda") for nb in needs]
+    for s in range(steps):
+        t = n0 + s
+        pos, lens = positions([t] * B), positions([t + 1] * B)
+        for li, (pair, K, V, q) in enumerate(layers):
+            k1, v1 = to_device(K[:, :, t:t + 1]), to_device(V[:, :, t:t + 1])
+            qd = to_device(q * np.float32(1.0 + 0.1 * s))
+            outs = [torch.full((B, Hq, HD), 9.0, dtype=torch.float32, device="cuda") for _ in range(2)]
+            kvq.kvq_decode_step(pair[0], k1, v1, 1, pos, qd, Hq, lens, n_max, 0.0, 0, outs[0], shared, shared_bytes)
+            kvq.kvq_decode_step(pair[1], k1, v1, 1, pos, qd, Hq, lens, n_max, 0.0, 0, outs[1], own[li], needs[li])
+            torch.cuda.synchronize()
+            assert torch.equal(outs[0], outs[1]), f"step {s} layer {li}: the shared workspace changed the output"
+            if s == steps - 1:
+                kb, vb, gs = modes[li]
+                got = outs[0].cpu().numpy()
+                for b in range(B):
+                    ref = oq.decode_step(kb, vb, gs, 0, 0, K[b][:, :t + 1], V[b][:, :t + 1],
+                                         q[b] * np.float32(1.0 + 0.1 * s), softmax_default(HD))
+                    assert_close(got[b], ref, f"shared workspace layer {li} b={b}")
+    for pair, *_ in layers:
+        for name in ("k_codes", "v_codes", "k_scales", "v_scales"):
+            a, b_ = getattr(pair[0], name), getattr(pair[1], name)
+            assert (a is None and b_ is None) or torch.equal(a, b_), name
