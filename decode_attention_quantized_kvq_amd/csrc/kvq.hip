@@ -151,8 +151,21 @@ int log2i(int x)
     return r;
 }
 
+// G = 8 query heads per KV head with scale groups inside the head run as
+// two workgroup heads of four per cache head (kv_shift 1): eight heads with
+// 2 or 4 groups keep too many per-head, per-group sums live (236-256 VGPRs,
+// one or two waves per SIMD), four run at the G = 4 rate, and reading each
+// cache byte twice costs less than that
+bool split_heads(const kvq_cache *c, int G) { return quant_modes(c) && G == 8 && groups_per_head(c) > 1; }
+
+// the query heads one workgroup handles, and the (sequence, KV head) units
+// (per workgroup head) of the split kernel's grid
+int unit_g(const kvq_cache *c, int G) { return split_heads(c, G) ? 4 : G; }
+int unit_kv(const kvq_cache *c, int G) { return split_heads(c, G) ? 2 * c->n_kv_heads : c->n_kv_heads; }
+
 size_t lds_bytes(const kvq_cache *c, int G, int chunk)
 {
+    G = unit_g(c, G);
     if (quant_modes(c)) {
         const int vg = groups_per_head(c);
         return (size_t)quant_smem(G, c->head_dim, vg, c->zero_point != 0).total;
@@ -244,7 +257,9 @@ QuantFn pick_quant_g(int G)
     case 1: return decode_quant_kernel<KB, VB, HD, 1, KG, PG, ZP>;
     case 2: return decode_quant_kernel<KB, VB, HD, 2, KG, PG, ZP>;
     case 4: return decode_quant_kernel<KB, VB, HD, 4, KG, PG, ZP>;
-    case 8: return decode_quant_kernel<KB, VB, HD, 8, KG, PG, ZP>;
+    case 8:
+        if constexpr (KG == 1) return decode_quant_kernel<KB, VB, HD, 8, KG, PG, ZP>;
+        return nullptr;                              // split into two heads of four
     }
     return nullptr;
 }
@@ -320,23 +335,31 @@ StepPrepFn pick_step(int kb, int hd, int G)
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace: ml [P][C][2] | acc [P][C][HD] | (quantized keys) query digits
-// [B*Hkv][S][qd_stride] int32 (each slot's [ND+1][K_COLS][G] padded to 256
+// the ticket-counter zone at the end of a workspace, for `pairs` (sequence,
+// cache KV head) pairs: two int32 counters each
+size_t cnt_zone_bytes(size_t pairs) { return align256(pairs * 2 * sizeof(int)); }
+
+// Workspace (U = B * the split kernel's heads per sequence, unit_kv): ml
+// [P][C][2] | acc [P][C][HD] | (quantized keys) query digits
+// [U][S][qd_stride] int32 (each slot's [ND+1][K_COLS][G] padded to 256
 // bytes; S = C slots, one per chunk for the one-launch step, when
 // C <= kStepMaxChunks, else 1) | query scales [P] float | extra-digit flags
-// [B*Hkv] int32 | ticket counters [B*Hkv] int32 (zero between calls; in the
-// last bytes of the caller's extent, see cnt_offset).
+// [U] int32 | the ticket counters' zone (the counters [U] int32, zero between
+// calls, sit in the last bytes of the caller's extent, see cnt_offset).
 struct WsLayout {
     size_t ml, acc, qdig, qsc, qflag, cnt, total;
 };
 
-// cnt_zone: a cache's workspace (kvq_workspace_bytes) ends with the zone of
-// the step's ticket counters, round_up(4 units, 256) bytes, on 16/32-bit
-// caches too (whose calls leave it untouched), so that the data of no call
-// reaches the counters of an 8/4-bit cache of as many (sequence, KV head)
-// pairs sharing the workspace; kvq_combine's partials alone have none.
+// n_kv_heads: the split kernel's heads per sequence (twice the cache's when
+// its heads are split, unit_kv).  cnt_zone: a cache's workspace
+// (kvq_workspace_bytes) ends with the zone of the step's ticket counters,
+// round_up(8 batch n_kv_cache, 256) bytes (room for two per (sequence, cache
+// KV head), as a split-head step takes), on 16/32-bit caches too (whose calls
+// leave it untouched), so that the data of no call reaches the counters of an
+// 8/4-bit cache of as many (sequence, KV head) pairs sharing the workspace;
+// kvq_combine's partials alone have none.
 WsLayout ws_layout(int batch, int n_q_heads, int head_dim, int n_chunks, int n_kv_heads, int k_bits,
-                   bool cnt_zone = true)
+                   bool cnt_zone = true, int n_kv_cache = 0)
 {
     const size_t P = (size_t)batch * n_q_heads;
     const size_t units = (size_t)batch * n_kv_heads;
@@ -355,10 +378,11 @@ WsLayout ws_layout(int batch, int n_q_heads, int head_dim, int n_chunks, int n_k
         off = w.qflag + units * sizeof(int32_t);
     }
     if (cnt_zone) {
-        // the step's ticket counters: the last round_up(4 units, 256) bytes
-        // (cnt_offset places them by the caller's workspace_bytes)
+        // the step's ticket counters: within the last round_up(8 (sequence,
+        // cache KV head) pairs, 256) bytes (cnt_offset places them by the
+        // caller's workspace_bytes)
         w.cnt = align256(off);
-        off = w.cnt + align256(units * sizeof(int));
+        off = w.cnt + cnt_zone_bytes((size_t)batch * (n_kv_cache ? n_kv_cache : n_kv_heads));
     }
     w.total = off;
     return w;
@@ -553,9 +577,15 @@ static int resolve_chunk(const kvq_cache *c, int n_q_heads, int max_seq_len, int
     return KVQ_OK;
 }
 
+static WsLayout cache_ws_layout(const kvq_cache *c, int n_q_heads, int n_chunks)
+{
+    const int G = n_q_heads / c->n_kv_heads;
+    return ws_layout(c->batch, n_q_heads, c->head_dim, n_chunks, unit_kv(c, G), c->k_bits, true, c->n_kv_heads);
+}
+
 static size_t cache_ws_bytes(const kvq_cache *c, int n_q_heads, int n_chunks)
 {
-    return ws_layout(c->batch, n_q_heads, c->head_dim, n_chunks, c->n_kv_heads, c->k_bits).total;
+    return cache_ws_layout(c, n_q_heads, n_chunks).total;
 }
 
 int kvq_chunk_count(const kvq_cache *c, int n_q_heads, int max_seq_len, int chunk_tokens)
@@ -615,7 +645,7 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
     const float scale = softmax_scale == 0.0f ? 1.0f / std::sqrt((float)c->head_dim) : softmax_scale;
     const float qk_scale = scale * 1.4426950408889634f;   // log2(e): scores kept in log2 units
     const int G = n_q_heads / c->n_kv_heads;
-    const WsLayout wl = ws_layout(c->batch, n_q_heads, c->head_dim, nc, c->n_kv_heads, c->k_bits);
+    const WsLayout wl = cache_ws_layout(c, n_q_heads, nc);
     char *ws = static_cast<char *>(workspace);
     hipStream_t st_ = static_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)nc, (unsigned)(c->batch * c->n_kv_heads));
@@ -650,10 +680,13 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
         return hip_status("decode_float_kernel launch");
     }
 
-    QuantFn fn = pick_quant(c->k_bits, c->v_bits, c->head_dim, G, groups_per_head(c), paged(c), c->zero_point != 0);
+    // the split kernel's units: (sequence, workgroup head) pairs of Gu query
+    // heads each (two per cache KV head when its heads are split)
+    const int Gu = unit_g(c, G), Hu = unit_kv(c, G);
+    QuantFn fn = pick_quant(c->k_bits, c->v_bits, c->head_dim, Gu, groups_per_head(c), paged(c), c->zero_point != 0);
     const int kg = c->zero_point ? groups_per_head(c) : 0;   // per-group query sums for the zero-point codec
-    PrepFn prep = pick_prep(c->k_bits, c->head_dim, G);
-    StepPrepFn sprep = pick_step(c->k_bits, c->head_dim, G);
+    PrepFn prep = pick_prep(c->k_bits, c->head_dim, Gu);
+    StepPrepFn sprep = pick_step(c->k_bits, c->head_dim, Gu);
     if (!fn || !prep || !sprep) return fail(KVQ_ERR_BITS, "no kernel for k_bits=%d v_bits=%d", c->k_bits, c->v_bits);
     int32_t *qdig = reinterpret_cast<int32_t *>(ws + wl.qdig);
     float *qsc = reinterpret_cast<float *>(ws + wl.qsc);
@@ -665,9 +698,9 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
     // in the one-launch step with several chunks, and in the two-launch one
     // (whose query preparation also zeroes them)
     int *cnt = (one_launch && nc > 1) || (out && !one_launch)
-                   ? reinterpret_cast<int *>(ws + cnt_offset(workspace_bytes, (size_t)c->batch * c->n_kv_heads))
+                   ? reinterpret_cast<int *>(ws + cnt_offset(workspace_bytes, (size_t)c->batch * Hu))
                    : nullptr;
-    const unsigned units = (unsigned)(c->batch * c->n_kv_heads);
+    const unsigned units = (unsigned)(c->batch * Hu);
     if (ap && ap_grid.x > 0 && (unsigned long long)ap_grid.x * ap_grid.y * 2 + units > 0x7FFFFFFFull)
         return fail(KVQ_ERR_SHAPE, "batch * n_new too large for a fused step");
     if ((phases & PHASE_PREP) && !one_launch) {
@@ -694,7 +727,9 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
     p.seq_len = seq_len;
     p.ws_ml = reinterpret_cast<float *>(ws + wl.ml);
     p.ws_acc = reinterpret_cast<float *>(ws + wl.acc);
-    p.n_kv_heads = c->n_kv_heads;
+    p.n_kv_heads = Hu;
+    p.n_kv_cache = c->n_kv_heads;
+    p.kv_shift = Hu == c->n_kv_heads ? 0 : 1;
     p.capacity = cap_u(c);
     p.cap4 = cap4_of(c);
     p.cap64 = cap64_of(c);
@@ -732,8 +767,7 @@ static int enqueue_partials(const kvq_cache *c, const float *q, int n_q_heads, c
         p.k_sc_h = p.v_sc_h = (long long)cap_u(c) * gph;
         p.k_sc_t = p.v_sc_t = gph;
     }
-    hipLaunchKernelGGL(fn, dim3((unsigned)nc, (unsigned)c->n_kv_heads, (unsigned)c->batch), dim3(QD_THREADS), lds,
-                       st_, p);
+    hipLaunchKernelGGL(fn, dim3((unsigned)nc, (unsigned)Hu, (unsigned)c->batch), dim3(QD_THREADS), lds, st_, p);
     return hip_status("decode_quant_kernel launch");
 }
 
@@ -846,9 +880,9 @@ static __device__ __align__(256) unsigned char scratch[KVQ_STATIC_SCRATCH_BYTES]
 namespace {
 
 constexpr int kMaxDevices = 64;
-// the static scratch's counter zone: room for the 65535 (sequence, KV head)
-// pairs a cache may have
-constexpr size_t kStaticCntZone = 256 * 1024;
+// the static scratch's counter zone: room for the two counters of each of
+// the 65535 (sequence, KV head) pairs a cache may have
+constexpr size_t kStaticCntZone = 512 * 1024;
 std::mutex g_scratch_mu;
 void *g_scratch_ptr[kMaxDevices] = {};
 
@@ -884,17 +918,16 @@ int kvq_decode_step_static(const kvq_cache *c, const float *k_new, const float *
     int st = resolve_chunk(c, n_q_heads, max_seq_len, chunk_tokens, &ch, &nc);
     if (st) return st;
     // The last kStaticCntZone bytes of the array hold the ticket counters of
-    // every geometry (each in the last round_up(4 units, 256) bytes); every
-    // step's other data stays below them, so no call writes over the
-    // counters of another, whatever their geometries.
-    const size_t units = (size_t)c->batch * c->n_kv_heads;
-    const size_t cnt = align256(units * sizeof(int));
+    // every geometry (each within the last round_up(8 (sequence, KV head)
+    // pairs, 256) bytes); every step's other data stays below them, so no
+    // call writes over the counters of another, whatever their geometries.
+    const size_t zone = cnt_zone_bytes((size_t)c->batch * c->n_kv_heads);
     const size_t need = cache_ws_bytes(c, n_q_heads, nc);
-    if (cnt > kStaticCntZone || need - cnt > (size_t)KVQ_STATIC_SCRATCH_BYTES - kStaticCntZone)
+    if (zone > kStaticCntZone || need - zone > (size_t)KVQ_STATIC_SCRATCH_BYTES - kStaticCntZone)
         return fail(KVQ_ERR_WORKSPACE,
-                    "this step needs %zu bytes of workspace and %zu (sequence, KV head) counters, beyond the static "
-                    "scratch's %zu bytes (its last %zu for counters)",
-                    need, units, (size_t)KVQ_STATIC_SCRATCH_BYTES, kStaticCntZone);
+                    "this step needs %zu bytes of workspace, beyond the static scratch's %zu bytes (its last %zu "
+                    "for ticket counters)",
+                    need, (size_t)KVQ_STATIC_SCRATCH_BYTES, kStaticCntZone);
     void *ws = nullptr;
     if ((st = static_scratch(&ws))) return st;
     return kvq_decode_step(c, k_new, v_new, n_new, start_pos, q, n_q_heads, seq_len, max_seq_len, softmax_scale, ch,

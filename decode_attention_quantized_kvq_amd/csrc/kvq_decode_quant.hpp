@@ -68,14 +68,15 @@ constexpr int QD_THREADS = 256;
 constexpr int QD_WAVES = QD_THREADS / 64;
 // Positions per wave sub-chunk: 512 while G x vg < 8, else 256 (the maxima,
 // merge and prologue then run half as often as at 128, and the compiler keeps
-// the G = 4, vg = 4 loop in 156 VGPRs instead of 245); G = 8 with 2 or 4
-// scale groups, and the zero-point codec's G x vg >= 16 (whose scale words
-// take twice the LDS), take 128, as 256 would not fit the 64 KiB of LDS.
+// the G = 4, vg = 4 loop in 156 VGPRs instead of 245); the zero-point codec's
+// G x vg >= 16 (whose scale words take twice the LDS) takes 128, as 256
+// would not fit the 64 KiB of LDS.  (G = 8 with 2 or 4 scale groups is not
+// instantiated: its heads run as two workgroup heads of four.)
 // (A sub-chunk's value sums stay exact in uint32: at most
 // 512 * 32767 * 255 < 2^32.)
 __host__ __device__ constexpr int qd_sub(int G, int vg, bool zp = false)
 {
-    return (G == 8 && vg >= 2) || (zp && G * vg >= 16) ? 128 : G * vg >= 8 ? 256 : 512;
+    return zp && G * vg >= 16 ? 128 : G * vg >= 8 ? 256 : 512;
 }
 constexpr int Q_RANGE = 30000;
 // the query's extra low digit: taken when max|q| > Q_OUTLIER * rms(q) for a
@@ -129,6 +130,11 @@ struct QuantParams {
     float *ws_ml;
     float *ws_acc;
     int n_kv_heads, capacity, cap4, cap64;   // capacity, cap4, cap64: per storage unit (sequence or page)
+    // the cache's KV heads: n_kv_cache = n_kv_heads >> kv_shift.  kv_shift 1:
+    // the G query heads of each cache head are split over two workgroup
+    // heads (grid.y = n_kv_heads, head kvh reading cache head kvh >> 1),
+    // each a unit of its own for the query digits and ticket counters
+    int n_kv_cache, kv_shift;
     // paged storage: slot s of sequence b in page block_table[b * pages_per_seq
     // + (s >> page_shift)] (paged kernels only)
     const int32_t *block_table;
@@ -141,7 +147,7 @@ struct QuantParams {
     // its (sequence, KV head) into out.  cnt == nullptr: partials only.
     int *cnt;
     float *out;
-    // one-launch decode step (step != 0; at most 4 chunks per (sequence, KV
+    // one-launch decode step (step != 0; at most 2 chunks per (sequence, KV
     // head)): each workgroup first stores the step's rows of its head whose
     // slots fall in its chunk (the last chunk also takes those past it) (ap)
     // and prepares its query (q, qk_scale: digits into its own slot of
@@ -385,7 +391,8 @@ void decode_quant_kernel(QuantParams p)
     // from it (the wave's range, its buffer descriptors) stays in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int chunk_id = blockIdx.x;                 // grid: (chunks, KV heads, sequences)
-    const int kvh = blockIdx.y;
+    const int kvh = blockIdx.y;                      // the unit's head (query heads kvh * G ..)
+    const int kvc = kvh >> p.kv_shift;               // the cache's KV head it reads
     const int b = blockIdx.z;
     const int bh = b * p.n_kv_heads + kvh;
     const int Hq = p.n_kv_heads * G;
@@ -414,7 +421,9 @@ void decode_quant_kernel(QuantParams p)
         // (block-uniform) this is the only workgroup of its (sequence, KV
         // head): the step's rows of its head, then its query's digits; every
         // store is complete before a wave reads the cache or the digits
-        append_head_rows<HD>(p.ap, b, kvh, t0, chunk_id == p.n_chunks - 1 ? 0x7FFFFFFF : t0 + CH);
+        // (with the heads split over two workgroups both store the same
+        // rows, byte for byte the same values, each before reading them)
+        append_head_rows<HD>(p.ap, b, kvc, t0, chunk_id == p.n_chunks - 1 ? 0x7FFFFFFF : t0 + CH);
         float *s_qv = reinterpret_cast<float *>(smem);
         float *s_amax = s_qv + G * HD;
         int *s_xflag = reinterpret_cast<int *>(s_amax + G);
@@ -557,13 +566,13 @@ void decode_quant_kernel(QuantParams p)
         const uint32_t rem = u < 0 ? 0u : (uint32_t)max(nw - tb, 0);
         const uint32_t kbytes = rem > 0 ? 64 * T::K_ROW : 0;
         const int uu = u < 0 ? 0 : u;
-        const uint8_t *kb = p.k_codes + (((size_t)uu * p.n_kv_heads + kvh) * p.cap64 + sl) * T::K_ROW;
+        const uint8_t *kb = p.k_codes + (((size_t)uu * p.n_kv_cache + kvc) * p.cap64 + sl) * T::K_ROW;
         const rsrc_t krs = make_rsrc(kb, kbytes);
         const rsrc_t ksrs = make_rsrc(reinterpret_cast<const char *>(p.k_scales) +
-                                          (uu * p.k_sc_b + kvh * p.k_sc_h + (size_t)sl * p.k_sc_t) * SCB,
+                                          (uu * p.k_sc_b + kvc * p.k_sc_h + (size_t)sl * p.k_sc_t) * SCB,
                                       rem * p.k_sc_t * SCB);
         const rsrc_t vsrs = make_rsrc(reinterpret_cast<const char *>(p.v_scales) +
-                                          (uu * p.v_sc_b + kvh * p.v_sc_h + (size_t)sl * p.v_sc_t) * SCB,
+                                          (uu * p.v_sc_b + kvc * p.v_sc_h + (size_t)sl * p.v_sc_t) * SCB,
                                       rem * p.v_sc_t * SCB);
         // (immediate offsets reach 4 KiB: int8 rows use a second descriptor
         // for slices 4..7)
@@ -727,7 +736,7 @@ void decode_quant_kernel(QuantParams p)
         VRs d;
         const int u = unit_of(4 * g0);
         const int uu = u < 0 ? 0 : u;
-        const uint8_t *vb = p.v_codes + (((size_t)uu * p.n_kv_heads + kvh) * p.cap4 + slot_of(4 * g0)) * T::V_ROW;
+        const uint8_t *vb = p.v_codes + (((size_t)uu * p.n_kv_cache + kvc) * p.cap4 + slot_of(4 * g0)) * T::V_ROW;
         const int left = u < 0 ? 0 : (ngw - g0) * 4 * T::V_ROW;   // bytes of the wave's range from the batch on
 #pragma unroll
         for (int r = 0; r < NR; r++) {
@@ -1138,15 +1147,16 @@ void decode_quant_kernel(QuantParams p)
 // Every (head_dim, query heads per KV head, scale groups per head)
 // instance of one (key width, value width, paged, zero point) family of the
 // split kernel: head_dim 64 with 1 or 2 scale groups, head_dim 128 with 1, 2
-// or 4; G in {1, 2, 4, 8}.  X(KB, VB, HD, G, KG, PG, ZP) is applied to each.
+// or 4; G in {1, 2, 4, 8}, G = 8 with one scale group only (with more, the
+// eight heads run as two workgroup heads of four, kv_shift 1).
+// X(KB, VB, HD, G, KG, PG, ZP) is applied to each.
 #define KVQ_QUANT_FAMILY(X, KB, VB, PG, ZP)                                                     \
     X(KB, VB, 64, 1, 1, PG, ZP) X(KB, VB, 64, 2, 1, PG, ZP) X(KB, VB, 64, 4, 1, PG, ZP)          \
     X(KB, VB, 64, 8, 1, PG, ZP) X(KB, VB, 64, 1, 2, PG, ZP) X(KB, VB, 64, 2, 2, PG, ZP)          \
-    X(KB, VB, 64, 4, 2, PG, ZP) X(KB, VB, 64, 8, 2, PG, ZP) X(KB, VB, 128, 1, 1, PG, ZP)         \
+    X(KB, VB, 64, 4, 2, PG, ZP) X(KB, VB, 128, 1, 1, PG, ZP)                                     \
     X(KB, VB, 128, 2, 1, PG, ZP) X(KB, VB, 128, 4, 1, PG, ZP) X(KB, VB, 128, 8, 1, PG, ZP)       \
     X(KB, VB, 128, 1, 2, PG, ZP) X(KB, VB, 128, 2, 2, PG, ZP) X(KB, VB, 128, 4, 2, PG, ZP)       \
-    X(KB, VB, 128, 8, 2, PG, ZP) X(KB, VB, 128, 1, 4, PG, ZP) X(KB, VB, 128, 2, 4, PG, ZP)       \
-    X(KB, VB, 128, 4, 4, PG, ZP) X(KB, VB, 128, 8, 4, PG, ZP)
+    X(KB, VB, 128, 1, 4, PG, ZP) X(KB, VB, 128, 2, 4, PG, ZP) X(KB, VB, 128, 4, 4, PG, ZP)
 
 // all families the library dispatches to: four width pairs, each contiguous
 // and paged, with the symmetric and the zero-point codec

@@ -240,13 +240,15 @@ int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n
  *                and one int32 ticket counter per (sequence, KV head) for
  *                kvq_decode_step follow.  An empty chunk has m = -inf, l = 0,
  *                acc = 0.  kvq_decode_step's ticket counters (8/4-bit
- *                caches): one int32 per (sequence, KV head) in the last
- *                round_up(4 * batch * n_kv_heads, 256) bytes of the
- *                workspace_bytes given (their start aligned down to 256
- *                bytes); a step needs them zero when it starts and leaves
- *                them zero.  kvq_workspace_bytes() of every cache, 16/32-bit
- *                ones too, ends with that zone, which no call's other data
- *                reaches.  Hand a workspace over zero-filled before its
+ *                caches): one int32 per (sequence, KV head), two when the
+ *                eight query heads of a KV head with scale groups inside
+ *                the head are split over two workgroups, within the last
+ *                round_up(8 * batch * n_kv_heads, 256) bytes of the
+ *                workspace_bytes given (the counters at its end, their
+ *                start aligned down to 256 bytes); a step needs them zero
+ *                when it starts and leaves them zero.  kvq_workspace_bytes()
+ *                of every cache, 16/32-bit ones too, ends with that zone,
+ *                which no call's other data reaches.  Hand a workspace over zero-filled before its
  *                first kvq_decode_step; calls that share it pass the same
  *                workspace_bytes (then no call of the same batch *
  *                n_kv_heads writes over the counters, whatever its widths,
@@ -356,10 +358,10 @@ int kvq_decode_step(const kvq_cache *c, const float *k_new, const float *v_new, 
  * the caller.  Nothing in it must be cleared: the array starts zero-filled,
  * every call passes its whole extent as workspace_bytes (so the ticket
  * counters sit in its last bytes), and each step leaves them zero.  The
- * last 256 KiB of the array are kept for those counters, whatever the
- * geometry (room for the 65535 (sequence, KV head) pairs a cache may have):
- * a step whose other workspace data would not fit below them is rejected
- * with KVQ_ERR_WORKSPACE.
+ * last 512 KiB of the array are kept for those counters, whatever the
+ * geometry (room for two counters for each of the 65535 (sequence, KV head)
+ * pairs a cache may have): a step whose other workspace data would not fit
+ * below them is rejected with KVQ_ERR_WORKSPACE.
  */
 #define KVQ_STATIC_SCRATCH_BYTES (32u << 20)
 

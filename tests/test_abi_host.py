@@ -293,13 +293,13 @@ def test_workspace_and_chunks(kvq):
     # int4 keys: the query's fixed-point digits (4 Horner digits and the extra low
     # one, per value; then two sums per scale group and head for the zero-point
     # codec; each unit's block padded to 256 bytes) and scales follow the partials,
-    # then one extra-digit flag and one ticket counter per (sequence, KV head) for
-    # the fused step
+    # then one extra-digit flag per (sequence, KV head) and the ticket counters'
+    # zone (room for two per (sequence, KV head))
     words = -(-(16 * 5 * 4 + 2 * 4 * 4) // 64) * 64
     digits = 32 * 8 * words * 4 + P * 4
-    counters = 2 * 32 * 8 * 4
+    counters = 32 * 8 * 4 + 2 * 32 * 8 * 4
     ws = kvq.kvq_workspace_bytes(d, 32, 32768, 0)
-    assert partials + digits + counters <= ws <= partials + digits + counters + 1024
+    assert partials + digits + counters <= ws <= partials + digits + counters + 768
     ws256 = kvq.kvq_workspace_bytes(d, 32, 32768, 256)
     assert ws256 >= ((P * 128 * 8 + 255) // 256) * 256 + P * 128 * 512
     # 8/4-bit caches take chunks in multiples of 256 slots
@@ -308,7 +308,7 @@ def test_workspace_and_chunks(kvq):
     assert e.value.status == -9
     # float caches need the partials, then the zone where an 8/4-bit cache of
     # as many (sequence, KV head) pairs sharing the workspace keeps its ticket
-    # counters (256 bytes for 4 pairs), left untouched
+    # counters (256 bytes for 4 pairs, 2 counters each), left untouched
     f = _desc(kvq, batch=2, n_kv_heads=2, capacity=1000, k_bits=16, v_bits=16)
     nc = -(-1000 // kvq.kvq_chunk_tokens(f, 8, 1000))
     fpart = ((16 * nc * 8 + 255) // 256) * 256 + 16 * nc * 128 * 4
@@ -403,19 +403,19 @@ def test_static_step_rejects_oversize(kvq):
         kvq.kvq_decode_step_static(d, None, None, 1, None, None, 32, None, 131072, 0.0, 64, None, stream=0)
     assert e.value.status == kvq.KVQ_ERR_WORKSPACE
     assert "static scratch" in kvq.kvq_last_error()
-    # the array's last 256 KiB are the ticket counters' zone: a step whose
+    # the array's last 512 KiB are the ticket counters' zone: a step whose
     # other data would reach into it is refused although its whole need fits
-    zone = 256 * 1024
+    zone = 512 * 1024
     f = _desc(kvq, batch=32, n_kv_heads=8, capacity=63 * 64, k_bits=16, v_bits=16)
     need = kvq.kvq_workspace_bytes(f, 32, 63 * 64, 64)
-    cnt = 32 * 8 * 4
+    cnt = 2 * 32 * 8 * 4
     assert kvq.KVQ_STATIC_SCRATCH_BYTES - zone < need - cnt and need <= kvq.KVQ_STATIC_SCRATCH_BYTES
     with pytest.raises(kvq.KvqError) as e:
         kvq.kvq_decode_step_static(f, None, None, 1, None, None, 32, None, 63 * 64, 0.0, 64, None, stream=0)
     assert e.value.status == kvq.KVQ_ERR_WORKSPACE
-    # (the zone holds the counters of the most (sequence, KV head) pairs a
-    # cache may have: 65535 x 4 bytes)
-    assert 65535 * 4 <= zone
+    # (the zone holds two counters for each of the most (sequence, KV head)
+    # pairs a cache may have: 65535 x 8 bytes)
+    assert 65535 * 8 <= zone
 
 
 def test_zero_point_rules(kvq):
@@ -495,3 +495,29 @@ int main(void)
     assert n == (1000 + ch - 1) // ch
     st, msg = out[3].split(" ", 1)
     assert int(st) == kvq.KVQ_ERR_SHAPE and msg == kvq.kvq_status_str(kvq.KVQ_ERR_SHAPE)
+
+
+def test_split_head_workspace(kvq):
+    """Eight query heads per KV head with scale groups inside the head run as
+    two workgroup heads of four: the query digits, scales, flags and ticket
+    counters are laid out per (sequence, workgroup head), each block holding
+    four heads' digits; one scale per head keeps one unit of eight."""
+    a256 = lambda x: (x + 255) // 256 * 256
+
+    def stride(G):                                   # int32 words of one unit's digits (int4 keys, HD 128)
+        return -(-(5 * 16 * G + 2 * 4 * G) // 64) * 64
+
+    def expect(B, Hkv, Hq, C, units, G):
+        P = B * Hq
+        off = a256(P * C * 8) + P * C * 128 * 4
+        off = a256(off) + units * (C if C <= 2 else 1) * stride(G) * 4
+        off = a256(off) + P * 4
+        off = a256(off) + units * 4
+        return a256(off) + a256(8 * B * Hkv)
+
+    for group, split in ((32, True), (64, True), (128, False)):
+        d = _desc(kvq, batch=4, n_kv_heads=8, capacity=32768, k_bits=4, v_bits=4, group_size=group)
+        C = kvq.kvq_chunk_count(d, 64, 32768, 2048)
+        assert C == 16
+        want = expect(4, 8, 64, C, 4 * 8 * (2 if split else 1), 4 if split else 8)
+        assert kvq.kvq_workspace_bytes(d, 64, 32768, 2048) == want, group

@@ -295,3 +295,20 @@ def test_shared_workspace_float_and_integer_layers(oq):
         for name in ("k_codes", "v_codes", "k_scales", "v_scales"):
             a, b_ = getattr(pair[0], name), getattr(pair[1], name)
             assert (a is None and b_ is None) or torch.equal(a, b_), name
+
+
+@pytest.mark.parametrize("kb,vb", PAIRS)
+@pytest.mark.parametrize("group,chunk", [(32, 512), (64, 256), (32, 0)])
+def test_split_head_step(oq, kb, vb, group, chunk):
+    """Eight query heads per KV head with scale groups inside the head run as
+    two workgroup heads of four per cache head: one launch merging two
+    chunks, two launches over three, and the library's chunk."""
+    _pair(oq, kb, vb, group, B=2, H=2, G=8, HD=128, n=700, n_new=1, chunk=chunk, seed=kb * 7 + vb + group + chunk)
+
+
+def test_split_head_step_window_paged(oq):
+    """The split heads over a ring with anchors (three rows a step) and over
+    pages."""
+    _pair(oq, 4, 4, 32, B=2, H=2, G=8, HD=128, n=1500, n_new=3, chunk=512, seed=31, n_anchor=64, window=512)
+    _pair(oq, 8, 4, 64, B=3, H=2, G=8, HD=128, n=640, n_new=1, chunk=512, seed=32, page=128)
+    _pair(oq, 4, 8, 32, B=2, H=2, G=8, HD=64, n=900, n_new=1, chunk=256, seed=33, page=64)

@@ -146,3 +146,11 @@ def test_zero_point_stress(oq, kb, vb, case):
         _make_faint(K, V, q, G, softmax_default(HD), 512, 1000.0)
     run_zp(oq, kb, vb, 128, B=B, H=H, G=G, HD=HD, n=n, seed=0, chunk=2048, sigma=sigma, data=(K, V, q), codes=False)
     run_zp(oq, kb, vb, 32, B=B, H=H, G=G, HD=HD, n=n, seed=0, sigma=sigma, data=(K, V, q), fused=True, codes=False)
+
+
+@pytest.mark.parametrize("kb,vb", PAIRS)
+def test_zero_point_split_heads(oq, kb, vb):
+    """Eight query heads per KV head with 32-value groups (two workgroup heads
+    of four per cache head): the separate calls and the one-launch step."""
+    run_zp(oq, kb, vb, 32, B=2, H=2, G=8, HD=128, n=900, seed=70 + kb + vb, chunk=512)
+    run_zp(oq, kb, vb, 32, B=2, H=2, G=8, HD=128, n=900, seed=71 + kb + vb, chunk=512, fused=True, codes=False)
