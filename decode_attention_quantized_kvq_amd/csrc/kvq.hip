@@ -389,10 +389,13 @@ WsLayout ws_layout(int batch, int n_q_heads, int head_dim, int n_chunks, int n_k
 }
 
 // Offset of the ticket counters in a workspace of `bytes` bytes: the last
-// round_up(4 units, 256) bytes, aligned down to 256.  It depends only on the
-// extent the caller hands over and on the number of (sequence, KV head)
-// pairs, so calls of other geometries sharing that workspace (and passing the
-// same extent) never write over them: their own data ends before.
+// round_up(4 units, 256) bytes, aligned down to 256, units being the split
+// kernel's (sequence, workgroup head) pairs (one or two per (sequence, KV
+// head)).  It depends only on the extent the caller hands over and on the
+// geometry's units, and it lies inside the counter zone that ends every
+// cache's workspace, so calls of other geometries sharing that workspace
+// (passing the same extent, with as many (sequence, KV head) pairs) never
+// write over them: their own data ends before the zone.
 size_t cnt_offset(size_t bytes, size_t units)
 {
     return (bytes - align256(units * sizeof(int))) & ~(size_t)255;

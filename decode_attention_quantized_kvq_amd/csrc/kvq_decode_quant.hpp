@@ -117,9 +117,11 @@ template <int KB, int VB, int HD, int G> struct QT {
     static constexpr int V_CP = (KB == 8 && VB == 4) ? 0 : CP_NT;
 };
 
+// (Hkv below: n_kv_heads, the workgroup heads per sequence; the cache
+// buffers have n_kv_cache heads)
 struct QuantParams {
-    const uint8_t *k_codes;    // [B][Hkv][cap64/64][K_ROW/16][64][16]  (tiles of 64 slots, slice-major)
-    const uint8_t *v_codes;    // [B][Hkv][cap4/4][V_ROW][4]  (4 positions interleaved per byte)
+    const uint8_t *k_codes;    // [B][n_kv_cache][cap64/64][K_ROW/16][64][16]  (tiles of 64 slots, slice-major)
+    const uint8_t *v_codes;    // [B][n_kv_cache][cap4/4][V_ROW][4]  (4 positions interleaved per byte)
     const uint16_t *k_scales;
     const uint16_t *v_scales;
     const int32_t *qdig;       // [B*Hkv][qd_stride] packed query digits: [ND + 1][K_COLS][G] (digit-major; digit ND the extra low one);
@@ -141,10 +143,11 @@ struct QuantParams {
     int page_shift, pages_per_seq, n_pages;
     int max_len;
     int chunk, n_chunks;
-    // one decode step in one launch pair: after writing its partials each
-    // workgroup takes a ticket on cnt[b * Hkv + kvh] (zeroed by the query
-    // preparation before the launch) and the last one merges the G rows of
-    // its (sequence, KV head) into out.  cnt == nullptr: partials only.
+    // the in-kernel merge: after writing its partials each workgroup takes a
+    // ticket on cnt[b * Hkv + kvh] (zero when the launch starts: zeroed by
+    // the query preparation of a two-launch step, left zero by the previous
+    // one-launch step) and the last one merges the G rows of its unit into
+    // out, setting the counter back to zero.  cnt == nullptr: partials only.
     int *cnt;
     float *out;
     // one-launch decode step (step != 0; at most 2 chunks per (sequence, KV
@@ -210,7 +213,8 @@ __host__ __device__ inline QuantSmem quant_smem(int G, int HD, int vg, bool zp =
 }
 
 // ---------------------------------------------------------------------------
-// Query digits: one block per (sequence, KV head).  For head h of the group,
+// Query digits: one block per unit (sequence and KV head, or workgroup head
+// when a KV head's query heads are split over two).  For head h of the group,
 // s_q = max|q| / 30000 and q_int = rint(q / s_q) in [-30000, 30000], split
 // into ND balanced digits; digit j of the channels of key dword `col` is
 // packed like the codes (int4: channel 8col+i in nibble i; int8: channel
