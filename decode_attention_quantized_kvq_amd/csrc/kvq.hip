@@ -564,6 +564,9 @@ static int resolve_chunk(const kvq_cache *c, int n_q_heads, int max_seq_len, int
     int st = check_geometry(c);
     if (st) return st;
     if ((st = check_heads(c, n_q_heads))) return st;
+    if (unit_kv(c, n_q_heads / c->n_kv_heads) > 65535)   // the split kernel's grid y
+        return fail(KVQ_ERR_SHAPE, "n_kv_heads %d: G = 8 with scale groups runs two workgroup heads per KV head, "
+                    "at most 65535", c->n_kv_heads);
     if (max_seq_len < 1) return fail(KVQ_ERR_ARG, "max_seq_len %d < 1", max_seq_len);
     int ch = chunk_tokens;
     if (ch == 0) ch = auto_chunk(c, n_q_heads, max_seq_len);

@@ -134,7 +134,7 @@ extern "C" {
  * in the high half, 4-byte aligned: twice the symmetric codec's bytes.
  */
 typedef struct kvq_cache {
-    int32_t batch;
+    int32_t batch;        /* batch * n_kv_heads <= 65535 */
     int32_t n_kv_heads;
     int32_t head_dim;     /* 64 or 128 */
     int32_t capacity;     /* slots per (sequence, KV head) */
@@ -223,7 +223,10 @@ int kvq_append(const kvq_cache *c, const float *k_new, const float *v_new, int n
  * several devices be merged by one kvq_combine().
  *
  * q, out       : float32 [batch][n_q_heads][head_dim], 16-byte aligned.
- *                n_q_heads must be n_kv_heads * G with G in {1, 2, 4, 8}.
+ *                n_q_heads must be n_kv_heads * G with G in {1, 2, 4, 8}
+ *                (G = 8 on an 8/4-bit cache with scale groups inside the
+ *                head, which runs as two workgroup heads per KV head:
+ *                n_kv_heads <= 32767).
  * seq_len      : int32 [batch] in device memory, positions written so far
  *                (the newest included).
  * max_seq_len  : host upper bound on seq_len[]; sizes the grid.  Slots at or

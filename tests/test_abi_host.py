@@ -521,3 +521,15 @@ def test_split_head_workspace(kvq):
         assert C == 16
         want = expect(4, 8, 64, C, 4 * 8 * (2 if split else 1), 4 if split else 8)
         assert kvq.kvq_workspace_bytes(d, 64, 32768, 2048) == want, group
+
+
+def test_split_head_limit(kvq):
+    """G = 8 with scale groups runs two workgroup heads per KV head, so the
+    split kernel's grid allows at most 32767 KV heads there (65535 otherwise)."""
+    big = _desc(kvq, batch=1, n_kv_heads=40000, head_dim=128, capacity=256, k_bits=4, v_bits=4, group_size=32)
+    assert kvq.kvq_chunk_count(big, 4 * 40000, 256, 0) == 1     # G = 4: one head per workgroup
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_chunk_count(big, 8 * 40000, 256, 0)
+    assert e.value.status == kvq.KVQ_ERR_SHAPE
+    per_head = _desc(kvq, batch=1, n_kv_heads=40000, head_dim=128, capacity=256, k_bits=4, v_bits=4)
+    assert kvq.kvq_chunk_count(per_head, 8 * 40000, 256, 0) == 1   # one scale per head: no split
