@@ -27,6 +27,14 @@
 //    positions at once against value codes stored four positions
 //    interleaved and offset binary (code + 8 or code + 128, never negative);
 //    the offset's share, bias * sum(w), is subtracted once at the end.
+// Four query heads at head_dim 128 with one key scale per position and head
+// score their keys on the matrix cores instead (the integer dots above would
+// take 4 VALU instructions per position for the keys alone, and the VALU is
+// this kernel's busiest unit): per 16 positions two v_mfma_i32_16x16x64_i8
+// multiply a 16 x 64 operand holding each head's two base-256 digits of
+// q_int and its extra low digit with 64 channels of the 16 positions (int4
+// codes unpacked to bytes 16 code, int8 codes as stored), which gives the
+// same exact integer sums; the VALU only unpacks nibbles and scales.
 // Rounding happens only in the query's digits and in w_int
 // (|dw| <= N / 65534, relative to the sub-chunk's own largest weight
 // whatever the spread of the value scales or of the softmax);
@@ -39,7 +47,9 @@
 // sub-chunk:
 //   1. keys, one lane per position: scores -> LDS; the query digits are
 //      wave-uniform and come from SGPRs (prepared per (sequence, KV head) by
-//      qprep_kernel, or by the workgroup itself in the one-launch step);
+//      qprep_kernel, or by the workgroup itself in the one-launch step; on
+//      the matrix cores one lane per position and head, the digits held in
+//      VGPRs as the product's A operand);
 //      value scales -> LDS; the sub-chunk's score maxima (DPP).
 //   2. weights, one lane per four positions: p = 2^(z - max) and the
 //      products p * s_v, whose maximum per head and group (DPP) sets the
@@ -89,9 +99,17 @@ __host__ __device__ constexpr int qx_base(int KB) { return KB == 4 ? 14 : 254; }
 // [QS_GROUPS][G] for q_int and [QS_GROUPS][G] for the extra low digit
 constexpr int QS_GROUPS = 4;
 __host__ __device__ constexpr int qd_digits(int KB, int HD, int G) { return ((KB == 4 ? 4 : 2) + 1) * (HD * KB / 32) * G; }
+// Four query heads at head_dim 128 score their keys on the matrix cores
+// (v_mfma_i32_16x16x64_i8): the sixteen rows of the product are the four
+// heads' low and high base-256 digits of q_int, their extra low digits and
+// a zero row.  The digit block then also holds that operand, one byte per
+// digit, head and channel ([3][G][HD]).
+__host__ __device__ constexpr bool qd_mfma(int HD, int G) { return G == 4 && HD == 128; }
+__host__ __device__ constexpr int qd_mf(int KB, int HD, int G) { return qd_digits(KB, HD, G) + 2 * QS_GROUPS * G; }
+__host__ __device__ constexpr int qd_mf_words(int HD, int G) { return qd_mfma(HD, G) ? 3 * G * HD / 4 : 0; }
 __host__ __device__ constexpr int qd_stride(int KB, int HD, int G)
 {
-    return (qd_digits(KB, HD, G) + 2 * QS_GROUPS * G + 63) / 64 * 64;
+    return (qd_mf(KB, HD, G) + qd_mf_words(HD, G) + 63) / 64 * 64;
 }
 constexpr int QD_PF = 16;       // value group loads in flight per lane
 constexpr int W_RANGE = 32767;
@@ -304,6 +322,28 @@ __device__ __forceinline__ void qprep_core(const float *__restrict__ qh, int32_t
         qd[qd_digits(KB, HD, G) + g * G + h] = sum;
         qd[qd_digits(KB, HD, G) + (QS_GROUPS + g) * G + h] = sumx;
     }
+    // The matrix-core operand: q_int = 256 hi + lo with lo in [-128, 127]
+    // (so |hi| <= 118), and the extra low digit d, one byte each.  Against
+    // 4-bit keys each 32-channel block holds its 16 even channels, then its
+    // 16 odd ones (the order the unpacked nibbles of 16 key bytes arrive in);
+    // against 8-bit keys the channels keep their order.
+    if constexpr (qd_mfma(HD, G)) {
+        int8_t *mf = reinterpret_cast<int8_t *>(qd + qd_mf(KB, HD, G));
+        for (int i = tid; i < G * HD; i += 256) {
+            const int h = i / HD, c = i - h * HD;
+            const float sq = s_amax[h] / (float)Q_RANGE;
+            const float inv = sq > 0.0f ? 1.0f / sq : 0.0f;
+            const float qq = s_qv[h * HD + c];
+            const int qi = (int)fminf(fmaxf(rintf(qq * inv), -(float)Q_RANGE), (float)Q_RANGE);
+            const int lo = ((qi + 128) & 255) - 128, hi = (qi - lo) / 256;
+            const int dx = xq ? (int)fminf(fmaxf(rintf(fmaf(qq, inv, -(float)qi) * XB), -(float)XMAX), (float)XMAX)
+                              : 0;
+            const int pos = KB == 4 ? (c & ~31) + 16 * (c & 1) + ((c & 31) >> 1) : c;
+            mf[(0 * G + h) * HD + pos] = (int8_t)lo;
+            mf[(1 * G + h) * HD + pos] = (int8_t)hi;
+            mf[(2 * G + h) * HD + pos] = (int8_t)dx;
+        }
+    }
     __syncthreads();
 }
 
@@ -371,23 +411,32 @@ __device__ __forceinline__ void pack_w(uint32_t w0, uint32_t w1, uint32_t w2, ui
 // KG = scale groups per head row for both keys and values (1: groups of
 // head_dim, or one scale per position shared by all heads; 2 or 4: groups of
 // head_dim / KG channels); key dots are summed per group.
-// waves per SIMD the register allocation must allow: the int4 key and value
-// instances with G x KG <= 4 fit 128 VGPRs (4 waves) when asked to (left
-// alone the compiler takes a few more and drops to 3); the others, and the
-// zero-point instances (which would spill at 128), take what they need
-__host__ __device__ constexpr int qd_min_waves(int KB, int VB, int G, int KG, bool paged, bool zp)
+// Instances whose key scores run on the matrix cores: four query heads at
+// head_dim 128, one key scale per position and head, the symmetric codec.
+__host__ __device__ constexpr bool qd_mf_keys(int HD, int G, int KG, bool zp)
 {
-    return KB == 4 && VB == 4 && G * KG <= 4 && !zp ? 4 : 1;
+    return qd_mfma(HD, G) && KG == 1 && !zp;
+}
+// waves per SIMD the register allocation must allow: the int4 key and value
+// instances with G x KG <= 4 scoring keys on the VALU fit 128 VGPRs (4 waves)
+// when asked to (left alone the compiler takes a few more and drops to 3);
+// the others take what they need: the zero-point instances would spill at
+// 128, and the matrix-core ones (143 VGPRs for K4V4, 3 waves) ran 8 % slower
+// at 128 with spills than at 3 waves (212 against 177 us at 32K)
+__host__ __device__ constexpr int qd_min_waves(int KB, int VB, int HD, int G, int KG, bool paged, bool zp)
+{
+    return KB == 4 && VB == 4 && G * KG <= 4 && !zp && !qd_mf_keys(HD, G, KG, zp) ? 4 : 1;
 }
 
 // ZP: the zero-point codec (32-bit scale words: fp16 scale | zero << 16;
 // keys stored as code - 2^(KB-1), values as the code).
 template <int KB, int VB, int HD, int G, int KG, bool PAGED, bool ZP = false>
-__global__ __launch_bounds__(QD_THREADS) __attribute__((amdgpu_waves_per_eu(qd_min_waves(KB, VB, G, KG, PAGED, ZP))))
+__global__ __launch_bounds__(QD_THREADS) __attribute__((amdgpu_waves_per_eu(qd_min_waves(KB, VB, HD, G, KG, PAGED, ZP))))
 void decode_quant_kernel(QuantParams p)
 {
     using T = QT<KB, VB, HD, G>;
     constexpr int S = qd_sub(G, KG, ZP);
+    constexpr bool MF = qd_mf_keys(HD, G, KG, ZP);   // key scores on the matrix cores
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -559,6 +608,7 @@ void decode_quant_kernel(QuantParams p)
     const KVQ_CONST int32_t *qd = (const KVQ_CONST int32_t *)(p.qdig + qslot * qd_stride(KB, HD, G));
     constexpr float XINV = 1.0f / (float)qx_base(KB);
     const uint32_t ko = lane * 16;
+    const uint32_t mko = (lane >> 4) * 1024 + (lane & 15) * 16;
     const uint32_t kso = lane * p.k_sc_t * SCB, vso = lane * p.v_sc_t * SCB;
     struct Tile {
         uint4 k[T::K_U4];
@@ -581,8 +631,23 @@ void decode_quant_kernel(QuantParams p)
         // (immediate offsets reach 4 KiB: int8 rows use a second descriptor
         // for slices 4..7)
         const rsrc_t krs2 = make_rsrc(kb + 4096, kbytes > 4096 ? kbytes - 4096 : 0);
+        if constexpr (MF) {
+            // the matrix-core layout: for each 16-position block t of the
+            // tile, lane l reads 16 bytes of position 16 t + l % 16, slice
+            // l / 16 (int4) or slices l / 16 and 4 + l / 16 (int8)
 #pragma unroll
-        for (int u4 = 0; u4 < T::K_U4; u4++) d.k[u4] = bld_u4<CP_NT>(u4 < 4 ? krs : krs2, ko + (u4 % 4) * 1024);
+            for (int t = 0; t < 4; t++) {
+                if constexpr (KB == 4) {
+                    d.k[t] = bld_u4<CP_NT>(krs, mko + t * 256);
+                } else {
+                    d.k[2 * t] = bld_u4<CP_NT>(krs, mko + t * 256);
+                    d.k[2 * t + 1] = bld_u4<CP_NT>(krs2, mko + t * 256);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int u4 = 0; u4 < T::K_U4; u4++) d.k[u4] = bld_u4<CP_NT>(u4 < 4 ? krs : krs2, ko + (u4 % 4) * 1024);
+        }
         // (a position's scale words are contiguous: one load each)
         if constexpr (SW == 1 && SCB * KG == 2) {
             d.ks[0] = bld_u16(ksrs, kso);
@@ -601,6 +666,21 @@ void decode_quant_kernel(QuantParams p)
         }
     };
     float mloc[G];                                   // per-lane score maxima of the current sub-chunk
+    float mown = -INFINITY;                          // (matrix cores) the same for the lane's own head, lane / 16
+    // the matrix-core query operand (A: row l % 16 = head (l % 16) / 4, digit
+    // lo, hi, extra, zero; the bytes of k-block l / 16)
+    i32x4_t mfa0 = {0, 0, 0, 0}, mfa1 = {0, 0, 0, 0};
+    if constexpr (MF) {
+        const int32_t *qm = p.qdig + qslot * qd_stride(KB, HD, G) + qd_mf(KB, HD, G);
+        const int r = lane & 15, hh = r >> 2, j = r & 3, g = lane >> 4;
+        if (j < 3) {
+            const uint8_t *src = reinterpret_cast<const uint8_t *>(qm) + (j * G + hh) * HD;
+            const uint4 a0 = ld_u4(src + (KB == 4 ? 32 * g : 16 * g));
+            const uint4 a1 = ld_u4(src + (KB == 4 ? 32 * g + 16 : 64 + 16 * g));
+            mfa0 = i32x4_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w};
+            mfa1 = i32x4_t{(int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        }
+    }
     // scores of one tile (tb: first position of the tile within the wave;
     // sc0: first position of the sub-chunk)
     auto compute = [&](int tb, int sc0, const Tile &c) {
@@ -609,6 +689,48 @@ void decode_quant_kernel(QuantParams p)
         // (zero past the wave's range: the load returned zero; every tile of
         // the sub-chunk lies inside its S rows of LDS)
         vs_wr(t - sc0, c.vs);
+        if constexpr (MF) {
+            // Per 16-position block: D = A B, A the query's digit rows, B 64
+            // channels of the block's 16 positions: int4 keys unpacked to
+            // bytes 16 code (each nibble moved to the top of its byte keeps
+            // its sign: even channels from the low nibbles, odd from the high
+            // ones), int8 codes as stored.  Lane l ends with head l / 16's
+            // sums over its low, high and extra digits for position l % 16:
+            // Σ q_int code = (256 hi + lo) / KS exactly (KS = 16 for int4).
+            // this lane's position's key scale / KS
+            const float skl = f16_bits_to_f32((uint16_t)sc_of(c.ks, 0)) * (KB == 4 ? 0.0625f : 1.0f);
+            const int n = lane & 15, hq = lane >> 4;
+#pragma unroll
+            for (int tt = 0; tt < 4; tt++) {
+                i32x4_t b0, b1;
+                if constexpr (KB == 4) {
+                    const uint4 w = c.k[tt];
+                    b0 = i32x4_t{(int)((w.x << 4) & 0xF0F0F0F0u), (int)((w.y << 4) & 0xF0F0F0F0u),
+                                 (int)((w.z << 4) & 0xF0F0F0F0u), (int)((w.w << 4) & 0xF0F0F0F0u)};
+                    b1 = i32x4_t{(int)(w.x & 0xF0F0F0F0u), (int)(w.y & 0xF0F0F0F0u), (int)(w.z & 0xF0F0F0F0u),
+                                 (int)(w.w & 0xF0F0F0F0u)};
+                } else {
+                    const uint4 w0 = c.k[2 * tt], w1 = c.k[2 * tt + 1];
+                    b0 = i32x4_t{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w};
+                    b1 = i32x4_t{(int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+                }
+                i32x4_t acc = mfma_i8(mfa0, b0, i32x4_t{0, 0, 0, 0});
+                acc = mfma_i8(mfa1, b1, acc);
+                const int pos = 16 * tt + n;         // within the tile
+                // the key scale of the position, from the lane that loaded it
+                const float sk = __builtin_bit_cast(
+                    float, __builtin_amdgcn_ds_bpermute(pos * 4, __builtin_bit_cast(int, skl)));
+                float z = (float)(acc[1] * 256 + acc[0]) * sk;
+                if (xq) z = fmaf((float)acc[2], sk * XINV, z);
+                z = tb + pos < nw ? z : -INFINITY;   // past the wave's range: -inf
+                mown = fmax_nc(mown, z);
+                zs[(size_t)(tb + pos - sc0) * G + hq] = z;
+                // one block at a time (interleaved, the blocks' operands
+                // would not fit the registers of four waves per SIMD)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            return;
+        }
         // an opaque zero offset, redefined every tile, keeps the digit loads
         // inside the loop (hoisted, they would need hundreds of SGPRs)
         int qz;
@@ -812,6 +934,7 @@ void decode_quant_kernel(QuantParams p)
         // ---------------- pass 1: scores of the sub-chunk ----------------------
 #pragma unroll
         for (int h = 0; h < G; h++) mloc[h] = -INFINITY;
+        mown = -INFINITY;
         // (tiles run in pairs, both halves unconditionally: a half past the
         // end sees only invalid lanes and zero rows, and the code stays free
         // of a merge point that would send the two register sets through
@@ -834,8 +957,16 @@ void decode_quant_kernel(QuantParams p)
         }
         compute(tb + 64, sc0, tb_);
         float ms[G];                                 // sub-chunk score maxima, wave-uniform
+        if constexpr (MF) {
+            // lanes 16 h .. 16 h + 15 hold head h
+            const float mr = row_max_u(mown);
 #pragma unroll
-        for (int h = 0; h < G; h++) ms[h] = wave_max_u(mloc[h]);
+            for (int h = 0; h < G; h++)
+                ms[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mr), 16 * h));
+        } else {
+#pragma unroll
+            for (int h = 0; h < G; h++) ms[h] = wave_max_u(mloc[h]);
+        }
 
         // ---------------- pass 2: weights, one lane per 4 positions ---------------
         // (a) p = 2^(qs * (z - ms)) <= 1, written over its score, and the

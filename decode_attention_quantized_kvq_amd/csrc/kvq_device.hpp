@@ -171,5 +171,27 @@ __device__ __forceinline__ int f2ord(float x)
 }
 __device__ __forceinline__ float ord2f(int k) { return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7FFFFFFF)); }
 __device__ __forceinline__ float wave_max_u(float v) { return ord2f(wave_max_ui(f2ord(v))); }
+// Maximum over each 16-lane row (the four in-row steps above): every lane
+// ends with its row's maximum.  All 64 lanes must be active.
+__device__ __forceinline__ float row_max_u(float x)
+{
+    int v = f2ord(x);
+    v = max(v, dpp_i<0xB1, 0xF, true>(0, v));
+    v = max(v, dpp_i<0x4E, 0xF, true>(0, v));
+    v = max(v, dpp_i<0x141, 0xF, true>(0, v));
+    v = max(v, dpp_i<0x140, 0xF, true>(0, v));
+    return ord2f(v);
+}
+
+// ------------------------------------------------------ matrix cores
+// v_mfma_i32_16x16x64_i8: D = A B + C for a 16 x 64 int8 A, a 64 x 16 int8
+// B and 16 x 16 int32 C / D.  Lane l holds 16 bytes of row l % 16 of A and
+// the same 16 k indices of column l % 16 of B (the k indices depend only on
+// l / 16), and D[4 (l / 16) + i][l % 16] in element i of its result.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t mfma_i8(i32x4_t a, i32x4_t b, i32x4_t c)
+{
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
 
 } // namespace kvq

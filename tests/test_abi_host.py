@@ -294,8 +294,10 @@ def test_workspace_and_chunks(kvq):
     # one, per value; then two sums per scale group and head for the zero-point
     # codec; each unit's block padded to 256 bytes) and scales follow the partials,
     # then one extra-digit flag per (sequence, KV head) and the ticket counters'
-    # zone (room for two per (sequence, KV head))
-    words = -(-(16 * 5 * 4 + 2 * 4 * 4) // 64) * 64
+    # zone (room for two per (sequence, KV head)); four heads at head_dim 128
+    # add the matrix-core operand, one byte per digit (low, high, extra), head
+    # and channel
+    words = -(-(16 * 5 * 4 + 2 * 4 * 4 + 3 * 4 * 128 // 4) // 64) * 64
     digits = 32 * 8 * words * 4 + P * 4
     counters = 32 * 8 * 4 + 2 * 32 * 8 * 4
     ws = kvq.kvq_workspace_bytes(d, 32, 32768, 0)
@@ -505,7 +507,8 @@ def test_split_head_workspace(kvq):
     a256 = lambda x: (x + 255) // 256 * 256
 
     def stride(G):                                   # int32 words of one unit's digits (int4 keys, HD 128)
-        return -(-(5 * 16 * G + 2 * 4 * G) // 64) * 64
+        mf = 3 * G * 128 // 4 if G == 4 else 0       # the matrix-core operand of four heads
+        return -(-(5 * 16 * G + 2 * 4 * G + mf) // 64) * 64
 
     def expect(B, Hkv, Hq, C, units, G):
         P = B * Hq
