@@ -412,10 +412,10 @@ __device__ __forceinline__ void pack_w(uint32_t w0, uint32_t w1, uint32_t w2, ui
 // head_dim, or one scale per position shared by all heads; 2 or 4: groups of
 // head_dim / KG channels); key dots are summed per group.
 // Instances whose key scores run on the matrix cores: four query heads at
-// head_dim 128, one key scale per position and head, the symmetric codec.
-__host__ __device__ constexpr bool qd_mf_keys(int HD, int G, int KG, bool zp)
+// head_dim 128 with the symmetric codec (1, 2 or 4 scale groups per head).
+__host__ __device__ constexpr bool qd_mf_keys(int KB, int VB, int HD, int G, int KG, bool zp)
 {
-    return qd_mfma(HD, G) && KG == 1 && !zp;
+    return qd_mfma(HD, G) && !zp && (KG < 4 || (KB == 4 && VB == 4));
 }
 // waves per SIMD the register allocation must allow: the int4 key and value
 // instances with G x KG <= 4 scoring keys on the VALU fit 128 VGPRs (4 waves)
@@ -425,7 +425,7 @@ __host__ __device__ constexpr bool qd_mf_keys(int HD, int G, int KG, bool zp)
 // at 128 with spills than at 3 waves (212 against 177 us at 32K)
 __host__ __device__ constexpr int qd_min_waves(int KB, int VB, int HD, int G, int KG, bool paged, bool zp)
 {
-    return KB == 4 && VB == 4 && G * KG <= 4 && !zp && !qd_mf_keys(HD, G, KG, zp) ? 4 : 1;
+    return qd_mf_keys(KB, VB, HD, G, KG, zp) ? 3 : KB == 4 && VB == 4 && G * KG <= 4 && !zp ? 4 : 1;
 }
 
 // ZP: the zero-point codec (32-bit scale words: fp16 scale | zero << 16;
@@ -436,7 +436,7 @@ void decode_quant_kernel(QuantParams p)
 {
     using T = QT<KB, VB, HD, G>;
     constexpr int S = qd_sub(G, KG, ZP);
-    constexpr bool MF = qd_mf_keys(HD, G, KG, ZP);   // key scores on the matrix cores
+    constexpr bool MF = qd_mf_keys(KB, VB, HD, G, KG, ZP);   // key scores on the matrix cores
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -667,18 +667,51 @@ void decode_quant_kernel(QuantParams p)
     };
     float mloc[G];                                   // per-lane score maxima of the current sub-chunk
     float mown = -INFINITY;                          // (matrix cores) the same for the lane's own head, lane / 16
-    // the matrix-core query operand (A: row l % 16 = head (l % 16) / 4, digit
-    // lo, hi, extra, zero; the bytes of k-block l / 16)
-    i32x4_t mfa0 = {0, 0, 0, 0}, mfa1 = {0, 0, 0, 0};
+    // The matrix-core query operands, one per row set and MFMA m = 0, 1 of a
+    // 16-position block (m: int4 keys, even / odd channels; int8 keys,
+    // slices 0-3 / 4-7).  Lane l supplies row l % 16 of A over k-block
+    // (m, l / 16): channels 32 (l / 16) .. + 31 (int4) or slice 4 m + l / 16
+    // (int8), scale group mf_grp(m, l / 16).  Rows 4 h + i belong to head h
+    // (so that lane l of the product holds head l / 16):
+    //   one scale group: one set, i = low, high and extra digit, zero;
+    //   2 or 4 groups: sets P = 0 .. KG / 2 - 1, i = 2 p + d for digit d
+    //   (low, high) of group 2 P + p, the A bytes zero in k-blocks of other
+    //   groups; then the extra digit's set, i = the group.
+    // A set whose every k-block of some m lies outside its groups skips that
+    // MFMA (int8 keys with 4 groups: each set sees one m).
+    constexpr int MF_NP = KG == 1 ? 1 : KG / 2;      // sets of low and high digits
+    constexpr int MF_NS = KG == 1 ? 1 : MF_NP + 1;   // + the extra digit's set
+    auto mf_grp = [](int m, int L) { return KB == 4 ? L * KG / 4 : (4 * m + L) * KG / 8; };
+    auto mf_live = [&](int P, int m) {
+        bool any = false;
+        for (int L = 0; L < 4; L++) any |= KG == 1 || mf_grp(m, L) / 2 == P;
+        return any;
+    };
+    // (the extra digit's set of 2 or 4 groups is loaded per block, and only
+    // when the query carries that digit: held throughout, its registers
+    // would cost a wave per SIMD)
+    i32x4_t mfa[MF_NP][2];
+#pragma unroll
+    for (int st = 0; st < MF_NP; st++) mfa[st][0] = mfa[st][1] = i32x4_t{0, 0, 0, 0};
+    const uint8_t *mfq = nullptr;                    // this lane's extra-digit bytes (2 or 4 groups)
     if constexpr (MF) {
-        const int32_t *qm = p.qdig + qslot * qd_stride(KB, HD, G) + qd_mf(KB, HD, G);
-        const int r = lane & 15, hh = r >> 2, j = r & 3, g = lane >> 4;
-        if (j < 3) {
-            const uint8_t *src = reinterpret_cast<const uint8_t *>(qm) + (j * G + hh) * HD;
-            const uint4 a0 = ld_u4(src + (KB == 4 ? 32 * g : 16 * g));
-            const uint4 a1 = ld_u4(src + (KB == 4 ? 32 * g + 16 : 64 + 16 * g));
-            mfa0 = i32x4_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w};
-            mfa1 = i32x4_t{(int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        const uint8_t *qm = reinterpret_cast<const uint8_t *>(p.qdig + qslot * qd_stride(KB, HD, G) + qd_mf(KB, HD, G));
+        const int r = lane & 15, hh = r >> 2, i = r & 3, L = lane >> 4;
+        auto digits = [&](int d, int m) {            // 16 bytes of digit plane d, head hh, k-block (m, L)
+            const uint4 a = ld_u4(qm + (d * G + hh) * HD + (KB == 4 ? 32 * L + 16 * m : 16 * (4 * m + L)));
+            return i32x4_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
+        };
+        mfq = qm + (2 * G + hh) * HD + (KB == 4 ? 32 * L : 16 * L);
+#pragma unroll
+        for (int m = 0; m < 2; m++) {
+            if constexpr (KG == 1) {
+                if (i < 3) mfa[0][m] = digits(i, m);
+            } else {
+                const int grp = mf_grp(m, L);
+#pragma unroll
+                for (int P = 0; P < MF_NP; P++)
+                    if (mf_live(P, m) && grp == 2 * P + (i >> 1)) mfa[P][m] = digits(i & 1, m);
+            }
         }
     }
     // scores of one tile (tb: first position of the tile within the wave;
@@ -695,38 +728,64 @@ void decode_quant_kernel(QuantParams p)
             // bytes 16 code (each nibble moved to the top of its byte keeps
             // its sign: even channels from the low nibbles, odd from the high
             // ones), int8 codes as stored.  Lane l ends with head l / 16's
-            // sums over its low, high and extra digits for position l % 16:
-            // Σ q_int code = (256 hi + lo) / KS exactly (KS = 16 for int4).
-            // this lane's position's key scale / KS
-            const float skl = f16_bits_to_f32((uint16_t)sc_of(c.ks, 0)) * (KB == 4 ? 0.0625f : 1.0f);
+            // sums for position l % 16 over its low, high and extra digits
+            // (per scale group): Σ q_int code = (256 hi + lo) / KS exactly,
+            // KS = 16 for int4 keys; each group's score then as on the VALU.
+            constexpr float KSI = KB == 4 ? 0.0625f : 1.0f;
             const int n = lane & 15, hq = lane >> 4;
 #pragma unroll
             for (int tt = 0; tt < 4; tt++) {
-                i32x4_t b0, b1;
+                i32x4_t bk[2];
                 if constexpr (KB == 4) {
                     const uint4 w = c.k[tt];
-                    b0 = i32x4_t{(int)((w.x << 4) & 0xF0F0F0F0u), (int)((w.y << 4) & 0xF0F0F0F0u),
-                                 (int)((w.z << 4) & 0xF0F0F0F0u), (int)((w.w << 4) & 0xF0F0F0F0u)};
-                    b1 = i32x4_t{(int)(w.x & 0xF0F0F0F0u), (int)(w.y & 0xF0F0F0F0u), (int)(w.z & 0xF0F0F0F0u),
-                                 (int)(w.w & 0xF0F0F0F0u)};
+                    bk[0] = i32x4_t{(int)((w.x << 4) & 0xF0F0F0F0u), (int)((w.y << 4) & 0xF0F0F0F0u),
+                                    (int)((w.z << 4) & 0xF0F0F0F0u), (int)((w.w << 4) & 0xF0F0F0F0u)};
+                    bk[1] = i32x4_t{(int)(w.x & 0xF0F0F0F0u), (int)(w.y & 0xF0F0F0F0u), (int)(w.z & 0xF0F0F0F0u),
+                                    (int)(w.w & 0xF0F0F0F0u)};
                 } else {
                     const uint4 w0 = c.k[2 * tt], w1 = c.k[2 * tt + 1];
-                    b0 = i32x4_t{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w};
-                    b1 = i32x4_t{(int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+                    bk[0] = i32x4_t{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w};
+                    bk[1] = i32x4_t{(int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
                 }
-                i32x4_t acc = mfma_i8(mfa0, b0, i32x4_t{0, 0, 0, 0});
-                acc = mfma_i8(mfa1, b1, acc);
+                i32x4_t acc[MF_NS];
+#pragma unroll
+                for (int st = 0; st < MF_NP; st++) {
+                    acc[st] = i32x4_t{0, 0, 0, 0};
+#pragma unroll
+                    for (int m = 0; m < 2; m++)
+                        if (mf_live(st, m)) acc[st] = mfma_i8(mfa[st][m], bk[m], acc[st]);
+                }
+                if (KG > 1 && xq) {
+                    // rows 4 h + g: the extra digit of group g, zero in other groups' k-blocks
+                    acc[MF_NS - 1] = i32x4_t{0, 0, 0, 0};
+#pragma unroll
+                    for (int m = 0; m < 2; m++) {
+                        const uint4 a = ld_u4(mfq + (KB == 4 ? 16 * m : 64 * m));
+                        const bool on = mf_grp(m, lane >> 4) == (lane & 3);
+                        const i32x4_t ax = i32x4_t{on ? (int)a.x : 0, on ? (int)a.y : 0, on ? (int)a.z : 0,
+                                                   on ? (int)a.w : 0};
+                        acc[MF_NS - 1] = mfma_i8(ax, bk[m], acc[MF_NS - 1]);
+                    }
+                }
                 const int pos = 16 * tt + n;         // within the tile
-                // the key scale of the position, from the lane that loaded it
-                const float sk = __builtin_bit_cast(
-                    float, __builtin_amdgcn_ds_bpermute(pos * 4, __builtin_bit_cast(int, skl)));
-                float z = (float)(acc[1] * 256 + acc[0]) * sk;
-                if (xq) z = fmaf((float)acc[2], sk * XINV, z);
+                // the key scale words of the position, from the lane that loaded them
+                uint32_t ksw[SW];
+#pragma unroll
+                for (int w = 0; w < SW; w++) ksw[w] = (uint32_t)__builtin_amdgcn_ds_bpermute(pos * 4, (int)c.ks[w]);
+                float z = 0.0f;
+#pragma unroll
+                for (int g = 0; g < KG; g++) {
+                    const float sk = f16_bits_to_f32((uint16_t)sc_of(ksw, g)) * KSI;
+                    const int e = KG == 1 ? 0 : 2 * (g & 1);
+                    const float sg = (float)(acc[g >> 1][e + 1] * 256 + acc[g >> 1][e]);
+                    z = g == 0 ? sg * sk : fmaf(sg, sk, z);
+                    if (xq) z = fmaf((float)(KG == 1 ? acc[0][2] : acc[MF_NS - 1][g]), sk * XINV, z);
+                }
                 z = tb + pos < nw ? z : -INFINITY;   // past the wave's range: -inf
                 mown = fmax_nc(mown, z);
                 zs[(size_t)(tb + pos - sc0) * G + hq] = z;
-                // one block at a time (interleaved, the blocks' operands
-                // would not fit the registers of four waves per SIMD)
+                // (blocks in order: a block's operands are dead before the
+                // next block's are made)
                 __builtin_amdgcn_sched_barrier(0);
             }
             return;

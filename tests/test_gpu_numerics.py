@@ -190,7 +190,7 @@ def test_faint_rows_large_values(oq, kb, vb, group, v_factor):
 
 
 @pytest.mark.parametrize("kb,vb", PAIRS)
-@pytest.mark.parametrize("group", GROUPS)
+@pytest.mark.parametrize("group", GROUPS + [64])
 @pytest.mark.parametrize("factor", [4.0, 100.0])
 def test_query_outlier_channel(oq, kb, vb, group, factor):
     """One query channel x 100 (the query takes its extra low digit) and
