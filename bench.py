@@ -599,7 +599,7 @@ def record_traffic(fetch_csv: str, write_csv: str, workload: str = "k4v4-32k", l
     write = counters["write"]["decode_raw"] * counters["write"]["factor"]
     rec.setdefault("workloads", {})[f"{w.name}/{mode.name}"] = {
         "kernel": kernel,
-        "bytes_per_launch": round(fetch + write),
+        "bytes_per_launch": round(fetch) + round(write),
         "fetch_bytes": round(fetch),
         "write_bytes": round(write),
         "algorithmic_bytes": split_bytes(w, mode),
