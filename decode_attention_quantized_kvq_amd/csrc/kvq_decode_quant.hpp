@@ -437,6 +437,11 @@ void decode_quant_kernel(QuantParams p)
     using T = QT<KB, VB, HD, G>;
     constexpr int S = qd_sub(G, KG, ZP);
     constexpr bool MF = qd_mf_keys(KB, VB, HD, G, KG, ZP);   // key scores on the matrix cores
+    // value sums on the matrix cores too (int4 keys and values, one scale
+    // group): the weights become two signed bytes, a low one in [-128, 127]
+    // and a high one in [0, 127], so their fixed-point range is 32639
+    constexpr bool MV = MF && KB == 4 && VB == 4 && KG == 1;
+    constexpr int WR = MV ? 32639 : W_RANGE;
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -973,6 +978,36 @@ void decode_quant_kernel(QuantParams p)
         }
     };
 
+    // ---- values on the matrix cores (MV): per 64-position block of the
+    // sub-chunk, 8 products D += A B over 16 channels each.  A: lane l holds
+    // row l % 16 = 4 h + b (b = 0, 1: head h's signed low and high weight
+    // bytes; b = 2, 3 zero) over the block's groups 4 (l / 16) .. + 3 (16
+    // positions, the block's weight words in LDS).  B: column n = l % 16 of
+    // product 4 t + q holds channel 64 t + 4 n + q of those 16 positions, the
+    // stored nibbles (code + 8) as bytes; lane l loads bytes 32 t + 2 n and
+    // + 1 of its four groups, one 8-byte load per group and t (16 lanes read
+    // 128 contiguous bytes).  D: lane l holds head l / 16's two sums for
+    // channel 64 t + 4 (l % 16) + q.
+    uint32_t vx[8][2];                               // the next block's value words, [t][group][byte]
+    auto vload_mv = [&](int gb) {                    // gb: the block's first group (within the wave)
+        const int u = unit_of(4 * gb);
+        const int uu = u < 0 ? 0 : u;
+        const uint8_t *vb = p.v_codes + (((size_t)uu * p.n_kv_cache + kvc) * p.cap4 + slot_of(4 * gb)) * T::V_ROW;
+        const int left = u < 0 ? 0 : (ngw - gb) * 4 * T::V_ROW;   // bytes of the wave's range from the block on
+        const rsrc_t rs = make_rsrc(vb, (uint32_t)max(left, 0));
+        const uint32_t o = (lane >> 4) * 16 * T::V_ROW + (lane & 15) * 8;
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const uint2 v = bld_u2<T::V_CP>(rs, o + i * 4 * T::V_ROW + t * 128);
+                vx[4 * t + i][0] = v.x;
+                vx[4 * t + i][1] = v.y;
+            }
+    };
+    i32x4_t vacc[8];
+    float afm[8];                                    // (MV) the lane's channels 64 t + 4 n + q of head l / 16
+
     // ---- the wave's running result: max M (unscaled score units), per-lane
     // partial sum of p, and the lane's output channels, all relative to M
     float M[G], lsum[G], af[G][T::V_ACC], bsum[KG][G];
@@ -985,6 +1020,8 @@ void decode_quant_kernel(QuantParams p)
 #pragma unroll
         for (int c = 0; c < T::V_ACC; c++) af[h][c] = 0.0f;
     }
+#pragma unroll
+    for (int t = 0; t < 8; t++) afm[t] = 0.0f;
 
     Tile ta, tb_;
     load(0, ta);
@@ -1009,7 +1046,9 @@ void decode_quant_kernel(QuantParams p)
         compute(tb, sc0, ta);
         // the sub-chunk's first batch of value loads, in flight during the
         // last key tile and the weights pass
-        {
+        if constexpr (MV) {
+            vload_mv(sc0 >> 2);
+        } else {
             const VRs rs = vrsrc(sc0 >> 2);
 #pragma unroll
             for (int f = 0; f < PF; f++) vload(f, rs);
@@ -1121,7 +1160,7 @@ void decode_quant_kernel(QuantParams p)
 #pragma unroll
                 for (int h = 0; h < G; h++) {
                     nrm[g][h] = __builtin_bit_cast(float, wave_max_ui(pmx[g][h]));
-                    fsc[g][h] = nrm[g][h] > 0.0f ? (float)W_RANGE * __builtin_amdgcn_rcpf(nrm[g][h]) : 0.0f;
+                    fsc[g][h] = nrm[g][h] > 0.0f ? (float)WR * __builtin_amdgcn_rcpf(nrm[g][h]) : 0.0f;
                 }
 #pragma unroll
             for (int t = 0; t < TURNS; t++) {
@@ -1160,10 +1199,24 @@ void decode_quant_kernel(QuantParams p)
                             uint32_t wb[4];
 #pragma unroll
                             for (int k = 0; k < 4; k++)
-                                wb[k] = __builtin_bit_cast(uint32_t, KG == 1 ? fmaf(pr[k][h], fsc[g][h], MAGIC)
+                                wb[k] = __builtin_bit_cast(uint32_t, KG == 1 ? fmaf(pr[k][h], fsc[g][h], MV ? MAGIC + 128.0f : MAGIC)
                                                                              : fmaf(pr[k][h] * fsc[g][h], sv[k], MAGIC));
                             uint32_t lo, hi;
                             pack_w(wb[0], wb[1], wb[2], wb[3], lo, hi);
+                            if constexpr (MV) {
+                                // the bytes of w + 128: the high byte is w's
+                                // signed high digit, the low byte less 128
+                                // its signed low digit (the same bits as w's
+                                // low byte with the top one flipped);
+                                // block-major words, [64 positions][head]
+                                // [low, high][16 groups]
+                                wsl[g][h] += (int)__builtin_amdgcn_udot4(lo, 0x01010101u, 0u, false)
+                                           + 256 * (int)__builtin_amdgcn_udot4(hi, 0x01010101u, 0u, false) - 512;
+                                uint32_t *dm = wdw + (size_t)((grp >> 4) * G + h) * 32 + (grp & 15);
+                                dm[0] = lo ^ 0x80808080u;
+                                dm[16] = hi;
+                                continue;
+                            }
                             if constexpr (ZP) {
                                 wzl[g][h] = __builtin_amdgcn_udot4(lo, zb, wzl[g][h], false);
                                 wzh[g][h] = __builtin_amdgcn_udot4(hi, zb, wzh[g][h], false);
@@ -1180,11 +1233,42 @@ void decode_quant_kernel(QuantParams p)
         }
 
         // ---------------- pass 3: values of the sub-chunk ------------------------
+        if constexpr (MV) {
 #pragma unroll
-        for (int h = 0; h < G; h++)
+            for (int t = 0; t < 8; t++) vacc[t] = i32x4_t{0, 0, 0, 0};
+            const int g0 = sc0 >> 2;                 // first group of the sub-chunk (within the wave)
+            const int nblk = (ns + 63) >> 6;         // its 64-position blocks
+            const int r = lane & 15, L = lane >> 4;
+            for (int bb = 0; bb < nblk; bb++) {
+                // the block's weight bytes (rows with b >= 2: zero); groups
+                // past the sub-chunk's positions meet zero value bytes
+                i32x4_t a = {0, 0, 0, 0};
+                if ((r & 3) < 2) {
+                    const uint4 w = *reinterpret_cast<const uint4 *>(wdw + (size_t)((bb * G + (r >> 2)) * 2 + (r & 3)) * 16 + 4 * L);
+                    a = i32x4_t{(int)w.x, (int)w.y, (int)w.z, (int)w.w};
+                }
 #pragma unroll
-            for (int c = 0; c < T::V_ACC; c++) accl[h][c] = acch[h][c] = 0u;
-        {
+                for (int t = 0; t < 2; t++) {
+                    i32x4_t bv[4];                   // channels 64 t + 4 n + q
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        bv[0][i] = (int)(vx[4 * t + i][0] & 0x0F0F0F0Fu);
+                        bv[1][i] = (int)((vx[4 * t + i][0] >> 4) & 0x0F0F0F0Fu);
+                        bv[2][i] = (int)(vx[4 * t + i][1] & 0x0F0F0F0Fu);
+                        bv[3][i] = (int)((vx[4 * t + i][1] >> 4) & 0x0F0F0F0Fu);
+                    }
+                    if (t == 1 && bb + 1 < nblk) vload_mv(g0 + 16 * (bb + 1));
+#pragma unroll
+                    for (int q = 0; q < 4; q++) vacc[4 * t + q] = mfma_i8(a, bv[q], vacc[4 * t + q]);
+                }
+            }
+            // the next sub-chunk's first key tile
+            load(sc0 + S, ta);
+        } else {
+#pragma unroll
+            for (int h = 0; h < G; h++)
+#pragma unroll
+                for (int c = 0; c < T::V_ACC; c++) accl[h][c] = acch[h][c] = 0u;
             // Full batches are straight-line code (the weight reads of later
             // groups are issued early); a partial last batch checks each group.
             const int g0 = sc0 >> 2;                 // first group of the sub-chunk (within the wave)
@@ -1218,6 +1302,7 @@ void decode_quant_kernel(QuantParams p)
         // w_int, the same for every channel) is kept as per-lane partial sums
         // and taken out once at the end.
         {
+            float fo_h[G], cs_h[G];                  // (MV) per head: the old part's factor, the new sums' scale
 #pragma unroll
             for (int h = 0; h < G; h++) {
                 const float Mn = fmaxf(M[h], ms[h]);
@@ -1228,13 +1313,16 @@ void decode_quant_kernel(QuantParams p)
                 float cg[KG];                        // c = fn * N / 32767 per scale group
 #pragma unroll
                 for (int g = 0; g < KG; g++) {
-                    cg[g] = fn * nrm[g][h] * (1.0f / (float)W_RANGE);
+                    cg[g] = fn * nrm[g][h] * (1.0f / (float)WR);
                     // the stored values' offset, in w_int units: bias * sum w
                     // (offset binary), or sum w * zero (zero point)
                     const float woff = ZP ? fmaf(256.0f, (float)wzh[g][h], (float)wzl[g][h])
                                           : (float)wsl[g][h] * (VB == 4 ? 8.0f : 128.0f);
                     bsum[g][h] = fmaf(bsum[g][h], fo, woff * cg[g]);
                 }
+                fo_h[h] = fo;
+                cs_h[h] = cg[0];
+                if constexpr (MV) continue;
                 // 256 * hi + lo is exact in uint32 (hi bytes <= 127, at most
                 // 128 groups a sub-chunk: <= 512 * 32767 * 255 < 2^32)
                 uint32_t vi[T::V_ACC];
@@ -1250,6 +1338,19 @@ void decode_quant_kernel(QuantParams p)
                     const float cs = (VB == 4 && (c & 1)) ? cg[g] * 0.0625f : cg[g];
                     af[h][c] = fmaf(af[h][c], fo, (float)vi[c] * cs);
                 }
+            }
+            if constexpr (MV) {
+                // the lane's head l / 16; 256 hi + lo = sum of w_int (code
+                // + 8), exact in int32 (|hi| sums <= 512 * 127 * 15)
+                const int hl = lane >> 4;
+                float fol = fo_h[0], csl = cs_h[0];
+#pragma unroll
+                for (int h = 1; h < G; h++) {
+                    fol = hl == h ? fo_h[h] : fol;
+                    csl = hl == h ? cs_h[h] : csl;
+                }
+#pragma unroll
+                for (int t = 0; t < 8; t++) afm[t] = fmaf(afm[t], fol, (float)(vacc[t][1] * 256 + vacc[t][0]) * csl);
             }
         }
     }
@@ -1276,6 +1377,11 @@ void decode_quant_kernel(QuantParams p)
 #pragma unroll
             for (int h = 0; h < G; h++) {
                 const float ob = wave_sum_u(bsum[g][h]);
+                if constexpr (MV) {
+#pragma unroll
+                    for (int t = 0; t < 8; t++) afm[t] -= (lane >> 4) == h ? ob : 0.0f;
+                    continue;
+                }
 #pragma unroll
                 for (int c = 0; c < T::V_ACC; c++)
                     if ((qsl * T::V_ACC + c) / (HD / KG) == g) af[h][c] -= ob;
@@ -1284,7 +1390,11 @@ void decode_quant_kernel(QuantParams p)
     __syncthreads();                                 // every wave is done with scores and weights
     float *pm = misc;                                // [QD_WAVES][G] wave maxima (log2 units)
     float *pl = pm + QD_WAVES * G;                   // [QD_WAVES][G] wave sums of p
-    if (gi == 0) {
+    if constexpr (MV) {
+#pragma unroll
+        for (int t = 0; t < 8; t++)
+            red[(wave * G + (lane >> 4)) * HD + 64 * (t >> 2) + 4 * (lane & 15) + (t & 3)] = afm[t];
+    } else if (gi == 0) {
 #pragma unroll
         for (int c = 0; c < T::V_ACC; c++)
 #pragma unroll

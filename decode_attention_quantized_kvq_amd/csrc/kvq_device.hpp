@@ -104,9 +104,10 @@ __device__ __forceinline__ uint4 bld_u4(rsrc_t r, uint32_t off)
     const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CP);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+template <int CP = 0>
 __device__ __forceinline__ uint2 bld_u2(rsrc_t r, uint32_t off)
 {
-    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, CP);
     return make_uint2(v.x, v.y);
 }
 template <int CP = 0>
