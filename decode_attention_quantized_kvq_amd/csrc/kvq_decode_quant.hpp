@@ -27,17 +27,20 @@
 //    positions at once against value codes stored four positions
 //    interleaved and offset binary (code + 8 or code + 128, never negative);
 //    the offset's share, bias * sum(w), is subtracted once at the end.
-// Four query heads at head_dim 128 with one key scale per position and head
-// score their keys on the matrix cores instead (the integer dots above would
-// take 4 VALU instructions per position for the keys alone, and the VALU is
-// this kernel's busiest unit): per 16 positions two v_mfma_i32_16x16x64_i8
-// multiply a 16 x 64 operand holding each head's two base-256 digits of
-// q_int and its extra low digit with 64 channels of the 16 positions (int4
-// codes unpacked to bytes 16 code, int8 codes as stored), which gives the
-// same exact integer sums; the VALU only unpacks nibbles and scales.
+// Four query heads at head_dim 128 (the symmetric codec) score their keys
+// on the matrix cores instead (the integer dots above would take 4 VALU
+// instructions per position for the keys alone, and the VALU was this
+// kernel's busiest unit): per 16 positions two v_mfma_i32_16x16x64_i8 (four
+// with four scale groups) multiply a 16 x 64 operand holding each head's two
+// base-256 digits of q_int and its extra low digit with 64 channels of the
+// 16 positions (int4 codes unpacked to bytes 16 code, int8 codes as
+// stored), which gives the same exact integer sums; the VALU only unpacks
+// nibbles and scales.  With int4 keys and values and one scale per head the
+// value sums run there too: the weights as two signed bytes (w_int <=
+// 32639), 8 products per 64 positions against the unpacked value nibbles.
 // Rounding happens only in the query's digits and in w_int
-// (|dw| <= N / 65534, relative to the sub-chunk's own largest weight
-// whatever the spread of the value scales or of the softmax);
+// (|dw| <= N / 65534, or N / 65278, relative to the sub-chunk's own largest
+// weight whatever the spread of the value scales or of the softmax);
 // accumulation is exact in int32, then fp32.
 //
 // Workgroup = 4 waves = one context chunk of one (sequence, KV head); each
