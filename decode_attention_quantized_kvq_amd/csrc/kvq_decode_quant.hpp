@@ -102,12 +102,12 @@ __host__ __device__ constexpr int qx_base(int KB) { return KB == 4 ? 14 : 254; }
 // [QS_GROUPS][G] for q_int and [QS_GROUPS][G] for the extra low digit
 constexpr int QS_GROUPS = 4;
 __host__ __device__ constexpr int qd_digits(int KB, int HD, int G) { return ((KB == 4 ? 4 : 2) + 1) * (HD * KB / 32) * G; }
-// Four query heads at head_dim 128 score their keys on the matrix cores
-// (v_mfma_i32_16x16x64_i8): the sixteen rows of the product are the four
-// heads' low and high base-256 digits of q_int, their extra low digits and
-// a zero row.  The digit block then also holds that operand, one byte per
+// Four or eight query heads at head_dim 128 score their keys on the matrix
+// cores (v_mfma_i32_16x16x64_i8): the sixteen rows of the product are the
+// four heads' low and high base-256 digits of q_int, their extra low digits
+// and a zero row, or the eight heads' low and high digits.  The digit block then also holds that operand, one byte per
 // digit, head and channel ([3][G][HD]).
-__host__ __device__ constexpr bool qd_mfma(int HD, int G) { return G == 4 && HD == 128; }
+__host__ __device__ constexpr bool qd_mfma(int HD, int G) { return (G == 4 || G == 8) && HD == 128; }
 __host__ __device__ constexpr int qd_mf(int KB, int HD, int G) { return qd_digits(KB, HD, G) + 2 * QS_GROUPS * G; }
 __host__ __device__ constexpr int qd_mf_words(int HD, int G) { return qd_mfma(HD, G) ? 3 * G * HD / 4 : 0; }
 __host__ __device__ constexpr int qd_stride(int KB, int HD, int G)
@@ -415,10 +415,11 @@ __device__ __forceinline__ void pack_w(uint32_t w0, uint32_t w1, uint32_t w2, ui
 // head_dim, or one scale per position shared by all heads; 2 or 4: groups of
 // head_dim / KG channels); key dots are summed per group.
 // Instances whose key scores run on the matrix cores: four query heads at
-// head_dim 128 with the symmetric codec (1, 2 or 4 scale groups per head).
+// head_dim 128 with the symmetric codec (1, 2 or 4 scale groups per head),
+// and eight with one scale group.
 __host__ __device__ constexpr bool qd_mf_keys(int KB, int VB, int HD, int G, int KG, bool zp)
 {
-    return qd_mfma(HD, G) && !zp && (KG < 4 || (KB == 4 && VB == 4));
+    return qd_mfma(HD, G) && !zp && (KG < 4 || (KB == 4 && VB == 4)) && (G == 4 || KG == 1);
 }
 // waves per SIMD the register allocation must allow: the int4 key and value
 // instances with G x KG <= 4 scoring keys on the VALU fit 128 VGPRs (4 waves)
@@ -428,7 +429,7 @@ __host__ __device__ constexpr bool qd_mf_keys(int KB, int VB, int HD, int G, int
 // at 128 with spills than at 3 waves (212 against 177 us at 32K)
 __host__ __device__ constexpr int qd_min_waves(int KB, int VB, int HD, int G, int KG, bool paged, bool zp)
 {
-    return qd_mf_keys(KB, VB, HD, G, KG, zp) ? 3 : KB == 4 && VB == 4 && G * KG <= 4 && !zp ? 4 : 1;
+    return qd_mf_keys(KB, VB, HD, G, KG, zp) ? (G == 8 ? 1 : 3) : KB == 4 && VB == 4 && G * KG <= 4 && !zp ? 4 : 1;
 }
 
 // ZP: the zero-point codec (32-bit scale words: fp16 scale | zero << 16;
@@ -440,10 +441,11 @@ void decode_quant_kernel(QuantParams p)
     using T = QT<KB, VB, HD, G>;
     constexpr int S = qd_sub(G, KG, ZP);
     constexpr bool MF = qd_mf_keys(KB, VB, HD, G, KG, ZP);   // key scores on the matrix cores
-    // value sums on the matrix cores too (int4 keys and values, one scale
-    // group): the weights become two signed bytes, a low one in [-128, 127]
-    // and a high one in [0, 127], so their fixed-point range is 32639
-    constexpr bool MV = MF && KB == 4 && VB == 4 && KG == 1;
+    // value sums on the matrix cores too (four heads, int4 keys and values,
+    // one scale group): the weights become two signed bytes, a low one in
+    // [-128, 127] and a high one in [0, 127], so their fixed-point range is
+    // 32639
+    constexpr bool MV = MF && G == 4 && KB == 4 && VB == 4 && KG == 1;
     constexpr int WR = MV ? 32639 : W_RANGE;
     extern __shared__ __align__(16) unsigned char smem[];
 
@@ -674,7 +676,7 @@ void decode_quant_kernel(QuantParams p)
         }
     };
     float mloc[G];                                   // per-lane score maxima of the current sub-chunk
-    float mown = -INFINITY;                          // (matrix cores) the same for the lane's own head, lane / 16
+    float mown[2] = {-INFINITY, -INFINITY};          // (matrix cores) the same for the lane's own head(s)
     // The matrix-core query operands, one per row set and MFMA m = 0, 1 of a
     // 16-position block (m: int4 keys, even / odd channels; int8 keys,
     // slices 0-3 / 4-7).  Lane l supplies row l % 16 of A over k-block
@@ -685,26 +687,29 @@ void decode_quant_kernel(QuantParams p)
     //   2 or 4 groups: sets P = 0 .. KG / 2 - 1, i = 2 p + d for digit d
     //   (low, high) of group 2 P + p, the A bytes zero in k-blocks of other
     //   groups; then the extra digit's set, i = the group.
+    // Eight heads (one scale group): rows 2 h + d, digit d (low, high) of
+    // head h, so lane l holds heads 2 (l / 16) and + 1; then the extra
+    // digit's set, rows 2 h.
     // A set whose every k-block of some m lies outside its groups skips that
     // MFMA (int8 keys with 4 groups: each set sees one m).
     constexpr int MF_NP = KG == 1 ? 1 : KG / 2;      // sets of low and high digits
-    constexpr int MF_NS = KG == 1 ? 1 : MF_NP + 1;   // + the extra digit's set
+    constexpr int MF_NS = KG == 1 && G == 4 ? 1 : MF_NP + 1;   // + the extra digit's set
     auto mf_grp = [](int m, int L) { return KB == 4 ? L * KG / 4 : (4 * m + L) * KG / 8; };
     auto mf_live = [&](int P, int m) {
         bool any = false;
         for (int L = 0; L < 4; L++) any |= KG == 1 || mf_grp(m, L) / 2 == P;
         return any;
     };
-    // (the extra digit's set of 2 or 4 groups is loaded per block, and only
-    // when the query carries that digit: held throughout, its registers
-    // would cost a wave per SIMD)
+    // (the extra digit's set of 2 or 4 groups or 8 heads is loaded per
+    // block, and only when the query carries that digit: held throughout,
+    // its registers would cost a wave per SIMD)
     i32x4_t mfa[MF_NP][2];
 #pragma unroll
     for (int st = 0; st < MF_NP; st++) mfa[st][0] = mfa[st][1] = i32x4_t{0, 0, 0, 0};
-    const uint8_t *mfq = nullptr;                    // this lane's extra-digit bytes (2 or 4 groups)
+    const uint8_t *mfq = nullptr;                    // this lane's extra-digit bytes (2 or 4 groups, 8 heads)
     if constexpr (MF) {
         const uint8_t *qm = reinterpret_cast<const uint8_t *>(p.qdig + qslot * qd_stride(KB, HD, G) + qd_mf(KB, HD, G));
-        const int r = lane & 15, hh = r >> 2, i = r & 3, L = lane >> 4;
+        const int r = lane & 15, hh = G == 8 ? r >> 1 : r >> 2, i = r & 3, L = lane >> 4;
         auto digits = [&](int d, int m) {            // 16 bytes of digit plane d, head hh, k-block (m, L)
             const uint4 a = ld_u4(qm + (d * G + hh) * HD + (KB == 4 ? 32 * L + 16 * m : 16 * (4 * m + L)));
             return i32x4_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
@@ -712,7 +717,9 @@ void decode_quant_kernel(QuantParams p)
         mfq = qm + (2 * G + hh) * HD + (KB == 4 ? 32 * L : 16 * L);
 #pragma unroll
         for (int m = 0; m < 2; m++) {
-            if constexpr (KG == 1) {
+            if constexpr (G == 8) {
+                mfa[0][m] = digits(r & 1, m);
+            } else if constexpr (KG == 1) {
                 if (i < 3) mfa[0][m] = digits(i, m);
             } else {
                 const int grp = mf_grp(m, L);
@@ -763,13 +770,14 @@ void decode_quant_kernel(QuantParams p)
                     for (int m = 0; m < 2; m++)
                         if (mf_live(st, m)) acc[st] = mfma_i8(mfa[st][m], bk[m], acc[st]);
                 }
-                if (KG > 1 && xq) {
-                    // rows 4 h + g: the extra digit of group g, zero in other groups' k-blocks
+                if ((KG > 1 || G == 8) && xq) {
+                    // rows 4 h + g: the extra digit of group g, zero in other
+                    // groups' k-blocks (eight heads: rows 2 h)
                     acc[MF_NS - 1] = i32x4_t{0, 0, 0, 0};
 #pragma unroll
                     for (int m = 0; m < 2; m++) {
                         const uint4 a = ld_u4(mfq + (KB == 4 ? 16 * m : 64 * m));
-                        const bool on = mf_grp(m, lane >> 4) == (lane & 3);
+                        const bool on = G == 8 ? (lane & 1) == 0 : mf_grp(m, lane >> 4) == (lane & 3);
                         const i32x4_t ax = i32x4_t{on ? (int)a.x : 0, on ? (int)a.y : 0, on ? (int)a.z : 0,
                                                    on ? (int)a.w : 0};
                         acc[MF_NS - 1] = mfma_i8(ax, bk[m], acc[MF_NS - 1]);
@@ -780,6 +788,21 @@ void decode_quant_kernel(QuantParams p)
                 uint32_t ksw[SW];
 #pragma unroll
                 for (int w = 0; w < SW; w++) ksw[w] = (uint32_t)__builtin_amdgcn_ds_bpermute(pos * 4, (int)c.ks[w]);
+                if constexpr (G == 8) {
+                    // heads 2 hq and 2 hq + 1: rows 4 hq .. + 3 = their low and high sums
+                    const float sk = f16_bits_to_f32((uint16_t)sc_of(ksw, 0)) * KSI;
+                    float z2[2];
+#pragma unroll
+                    for (int e = 0; e < 2; e++) {
+                        float z = (float)(acc[0][2 * e + 1] * 256 + acc[0][2 * e]) * sk;
+                        if (xq) z = fmaf((float)acc[1][2 * e], sk * XINV, z);
+                        z2[e] = tb + pos < nw ? z : -INFINITY;
+                        mown[e] = fmax_nc(mown[e], z2[e]);
+                    }
+                    *reinterpret_cast<float2 *>(zs + (size_t)(tb + pos - sc0) * G + 2 * hq) = make_float2(z2[0], z2[1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    continue;
+                }
                 float z = 0.0f;
 #pragma unroll
                 for (int g = 0; g < KG; g++) {
@@ -790,7 +813,7 @@ void decode_quant_kernel(QuantParams p)
                     if (xq) z = fmaf((float)(KG == 1 ? acc[0][2] : acc[MF_NS - 1][g]), sk * XINV, z);
                 }
                 z = tb + pos < nw ? z : -INFINITY;   // past the wave's range: -inf
-                mown = fmax_nc(mown, z);
+                mown[0] = fmax_nc(mown[0], z);
                 zs[(size_t)(tb + pos - sc0) * G + hq] = z;
                 // (blocks in order: a block's operands are dead before the
                 // next block's are made)
@@ -1033,7 +1056,7 @@ void decode_quant_kernel(QuantParams p)
         // ---------------- pass 1: scores of the sub-chunk ----------------------
 #pragma unroll
         for (int h = 0; h < G; h++) mloc[h] = -INFINITY;
-        mown = -INFINITY;
+        mown[0] = mown[1] = -INFINITY;
         // (tiles run in pairs, both halves unconditionally: a half past the
         // end sees only invalid lanes and zero rows, and the code stays free
         // of a merge point that would send the two register sets through
@@ -1059,11 +1082,16 @@ void decode_quant_kernel(QuantParams p)
         compute(tb + 64, sc0, tb_);
         float ms[G];                                 // sub-chunk score maxima, wave-uniform
         if constexpr (MF) {
-            // lanes 16 h .. 16 h + 15 hold head h
-            const float mr = row_max_u(mown);
+            // lanes 16 h .. 16 h + 15 hold head h (eight heads: heads 2 h
+            // and 2 h + 1, in mown[0] and mown[1])
+            const float mr0 = row_max_u(mown[0]);
+            const float mr1 = G == 8 ? row_max_u(mown[1]) : mr0;
 #pragma unroll
-            for (int h = 0; h < G; h++)
-                ms[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mr), 16 * h));
+            for (int h = 0; h < G; h++) {
+                const float mr = G == 8 && (h & 1) ? mr1 : mr0;
+                ms[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mr),
+                                                                            16 * (G == 8 ? h >> 1 : h)));
+            }
         } else {
 #pragma unroll
             for (int h = 0; h < G; h++) ms[h] = wave_max_u(mloc[h]);

@@ -507,7 +507,7 @@ def test_split_head_workspace(kvq):
     a256 = lambda x: (x + 255) // 256 * 256
 
     def stride(G):                                   # int32 words of one unit's digits (int4 keys, HD 128)
-        mf = 3 * G * 128 // 4 if G == 4 else 0       # the matrix-core operand of four heads
+        mf = 3 * G * 128 // 4 if G in (4, 8) else 0  # the matrix-core operand of four or eight heads
         return -(-(5 * 16 * G + 2 * 4 * G + mf) // 64) * 64
 
     def expect(B, Hkv, Hq, C, units, G):
