@@ -27,17 +27,18 @@
 //    positions at once against value codes stored four positions
 //    interleaved and offset binary (code + 8 or code + 128, never negative);
 //    the offset's share, bias * sum(w), is subtracted once at the end.
-// Four query heads at head_dim 128 (the symmetric codec) score their keys
-// on the matrix cores instead (the integer dots above would take 4 VALU
-// instructions per position for the keys alone, and the VALU was this
-// kernel's busiest unit): per 16 positions two v_mfma_i32_16x16x64_i8 (four
-// with four scale groups) multiply a 16 x 64 operand holding each head's two
-// base-256 digits of q_int and its extra low digit with 64 channels of the
-// 16 positions (int4 codes unpacked to bytes 16 code, int8 codes as
-// stored), which gives the same exact integer sums; the VALU only unpacks
-// nibbles and scales.  With int4 keys and values and one scale per head the
-// value sums run there too: the weights as two signed bytes (w_int <=
-// 32639), 8 products per 64 positions against the unpacked value nibbles.
+// Four or eight query heads at head_dim 128 (the symmetric codec) score
+// their keys on the matrix cores instead (the integer dots above take 4 VALU
+// instructions per position for the keys alone at G = 4, and the VALU was
+// this kernel's busiest unit): per 16 positions two v_mfma_i32_16x16x64_i8
+// (four with four scale groups) multiply a 16 x 64 operand holding the
+// heads' two base-256 digits of q_int (and, for four heads, the extra low
+// digit) with 64 channels of the 16 positions (int4 codes unpacked to bytes
+// 16 code, int8 codes as stored), which gives the same exact integer sums;
+// the VALU only unpacks nibbles and scales.  With four heads, int4 keys and
+// values and one scale per head the value sums run there too: the weights
+// as two signed bytes (w_int <= 32639), 8 products per 64 positions against
+// the unpacked value nibbles.
 // Rounding happens only in the query's digits and in w_int
 // (|dw| <= N / 65534, or N / 65278, relative to the sub-chunk's own largest
 // weight whatever the spread of the value scales or of the softmax);
@@ -105,8 +106,9 @@ __host__ __device__ constexpr int qd_digits(int KB, int HD, int G) { return ((KB
 // Four or eight query heads at head_dim 128 score their keys on the matrix
 // cores (v_mfma_i32_16x16x64_i8): the sixteen rows of the product are the
 // four heads' low and high base-256 digits of q_int, their extra low digits
-// and a zero row, or the eight heads' low and high digits.  The digit block then also holds that operand, one byte per
-// digit, head and channel ([3][G][HD]).
+// and a zero row, or the eight heads' low and high digits.  The digit block
+// then also holds that operand, one byte per digit, head and channel
+// ([3][G][HD]).
 __host__ __device__ constexpr bool qd_mfma(int HD, int G) { return (G == 4 || G == 8) && HD == 128; }
 __host__ __device__ constexpr int qd_mf(int KB, int HD, int G) { return qd_digits(KB, HD, G) + 2 * QS_GROUPS * G; }
 __host__ __device__ constexpr int qd_mf_words(int HD, int G) { return qd_mfma(HD, G) ? 3 * G * HD / 4 : 0; }
@@ -424,9 +426,10 @@ __host__ __device__ constexpr bool qd_mf_keys(int KB, int VB, int HD, int G, int
 // waves per SIMD the register allocation must allow: the int4 key and value
 // instances with G x KG <= 4 scoring keys on the VALU fit 128 VGPRs (4 waves)
 // when asked to (left alone the compiler takes a few more and drops to 3);
-// the others take what they need: the zero-point instances would spill at
-// 128, and the matrix-core ones (143 VGPRs for K4V4, 3 waves) ran 8 % slower
-// at 128 with spills than at 3 waves (212 against 177 us at 32K)
+// the four-head matrix-core ones are held to 3 (K4V4: 167 VGPRs; with keys
+// only on the matrix cores, held to 128 it spilled and ran 212 against 177
+// us at 32K); the others take what they need: the zero-point instances would
+// spill at 128, the eight-head matrix-core ones at 168
 __host__ __device__ constexpr int qd_min_waves(int KB, int VB, int HD, int G, int KG, bool paged, bool zp)
 {
     return qd_mf_keys(KB, VB, HD, G, KG, zp) ? (G == 8 ? 1 : 3) : KB == 4 && VB == 4 && G * KG <= 4 && !zp ? 4 : 1;
