@@ -202,6 +202,19 @@ def test_query_outlier_channel(oq, kb, vb, group, factor):
     _run(oq, kb, vb, group, K, V, q, 1.0 / np.sqrt(c["HD"]), fused=True, codes=False)
 
 
+@pytest.mark.parametrize("kb,vb", PAIRS)
+@pytest.mark.parametrize("group", GROUPS)
+@pytest.mark.parametrize("factor", [4.0, 100.0])
+def test_query_outlier_channel_eight_heads(oq, kb, vb, group, factor):
+    """The same with eight query heads per KV head: with one scale per head
+    they are one unit of eight (the extra digit a product of its own on the
+    matrix cores), with 32-value groups two workgroup heads of four."""
+    K, V, q = _base(2, 2, 8, 600, 128, 660 + kb + vb + group + int(factor))
+    q[:, :, 5] *= np.float32(factor)
+    _run(oq, kb, vb, group, K, V, q, 1.0 / np.sqrt(128), chunk=2048)
+    _run(oq, kb, vb, group, K, V, q, 1.0 / np.sqrt(128), fused=True, codes=False)
+
+
 LONG = dict(B=1, H=2, G=4, n_pos=32768, HD=128)
 
 
