@@ -444,11 +444,11 @@ void decode_quant_kernel(QuantParams p)
     using T = QT<KB, VB, HD, G>;
     constexpr int S = qd_sub(G, KG, ZP);
     constexpr bool MF = qd_mf_keys(KB, VB, HD, G, KG, ZP);   // key scores on the matrix cores
-    // value sums on the matrix cores too (four heads, int4 keys and values,
-    // one scale group): the weights become two signed bytes, a low one in
-    // [-128, 127] and a high one in [0, 127], so their fixed-point range is
-    // 32639
-    constexpr bool MV = MF && G == 4 && KB == 4 && VB == 4 && KG == 1;
+    // value sums on the matrix cores too (int4 keys and values, one scale
+    // group): the weights become two signed bytes, a low one in [-128, 127]
+    // and a high one in [0, 127], so their fixed-point range is 32639
+    constexpr bool MV = MF && KB == 4 && VB == 4 && KG == 1;
+    constexpr int NHL = G / 4;                       // (MV) heads per lane in the products
     constexpr int WR = MV ? 32639 : W_RANGE;
     extern __shared__ __align__(16) unsigned char smem[];
 
@@ -1010,13 +1010,14 @@ void decode_quant_kernel(QuantParams p)
     // ---- values on the matrix cores (MV): per 64-position block of the
     // sub-chunk, 8 products D += A B over 16 channels each.  A: lane l holds
     // row l % 16 = 4 h + b (b = 0, 1: head h's signed low and high weight
-    // bytes; b = 2, 3 zero) over the block's groups 4 (l / 16) .. + 3 (16
-    // positions, the block's weight words in LDS).  B: column n = l % 16 of
+    // bytes; b = 2, 3 zero; eight heads: row 2 h + b) over the block's groups
+    // 4 (l / 16) .. + 3 (16 positions, the block's weight words in LDS).  B: column n = l % 16 of
     // product 4 t + q holds channel 64 t + 4 n + q of those 16 positions, the
     // stored nibbles (code + 8) as bytes; lane l loads bytes 32 t + 2 n and
     // + 1 of its four groups, one 8-byte load per group and t (16 lanes read
     // 128 contiguous bytes).  D: lane l holds head l / 16's two sums for
-    // channel 64 t + 4 (l % 16) + q.
+    // channel 64 t + 4 (l % 16) + q (eight heads: heads 2 (l / 16) + e, e =
+    // 0, 1, in elements 2 e and 2 e + 1).
     uint32_t vx[8][2];                               // the next block's value words, [t][group][byte]
     auto vload_mv = [&](int gb) {                    // gb: the block's first group (within the wave)
         const int u = unit_of(4 * gb);
@@ -1035,7 +1036,7 @@ void decode_quant_kernel(QuantParams p)
             }
     };
     i32x4_t vacc[8];
-    float afm[8];                                    // (MV) the lane's channels 64 t + 4 n + q of head l / 16
+    float afm[NHL > 0 ? NHL : 1][8];                  // (MV) the lane's channels 64 t + 4 n + q of its head(s)
 
     // ---- the wave's running result: max M (unscaled score units), per-lane
     // partial sum of p, and the lane's output channels, all relative to M
@@ -1050,7 +1051,7 @@ void decode_quant_kernel(QuantParams p)
         for (int c = 0; c < T::V_ACC; c++) af[h][c] = 0.0f;
     }
 #pragma unroll
-    for (int t = 0; t < 8; t++) afm[t] = 0.0f;
+    for (int t = 0; t < 8; t++) afm[0][t] = afm[NHL > 1 ? 1 : 0][t] = 0.0f;
 
     Tile ta, tb_;
     load(0, ta);
@@ -1277,8 +1278,9 @@ void decode_quant_kernel(QuantParams p)
                 // the block's weight bytes (rows with b >= 2: zero); groups
                 // past the sub-chunk's positions meet zero value bytes
                 i32x4_t a = {0, 0, 0, 0};
-                if ((r & 3) < 2) {
-                    const uint4 w = *reinterpret_cast<const uint4 *>(wdw + (size_t)((bb * G + (r >> 2)) * 2 + (r & 3)) * 16 + 4 * L);
+                const int ha = G == 8 ? r >> 1 : r >> 2, ba = G == 8 ? r & 1 : r & 3;
+                if (ba < 2) {
+                    const uint4 w = *reinterpret_cast<const uint4 *>(wdw + (size_t)((bb * G + ha) * 2 + ba) * 16 + 4 * L);
                     a = i32x4_t{(int)w.x, (int)w.y, (int)w.z, (int)w.w};
                 }
 #pragma unroll
@@ -1374,17 +1376,21 @@ void decode_quant_kernel(QuantParams p)
                 }
             }
             if constexpr (MV) {
-                // the lane's head l / 16; 256 hi + lo = sum of w_int (code
-                // + 8), exact in int32 (|hi| sums <= 512 * 127 * 15)
-                const int hl = lane >> 4;
-                float fol = fo_h[0], csl = cs_h[0];
+                // the lane's head(s) NHL (l / 16) + e; 256 hi + lo = sum of
+                // w_int (code + 8), exact in int32 (|hi| sums <= 512 * 127 * 15)
 #pragma unroll
-                for (int h = 1; h < G; h++) {
-                    fol = hl == h ? fo_h[h] : fol;
-                    csl = hl == h ? cs_h[h] : csl;
+                for (int e = 0; e < NHL; e++) {
+                    const int hl = NHL * (lane >> 4) + e;
+                    float fol = fo_h[0], csl = cs_h[0];
+#pragma unroll
+                    for (int h = 1; h < G; h++) {
+                        fol = hl == h ? fo_h[h] : fol;
+                        csl = hl == h ? cs_h[h] : csl;
+                    }
+#pragma unroll
+                    for (int t = 0; t < 8; t++)
+                        afm[e][t] = fmaf(afm[e][t], fol, (float)(vacc[t][2 * e + 1] * 256 + vacc[t][2 * e]) * csl);
                 }
-#pragma unroll
-                for (int t = 0; t < 8; t++) afm[t] = fmaf(afm[t], fol, (float)(vacc[t][1] * 256 + vacc[t][0]) * csl);
             }
         }
     }
@@ -1413,7 +1419,9 @@ void decode_quant_kernel(QuantParams p)
                 const float ob = wave_sum_u(bsum[g][h]);
                 if constexpr (MV) {
 #pragma unroll
-                    for (int t = 0; t < 8; t++) afm[t] -= (lane >> 4) == h ? ob : 0.0f;
+                    for (int e = 0; e < NHL; e++)
+#pragma unroll
+                        for (int t = 0; t < 8; t++) afm[e][t] -= NHL * (lane >> 4) + e == h ? ob : 0.0f;
                     continue;
                 }
 #pragma unroll
@@ -1426,8 +1434,10 @@ void decode_quant_kernel(QuantParams p)
     float *pl = pm + QD_WAVES * G;                   // [QD_WAVES][G] wave sums of p
     if constexpr (MV) {
 #pragma unroll
-        for (int t = 0; t < 8; t++)
-            red[(wave * G + (lane >> 4)) * HD + 64 * (t >> 2) + 4 * (lane & 15) + (t & 3)] = afm[t];
+        for (int e = 0; e < NHL; e++)
+#pragma unroll
+            for (int t = 0; t < 8; t++)
+                red[(wave * G + NHL * (lane >> 4) + e) * HD + 64 * (t >> 2) + 4 * (lane & 15) + (t & 3)] = afm[e][t];
     } else if (gi == 0) {
 #pragma unroll
         for (int c = 0; c < T::V_ACC; c++)
