@@ -35,10 +35,10 @@
 // heads' two base-256 digits of q_int (and, for four heads, the extra low
 // digit) with 64 channels of the 16 positions (int4 codes unpacked to bytes
 // 16 code, int8 codes as stored), which gives the same exact integer sums;
-// the VALU only unpacks nibbles and scales.  With four heads, int4 keys and
-// values and one scale per head the value sums run there too: the weights
-// as two signed bytes (w_int <= 32639), 8 products per 64 positions against
-// the unpacked value nibbles.
+// the VALU only unpacks nibbles and scales.  With int4 keys and values and
+// one scale per head the value sums run there too: the weights as two
+// signed bytes (w_int <= 32639), 8 products per 64 positions against the
+// unpacked value nibbles.
 // Rounding happens only in the query's digits and in w_int
 // (|dw| <= N / 65534, or N / 65278, relative to the sub-chunk's own largest
 // weight whatever the spread of the value scales or of the softmax);
