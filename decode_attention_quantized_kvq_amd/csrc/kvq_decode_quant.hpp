@@ -429,7 +429,7 @@ __host__ __device__ constexpr bool qd_mf_keys(int KB, int VB, int HD, int G, int
 // the four-head matrix-core ones are held to 3 (K4V4: 167 VGPRs; with keys
 // only on the matrix cores, held to 128 it spilled and ran 212 against 177
 // us at 32K); the others take what they need: the zero-point instances would
-// spill at 128, the eight-head matrix-core ones at 168 (37 registers)
+// spill at 128, the eight-head matrix-core ones at 168 (32-37 registers)
 __host__ __device__ constexpr int qd_min_waves(int KB, int VB, int HD, int G, int KG, bool paged, bool zp)
 {
     return qd_mf_keys(KB, VB, HD, G, KG, zp) ? (G == 8 ? 1 : 3) : KB == 4 && VB == 4 && G * KG <= 4 && !zp ? 4 : 1;
